@@ -1,0 +1,666 @@
+/*
+ * qs_oracle.c -- CPU oracle for the quantized recurrent-state decode step.
+ *
+ * TEST INFRASTRUCTURE ONLY (see qs_oracle.h).  Plain scalar C; every
+ * function follows one stated passage and is written for reading, not speed.
+ *
+ * Logical state per (b,h): S[v][k], v the value index (a "value column" of
+ * the pages' S, i.e. one output channel), k the key index.  One row v is one
+ * value-axis scale group.
+ */
+#include "qs_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------ */
+/* Philox4x32-10 (Salmon et al., SC'11, the Philox family section): a       */
+/* counter-based generator.  One round multiplies counter words 0 and 2 by  */
+/* the two Philox multipliers, keeps both halves of the 64-bit products and */
+/* mixes the high halves with the other two counter words and the key; the  */
+/* key is bumped by the two Weyl constants between rounds.                  */
+/* ------------------------------------------------------------------------ */
+#define PHILOX_MUL0 0xD2511F53u
+#define PHILOX_MUL1 0xCD9E8D57u
+#define PHILOX_WEYL0 0x9E3779B9u
+#define PHILOX_WEYL1 0xBB67AE85u
+
+void orc_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+  uint32_t x0 = ctr[0], x1 = ctr[1], x2 = ctr[2], x3 = ctr[3];
+  uint32_t k0 = key[0], k1 = key[1];
+  for (int round = 0; round < 10; ++round) {
+    if (round > 0) {
+      k0 += PHILOX_WEYL0;
+      k1 += PHILOX_WEYL1;
+    }
+    uint64_t p0 = (uint64_t)PHILOX_MUL0 * (uint64_t)x0;
+    uint64_t p1 = (uint64_t)PHILOX_MUL1 * (uint64_t)x2;
+    uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+    uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
+    uint32_t y0 = hi1 ^ x1 ^ k0;
+    uint32_t y1 = lo1;
+    uint32_t y2 = hi0 ^ x3 ^ k1;
+    uint32_t y3 = lo0;
+    x0 = y0; x1 = y1; x2 = y2; x3 = y3;
+  }
+  out[0] = x0; out[1] = x1; out[2] = x2; out[3] = x3;
+}
+
+/* Random integer for logical element e at decode step `step`.
+ * Key = seed; counter = (element group as 64 bits, step as 64 bits).
+ * 16-bit mode: 8 elements per Philox block, element e takes the low half of
+ * word (e>>1)&3 when e is even, the high half when odd.
+ * 8-bit mode: 16 elements per block, byte e&3 of word (e>>2)&3. */
+uint32_t orc_random_bits(const orc_cfg* c, uint64_t e, uint64_t step) {
+  uint32_t key[2] = {(uint32_t)c->seed, (uint32_t)(c->seed >> 32)};
+  uint64_t grp = (c->sr_bits == 16) ? (e >> 3) : (e >> 4);
+  uint32_t ctr[4] = {(uint32_t)grp, (uint32_t)(grp >> 32), (uint32_t)step,
+                     (uint32_t)(step >> 32)};
+  uint32_t out[4];
+  orc_philox4x32_10(ctr, key, out);
+  if (c->sr_bits == 16) {
+    uint32_t w = out[(e >> 1) & 3];
+    return (e & 1) ? (w >> 16) : (w & 0xFFFFu);
+  }
+  uint32_t w = out[(e >> 2) & 3];
+  return (w >> (8 * (e & 3))) & 0xFFu;
+}
+
+/* Stochastic rounding of x with an sr_bits-bit uniform integer u:
+ * floor(x) plus one when u < frac(x) * 2^sr_bits.  frac(x) = x - floor(x)
+ * and the scaling by 2^sr_bits are exact, so the decision is exact. */
+float orc_sr_round(float x, uint32_t u, int32_t sr_bits) {
+  float f = floorf(x);
+  float r = x - f;
+  float scale = (sr_bits == 16) ? 65536.0f : 256.0f;
+  return ((float)u < r * scale) ? f + 1.0f : f;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Round-to-nearest-even into a binary format with `mbits` fraction bits and */
+/* `ebits` exponent bits (IEEE-style bias, subnormals, infinities).  Written */
+/* from the format's definition with exact fp64 scaling; used for bf16      */
+/* (8,7) and fp16 (5,10) storage of protected units.                        */
+/* ------------------------------------------------------------------------ */
+static uint32_t rne_encode(float f, int ebits, int mbits) {
+  const uint32_t sign = signbit(f) ? 1u : 0u;
+  const int bias = (1 << (ebits - 1)) - 1;
+  const int emin = 1 - bias, emax = bias;
+  const uint32_t eall = (1u << ebits) - 1u;
+  const uint32_t sbit = sign << (ebits + mbits);
+  if (isnan(f)) return sbit | (eall << mbits) | (1u << (mbits - 1));
+  if (isinf(f)) return sbit | (eall << mbits);
+  double a = fabs((double)f);
+  if (a == 0.0) return sbit;
+  int e;
+  (void)frexp(a, &e);
+  e -= 1;                       /* a = m * 2^e with m in [1,2) */
+  if (e < emin) e = emin;       /* subnormal range: fixed exponent */
+  double q = rint(ldexp(a, mbits - e));   /* units in the last place */
+  if (q >= ldexp(1.0, mbits + 1)) {       /* rounding carried into the exponent */
+    q = ldexp(q, -1);
+    e += 1;
+  }
+  if (e > emax) return sbit | (eall << mbits);
+  if (q < ldexp(1.0, mbits)) return sbit | (uint32_t)q;  /* subnormal */
+  return sbit | ((uint32_t)(e + bias) << mbits) | ((uint32_t)q - (1u << mbits));
+}
+
+static float decode_bits(uint32_t bits, int ebits, int mbits) {
+  const int bias = (1 << (ebits - 1)) - 1;
+  const uint32_t eall = (1u << ebits) - 1u;
+  uint32_t sign = (bits >> (ebits + mbits)) & 1u;
+  uint32_t ex = (bits >> mbits) & eall;
+  uint32_t man = bits & ((1u << mbits) - 1u);
+  double v;
+  if (ex == eall) v = man ? NAN : INFINITY;
+  else if (ex == 0) v = ldexp((double)man, 1 - bias - mbits);
+  else v = ldexp((double)(man | (1u << mbits)), (int)ex - bias - mbits);
+  return (float)(sign ? -v : v);
+}
+
+uint16_t orc_to_bf16(float f) { return (uint16_t)rne_encode(f, 8, 7); }
+uint16_t orc_to_fp16(float f) { return (uint16_t)rne_encode(f, 5, 10); }
+float orc_from_bf16(uint16_t h) { return decode_bits(h, 8, 7); }
+float orc_from_fp16(uint16_t h) { return decode_bits(h, 5, 10); }
+
+/* ------------------------------------------------------------------------ */
+/* Decay-based mixed precision (LoReS abstract: protect slowly decaying      */
+/* heads or channels).  Within each group of `per_group` units, flag the     */
+/* round-half-up(frac * per_group) units with the smallest decay-rate        */
+/* statistic (slowest decay); ties go to the lower index.                    */
+/* ------------------------------------------------------------------------ */
+int orc_build_map(const double* stat, int32_t groups, int32_t per_group, double frac,
+                  uint8_t* map) {
+  if (groups < 0 || per_group <= 0 || !(frac >= 0.0 && frac <= 1.0)) return -1;
+  int32_t count = (int32_t)floor(frac * per_group + 0.5);
+  for (int32_t g = 0; g < groups; ++g) {
+    const double* s = stat + (int64_t)g * per_group;
+    uint8_t* m = map + (int64_t)g * per_group;
+    for (int32_t i = 0; i < per_group; ++i) {
+      /* rank of unit i = number of units that come before it in the order
+       * (smaller statistic, or equal statistic and lower index) */
+      int32_t rank = 0;
+      for (int32_t j = 0; j < per_group; ++j)
+        if (s[j] < s[i] || (s[j] == s[i] && j < i)) ++rank;
+      m[i] = (rank < count) ? 1 : 0;
+    }
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Storage layout (the library's documented format, written out here         */
+/* independently).  Per head h: nq(h) quantized key channels, in ascending   */
+/* k, each row taking ceil(nq*qbits/8) bytes (int4: two codes per byte, low  */
+/* nibble first); the head's code block is dv rows, padded to 16 bytes.      */
+/* Protected channels, in ascending k, form a second per-head block of dv    */
+/* rows of 16-bit (or fp32) values, also padded to 16 bytes.  Blocks of one  */
+/* batch element follow head order; batch elements follow each other.        */
+/* ------------------------------------------------------------------------ */
+static int is_quantized(const orc_cfg* c, int h, int k) {
+  if (c->map_mode == 0) return 1;
+  if (c->map_mode == 1) return c->map[h] == 0;
+  return c->map[(int64_t)h * c->dk + k] == 0;
+}
+
+static int hp_bytes(const orc_cfg* c) { return c->hp_dtype == 0 ? 4 : 2; }
+
+static uint64_t round16(uint64_t x) { return (x + 15u) & ~(uint64_t)15u; }
+
+static int check_cfg(const orc_cfg* c) {
+  if (c->kind != 0 && c->kind != 1) return -1;
+  if (c->decay_mode != 0 && c->decay_mode != 1) return -1;
+  if (c->kind == 1 && c->decay_mode != 0) return -1;
+  if (c->B < 0 || c->H <= 0 || c->dk <= 0 || c->dv <= 0) return -1;
+  if (c->qbits != 8 && c->qbits != 4) return -1;
+  if (c->hp_dtype < 0 || c->hp_dtype > 2) return -1;
+  if (c->map_mode < 0 || c->map_mode > 2) return -1;
+  if (c->map_mode != 0 && !c->map) return -1;
+  if (c->rounding != 0 && c->rounding != 1) return -1;
+  if (c->rounding == 1 && c->sr_bits != 16 && c->sr_bits != 8) return -1;
+  if (c->lrb_rank < 0) return -1;
+  if (c->lrb_rank > 0 && (c->kind != 0 || c->map_mode != 0 || c->lrb_period <= 0))
+    return -1;
+  return 0;
+}
+
+int orc_layout(const orc_cfg* c, orc_sizes* s, uint64_t* code_off, uint64_t* hp_off,
+               int32_t* nq_out) {
+  if (check_cfg(c)) return -1;
+  uint64_t coff = 0, hoff = 0;
+  for (int h = 0; h < c->H; ++h) {
+    int nq = 0;
+    for (int k = 0; k < c->dk; ++k) nq += is_quantized(c, h, k);
+    int nhp = c->dk - nq;
+    if (code_off) code_off[h] = coff;
+    if (hp_off) hp_off[h] = hoff;
+    if (nq_out) nq_out[h] = nq;
+    uint64_t row_bytes = ((uint64_t)nq * (uint64_t)c->qbits + 7u) / 8u;
+    coff += round16((uint64_t)c->dv * row_bytes);
+    hoff += round16((uint64_t)c->dv * (uint64_t)nhp * (uint64_t)hp_bytes(c));
+  }
+  uint64_t BH = (uint64_t)c->B * (uint64_t)c->H;
+  s->code_bstride = coff;
+  s->hp_bstride = hoff;
+  s->codes = (uint64_t)c->B * coff;
+  s->hp = (uint64_t)c->B * hoff;
+  s->scales = BH * (uint64_t)c->dv * 4u;
+  s->W = BH * (uint64_t)c->dv * (uint64_t)c->lrb_rank * 4u;
+  s->U = BH * (uint64_t)c->dk * (uint64_t)c->lrb_rank * 4u;
+  s->n = c->lrb_rank > 0 ? BH * 4u : 0u;
+  return 0;
+}
+
+/* Whole-config layout, computed once per call. */
+typedef struct {
+  orc_sizes s;
+  uint64_t* code_off;
+  uint64_t* hp_off;
+  int32_t* nq;
+} layout_t;
+
+static int layout_make(const orc_cfg* c, layout_t* L) {
+  L->code_off = (uint64_t*)malloc(sizeof(uint64_t) * (size_t)c->H);
+  L->hp_off = (uint64_t*)malloc(sizeof(uint64_t) * (size_t)c->H);
+  L->nq = (int32_t*)malloc(sizeof(int32_t) * (size_t)c->H);
+  return orc_layout(c, &L->s, L->code_off, L->hp_off, L->nq);
+}
+
+static void layout_free(layout_t* L) {
+  free(L->code_off);
+  free(L->hp_off);
+  free(L->nq);
+}
+
+/* Addressing of one head: its code block, its protected block, and for each
+ * key channel its slot among the quantized (>= 0) or protected (~slot) ones. */
+typedef struct {
+  uint8_t* code;
+  uint8_t* hpb;
+  uint64_t row_bytes;
+  int nq, nhp;
+  int* slot;
+} head_addr;
+
+static void head_address(const orc_cfg* c, const layout_t* L, const orc_state* st,
+                         int64_t bh, head_addr* a, int* slot_buf) {
+  int64_t b = bh / c->H;
+  int h = (int)(bh % c->H);
+  a->nq = L->nq[h];
+  a->nhp = c->dk - a->nq;
+  a->row_bytes = ((uint64_t)a->nq * (uint64_t)c->qbits + 7u) / 8u;
+  a->code = st->codes ? st->codes + (uint64_t)b * L->s.code_bstride + L->code_off[h] : NULL;
+  a->hpb = st->hp ? (uint8_t*)st->hp + (uint64_t)b * L->s.hp_bstride + L->hp_off[h] : NULL;
+  int iq = 0, ih = 0;
+  for (int k = 0; k < c->dk; ++k) slot_buf[k] = is_quantized(c, h, k) ? iq++ : ~(ih++);
+  a->slot = slot_buf;
+}
+
+static int32_t get_code(const orc_cfg* c, const head_addr* a, int v, int slot) {
+  const uint8_t* row = a->code + (uint64_t)v * a->row_bytes;
+  if (c->qbits == 8) return (int32_t)(int8_t)row[slot];
+  uint8_t byte = row[slot >> 1];
+  int32_t nib = (slot & 1) ? (byte >> 4) : (byte & 0xF);
+  return nib >= 8 ? nib - 16 : nib;   /* two's-complement nibble */
+}
+
+static void put_code(const orc_cfg* c, const head_addr* a, int v, int slot, int32_t code) {
+  uint8_t* row = a->code + (uint64_t)v * a->row_bytes;
+  if (c->qbits == 8) {
+    row[slot] = (uint8_t)(int8_t)code;
+    return;
+  }
+  uint8_t nib = (uint8_t)(code & 0xF);
+  uint8_t* byte = &row[slot >> 1];
+  if (slot & 1) *byte = (uint8_t)((*byte & 0x0F) | (nib << 4));
+  else *byte = (uint8_t)((*byte & 0xF0) | nib);
+}
+
+static float get_hp(const orc_cfg* c, const head_addr* a, int v, int hslot) {
+  uint64_t idx = (uint64_t)v * (uint64_t)a->nhp + (uint64_t)hslot;
+  if (c->hp_dtype == 0) {
+    float f;
+    memcpy(&f, a->hpb + idx * 4u, 4);
+    return f;
+  }
+  uint16_t bits;
+  memcpy(&bits, a->hpb + idx * 2u, 2);
+  return c->hp_dtype == 1 ? orc_from_bf16(bits) : orc_from_fp16(bits);
+}
+
+static void put_hp(const orc_cfg* c, const head_addr* a, int v, int hslot, float x) {
+  uint64_t idx = (uint64_t)v * (uint64_t)a->nhp + (uint64_t)hslot;
+  if (c->hp_dtype == 0) {
+    memcpy(a->hpb + idx * 4u, &x, 4);
+    return;
+  }
+  uint16_t bits = c->hp_dtype == 1 ? orc_to_bf16(x) : orc_to_fp16(x);
+  memcpy(a->hpb + idx * 2u, &bits, 2);
+}
+
+/* Dequantized value of element (v,k) of a head: scale times code for a
+ * quantized channel, the widened stored value for a protected one. */
+static float dequant_elem(const orc_cfg* c, const head_addr* a, float scale, int v, int k) {
+  int slot = a->slot[k];
+  if (slot < 0) return get_hp(c, a, v, ~slot);
+  return scale * (float)get_code(c, a, v, slot);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Requantization of one row (value-axis scale grouping, LoReS abstract):    */
+/* the row's scale is its largest magnitude over quantized channels divided  */
+/* by Q (127 for 8 bits, 7 for 4 bits; symmetric grid, no zero point).       */
+/* Each element is x = value * (Q / max), rounded to nearest even or         */
+/* stochastically (LoReS abstract); with BDR (abstract of the page on        */
+/* preserving updates: reversed elements are rounded toward their update) an */
+/* element whose new level lies on the wrong side of its previous value by   */
+/* more than the bound takes the other neighbour of x instead.  Codes are    */
+/* clamped to [-Q, Q].  Protected channels store the nearest 16-bit (or the  */
+/* fp32) value.  `old` is the value before the step (BDR only; may be NULL). */
+/* Returns the row's new scale.                                             */
+/* ------------------------------------------------------------------------ */
+static float requantize_row(const orc_cfg* c, const head_addr* a, int64_t bh, int v,
+                            const float* sp, const float* old, uint64_t step) {
+  const int dk = c->dk;
+  const float Q = (c->qbits == 8) ? 127.0f : 7.0f;
+  float m = 0.0f;
+  for (int k = 0; k < dk; ++k)
+    if (a->slot[k] >= 0) {
+      float mag = fabsf(sp[k]);
+      if (mag > m) m = mag;
+    }
+  float scale = 0.0f, inv = 0.0f;
+  if (m > 0.0f) {
+    scale = m / Q;
+    inv = Q / m;
+    if (!isfinite(inv)) {   /* max below Q / FLT_MAX: the row is stored as zero */
+      scale = 0.0f;
+      inv = 0.0f;
+    }
+  }
+  for (int k = 0; k < dk; ++k) {
+    int slot = a->slot[k];
+    if (slot < 0) {
+      put_hp(c, a, v, ~slot, sp[k]);
+      continue;
+    }
+    float code = 0.0f;
+    if (inv != 0.0f) {
+      float x = sp[k] * inv;
+      if (c->rounding == 0) {
+        code = rintf(x);
+      } else {
+        uint64_t e = ((uint64_t)bh * (uint64_t)c->dv + (uint64_t)v) * (uint64_t)dk + (uint64_t)k;
+        code = orc_sr_round(x, orc_random_bits(c, e, step), c->sr_bits);
+      }
+      if (c->bdr && old) {
+        float xo = old[k] * inv;
+        float d = sp[k] - old[k];
+        if (d > 0.0f && code < xo - c->bdr_bound) code = ceilf(x);
+        else if (d < 0.0f && code > xo + c->bdr_bound) code = floorf(x);
+      }
+      if (code > Q) code = Q;
+      if (code < -Q) code = -Q;
+    }
+    put_code(c, a, v, slot, (int32_t)code);
+  }
+  return scale;
+}
+
+/* fp32 logical state [B,H,dv,dk] -> stored state.  No previous value, so no
+ * BDR; the low-rank bypass buffer starts empty. */
+int orc_quantize(const orc_cfg* c, const float* S, orc_state* st, uint64_t step) {
+  layout_t L;
+  if (layout_make(c, &L)) {
+    layout_free(&L);
+    return -1;
+  }
+  const int dk = c->dk, dv = c->dv, r = c->lrb_rank;
+  int* slot = (int*)malloc(sizeof(int) * (size_t)dk);
+  int64_t BH = (int64_t)c->B * c->H;
+  for (int64_t bh = 0; bh < BH; ++bh) {
+    head_addr a;
+    head_address(c, &L, st, bh, &a, slot);
+    for (int v = 0; v < dv; ++v) {
+      const float* row = S + ((uint64_t)bh * dv + (uint64_t)v) * (uint64_t)dk;
+      st->scales[(uint64_t)bh * dv + v] = requantize_row(c, &a, bh, v, row, NULL, step);
+    }
+    if (r > 0) {
+      memset(st->W + (uint64_t)bh * dv * r, 0, sizeof(float) * (size_t)dv * (size_t)r);
+      memset(st->U + (uint64_t)bh * dk * r, 0, sizeof(float) * (size_t)dk * (size_t)r);
+      st->n[bh] = 0;
+    }
+  }
+  free(slot);
+  layout_free(&L);
+  return 0;
+}
+
+/* Low-rank buffer column k as seen by row v: sum over the first n basis
+ * vectors of W[v][j] * U[k][j], as an fp32 fused multiply-add chain in
+ * ascending j. */
+static float lrb_entry(const float* W, const float* U, int r, int n, int v, int k) {
+  float acc = 0.0f;
+  for (int j = 0; j < n; ++j) acc = fmaf(W[v * r + j], U[k * r + j], acc);
+  return acc;
+}
+
+/* stored state -> fp32 effective state [B,H,dv,dk]: dequantized state plus
+ * the low-rank bypass buffer W U^T when it is on. */
+int orc_dequantize(const orc_cfg* c, const orc_state* st, float* S) {
+  layout_t L;
+  if (layout_make(c, &L)) {
+    layout_free(&L);
+    return -1;
+  }
+  const int dk = c->dk, dv = c->dv, r = c->lrb_rank;
+  int* slot = (int*)malloc(sizeof(int) * (size_t)dk);
+  int64_t BH = (int64_t)c->B * c->H;
+  for (int64_t bh = 0; bh < BH; ++bh) {
+    head_addr a;
+    head_address(c, &L, st, bh, &a, slot);
+    for (int v = 0; v < dv; ++v) {
+      float scale = st->scales[(uint64_t)bh * dv + v];
+      float* row = S + ((uint64_t)bh * dv + (uint64_t)v) * (uint64_t)dk;
+      for (int k = 0; k < dk; ++k) {
+        float x = dequant_elem(c, &a, scale, v, k);
+        if (r > 0) x = x + lrb_entry(st->W + (uint64_t)bh * dv * r, st->U + (uint64_t)bh * dk * r,
+                                     r, st->n[bh], v, k);
+        row[k] = x;
+      }
+    }
+  }
+  free(slot);
+  layout_free(&L);
+  return 0;
+}
+
+static double dot_d(const float* a, const float* b, int n) {
+  double s = 0.0;
+  for (int i = 0; i < n; ++i) s += (double)a[i] * (double)b[i];
+  return s;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Low-Rank Bypass (abstract of the page on preserving updates: small        */
+/* updates accumulate in a compact low-rank buffer whose sufficiently large  */
+/* elements are merged into the state periodically).  Additive recurrences   */
+/* only.  Buffer of one head: L = W U^T, W [dv][r] with orthonormal columns  */
+/* 0..n-1, U [dk][r].  Reading taken (the page gives one sentence):          */
+/*  1. the buffer decays with the state: U[k][:] *= d[k];                    */
+/*  2. while n < r, the write vector u (Gram-Schmidt, two passes, against the */
+/*     basis) adds a basis column when its new part is above 2^-10 |u|;      */
+/*  3. coefficients c = W^T u, remainder u_perp = u - W c;                   */
+/*  4. key channel k is small when |k_k| * max_v(|u_v| / s_v) < theta (the   */
+/*     update is under theta LSB in every row, s = scales on entry); a small */
+/*     channel sends c k_k into U[k] and only u_perp k_k into the state;     */
+/*  5. on a merge step, a buffer column whose entry reaches theta * s_v in   */
+/*     some row is added to the state before rounding and cleared; when the  */
+/*     whole buffer is clear the basis is reset (n = 0).                     */
+/* Outputs: per-channel flags, u_perp, merged columns [dv][dk] (0 if none). */
+/* ------------------------------------------------------------------------ */
+static void lrb_phase(const orc_cfg* c, float* W, float* U, int32_t* np_, const float* u,
+                      const float* kk, const float* d, const float* s_old, uint64_t step,
+                      int* small, float* u_perp, float* merged, int* merge_flag) {
+  const int dk = c->dk, dv = c->dv, r = c->lrb_rank;
+  const float theta = c->lrb_theta;
+  int n = *np_;
+  /* 1. decay */
+  for (int k = 0; k < dk; ++k)
+    for (int j = 0; j < r; ++j) U[k * r + j] = d[k] * U[k * r + j];
+  /* 2. grow the basis */
+  if (n < r) {
+    float* y = (float*)malloc(sizeof(float) * (size_t)dv);
+    float* wj = (float*)malloc(sizeof(float) * (size_t)dv);
+    for (int v = 0; v < dv; ++v) y[v] = u[v];
+    for (int pass = 0; pass < 2; ++pass)
+      for (int j = 0; j < n; ++j) {
+        for (int v = 0; v < dv; ++v) wj[v] = W[v * r + j];
+        float p = (float)dot_d(wj, y, dv);
+        for (int v = 0; v < dv; ++v) y[v] = fmaf(-p, W[v * r + j], y[v]);
+      }
+    float ny = sqrtf((float)dot_d(y, y, dv));
+    float nu = sqrtf((float)dot_d(u, u, dv));
+    if (ny > ldexpf(nu, -10)) {
+      for (int v = 0; v < dv; ++v) W[v * r + n] = y[v] / ny;
+      n += 1;
+    }
+    free(y);
+    free(wj);
+  }
+  /* 3. project */
+  float* cj = (float*)calloc((size_t)r, sizeof(float));
+  float* wj = (float*)malloc(sizeof(float) * (size_t)dv);
+  for (int j = 0; j < n; ++j) {
+    for (int v = 0; v < dv; ++v) wj[v] = W[v * r + j];
+    cj[j] = (float)dot_d(wj, u, dv);
+  }
+  for (int v = 0; v < dv; ++v) {
+    float t = u[v];
+    for (int j = 0; j < n; ++j) t = fmaf(-cj[j], W[v * r + j], t);
+    u_perp[v] = t;
+  }
+  /* 4. small key channels */
+  float g = 0.0f;
+  for (int v = 0; v < dv; ++v) {
+    float au = fabsf(u[v]);
+    float gv = (s_old[v] > 0.0f) ? au / s_old[v] : (au > 0.0f ? INFINITY : 0.0f);
+    if (gv > g) g = gv;
+  }
+  for (int k = 0; k < dk; ++k) {
+    small[k] = isfinite(g) && (fabsf(kk[k]) * g < theta);
+    if (small[k])
+      for (int j = 0; j < n; ++j) U[k * r + j] = fmaf(kk[k], cj[j], U[k * r + j]);
+  }
+  /* 5. merge */
+  for (int k = 0; k < dk; ++k) merge_flag[k] = 0;
+  memset(merged, 0, sizeof(float) * (size_t)dv * (size_t)dk);
+  if (c->lrb_period > 0 && ((step + 1u) % (uint64_t)c->lrb_period) == 0u) {
+    int any_left = 0;
+    for (int k = 0; k < dk; ++k) {
+      int big = 0;
+      for (int v = 0; v < dv; ++v) {
+        float col = lrb_entry(W, U, r, n, v, k);
+        if (col != 0.0f && fabsf(col) >= theta * s_old[v]) big = 1;
+      }
+      if (big) {
+        merge_flag[k] = 1;
+        for (int v = 0; v < dv; ++v) merged[v * dk + k] = lrb_entry(W, U, r, n, v, k);
+        for (int j = 0; j < r; ++j) U[k * r + j] = 0.0f;
+      }
+    }
+    for (int k = 0; k < dk; ++k)
+      for (int j = 0; j < r; ++j)
+        if (U[k * r + j] != 0.0f) any_left = 1;
+    if (!any_left) n = 0;
+  }
+  *np_ = n;
+  free(cj);
+  free(wj);
+}
+
+/* ------------------------------------------------------------------------ */
+/* One decode step of one head, in the order the method states: dequantize  */
+/* the state, apply decay and the update, compute the output from the        */
+/* pre-rounding state, requantize.                                           */
+/*   additive (GLA, Mamba2, RetNet): S <- diag-decay(S) + u k^T, u = beta v  */
+/*   delta rule (Gated DeltaNet):   S <- alpha S + u k^T,                     */
+/*                                   u = beta (v - alpha S k)                 */
+/* i.e. alpha (S - beta S k k^T) + beta v k^T written in factored form.      */
+/* Element update: Sp = fmaf(u_v, k_k, d_k * Shat), with Shat the            */
+/* dequantized value; readout o_v = sum_k Sp[v][k] q_k (+ buffer term).      */
+/* ------------------------------------------------------------------------ */
+static void head_step(const orc_cfg* c, const layout_t* L, orc_state* st, int64_t bh,
+                      const float* q, const float* kin, const float* vin, const float* decay,
+                      const float* beta, float* out, uint64_t step, float* sp_dbg) {
+  const int dk = c->dk, dv = c->dv, r = c->lrb_rank;
+  int* slot = (int*)malloc(sizeof(int) * (size_t)dk);
+  head_addr a;
+  head_address(c, L, st, bh, &a, slot);
+  const float* qh = q + (uint64_t)bh * dk;
+  const float* kh = kin + (uint64_t)bh * dk;
+  const float* vh = vin + (uint64_t)bh * dv;
+  float* d = (float*)malloc(sizeof(float) * (size_t)dk);
+  for (int k = 0; k < dk; ++k)
+    d[k] = (c->decay_mode == 0) ? decay[bh] : decay[(uint64_t)bh * dk + k];
+  const float bt = beta ? beta[bh] : 1.0f;
+  float* scales = st->scales + (uint64_t)bh * dv;
+
+  float* sh = (float*)malloc(sizeof(float) * (size_t)dv * (size_t)dk);
+  float* sp = (float*)malloc(sizeof(float) * (size_t)dv * (size_t)dk);
+  float* u = (float*)malloc(sizeof(float) * (size_t)dv);
+  float* s_old = (float*)malloc(sizeof(float) * (size_t)dv);
+
+  /* dequantize */
+  for (int v = 0; v < dv; ++v) {
+    s_old[v] = scales[v];
+    for (int k = 0; k < dk; ++k) sh[v * dk + k] = dequant_elem(c, &a, s_old[v], v, k);
+  }
+  /* write vector */
+  for (int v = 0; v < dv; ++v) {
+    if (c->kind == 0) {
+      u[v] = bt * vh[v];
+    } else {
+      float w = (float)dot_d(sh + (uint64_t)v * dk, kh, dk);
+      u[v] = bt * (vh[v] - d[0] * w);
+    }
+  }
+  /* low-rank bypass */
+  int* small = (int*)calloc((size_t)dk, sizeof(int));
+  int* mflag = (int*)calloc((size_t)dk, sizeof(int));
+  float* u_perp = (float*)malloc(sizeof(float) * (size_t)dv);
+  float* merged = NULL;
+  float* W = NULL;
+  float* U = NULL;
+  if (r > 0) {
+    W = st->W + (uint64_t)bh * dv * r;
+    U = st->U + (uint64_t)bh * dk * r;
+    merged = (float*)malloc(sizeof(float) * (size_t)dv * (size_t)dk);
+    lrb_phase(c, W, U, &st->n[bh], u, kh, d, s_old, step, small, u_perp, merged, mflag);
+  }
+  /* decay + update (+ merged buffer columns) */
+  for (int v = 0; v < dv; ++v)
+    for (int k = 0; k < dk; ++k) {
+      float uu = small[k] ? u_perp[v] : u[v];
+      float x = fmaf(uu, kh[k], d[k] * sh[v * dk + k]);
+      if (mflag[k]) x = x + merged[v * dk + k];
+      sp[v * dk + k] = x;
+    }
+  /* readout from the pre-rounding state (+ buffer W (U^T q)) */
+  double* z = NULL;
+  if (r > 0) {
+    z = (double*)calloc((size_t)r, sizeof(double));
+    int n = st->n[bh];
+    for (int j = 0; j < n; ++j)
+      for (int k = 0; k < dk; ++k) z[j] += (double)U[k * r + j] * (double)qh[k];
+  }
+  for (int v = 0; v < dv; ++v) {
+    double acc = dot_d(sp + (uint64_t)v * dk, qh, dk);
+    if (r > 0)
+      for (int j = 0; j < st->n[bh]; ++j) acc += (double)W[v * r + j] * z[j];
+    out[(uint64_t)bh * dv + v] = (float)acc;
+  }
+  if (sp_dbg) memcpy(sp_dbg + (uint64_t)bh * dv * dk, sp, sizeof(float) * (size_t)dv * (size_t)dk);
+  /* requantize */
+  for (int v = 0; v < dv; ++v)
+    scales[v] = requantize_row(c, &a, bh, v, sp + (uint64_t)v * dk, sh + (uint64_t)v * dk, step);
+
+  free(z);
+  free(merged);
+  free(u_perp);
+  free(small);
+  free(mflag);
+  free(s_old);
+  free(u);
+  free(sp);
+  free(sh);
+  free(d);
+  free(slot);
+}
+
+int orc_step(const orc_cfg* c, orc_state* st, const float* q, const float* k, const float* v,
+             const float* decay, const float* beta, float* out, uint64_t step, float* sp_dbg,
+             const int64_t* heads, int64_t nheads) {
+  layout_t L;
+  if (layout_make(c, &L)) {
+    layout_free(&L);
+    return -1;
+  }
+  int64_t BH = (int64_t)c->B * c->H;
+  if (heads) {
+    for (int64_t i = 0; i < nheads; ++i) {
+      if (heads[i] < 0 || heads[i] >= BH) {
+        layout_free(&L);
+        return -1;
+      }
+      head_step(c, &L, st, heads[i], q, k, v, decay, beta, out, step, sp_dbg);
+    }
+  } else {
+    for (int64_t bh = 0; bh < BH; ++bh)
+      head_step(c, &L, st, bh, q, k, v, decay, beta, out, step, sp_dbg);
+  }
+  layout_free(&L);
+  return 0;
+}

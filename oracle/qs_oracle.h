@@ -1,0 +1,86 @@
+/*
+ * qs_oracle.h -- CPU oracle for the quantized recurrent-state decode step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This oracle is a plain, slow, scalar C
+ * implementation of what the decode step computes.  Only the test suite,
+ * the smoke check and the CPU-baseline leg of the benchmark may load it.
+ * It shares no code, header, table or constant with the HIP library.
+ *
+ * What it follows (pages as cited in the repository's design notes):
+ *  - "Quantizing Recurrent Language Models Is Easier Than You Think"
+ *    (LoReS, arXiv 2611.01864), abstract: value-axis scale grouping,
+ *    decay-based mixed precision for slowly decaying heads or channels,
+ *    stochastic rounding under repeated requantization.
+ *  - "Preserving Updates in Low-Bit Recurrent State Quantization"
+ *    (arXiv 2610.15709), abstract: requantization after every update,
+ *    Low-Rank Bypass (LRB), Bounded Directional Rounding (BDR), INT4.
+ *  - Philox4x32-10 from Salmon, Moraes, Dror, Shaw, "Parallel Random
+ *    Numbers: As Easy as 1, 2, 3" (SC'11), section on the Philox family.
+ *
+ * Element arithmetic is fp32 (the stored state format is fp32 scales times
+ * integer codes, so that is the precision every rounding decision is taken
+ * in); every reduction (dot products, norms) accumulates in fp64 and is
+ * rounded to fp32 once.  Build with -ffp-contract=off: each fused
+ * multiply-add below is an explicit fmaf().
+ */
+#ifndef QS_ORACLE_H
+#define QS_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct {
+  int32_t kind;        /* 0 additive (GLA, Mamba2, RetNet), 1 delta rule (Gated DeltaNet) */
+  int32_t decay_mode;  /* 0 one decay per (b,h); 1 one decay per (b,h,k) */
+  int32_t B, H, dk, dv;
+  int32_t qbits;       /* 8 or 4 */
+  int32_t hp_dtype;    /* storage of protected units: 0 fp32, 1 bf16, 2 fp16 */
+  int32_t map_mode;    /* 0 none, 1 one flag per head, 2 one flag per (head, key channel) */
+  const uint8_t* map;  /* [H] or [H*dk]; nonzero = kept in high precision */
+  int32_t rounding;    /* 0 round to nearest even, 1 stochastic */
+  int32_t sr_bits;     /* random bits per element for stochastic rounding: 16 or 8 */
+  int32_t bdr;         /* bounded directional rounding on/off */
+  float   bdr_bound;   /* tolerated reversal, in LSB of the new grid */
+  int32_t lrb_rank;    /* 0 = low-rank bypass off */
+  int32_t lrb_period;  /* merge when (step+1) % period == 0 */
+  float   lrb_theta;   /* merge / smallness threshold, in LSB */
+  uint64_t seed;       /* Philox key */
+} orc_cfg;
+
+typedef struct {
+  uint8_t* codes;   /* packed codes, per-head blocks */
+  float*   scales;  /* [B,H,dv] */
+  void*    hp;      /* protected values, per-head blocks (uint16 bits or fp32) */
+  float*   W;       /* [B,H,dv,r] */
+  float*   U;       /* [B,H,dk,r] */
+  int32_t* n;       /* [B,H] */
+} orc_state;
+
+typedef struct {
+  uint64_t codes, scales, hp, W, U, n;   /* bytes */
+  uint64_t code_bstride, hp_bstride;     /* bytes per batch element */
+} orc_sizes;
+
+int  orc_layout(const orc_cfg* c, orc_sizes* s, uint64_t* code_off, uint64_t* hp_off,
+                int32_t* nq);
+void orc_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]);
+uint32_t orc_random_bits(const orc_cfg* c, uint64_t e, uint64_t step);
+float orc_sr_round(float x, uint32_t rbits, int32_t sr_bits);
+uint16_t orc_to_bf16(float f);
+uint16_t orc_to_fp16(float f);
+float orc_from_bf16(uint16_t h);
+float orc_from_fp16(uint16_t h);
+int  orc_build_map(const double* stat, int32_t groups, int32_t per_group, double frac,
+                   uint8_t* map);
+int  orc_quantize(const orc_cfg* c, const float* S, orc_state* st, uint64_t step);
+int  orc_dequantize(const orc_cfg* c, const orc_state* st, float* S);
+int  orc_step(const orc_cfg* c, orc_state* st, const float* q, const float* k,
+              const float* v, const float* decay, const float* beta, float* out,
+              uint64_t step, float* sp_dbg, const int64_t* heads, int64_t nheads);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
