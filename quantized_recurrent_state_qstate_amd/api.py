@@ -1,0 +1,172 @@
+"""Python front end of libqstate: a handle plus torch-owned device buffers.
+
+torch provides device memory and streams only; every computation of the
+decode path (dequantize, decay + update, readout, requantize) runs in the
+library's kernels through the C ABI of include/qstate.h.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+from . import _lib
+
+
+@dataclasses.dataclass
+class StateConfig:
+    """Mirror of qstate_config with readable enumerations."""
+    kind: str = "additive"          # additive | delta
+    decay_mode: str = "head"        # head | key
+    B: int = 1
+    H: int = 1
+    dk: int = 128
+    dv: int = 128
+    qbits: int = 8                  # 8 | 4
+    hp_dtype: str = "bf16"          # fp32 | bf16 | fp16
+    map_mode: str = "none"          # none | head | key
+    map: Optional[np.ndarray] = None
+    in_dtype: str = "bf16"          # fp32 | bf16
+    rounding: str = "stochastic"    # nearest | stochastic
+    sr_bits: int = 16
+    bdr: bool = False
+    bdr_bound: float = 0.0
+    lrb_rank: int = 0
+    lrb_period: int = 64
+    lrb_theta: float = 0.5
+    seed: int = 0
+
+    def to_c(self) -> _lib.Config:
+        c = _lib.Config()
+        c.abi_version = _lib.ABI_VERSION
+        c.kind = _lib.KIND[self.kind]
+        c.decay_mode = _lib.DECAY[self.decay_mode]
+        c.B, c.H, c.dk, c.dv = self.B, self.H, self.dk, self.dv
+        c.qbits = self.qbits
+        c.hp_dtype = _lib.DTYPE[self.hp_dtype]
+        c.map_mode = _lib.MAP[self.map_mode]
+        if self.map is not None:
+            self._map_keep = np.ascontiguousarray(self.map, dtype=np.uint8).ravel()
+            c.map = self._map_keep.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8))
+        c.in_dtype = _lib.DTYPE[self.in_dtype]
+        c.rounding = _lib.ROUNDING[self.rounding]
+        c.sr_bits = self.sr_bits
+        c.bdr = int(self.bdr)
+        c.bdr_bound = self.bdr_bound
+        c.lrb_rank, c.lrb_period, c.lrb_theta = self.lrb_rank, self.lrb_period, self.lrb_theta
+        c.seed = self.seed
+        return c
+
+
+def plan(cfg: StateConfig) -> dict:
+    """Buffer sizes in bytes (host only; no GPU needed)."""
+    c = cfg.to_c()
+    s = _lib.Sizes()
+    _lib.check(_lib.lib().qstate_plan(ctypes.byref(c), ctypes.byref(s)), "qstate_plan")
+    return {n: int(getattr(s, n)) for n, _ in _lib.Sizes._fields_}
+
+
+def build_map(stat, groups: int, per_group: int, frac: float) -> np.ndarray:
+    """Decay-based mixed-precision map: smallest decay-rate units flagged (host)."""
+    stat = np.ascontiguousarray(stat, dtype=np.float32).ravel()
+    assert stat.size == groups * per_group
+    m = np.zeros(groups * per_group, np.uint8)
+    _lib.check(_lib.lib().qstate_build_map(stat.ctypes.data, groups, per_group, frac, m.ctypes.data),
+               "qstate_build_map")
+    return m
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+class QState:
+    """A libqstate handle for one configuration on the current HIP device."""
+
+    def __init__(self, cfg: StateConfig):
+        import torch
+        self.cfg = cfg
+        self._c = cfg.to_c()
+        self._h = ctypes.c_void_p()
+        s = _lib.Sizes()
+        _lib.check(_lib.lib().qstate_init(ctypes.byref(self._c), ctypes.byref(self._h), ctypes.byref(s)),
+                   "qstate_init")
+        self.sizes = {n: int(getattr(s, n)) for n, _ in _lib.Sizes._fields_}
+        self.device = torch.device("cuda", torch.cuda.current_device())
+
+    def close(self) -> None:
+        if self._h:
+            _lib.lib().qstate_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def kernel_name(self) -> str:
+        return _lib.lib().qstate_kernel_name(self._h).decode()
+
+    def new_state(self) -> dict:
+        """Zero-filled state buffers (the state S = 0), owned by torch."""
+        import torch
+        z = self.sizes
+        dev = self.device
+
+        def buf(nbytes, dtype, item):
+            return torch.zeros(max(nbytes // item, 1 if nbytes else 0), dtype=dtype, device=dev)
+
+        return {
+            "codes": buf(z["codes"], torch.uint8, 1),
+            "scales": buf(z["scales"], torch.float32, 4),
+            "hp": buf(z["hp"], torch.uint8, 1),
+            "lrb_W": buf(z["lrb_W"], torch.float32, 4),
+            "lrb_U": buf(z["lrb_U"], torch.float32, 4),
+            "lrb_n": buf(z["lrb_n"], torch.int32, 4),
+        }
+
+    @staticmethod
+    def _tensors(st: dict) -> _lib.Tensors:
+        t = _lib.Tensors()
+        for n in ("codes", "scales", "hp", "lrb_W", "lrb_U", "lrb_n"):
+            x = st.get(n)
+            setattr(t, n, x.data_ptr() if (x is not None and x.numel() > 0) else None)
+        return t
+
+    @staticmethod
+    def _stream(stream) -> Optional[int]:
+        import torch
+        if stream is None:
+            stream = torch.cuda.current_stream()
+        return stream.cuda_stream
+
+    def quantize(self, S, st: dict, step: int = 0, stream=None) -> None:
+        t = self._tensors(st)
+        _lib.check(_lib.lib().qstate_quantize(self._h, _ptr(S), ctypes.byref(t), step, self._stream(stream)),
+                   "qstate_quantize")
+
+    def dequantize(self, st: dict, out=None, stream=None):
+        import torch
+        c = self.cfg
+        if out is None:
+            out = torch.empty((c.B, c.H, c.dv, c.dk), dtype=torch.float32, device=self.device)
+        t = self._tensors(st)
+        _lib.check(_lib.lib().qstate_dequantize(self._h, ctypes.byref(t), _ptr(out), self._stream(stream)),
+                   "qstate_dequantize")
+        return out
+
+    def step(self, st: dict, q, k, v, decay, beta=None, out=None, step: int = 0, stream=None):
+        """One decode step in place on `st`; returns o [B,H,dv] fp32."""
+        import torch
+        c = self.cfg
+        if out is None:
+            out = torch.empty((c.B, c.H, c.dv), dtype=torch.float32, device=self.device)
+        t = self._tensors(st)
+        inp = _lib.Inputs(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(beta))
+        _lib.check(_lib.lib().qstate_decode_step(self._h, ctypes.byref(t), ctypes.byref(inp), _ptr(out), step,
+                                                 self._stream(stream)), "qstate_decode_step")
+        return out

@@ -1,0 +1,301 @@
+// Device helpers of libqstate's gfx950 kernels: Philox4x32-10, 8-lane DPP
+// reductions, vector loads/stores, 16-bit conversions, element rounding.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qs {
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10 (Salmon et al., SC'11, Philox family): ten rounds, each
+// multiplying counter words 0 and 2 by the two Philox multipliers; the high
+// product halves are xored with the other counter words and the round key,
+// the low halves move into words 1 and 3; the key advances by the two Weyl
+// constants after every round.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void philox10(uint32_t (&x)[4], uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * (uint64_t)x[0];
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * (uint64_t)x[2];
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ x[1] ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ x[3] ^ k1;
+    x[1] = (uint32_t)p1;
+    x[3] = (uint32_t)p0;
+    x[0] = n0;
+    x[2] = n2;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+}
+
+// Random integers for EPL consecutive elements starting at logical index e0
+// (e0 a multiple of 8).  RND 1: 16 bits per element, block g = e>>3, low
+// half of word (e>>1)&3 for even e.  RND 2: 8 bits, block g = e>>4, byte
+// e&3 of word (e>>2)&3.  Counter = (g lo, g hi, step lo, step hi).
+template <int RND, int EPL>
+__device__ __forceinline__ void rand_bits(uint64_t e0, uint32_t s0, uint32_t s1, uint32_t t0,
+                                          uint32_t t1, uint32_t (&rb)[EPL]) {
+  if constexpr (RND == 1) {
+#pragma unroll
+    for (int g = 0; g < EPL / 8; ++g) {
+      const uint64_t n = (e0 >> 3) + (uint64_t)g;
+      uint32_t x[4] = {(uint32_t)n, (uint32_t)(n >> 32), t0, t1};
+      philox10(x, s0, s1);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) rb[g * 8 + j] = (j & 1) ? (x[j >> 1] >> 16) : (x[j >> 1] & 0xFFFFu);
+    }
+  } else if constexpr (RND == 2) {
+    if constexpr (EPL >= 16) {
+#pragma unroll
+      for (int g = 0; g < EPL / 16; ++g) {
+        const uint64_t n = (e0 >> 4) + (uint64_t)g;
+        uint32_t x[4] = {(uint32_t)n, (uint32_t)(n >> 32), t0, t1};
+        philox10(x, s0, s1);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) rb[g * 16 + j] = (x[j >> 2] >> (8 * (j & 3))) & 0xFFu;
+      }
+    } else {
+      const uint64_t n = e0 >> 4;
+      uint32_t x[4] = {(uint32_t)n, (uint32_t)(n >> 32), t0, t1};
+      philox10(x, s0, s1);
+      const bool hi = (e0 & 8u) != 0;   // second half of the 16-element block
+      const uint32_t w0 = hi ? x[2] : x[0];
+      const uint32_t w1 = hi ? x[3] : x[1];
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) rb[j] = (((j < 4) ? w0 : w1) >> (8 * (j & 3))) & 0xFFu;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Reductions over the 8 lanes of a row group (lanes 8i..8i+7) with DPP:
+// swap neighbours, swap pairs, mirror the half-row.  Every lane ends with
+// the same bits (each step combines two equal multisets commutatively).
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dppf(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // row_half_mirror
+
+__device__ __forceinline__ float sum8(float x) {
+  x = x + dppf<kDppXor1>(x);
+  x = x + dppf<kDppXor2>(x);
+  x = x + dppf<kDppHalfMirror>(x);
+  return x;
+}
+__device__ __forceinline__ float max8(float x) {
+  x = fmaxf(x, dppf<kDppXor1>(x));
+  x = fmaxf(x, dppf<kDppXor2>(x));
+  x = fmaxf(x, dppf<kDppHalfMirror>(x));
+  return x;
+}
+
+// ---------------------------------------------------------------------------
+// Vector memory access of N bytes (N = 4, 8 or a multiple of 16; p aligned).
+// ---------------------------------------------------------------------------
+template <int N>
+__device__ __forceinline__ void load_bytes(const uint8_t* p, uint32_t (&w)[N / 4]) {
+  if constexpr (N == 4) {
+    w[0] = *reinterpret_cast<const uint32_t*>(p);
+  } else if constexpr (N == 8) {
+    const uint2 t = *reinterpret_cast<const uint2*>(p);
+    w[0] = t.x;
+    w[1] = t.y;
+  } else {
+#pragma unroll
+    for (int i = 0; i < N / 16; ++i) {
+      const uint4 t = reinterpret_cast<const uint4*>(p)[i];
+      w[4 * i + 0] = t.x;
+      w[4 * i + 1] = t.y;
+      w[4 * i + 2] = t.z;
+      w[4 * i + 3] = t.w;
+    }
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void store_bytes(uint8_t* p, const uint32_t (&w)[N / 4]) {
+  if constexpr (N == 4) {
+    *reinterpret_cast<uint32_t*>(p) = w[0];
+  } else if constexpr (N == 8) {
+    *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < N / 16; ++i)
+      reinterpret_cast<uint4*>(p)[i] = make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 16-bit formats.  bf16: round to nearest even on the fp32 bit pattern (add
+// 0x7FFF plus the lowest kept bit), NaN -> quiet NaN.  fp16: the hardware
+// conversion (round to nearest even, subnormals kept).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return ((u >> 16) & 0x8000u) | 0x7FC0u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t b) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+}
+
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// Scalar input element (bf16 or fp32).
+__device__ __forceinline__ float load_in1(const void* base, int bf16, uint64_t idx) {
+  if (bf16) return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(base)[idx]);
+  return reinterpret_cast<const float*>(base)[idx];
+}
+
+// EPL consecutive input elements (bf16 or fp32) starting at element idx.
+template <int EPL>
+__device__ __forceinline__ void load_in(const void* base, int bf16, uint64_t idx, float (&f)[EPL]) {
+  if (bf16) {
+    uint32_t w[EPL / 2];
+    load_bytes<EPL * 2>(reinterpret_cast<const uint8_t*>(base) + idx * 2u, w);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) f[i] = bf16_bits_to_f32((w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
+  } else {
+    uint32_t w[EPL];
+    load_bytes<EPL * 4>(reinterpret_cast<const uint8_t*>(base) + idx * 4u, w);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) f[i] = __uint_as_float(w[i]);
+  }
+}
+
+template <int EPL>
+__device__ __forceinline__ void load_f32(const float* p, float (&f)[EPL]) {
+  uint32_t w[EPL];
+  load_bytes<EPL * 4>(reinterpret_cast<const uint8_t*>(p), w);
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) f[i] = __uint_as_float(w[i]);
+}
+
+// Dequantize EPL codes of one row slice: scale * code.
+template <int QB, int EPL>
+__device__ __forceinline__ void load_codes(const uint8_t* p, float s, float (&sh)[EPL]) {
+  constexpr int NB = EPL * QB / 8;
+  uint32_t w[NB / 4];
+  load_bytes<NB>(p, w);
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    int32_t c;
+    if constexpr (QB == 8) c = (int32_t)(int8_t)(w[i >> 2] >> (8 * (i & 3)));
+    else c = (int32_t)(w[i >> 3] << (28 - 4 * (i & 7))) >> 28;
+    sh[i] = s * (float)c;
+  }
+}
+
+template <int QB, int EPL>
+__device__ __forceinline__ void store_codes(uint8_t* p, const int32_t (&c)[EPL]) {
+  constexpr int NB = EPL * QB / 8;
+  uint32_t w[NB / 4];
+#pragma unroll
+  for (int i = 0; i < NB / 4; ++i) w[i] = 0u;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    if constexpr (QB == 8) w[i >> 2] |= ((uint32_t)c[i] & 0xFFu) << (8 * (i & 3));
+    else w[i >> 3] |= ((uint32_t)c[i] & 0xFu) << (4 * (i & 7));
+  }
+  store_bytes<NB>(p, w);
+}
+
+// Protected row slice: widen / store in hp_dtype (0 fp32, 1 bf16, 2 fp16).
+template <int EPL>
+__device__ __forceinline__ void load_hp(const uint8_t* p, int dt, float (&f)[EPL]) {
+  if (dt == 0) {
+    uint32_t w[EPL];
+    load_bytes<EPL * 4>(p, w);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) f[i] = __uint_as_float(w[i]);
+  } else {
+    uint32_t w[EPL / 2];
+    load_bytes<EPL * 2>(p, w);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const uint32_t b = (w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+      f[i] = (dt == 1) ? bf16_bits_to_f32(b) : f16_bits_to_f32(b);
+    }
+  }
+}
+
+template <int EPL>
+__device__ __forceinline__ void store_hp(uint8_t* p, int dt, const float (&f)[EPL]) {
+  if (dt == 0) {
+    uint32_t w[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) w[i] = __float_as_uint(f[i]);
+    store_bytes<EPL * 4>(p, w);
+  } else {
+    uint32_t w[EPL / 2];
+#pragma unroll
+    for (int i = 0; i < EPL / 2; ++i) w[i] = 0u;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const uint32_t b = (dt == 1) ? f32_to_bf16_bits(f[i]) : f32_to_f16_bits(f[i]);
+      w[i >> 1] |= b << (16 * (i & 1));
+    }
+    store_bytes<EPL * 2>(p, w);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Row scale (value-axis grouping): scale = max / Q, inv = Q / max, both
+// correctly rounded; a zero row, or one whose inverse overflows, is zero.
+// ---------------------------------------------------------------------------
+template <int QB>
+__device__ __forceinline__ void row_scale(float m, float& scale, float& inv) {
+  constexpr float Q = (QB == 8) ? 127.0f : 7.0f;
+  scale = 0.0f;
+  inv = 0.0f;
+  if (m > 0.0f) {
+    scale = m / Q;
+    inv = Q / m;
+    if (!__builtin_isfinite(inv)) {
+      scale = 0.0f;
+      inv = 0.0f;
+    }
+  }
+}
+
+// Round one element x = sp * inv to a code: nearest-even (RND 0) or
+// stochastic with random integer rb (RND 1: 16 bits, RND 2: 8 bits); with
+// BDR, a level on the wrong side of the old value (sh) by more than `bound`
+// is replaced by the neighbour of x toward the update; clamp to [-Q, Q].
+template <int QB, int RND>
+__device__ __forceinline__ int32_t round_elem(float sp, float sh, float inv, uint32_t rb, int bdr,
+                                              float bound) {
+  constexpr float Q = (QB == 8) ? 127.0f : 7.0f;
+  if (inv == 0.0f) return 0;
+  const float x = sp * inv;
+  float c;
+  if constexpr (RND == 0) {
+    c = rintf(x);
+  } else {
+    const float f = floorf(x);
+    const float r = x - f;
+    constexpr float sc = (RND == 1) ? 65536.0f : 256.0f;
+    c = ((float)rb < r * sc) ? f + 1.0f : f;
+  }
+  if (bdr) {
+    const float xo = sh * inv;
+    const float d = sp - sh;
+    if (d > 0.0f && c < xo - bound) c = ceilf(x);
+    else if (d < 0.0f && c > xo + bound) c = floorf(x);
+  }
+  c = fminf(fmaxf(c, -Q), Q);
+  return (int32_t)c;
+}
+
+}  // namespace qs

@@ -1,0 +1,407 @@
+// C-ABI host side of libqstate: argument validation, layout planning,
+// handle management and kernel launch.  Validation and planning make no HIP
+// call, so qstate_plan and every argument error path run without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <numeric>
+#include <string>
+#include <vector>
+
+#include "qstate.h"
+#include "qstate_internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+qs_status fail(qs_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+qs_status ok() {
+  g_last_error.clear();
+  return QS_OK;
+}
+
+constexpr int kMaxRank = 16;
+constexpr uint32_t kMaxLds = 64u * 1024u;
+
+uint64_t round16(uint64_t x) { return (x + 15u) & ~uint64_t(15); }
+
+struct Plan {
+  std::vector<uint64_t> code_off, hp_off;
+  std::vector<int32_t> nq;
+  std::vector<uint8_t> head_type;
+  std::vector<uint16_t> slots;
+  uint64_t code_bstride = 0, hp_bstride = 0;
+  qstate_sizes sizes{};
+  int family = qs::kFamDense;
+  int row_chunks = 1;
+  uint32_t lds = 0;
+};
+
+bool protected_channel(const qstate_config* c, int h, int k) {
+  if (c->map_mode == QS_MAP_NONE) return false;
+  if (c->map_mode == QS_MAP_HEAD) return c->map[h] != 0;
+  return c->map[(size_t)h * (size_t)c->dk + (size_t)k] != 0;
+}
+
+qs_status validate(const qstate_config* c) {
+  if (!c) return fail(QS_EINVAL, "config is NULL");
+  if (c->abi_version != QSTATE_ABI_VERSION)
+    return fail(QS_EINVAL, "abi_version %u, library expects %u", c->abi_version, QSTATE_ABI_VERSION);
+  if (c->kind != QS_KIND_ADDITIVE && c->kind != QS_KIND_DELTA) return fail(QS_EINVAL, "kind %d", c->kind);
+  if (c->decay_mode != QS_DECAY_HEAD && c->decay_mode != QS_DECAY_KEY)
+    return fail(QS_EINVAL, "decay_mode %d", c->decay_mode);
+  if (c->kind == QS_KIND_DELTA && c->decay_mode != QS_DECAY_HEAD)
+    return fail(QS_EUNSUPPORTED, "the delta rule takes one decay per head");
+  if (c->B < 0) return fail(QS_EINVAL, "B = %d", c->B);
+  if (c->H < 1) return fail(QS_EINVAL, "H = %d", c->H);
+  if (c->dk < 1 || c->dv < 1) return fail(QS_EINVAL, "dk = %d, dv = %d", c->dk, c->dv);
+  if (c->dk != 64 && c->dk != 128 && c->dk != 256)
+    return fail(QS_EUNSUPPORTED, "dk = %d (supported: 64, 128, 256)", c->dk);
+  if (c->dv > 256) return fail(QS_EUNSUPPORTED, "dv = %d (supported: 1..256)", c->dv);
+  if (c->qbits != 8 && c->qbits != 4) return fail(QS_EUNSUPPORTED, "qbits = %d (supported: 4, 8)", c->qbits);
+  if (c->hp_dtype != QS_FP32 && c->hp_dtype != QS_BF16 && c->hp_dtype != QS_FP16)
+    return fail(QS_EINVAL, "hp_dtype %d", c->hp_dtype);
+  if (c->map_mode != QS_MAP_NONE && c->map_mode != QS_MAP_HEAD && c->map_mode != QS_MAP_KEY)
+    return fail(QS_EINVAL, "map_mode %d", c->map_mode);
+  if (c->map_mode != QS_MAP_NONE && !c->map) return fail(QS_EINVAL, "map is NULL with map_mode %d", c->map_mode);
+  if (c->in_dtype != QS_FP32 && c->in_dtype != QS_BF16)
+    return fail(c->in_dtype == QS_FP16 ? QS_EUNSUPPORTED : QS_EINVAL, "in_dtype %d (supported: fp32, bf16)",
+                c->in_dtype);
+  if (c->rounding != QS_ROUND_NEAREST && c->rounding != QS_ROUND_STOCHASTIC)
+    return fail(QS_EINVAL, "rounding %d", c->rounding);
+  if (c->rounding == QS_ROUND_STOCHASTIC && c->sr_bits != 16 && c->sr_bits != 8)
+    return fail(QS_EUNSUPPORTED, "sr_bits = %d (supported: 8, 16)", c->sr_bits);
+  if (c->bdr != 0 && c->bdr != 1) return fail(QS_EINVAL, "bdr %d", c->bdr);
+  if (!std::isfinite(c->bdr_bound) || c->bdr_bound < 0.0f) return fail(QS_EINVAL, "bdr_bound %g", c->bdr_bound);
+  if (c->lrb_rank < 0) return fail(QS_EINVAL, "lrb_rank %d", c->lrb_rank);
+  if (c->lrb_rank > 0) {
+    if (c->lrb_rank > kMaxRank) return fail(QS_EUNSUPPORTED, "lrb_rank %d (max %d)", c->lrb_rank, kMaxRank);
+    if (c->kind != QS_KIND_ADDITIVE) return fail(QS_EUNSUPPORTED, "low-rank bypass needs the additive kind");
+    if (c->map_mode != QS_MAP_NONE) return fail(QS_EUNSUPPORTED, "low-rank bypass needs map_mode NONE");
+    if (c->lrb_period < 1) return fail(QS_EINVAL, "lrb_period %d", c->lrb_period);
+    if (!std::isfinite(c->lrb_theta) || c->lrb_theta <= 0.0f) return fail(QS_EINVAL, "lrb_theta %g", c->lrb_theta);
+  }
+  return QS_OK;
+}
+
+qs_status make_plan(const qstate_config* c, Plan* p) {
+  qs_status s = validate(c);
+  if (s != QS_OK) return s;
+  const int H = c->H, dk = c->dk, dv = c->dv;
+  const uint64_t hpb = c->hp_dtype == QS_FP32 ? 4u : 2u;
+  p->code_off.assign(H, 0);
+  p->hp_off.assign(H, 0);
+  p->nq.assign(H, 0);
+  p->head_type.assign(H, qs::kHeadQuant);
+  p->slots.assign((size_t)H * dk, 0);
+  uint64_t coff = 0, hoff = 0;
+  bool any_mixed = false;
+  for (int h = 0; h < H; ++h) {
+    int iq = 0, ip = 0;
+    for (int k = 0; k < dk; ++k) {
+      if (protected_channel(c, h, k)) p->slots[(size_t)h * dk + k] = (uint16_t)(qs::kSlotProt | ip++);
+      else p->slots[(size_t)h * dk + k] = (uint16_t)iq++;
+    }
+    p->nq[h] = iq;
+    p->head_type[h] = iq == dk ? qs::kHeadQuant : (iq == 0 ? qs::kHeadProt : qs::kHeadMixed);
+    any_mixed = any_mixed || p->head_type[h] == qs::kHeadMixed;
+    p->code_off[h] = coff;
+    p->hp_off[h] = hoff;
+    coff += round16((uint64_t)dv * (((uint64_t)iq * (uint64_t)c->qbits + 7u) / 8u));
+    hoff += round16((uint64_t)dv * (uint64_t)ip * hpb);
+  }
+  p->code_bstride = coff;
+  p->hp_bstride = hoff;
+  const uint64_t B = (uint64_t)c->B, BH = B * (uint64_t)H, r = (uint64_t)c->lrb_rank;
+  p->sizes.codes = B * coff;
+  p->sizes.hp = B * hoff;
+  p->sizes.scales = BH * (uint64_t)dv * 4u;
+  p->sizes.lrb_W = BH * (uint64_t)dv * r * 4u;
+  p->sizes.lrb_U = BH * (uint64_t)dk * r * 4u;
+  p->sizes.lrb_n = r > 0 ? BH * 4u : 0u;
+
+  p->row_chunks = (dv + 31) / 32;
+  if (c->lrb_rank > 0) {
+    p->family = qs::kFamLrb;
+    const uint64_t floats = (uint64_t)dv * r + (uint64_t)dk * r + 4u * (uint64_t)dv + 3u * (uint64_t)dk + 36u;
+    p->lds = (uint32_t)(floats * 4u + 2u * (uint64_t)dk);
+  } else if (c->map_mode == QS_MAP_KEY) {
+    p->family = qs::kFamMixed;
+    uint64_t mx = 0;
+    for (int h = 0; h < H; ++h) {
+      const uint64_t cb = round16((uint64_t)dv * (((uint64_t)p->nq[h] * (uint64_t)c->qbits + 7u) / 8u));
+      const uint64_t hb = round16((uint64_t)dv * (uint64_t)(dk - p->nq[h]) * hpb);
+      mx = std::max(mx, cb + hb);
+    }
+    p->lds = (uint32_t)std::min<uint64_t>(mx, 0xFFFFFFFFu);
+    (void)any_mixed;
+  } else {
+    p->family = qs::kFamDense;
+  }
+  if (p->lds > kMaxLds)
+    return fail(QS_EUNSUPPORTED, "a head needs %u bytes of LDS staging (max %u)", p->lds, kMaxLds);
+  const uint64_t grid = BH * (p->family == qs::kFamDense ? (uint64_t)p->row_chunks : 1u);
+  if (grid > 0x7FFFFFFFu) return fail(QS_EUNSUPPORTED, "B*H too large for one launch");
+  return QS_OK;
+}
+
+int rnd_code(const qstate_config* c) {
+  if (c->rounding == QS_ROUND_NEAREST) return 0;
+  return c->sr_bits == 16 ? 1 : 2;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1u)) == 0u; }
+
+}  // namespace
+
+struct qstate_handle {
+  qstate_config cfg{};
+  std::vector<uint8_t> map;
+  Plan plan;
+  void* dev = nullptr;   // one device allocation holding the tables
+  qs::DevTables t{};
+  int device = -1;
+  int rnd = 0;
+  std::string kname;
+};
+
+namespace {
+
+qs_status check_tensors(const qstate_handle* h, const qstate_tensors* st) {
+  if (!st) return fail(QS_EINVAL, "state tensors are NULL");
+  const qstate_sizes& z = h->plan.sizes;
+  if (z.codes && (!st->codes || !aligned(st->codes, 16))) return fail(QS_EINVAL, "codes NULL or not 16-byte aligned");
+  if (z.scales && (!st->scales || !aligned(st->scales, 16))) return fail(QS_EINVAL, "scales NULL or not 16-byte aligned");
+  if (z.hp && (!st->hp || !aligned(st->hp, 16))) return fail(QS_EINVAL, "hp NULL or not 16-byte aligned");
+  if (z.lrb_W && (!st->lrb_W || !aligned(st->lrb_W, 16))) return fail(QS_EINVAL, "lrb_W NULL or not 16-byte aligned");
+  if (z.lrb_U && (!st->lrb_U || !aligned(st->lrb_U, 16))) return fail(QS_EINVAL, "lrb_U NULL or not 16-byte aligned");
+  if (z.lrb_n && (!st->lrb_n || !aligned(st->lrb_n, 4))) return fail(QS_EINVAL, "lrb_n NULL or misaligned");
+  return QS_OK;
+}
+
+qs_status check_device(const qstate_handle* h) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(QS_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev != h->device) return fail(QS_EINVAL, "handle was made on device %d, current device is %d", h->device, dev);
+  return QS_OK;
+}
+
+qs::Args base_args(const qstate_handle* h, const qstate_tensors* st) {
+  qs::Args a{};
+  const qstate_config& c = h->cfg;
+  a.codes = reinterpret_cast<uint8_t*>(st->codes);
+  a.scales = st->scales;
+  a.hp = reinterpret_cast<uint8_t*>(st->hp);
+  a.W = st->lrb_W;
+  a.U = st->lrb_U;
+  a.n = st->lrb_n;
+  a.B = c.B;
+  a.H = c.H;
+  a.dk = c.dk;
+  a.dv = c.dv;
+  a.code_bstride = h->plan.code_bstride;
+  a.hp_bstride = h->plan.hp_bstride;
+  a.t = h->t;
+  a.row_chunks = h->plan.row_chunks;
+  a.hp_dtype = c.hp_dtype == QS_FP32 ? 0 : (c.hp_dtype == QS_BF16 ? 1 : 2);
+  a.in_bf16 = c.in_dtype == QS_BF16 ? 1 : 0;
+  a.decay_key = c.decay_mode == QS_DECAY_KEY ? 1 : 0;
+  a.rounding = c.rounding;
+  a.sr_bits = c.sr_bits;
+  a.bdr = c.bdr;
+  a.bdr_bound = c.bdr_bound;
+  a.lrb_rank = c.lrb_rank;
+  a.lrb_period = c.lrb_period;
+  a.lrb_theta = c.lrb_theta;
+  a.qbits = c.qbits;
+  a.seed_lo = (uint32_t)c.seed;
+  a.seed_hi = (uint32_t)(c.seed >> 32);
+  a.mixed_lds = h->plan.lds;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+qs_status qstate_plan(const qstate_config* cfg, qstate_sizes* sizes) {
+  if (!sizes) return fail(QS_EINVAL, "sizes is NULL");
+  Plan p;
+  qs_status s = make_plan(cfg, &p);
+  if (s != QS_OK) return s;
+  *sizes = p.sizes;
+  return ok();
+}
+
+qs_status qstate_init(const qstate_config* cfg, qstate_handle** out, qstate_sizes* sizes) {
+  if (!out) return fail(QS_EINVAL, "out handle pointer is NULL");
+  *out = nullptr;
+  qstate_handle* h = new (std::nothrow) qstate_handle();
+  if (!h) return fail(QS_ENOMEM, "host allocation failed");
+  qs_status s = make_plan(cfg, &h->plan);
+  if (s != QS_OK) {
+    delete h;
+    return s;
+  }
+  h->cfg = *cfg;
+  if (cfg->map_mode != QS_MAP_NONE) {
+    const size_t n = cfg->map_mode == QS_MAP_HEAD ? (size_t)cfg->H : (size_t)cfg->H * (size_t)cfg->dk;
+    h->map.assign(cfg->map, cfg->map + n);
+  }
+  h->cfg.map = h->map.empty() ? nullptr : h->map.data();
+  h->rnd = rnd_code(cfg);
+  h->kname = qs::step_kernel_name(h->plan.family, cfg->qbits, h->rnd, cfg->kind == QS_KIND_DELTA, cfg->dk);
+
+  hipError_t e = hipGetDevice(&h->device);
+  if (e != hipSuccess) {
+    delete h;
+    return fail(QS_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  }
+  const size_t H = (size_t)cfg->H, dk = (size_t)cfg->dk;
+  const size_t off_codes = 0, off_hp = off_codes + 8 * H, off_nq = off_hp + 8 * H;
+  const size_t off_type = off_nq + 4 * H, off_slots = (off_type + H + 15) & ~size_t(15);
+  const size_t total = off_slots + 2 * H * dk;
+  std::vector<uint8_t> host(total, 0);
+  std::memcpy(host.data() + off_codes, h->plan.code_off.data(), 8 * H);
+  std::memcpy(host.data() + off_hp, h->plan.hp_off.data(), 8 * H);
+  std::memcpy(host.data() + off_nq, h->plan.nq.data(), 4 * H);
+  std::memcpy(host.data() + off_type, h->plan.head_type.data(), H);
+  std::memcpy(host.data() + off_slots, h->plan.slots.data(), 2 * H * dk);
+  e = hipMalloc(&h->dev, total);
+  if (e != hipSuccess) {
+    delete h;
+    return fail(e == hipErrorOutOfMemory ? QS_ENOMEM : QS_EHIP, "hipMalloc: %s", hipGetErrorString(e));
+  }
+  e = hipMemcpy(h->dev, host.data(), total, hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    (void)hipFree(h->dev);
+    delete h;
+    return fail(QS_EHIP, "hipMemcpy: %s", hipGetErrorString(e));
+  }
+  uint8_t* d = reinterpret_cast<uint8_t*>(h->dev);
+  h->t.code_off = reinterpret_cast<uint64_t*>(d + off_codes);
+  h->t.hp_off = reinterpret_cast<uint64_t*>(d + off_hp);
+  h->t.nq = reinterpret_cast<int32_t*>(d + off_nq);
+  h->t.head_type = d + off_type;
+  h->t.slots = reinterpret_cast<uint16_t*>(d + off_slots);
+  if (sizes) *sizes = h->plan.sizes;
+  *out = h;
+  return ok();
+}
+
+qs_status qstate_quantize(qstate_handle* h, const float* S, const qstate_tensors* dst, uint64_t step,
+                          void* stream) {
+  if (!h) return fail(QS_EINVAL, "handle is NULL");
+  qs_status s = check_tensors(h, dst);
+  if (s != QS_OK) return s;
+  if (h->cfg.B == 0) return ok();
+  if (!S || !aligned(S, 16)) return fail(QS_EINVAL, "S NULL or not 16-byte aligned");
+  if ((s = check_device(h)) != QS_OK) return s;
+  qs::Args a = base_args(h, dst);
+  a.S = S;
+  a.step_lo = (uint32_t)step;
+  a.step_hi = (uint32_t)(step >> 32);
+  hipError_t e = qs::launch_quantize(a, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(QS_EHIP, "quantize launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+qs_status qstate_decode_step(qstate_handle* h, const qstate_tensors* state, const qstate_inputs* in,
+                             float* out, uint64_t step, void* stream) {
+  if (!h) return fail(QS_EINVAL, "handle is NULL");
+  qs_status s = check_tensors(h, state);
+  if (s != QS_OK) return s;
+  if (!in) return fail(QS_EINVAL, "inputs are NULL");
+  if (h->cfg.B == 0) return ok();
+  if (!in->q || !in->k || !in->v || !in->decay) return fail(QS_EINVAL, "q, k, v or decay is NULL");
+  if (!aligned(in->q, 16) || !aligned(in->k, 16) || !aligned(in->v, 16) || !aligned(in->decay, 16))
+    return fail(QS_EINVAL, "q, k, v and decay must be 16-byte aligned");
+  if (in->beta && !aligned(in->beta, 4)) return fail(QS_EINVAL, "beta misaligned");
+  if (!out || !aligned(out, 4)) return fail(QS_EINVAL, "out NULL or misaligned");
+  if ((s = check_device(h)) != QS_OK) return s;
+  qs::Args a = base_args(h, state);
+  a.q = in->q;
+  a.k = in->k;
+  a.v = in->v;
+  a.decay = in->decay;
+  a.beta = in->beta;
+  a.out = out;
+  a.step_lo = (uint32_t)step;
+  a.step_hi = (uint32_t)(step >> 32);
+  hipError_t e = qs::launch_step(h->plan.family, h->cfg.qbits, h->rnd, h->cfg.kind == QS_KIND_DELTA, a,
+                                 reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(QS_EHIP, "step launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+qs_status qstate_dequantize(qstate_handle* h, const qstate_tensors* src, float* S, void* stream) {
+  if (!h) return fail(QS_EINVAL, "handle is NULL");
+  qs_status s = check_tensors(h, src);
+  if (s != QS_OK) return s;
+  if (h->cfg.B == 0) return ok();
+  if (!S || !aligned(S, 16)) return fail(QS_EINVAL, "S NULL or not 16-byte aligned");
+  if ((s = check_device(h)) != QS_OK) return s;
+  qs::Args a = base_args(h, src);
+  a.S_out = S;
+  hipError_t e = qs::launch_dequantize(a, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(QS_EHIP, "dequantize launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+qs_status qstate_build_map(const float* stat, int32_t groups, int32_t per_group, float frac, uint8_t* map) {
+  if (!stat || !map) return fail(QS_EINVAL, "stat or map is NULL");
+  if (groups < 0 || per_group < 1) return fail(QS_EINVAL, "groups %d, per_group %d", groups, per_group);
+  if (!(frac >= 0.0f && frac <= 1.0f)) return fail(QS_EINVAL, "frac %g not in [0,1]", frac);
+  const int32_t count = (int32_t)std::floor((double)frac * (double)per_group + 0.5);
+  std::vector<int32_t> idx((size_t)per_group);
+  for (int32_t g = 0; g < groups; ++g) {
+    const float* s = stat + (size_t)g * per_group;
+    for (int32_t i = 0; i < per_group; ++i)
+      if (std::isnan(s[i])) return fail(QS_EINVAL, "stat[%d] is NaN", g * per_group + i);
+    std::iota(idx.begin(), idx.end(), 0);
+    std::stable_sort(idx.begin(), idx.end(), [s](int32_t x, int32_t y) { return s[x] < s[y]; });
+    uint8_t* m = map + (size_t)g * per_group;
+    std::fill(m, m + per_group, 0);
+    for (int32_t i = 0; i < count; ++i) m[idx[(size_t)i]] = 1;
+  }
+  return ok();
+}
+
+void qstate_destroy(qstate_handle* h) {
+  if (!h) return;
+  if (h->dev) (void)hipFree(h->dev);
+  delete h;
+}
+
+const char* qstate_strerror(qs_status s) {
+  switch (s) {
+    case QS_OK: return "ok";
+    case QS_EINVAL: return "invalid argument";
+    case QS_EUNSUPPORTED: return "unsupported configuration";
+    case QS_ENOMEM: return "out of memory";
+    case QS_EHIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* qstate_last_error(void) { return g_last_error.c_str(); }
+
+const char* qstate_kernel_name(const qstate_handle* h) { return h ? h->kname.c_str() : ""; }
+
+}  // extern "C"

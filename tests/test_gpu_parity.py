@@ -1,0 +1,323 @@
+"""GPU parity of libqstate against the CPU oracle, through the C ABI.
+
+Bar (per step, teacher-forced: the oracle starts every step from the GPU's
+state):
+* quantize, and the step of additive recurrences without the low-rank
+  buffer: codes, scales and protected values bit-exact (the pre-rounding
+  value is elementwise in fp32 on both sides; the row maximum is exact);
+* delta rule and low-rank bypass, where a dot product feeds the rounding
+  and the two sides sum in different orders: at most 1 LSB on at most 1e-4
+  of the codes, scales within 1e-5 relative;
+* outputs: ||o - o_ref|| <= 1e-3 ||o_ref|| for every (b, h).
+Full-size cases run the launch configuration of the benchmark and check
+sampled heads.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from quantized_recurrent_state_qstate_amd import QState, StateConfig
+from quantized_recurrent_state_qstate_amd.workloads import WORKLOADS
+
+from helpers import (code_values, gpu_state_to_oracle, inputs_f32, lib_cfg, oracle_cfg,
+                     oracle_state_to_gpu, workload_map)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def _dev_inputs(inp):
+    return {k: (None if v is None else v.to(DEV)) for k, v in inp.items()}
+
+
+def _head_slices(ocfg):
+    """Per (b,h): slices of the code bytes, protected elements, scales, W, U."""
+    L = oracle.layout(ocfg)
+    hp_item = 4 if ocfg.hp_dtype == "fp32" else 2
+    B, H, dv, dk, r = ocfg.B, ocfg.H, ocfg.dv, ocfg.dk, ocfg.lrb_rank
+    out = []
+    for bh in range(B * H):
+        b, h = divmod(bh, H)
+        nq = int(L["nq"][h])
+        cb = dv * ((nq * ocfg.qbits + 7) // 8)
+        c0 = b * L["code_bstride"] + int(L["code_off"][h])
+        hb = dv * (dk - nq)
+        h0 = (b * L["hp_bstride"] + int(L["hp_off"][h])) // hp_item
+        out.append(dict(codes=slice(c0, c0 + cb), hp=slice(h0, h0 + hb), scales=slice(bh * dv, bh * dv + dv),
+                        quant=nq > 0, W=slice(bh * dv * r, (bh + 1) * dv * r),
+                        U=slice(bh * dk * r, (bh + 1) * dk * r)))
+    return out
+
+
+def compare(ocfg, exact, ref, got, o_ref, o_got, heads=None, what=""):
+    """Compare oracle state `ref` with GPU state `got` (numpy dicts) on `heads`."""
+    sl = _head_slices(ocfg)
+    heads = range(ocfg.B * ocfg.H) if heads is None else heads
+    ndiff = ntot = 0
+    o_ref = o_ref.reshape(-1, ocfg.dv).astype(np.float64)
+    o_got = o_got.reshape(-1, ocfg.dv).astype(np.float64)
+    for bh in heads:
+        s = sl[bh]
+        cr = code_values(ref["codes"][s["codes"]], ocfg.qbits)
+        cg = code_values(got["codes"][s["codes"]], ocfg.qbits)
+        d = np.abs(cr - cg)
+        if exact:
+            assert d.max(initial=0) == 0, f"{what} head {bh}: codes differ at {np.nonzero(d)[0][:8]}"
+            if s["quant"]:
+                assert np.array_equal(ref["scales"][s["scales"]], got["scales"][s["scales"]]), f"{what} {bh} scales"
+            assert np.array_equal(ref["hp"][s["hp"]], got["hp"][s["hp"]]), f"{what} head {bh}: protected values"
+        else:
+            assert d.max(initial=0) <= 1, f"{what} head {bh}: code off by {d.max()}"
+            ndiff += int((d > 0).sum())
+            ntot += d.size
+            if s["quant"]:
+                np.testing.assert_allclose(got["scales"][s["scales"]], ref["scales"][s["scales"]], rtol=1e-5,
+                                           atol=0, err_msg=f"{what} head {bh} scales")
+            hr, hg = ref["hp"][s["hp"]], got["hp"][s["hp"]]
+            if hr.size:
+                if ocfg.hp_dtype == "fp32":
+                    np.testing.assert_allclose(hg, hr, rtol=1e-5, atol=1e-6)
+                else:
+                    # 16-bit values: at most one unit in the last place apart
+                    assert (np.abs(hr.astype(np.int64) - hg.astype(np.int64)) <= 1).all()
+        if ocfg.lrb_rank:
+            assert got["n"][bh] == ref["n"][bh], f"{what} head {bh}: buffer rank"
+            np.testing.assert_allclose(got["W"][s["W"]], ref["W"][s["W"]], rtol=0, atol=2e-5)
+            np.testing.assert_allclose(got["U"][s["U"]], ref["U"][s["U"]], rtol=2e-4,
+                                       atol=2e-5 * (np.abs(ref["U"][s["U"]]).max(initial=0) + 1e-3))
+        nr = np.linalg.norm(o_ref[bh])
+        assert np.linalg.norm(o_got[bh] - o_ref[bh]) <= 1e-3 * nr + 1e-30, f"{what} head {bh}: output"
+    if not exact and ntot:
+        assert ndiff <= max(1e-4 * ntot, 2), f"{what}: {ndiff} of {ntot} codes differ by 1 LSB"
+    return ndiff, ntot
+
+
+def _exact_kind(w):
+    return w.kind == "additive" and w.lrb_rank == 0
+
+
+def run_teacher_forced(w, B, T, heads=None, warm=0, t0=0):
+    ocfg = oracle_cfg(w, B=B)
+    qs = QState(lib_cfg(w, B=B))
+    st = qs.new_state()
+    for t in range(t0, t0 + warm):
+        qs.step(st, **_dev_inputs(w.step_inputs(t, B)), step=t)
+    stats = [0, 0]
+    for t in range(t0 + warm, t0 + warm + T):
+        inp = w.step_inputs(t, B)
+        ref = gpu_state_to_oracle(st, w.hp_dtype)
+        o_ref = oracle.step(ocfg, ref, **inputs_f32(inp), step=t, heads=heads)
+        o = qs.step(st, **_dev_inputs(inp), step=t)
+        torch.cuda.synchronize()
+        got = gpu_state_to_oracle(st, w.hp_dtype)
+        nd, nt = compare(ocfg, _exact_kind(w), ref, got, o_ref, o.cpu().numpy(), heads, f"{w.name} t={t}")
+        stats[0] += nd
+        stats[1] += nt
+    qs.close()
+    return stats
+
+
+SMALL = {
+    "gla_small": dict(B=1, T=32),
+    "gdn": dict(B=3, T=6),
+    "mamba2": dict(B=3, T=6),
+    "gla_int4": dict(B=2, T=6),
+    "gdn_large": dict(B=2, T=6),
+}
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_step_teacher_forced_small(name):
+    w = WORKLOADS[name]
+    p = SMALL[name]
+    _log(f"[parity] teacher-forced {name} B={p['B']} T={p['T']}")
+    run_teacher_forced(w, p["B"], p["T"], warm=4 if name != "gla_small" else 0)
+
+
+def test_gla_int4_merge_steps():
+    """Low-rank bypass across a merge (period 64: steps 63 and 127)."""
+    w = WORKLOADS["gla_int4"]
+    _log("[parity] gla_int4 merge steps 60..66")
+    run_teacher_forced(w, 2, 7, warm=60)
+
+
+def test_gla_small_free_running_bitexact():
+    w = WORKLOADS["gla_small"]
+    ocfg = oracle_cfg(w)
+    qs = QState(lib_cfg(w))
+    st = qs.new_state()
+    ost = oracle.new_state(ocfg)
+    for t in range(w.T):
+        inp = w.step_inputs(t)
+        o_ref = oracle.step(ocfg, ost, **inputs_f32(inp), step=t)
+        o = qs.step(st, **_dev_inputs(inp), step=t)
+        torch.cuda.synchronize()
+        got = gpu_state_to_oracle(st, w.hp_dtype)
+        assert np.array_equal(got["codes"], ost["codes"]), f"t={t}"
+        assert np.array_equal(got["scales"], ost["scales"]), f"t={t}"
+        compare(ocfg, True, ost, got, o_ref, o.cpu().numpy(), what=f"free t={t}")
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_quantize_dequantize_bitexact(name):
+    w = WORKLOADS[name]
+    B = 2
+    ocfg = oracle_cfg(w, B=B)
+    qs = QState(lib_cfg(w, B=B))
+    st = qs.new_state()
+    g = torch.Generator().manual_seed(77)
+    S = torch.randn(B, w.H, w.dv, w.dk, generator=g) * torch.rand(B, w.H, w.dv, 1, generator=g) * 3
+    S[0, 0, 0] = 0.0
+    _log(f"[parity] quantize/dequantize {name}")
+    qs.quantize(S.to(DEV), st, step=11)
+    torch.cuda.synchronize()
+    ost = oracle.new_state(ocfg)
+    oracle.quantize(ocfg, S.numpy(), ost, step=11)
+    got = gpu_state_to_oracle(st, w.hp_dtype)
+    assert np.array_equal(got["codes"], ost["codes"])
+    assert np.array_equal(got["scales"], ost["scales"])
+    assert np.array_equal(got["hp"].view(np.uint8), ost["hp"].view(np.uint8))
+    D = qs.dequantize(st).cpu().numpy()
+    assert np.array_equal(D, oracle.dequantize(ocfg, ost))
+
+
+def test_dequantize_with_buffer():
+    w = WORKLOADS["gla_int4"]
+    B = 2
+    ocfg = oracle_cfg(w, B=B)
+    qs = QState(lib_cfg(w, B=B))
+    st = qs.new_state()
+    for t in range(20):
+        qs.step(st, **_dev_inputs(w.step_inputs(t, B)), step=t)
+    torch.cuda.synchronize()
+    got = gpu_state_to_oracle(st, w.hp_dtype)
+    assert got["n"].max() > 0 and np.abs(got["U"]).max() > 0
+    D = qs.dequantize(st).cpu().numpy()
+    assert np.array_equal(D, oracle.dequantize(ocfg, got))
+
+
+# Full size, in the benchmark's launch configuration, sampled heads.
+FULL_STEPS = {"gdn": 2, "mamba2": 2, "gla_int4": 2, "gdn_large": 1}
+
+
+@pytest.mark.parametrize("name", ["gdn", "mamba2", "gla_int4", "gdn_large"])
+def test_full_size_sampled_heads(name):
+    w = WORKLOADS[name]
+    r = np.random.default_rng(5)
+    nh = w.B * w.H
+    heads = np.unique(np.concatenate([r.choice(nh, 64, replace=False), [0, nh - 1, w.H - 1, w.H]]))
+    _log(f"[parity] full size {name} B={w.B} heads={heads.size}")
+    run_teacher_forced(w, w.B, FULL_STEPS[name], heads=heads, warm=3)
+
+
+# Edge cases ----------------------------------------------------------------
+EDGE = {
+    "ragged_dv40": dict(kind="additive", decay_mode="key", dk=128, dv=40, H=3, B=2, qbits=8),
+    "dv1": dict(kind="delta", decay_mode="head", dk=64, dv=1, H=2, B=3, qbits=8),
+    "dk256_int4": dict(kind="additive", decay_mode="head", dk=256, dv=72, H=2, B=2, qbits=4),
+    "dk64_int4_sr8": dict(kind="additive", decay_mode="key", dk=64, dv=64, H=2, B=2, qbits=4, sr_bits=8),
+    "delta_fp32_in": dict(kind="delta", decay_mode="head", dk=128, dv=128, H=2, B=2, in_dtype="fp32"),
+    "int4_keymap_bf16": dict(kind="additive", decay_mode="key", dk=128, dv=64, H=3, B=2, qbits=4,
+                             map_mode="key", hp_dtype="bf16"),
+    "int8_keymap_fp32": dict(kind="delta", decay_mode="head", dk=64, dv=48, H=3, B=2, qbits=8,
+                             map_mode="key", hp_dtype="fp32"),
+    "headmap_fp16_rtn_bdr": dict(kind="additive", decay_mode="head", dk=128, dv=64, H=4, B=2, qbits=8,
+                                 map_mode="head", hp_dtype="fp16", rounding="nearest", bdr=True),
+    "sr_bdr_int8": dict(kind="additive", decay_mode="key", dk=128, dv=32, H=2, B=2, qbits=8, bdr=True),
+    "lrb_headdecay_sr": dict(kind="additive", decay_mode="head", dk=64, dv=48, H=2, B=2, qbits=8,
+                             lrb_rank=4, lrb_period=3),
+}
+
+
+def _edge_inputs(kw, t):
+    g = torch.Generator().manual_seed(500 + t)
+    B, H, dk, dv = kw["B"], kw["H"], kw["dk"], kw["dv"]
+    indt = torch.float32 if kw.get("in_dtype") == "fp32" else torch.bfloat16
+    q = torch.randn(B, H, dk, generator=g)
+    k = torch.randn(B, H, dk, generator=g)
+    if kw["kind"] == "delta":
+        k = k / k.norm(dim=-1, keepdim=True)
+    else:
+        k = k * 0.3
+    v = torch.randn(B, H, dv, generator=g)
+    shape = (B, H, dk) if kw["decay_mode"] == "key" else (B, H)
+    d = torch.sigmoid(torch.randn(shape, generator=g) + 3)
+    beta = torch.sigmoid(torch.randn(B, H, generator=g)) if kw["decay_mode"] == "head" else None
+    return {"q": q.to(indt), "k": k.to(indt), "v": v.to(indt), "decay": d, "beta": beta}
+
+
+@pytest.mark.parametrize("case", list(EDGE))
+def test_edge_cases(case):
+    kw = dict(EDGE[case])
+    r = np.random.default_rng(1)
+    m = None
+    if kw.get("map_mode") == "head":
+        m = (np.arange(kw["H"]) % 2).astype(np.uint8)
+    elif kw.get("map_mode") == "key":
+        m = (r.random((kw["H"], kw["dk"])) < 0.2).astype(np.uint8)
+        m[0, :] = 0
+        if kw["H"] > 2:
+            m[2, :] = 1
+    lkw = dict(kw)
+    lkw.setdefault("rounding", "stochastic")
+    lcfg = StateConfig(map=m, seed=0x1234_5678_9ABC, **lkw)
+    okw = {k: v for k, v in kw.items() if k != "in_dtype"}
+    okw["rounding"] = "rtn" if lkw["rounding"] == "nearest" else "sr"
+    ocfg = oracle.Cfg(map=m, seed=0x1234_5678_9ABC, **okw)
+    qs = QState(lcfg)
+    st = qs.new_state()
+    exact = kw["kind"] == "additive" and not kw.get("lrb_rank")
+    _log(f"[parity] edge {case}")
+    big = (1 << 33) + 5      # Philox step with a nonzero high word
+    for t in range(8):
+        step = big + t
+        inp = _edge_inputs(kw, t)
+        ref = gpu_state_to_oracle(st, ocfg.hp_dtype)
+        o_ref = oracle.step(ocfg, ref, **inputs_f32(inp), step=step)
+        o = qs.step(st, **_dev_inputs(inp), step=step)
+        torch.cuda.synchronize()
+        compare(ocfg, exact, ref, gpu_state_to_oracle(st, ocfg.hp_dtype), o_ref, o.cpu().numpy(),
+                what=f"{case} t={t}")
+
+
+def test_empty_batch_is_a_noop():
+    qs = QState(StateConfig(B=0, H=4, dk=128, dv=64))
+    st = qs.new_state()
+    x = torch.zeros(16, device=DEV)
+    assert qs.step(st, x, x, x, x, out=x) is x
+
+
+def test_deterministic_and_resumable():
+    w = WORKLOADS["mamba2"]
+    B, T = 4, 10
+    qs = QState(lib_cfg(w, B=B))
+    runs = []
+    for split in (None, 5):
+        st = qs.new_state()
+        for t in range(T):
+            if split is not None and t == split:
+                host = {k: v.cpu() for k, v in st.items()}      # checkpoint
+                st = {k: v.to(DEV) for k, v in host.items()}    # resume
+            qs.step(st, **_dev_inputs(w.step_inputs(t, B)), step=t)
+        torch.cuda.synchronize()
+        runs.append({k: v.cpu() for k, v in st.items()})
+    for k in runs[0]:
+        assert torch.equal(runs[0][k], runs[1][k]), k
+
+
+def test_misaligned_pointer_is_rejected():
+    from quantized_recurrent_state_qstate_amd import _lib
+    qs = QState(StateConfig(B=1, H=1, dk=64, dv=8, in_dtype="fp32"))
+    st = qs.new_state()
+    buf = torch.zeros(256, device=DEV)
+    with pytest.raises(_lib.QStateError) as e:
+        qs.step(st, buf[1:], buf, buf, buf)
+    assert e.value.status == _lib.QS_EINVAL
