@@ -67,14 +67,15 @@ uint32_t orc_random_bits(const orc_cfg* c, uint64_t e, uint64_t step) {
   return (w >> (8 * (e & 3))) & 0xFFu;
 }
 
-/* Stochastic rounding of x with an sr_bits-bit uniform integer u:
- * floor(x) plus one when u < frac(x) * 2^sr_bits.  frac(x) = x - floor(x)
- * and the scaling by 2^sr_bits are exact, so the decision is exact. */
-float orc_sr_round(float x, uint32_t u, int32_t sr_bits) {
-  float f = floorf(x);
-  float r = x - f;
-  float scale = (sr_bits == 16) ? 65536.0f : 256.0f;
-  return ((float)u < r * scale) ? f + 1.0f : f;
+/* Stochastic rounding (LoReS abstract) in fixed point: x is first rounded
+ * to sr_bits fractional bits (nearest even), X = rne(x * 2^sr_bits); the
+ * element's sr_bits-bit uniform integer u is added below the LSB and the sum
+ * truncated: code = floor((X + u) / 2^sr_bits).  Integer arithmetic, so the
+ * decision is exact; E[code] = X / 2^sr_bits, within 2^-(sr_bits+1) of x.
+ * `xb` is x * 2^sr_bits. */
+float orc_sr_round(float xb, uint32_t u, int32_t sr_bits) {
+  double X = (double)rintf(xb);
+  return (float)floor((X + (double)u) / ldexp(1.0, sr_bits));
 }
 
 /* ------------------------------------------------------------------------ */
@@ -331,13 +332,18 @@ static float requantize_row(const orc_cfg* c, const head_addr* a, int64_t bh, in
       float mag = fabsf(sp[k]);
       if (mag > m) m = mag;
     }
-  float scale = 0.0f, inv = 0.0f;
+  /* Scale and its inverse; a row whose inverse (times 2^sr_bits under
+   * stochastic rounding) overflows, i.e. max below about Q*2^16/FLT_MAX, is
+   * stored as zero. */
+  float scale = 0.0f, inv = 0.0f, invb = 0.0f;
   if (m > 0.0f) {
     scale = m / Q;
     inv = Q / m;
-    if (!isfinite(inv)) {   /* max below Q / FLT_MAX: the row is stored as zero */
+    invb = (c->rounding == 1) ? ldexpf(inv, c->sr_bits) : inv;
+    if (!isfinite(inv) || !isfinite(invb)) {
       scale = 0.0f;
       inv = 0.0f;
+      invb = 0.0f;
     }
   }
   for (int k = 0; k < dk; ++k) {
@@ -346,24 +352,22 @@ static float requantize_row(const orc_cfg* c, const head_addr* a, int64_t bh, in
       put_hp(c, a, v, ~slot, sp[k]);
       continue;
     }
-    float code = 0.0f;
-    if (inv != 0.0f) {
-      float x = sp[k] * inv;
-      if (c->rounding == 0) {
-        code = rintf(x);
-      } else {
-        uint64_t e = ((uint64_t)bh * (uint64_t)c->dv + (uint64_t)v) * (uint64_t)dk + (uint64_t)k;
-        code = orc_sr_round(x, orc_random_bits(c, e, step), c->sr_bits);
-      }
-      if (c->bdr && old) {
-        float xo = old[k] * inv;
-        float d = sp[k] - old[k];
-        if (d > 0.0f && code < xo - c->bdr_bound) code = ceilf(x);
-        else if (d < 0.0f && code > xo + c->bdr_bound) code = floorf(x);
-      }
-      if (code > Q) code = Q;
-      if (code < -Q) code = -Q;
+    float x = sp[k] * inv;
+    float code;
+    if (c->rounding == 0) {
+      code = rintf(x);
+    } else {
+      uint64_t e = ((uint64_t)bh * (uint64_t)c->dv + (uint64_t)v) * (uint64_t)dk + (uint64_t)k;
+      code = orc_sr_round(sp[k] * invb, orc_random_bits(c, e, step), c->sr_bits);
     }
+    if (c->bdr && old) {
+      float xo = old[k] * inv;
+      float d = sp[k] - old[k];
+      if (d > 0.0f && code < xo - c->bdr_bound) code = ceilf(x);
+      else if (d < 0.0f && code > xo + c->bdr_bound) code = floorf(x);
+    }
+    if (code > Q) code = Q;
+    if (code < -Q) code = -Q;
     put_code(c, a, v, slot, (int32_t)code);
   }
   return scale;
