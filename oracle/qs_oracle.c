@@ -553,8 +553,9 @@ static void lrb_phase(const orc_cfg* c, float* W, float* U, int32_t* np_, const 
 /*   delta rule (Gated DeltaNet):   S <- alpha S + u k^T,                     */
 /*                                   u = beta (v - alpha S k)                 */
 /* i.e. alpha (S - beta S k k^T) + beta v k^T written in factored form.      */
-/* Element update: Sp = fmaf(u_v, k_k, d_k * Shat), with Shat the            */
-/* dequantized value; readout o_v = sum_k Sp[v][k] q_k (+ buffer term).      */
+/* Element update: Sp = fmaf(u_v, k_k, (d_k * s_v) * code) for a quantized   */
+/* channel (the decay scales the row scale), fmaf(u_v, k_k, d_k * value) for */
+/* a protected one; readout o_v = sum_k Sp[v][k] q_k (+ buffer term).        */
 /* ------------------------------------------------------------------------ */
 static void head_step(const orc_cfg* c, const layout_t* L, orc_state* st, int64_t bh,
                       const float* q, const float* kin, const float* vin, const float* decay,
@@ -604,11 +605,16 @@ static void head_step(const orc_cfg* c, const layout_t* L, orc_state* st, int64_
     merged = (float*)malloc(sizeof(float) * (size_t)dv * (size_t)dk);
     lrb_phase(c, W, U, &st->n[bh], u, kh, d, s_old, step, small, u_perp, merged, mflag);
   }
-  /* decay + update (+ merged buffer columns) */
+  /* decay + update (+ merged buffer columns).  The decay multiplies the
+   * row scale before the code: (d_k * s_v) * code for a quantized channel,
+   * d_k * value for a protected one. */
   for (int v = 0; v < dv; ++v)
     for (int k = 0; k < dk; ++k) {
       float uu = small[k] ? u_perp[v] : u[v];
-      float x = fmaf(uu, kh[k], d[k] * sh[v * dk + k]);
+      float decayed;
+      if (a.slot[k] >= 0) decayed = (d[k] * s_old[v]) * (float)get_code(c, &a, v, a.slot[k]);
+      else decayed = d[k] * sh[v * dk + k];
+      float x = fmaf(uu, kh[k], decayed);
       if (mflag[k]) x = x + merged[v * dk + k];
       sp[v * dk + k] = x;
     }
