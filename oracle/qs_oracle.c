@@ -68,13 +68,13 @@ uint32_t orc_random_bits(const orc_cfg* c, uint64_t e, uint64_t step) {
 }
 
 /* Stochastic rounding (LoReS abstract) in fixed point: x is first rounded
- * to sr_bits fractional bits (nearest even), X = rne(x * 2^sr_bits); the
- * element's sr_bits-bit uniform integer u is added below the LSB and the sum
- * truncated: code = floor((X + u) / 2^sr_bits).  Integer arithmetic, so the
- * decision is exact; E[code] = X / 2^sr_bits, within 2^-(sr_bits+1) of x.
- * `xb` is x * 2^sr_bits. */
+ * to sr_bits fractional bits, halves up, X = floor(x * 2^sr_bits + 1/2);
+ * the element's sr_bits-bit uniform integer u is added below the LSB and the
+ * sum truncated: code = floor((X + u) / 2^sr_bits).  Integer arithmetic, so
+ * the decision is exact; E[code] = X / 2^sr_bits, within 2^-(sr_bits+1) of
+ * x.  `xb` is x * 2^sr_bits. */
 float orc_sr_round(float xb, uint32_t u, int32_t sr_bits) {
-  double X = (double)rintf(xb);
+  double X = floor((double)xb + 0.5);
   return (float)floor((X + (double)u) / ldexp(1.0, sr_bits));
 }
 

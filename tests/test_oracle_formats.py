@@ -5,8 +5,8 @@
   independent float -> bfloat16 / float16 conversions, over random values,
   exact ties, subnormals, overflow and signed zeros.
 * stochastic rounding (LoReS abstract): enumerating all 2^16 (2^8) random
-  integers gives the exact expectation: x rounded to 16 (8) fractional bits,
-  within 2^-17 (2^-9) of x.
+  integers gives the exact expectation: x rounded to 16 (8) fractional bits
+  (halves up), within 2^-17 (2^-9) of x.
 * the map builder keeps the round-half-up(frac * n) units of smallest decay
   rate per group, ties to the lower index (hand-made statistics).
 """
@@ -61,7 +61,7 @@ def test_16bit_widening_matches_torch(fmt):
                                0.5 + 2.0 ** -17, -7.0 - 2.0 ** -9])
 def test_sr_expectation_exact(bits, x):
     """Enumerating every random integer: outcomes are floor(x) or floor(x)+1 and
-    their mean is x rounded to `bits` fractional bits (nearest even)."""
+    their mean is x rounded to `bits` fractional bits (halves up)."""
     x = float(np.float32(x))
     n = 1 << bits
     xb = float(np.float32(x) * np.float32(n))          # exact scaling
@@ -69,7 +69,7 @@ def test_sr_expectation_exact(bits, x):
     f = np.floor(x)
     assert set(np.unique(outs)) <= {f, f + 1}
     mean = outs.mean()
-    assert mean == np.round(x * n) / n                  # numpy rounds half to even
+    assert mean == np.floor(x * n + 0.5) / n
     assert abs(mean - x) <= 2.0 ** -(bits + 1)
     if x == f:
         assert (outs == x).all()   # values on the grid never move
