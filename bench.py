@@ -32,14 +32,15 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E peak
 METRIC = "quantized-state decode steps/sec and state GB/s (% HBM peak) at B=256, 1 GPU"
-KERNEL_SOURCES = ["quantized_recurrent_state_qstate_amd/csrc/qstate_kernels.hip",
-                  "quantized_recurrent_state_qstate_amd/csrc/qstate_device.hpp"]
+CSRC = os.path.join(ROOT, "quantized_recurrent_state_qstate_amd", "csrc")
 
 
 def kernel_hash() -> str:
+    """Hash of the device sources: counter-derived traffic is valid only for these."""
+    import glob
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
+    for p in sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.hpp"))):
+        with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -126,6 +127,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--graph", action="store_true", help="replay the launches as one captured HIP graph")
+    ap.add_argument("--sr-bits", type=int, default=0, help="override the workload's random bits per element")
+    ap.add_argument("--rounding", choices=["nearest", "stochastic"], default=None,
+                    help="override the workload's rounding mode")
+    ap.add_argument("--map-frac", type=float, default=None,
+                    help="override the fraction of protected heads or channels")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run one device copy of this size (for counter calibration)")
     args = ap.parse_args()
@@ -142,6 +148,12 @@ def main():
     from quantized_recurrent_state_qstate_amd.workloads import WORKLOADS
 
     w = WORKLOADS[args.workload]
+    if args.sr_bits:
+        w = w.scaled(sr_bits=args.sr_bits)
+    if args.rounding:
+        w = w.scaled(rounding=args.rounding)
+    if args.map_frac is not None:
+        w = w.scaled(map_frac=args.map_frac)
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
     m = None
@@ -257,7 +269,9 @@ def main():
         "dtype": "int8+bf16 state, fp32 arithmetic" if w.qbits == 8 else "int4 state, fp32 arithmetic",
         "data": "synthetic",
         "config": {"workload": f"{w.name}: {w.recurrence}, B={w.B}, H={w.H}, dk={w.dk}, dv={w.dv}, "
-                               f"{'int%d' % w.qbits}, map={w.map_mode}:{w.map_frac}, {w.rounding}",
+                               f"{'int%d' % w.qbits}, map={w.map_mode}:{w.map_frac}, {w.rounding}"
+                               + (f" {w.sr_bits}-bit" if w.rounding == "stochastic" else "")
+                               + (", bdr" if w.bdr else "") + (f", lrb r={w.lrb_rank}" if w.lrb_rank else ""),
                    "mode": args.mode, "replicas": R, "graph": bool(graph is not None),
                    "tokens_per_s": round(steps_per_s * w.B, 1)},
         "state_GBps": round(state_gbps, 1),

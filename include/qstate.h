@@ -52,15 +52,18 @@
  *   All-zero buffers are the state S = 0.
  *
  * Rounding of a quantized element x = S_pre * (Q / max):
- *   nearest: ties to even.  stochastic: floor(x) + (u < frac(x) * 2^bits)
- *   with u the element's sr_bits-bit Philox integer, key = seed,
- *   counter = (g as 64 bits, step as 64 bits); e = ((b*H+h)*dv+v)*dk+k is
- *   the logical element index; 16 bits: g = e>>3, half (e&1) of word
- *   (e>>1)&3 (low half for even e); 8 bits: g = e>>4, byte e&3 of word
- *   (e>>2)&3.  BDR: with D = S_pre - S_old and xo = S_old * (Q / max), an
- *   element with D > 0 and code < xo - bound takes ceil(x); with D < 0 and
- *   code > xo + bound takes floor(x).  Codes are clamped to [-Q, Q].
- *   Protected values are stored as the nearest (ties to even) bf16/fp16.
+ *   nearest: ties to even.  stochastic (fixed point, b = sr_bits):
+ *   X = floor(x * 2^b + 1/2), code = floor((X + u) / 2^b), with u the
+ *   element's b-bit Philox integer, key = seed, counter = (g as 64 bits,
+ *   step as 64 bits); e = ((b*H+h)*dv+v)*dk+k is the logical element index;
+ *   16 bits: g = e>>3, half (e&1) of word (e>>1)&3 (low half for even e);
+ *   8 bits: g = e>>4, byte e&3 of word (e>>2)&3.  E[code] = X / 2^b.
+ *   BDR: with D = S_pre - S_old and xo = S_old * (Q / max), an element with
+ *   D > 0 and code < xo - bound takes ceil(x); with D < 0 and code > xo +
+ *   bound takes floor(x).  Codes are clamped to [-Q, Q].  Protected values
+ *   are stored as the nearest (ties to even) bf16/fp16.
+ *   Element update: S_pre = fma(u_v, k_k, (d_k * s_v) * code) for a
+ *   quantized channel, fma(u_v, k_k, d_k * value) for a protected one.
  *
  * Conventions: every call is asynchronous on `stream` (a hipStream_t; NULL
  * = the null stream).  The return code reports errors found on the host
@@ -99,7 +102,8 @@ typedef struct {
   uint32_t abi_version;   /* QSTATE_ABI_VERSION */
   int32_t kind;           /* qs_kind */
   int32_t decay_mode;     /* qs_decay_mode; the delta rule takes HEAD only */
-  int32_t B, H;           /* batch (>= 0; 0 = every call is a no-op), heads (>= 1) */
+  int32_t B, H;           /* batch (>= 0; 0 = every call is a no-op), heads (>= 1);
+                             B*H*dv*dk must stay below 2^35 */
   int32_t dk;             /* key dim: 64, 128 or 256 */
   int32_t dv;             /* value dim: 1..256 */
   int32_t qbits;          /* 8 or 4 */

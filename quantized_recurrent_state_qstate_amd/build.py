@@ -1,5 +1,10 @@
 """Build libqstate.so (gfx950) in-tree with hipcc.
 
+Each kernel translation unit (one per qbits x rounding mode, plus the
+quantize/dequantize one) and the host C-ABI file compile in parallel to
+objects under build/, then link into quantized_recurrent_state_qstate_amd/
+libqstate.so.
+
 Flags:
   --offload-arch=gfx950            CDNA4 code object only
   -ffp-contract=off                only the explicit fmaf() calls fuse, so the
@@ -10,6 +15,8 @@ Flags:
 """
 from __future__ import annotations
 
+import concurrent.futures
+import glob
 import os
 import subprocess
 import sys
@@ -18,33 +25,54 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
+OBJ = os.path.join(ROOT, "build", "qstate")
 LIB = os.path.join(PKG, "libqstate.so")
-SOURCES = [os.path.join(CSRC, "qstate_kernels.hip"), os.path.join(CSRC, "qstate_host.cpp")]
-HEADERS = [os.path.join(CSRC, "qstate_internal.hpp"), os.path.join(CSRC, "qstate_device.hpp"),
-           os.path.join(INCLUDE, "qstate.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-ffp-contract=off", "-fno-gpu-flush-denormals-to-zero",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-Wall", "-Wno-unused-result",
+    "-Wall", "-Wno-unused-result", "-Wno-unused-function",
 ]
+
+
+def sources():
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip"))) + [os.path.join(CSRC, "qstate_host.cpp")]
+
+
+def headers():
+    return sorted(glob.glob(os.path.join(CSRC, "*.hpp"))) + [os.path.join(INCLUDE, "qstate.h")]
 
 
 def stale() -> bool:
     if not os.path.exists(LIB):
         return True
     t = os.path.getmtime(LIB)
-    return any(os.path.getmtime(p) > t for p in SOURCES + HEADERS)
+    return any(os.path.getmtime(p) > t for p in sources() + headers())
 
 
-def build(force: bool = True, verbose: bool = False) -> str:
+def _compile(src: str, verbose: bool) -> str:
+    obj = os.path.join(OBJ, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
+    if verbose:
+        print(" ".join(cmd), file=sys.stderr)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
+    return obj
+
+
+def build(force: bool = True, verbose: bool = False, jobs: int = 0) -> str:
     """Compile libqstate.so; returns its path."""
     if not force and not stale():
         return LIB
+    os.makedirs(OBJ, exist_ok=True)
+    jobs = jobs or min(8, os.cpu_count() or 1)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), sources()))
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-I", CSRC, *SOURCES, "-o", tmp]
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
     subprocess.run(cmd, check=True)
@@ -53,4 +81,4 @@ def build(force: bool = True, verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build(force=True, verbose=True))
+    print(build(force=True, verbose="-v" in sys.argv))

@@ -18,8 +18,9 @@ __device__ __forceinline__ void philox10(uint32_t (&x)[4], uint32_t k0, uint32_t
   for (int r = 0; r < 10; ++r) {
     const uint64_t p0 = (uint64_t)0xD2511F53u * (uint64_t)x[0];
     const uint64_t p1 = (uint64_t)0xCD9E8D57u * (uint64_t)x[2];
-    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ x[1] ^ k0;
-    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ x[3] ^ k1;
+    // three-input xor in one v_bitop3_b32 (truth table 0x96 = a ^ b ^ c)
+    const uint32_t n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), x[1], k0, 0x96);
+    const uint32_t n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), x[3], k1, 0x96);
     x[1] = (uint32_t)p1;
     x[3] = (uint32_t)p0;
     x[0] = n0;
@@ -32,15 +33,16 @@ __device__ __forceinline__ void philox10(uint32_t (&x)[4], uint32_t k0, uint32_t
 // Random integers for EPL consecutive elements starting at logical index e0
 // (e0 a multiple of 8).  RND 1: 16 bits per element, block g = e>>3, low
 // half of word (e>>1)&3 for even e.  RND 2: 8 bits, block g = e>>4, byte
-// e&3 of word (e>>2)&3.  Counter = (g lo, g hi, step lo, step hi).
+// e&3 of word (e>>2)&3.  Counter = (g lo, g hi, step lo, step hi); element
+// indices stay below 2^35 (checked at init), so g hi is 0.
 template <int RND, int EPL>
 __device__ __forceinline__ void rand_bits(uint64_t e0, uint32_t s0, uint32_t s1, uint32_t t0,
                                           uint32_t t1, uint32_t (&rb)[EPL]) {
   if constexpr (RND == 1) {
 #pragma unroll
     for (int g = 0; g < EPL / 8; ++g) {
-      const uint64_t n = (e0 >> 3) + (uint64_t)g;
-      uint32_t x[4] = {(uint32_t)n, (uint32_t)(n >> 32), t0, t1};
+      const uint32_t n = (uint32_t)(e0 >> 3) + (uint32_t)g;
+      uint32_t x[4] = {n, 0u, t0, t1};
       philox10(x, s0, s1);
 #pragma unroll
       for (int j = 0; j < 8; ++j) rb[g * 8 + j] = (j & 1) ? (x[j >> 1] >> 16) : (x[j >> 1] & 0xFFFFu);
@@ -49,15 +51,15 @@ __device__ __forceinline__ void rand_bits(uint64_t e0, uint32_t s0, uint32_t s1,
     if constexpr (EPL >= 16) {
 #pragma unroll
       for (int g = 0; g < EPL / 16; ++g) {
-        const uint64_t n = (e0 >> 4) + (uint64_t)g;
-        uint32_t x[4] = {(uint32_t)n, (uint32_t)(n >> 32), t0, t1};
+        const uint32_t n = (uint32_t)(e0 >> 4) + (uint32_t)g;
+        uint32_t x[4] = {n, 0u, t0, t1};
         philox10(x, s0, s1);
 #pragma unroll
         for (int j = 0; j < 16; ++j) rb[g * 16 + j] = (x[j >> 2] >> (8 * (j & 3))) & 0xFFu;
       }
     } else {
-      const uint64_t n = e0 >> 4;
-      uint32_t x[4] = {(uint32_t)n, (uint32_t)(n >> 32), t0, t1};
+      const uint32_t n = (uint32_t)(e0 >> 4);
+      uint32_t x[4] = {n, 0u, t0, t1};
       philox10(x, s0, s1);
       const bool hi = (e0 & 8u) != 0;   // second half of the 16-element block
       const uint32_t w0 = hi ? x[2] : x[0];
@@ -92,6 +94,21 @@ __device__ __forceinline__ float max8(float x) {
   x = fmaxf(x, dppf<kDppXor2>(x));
   x = fmaxf(x, dppf<kDppHalfMirror>(x));
   return x;
+}
+
+// Maximum of non-negative floats over the row group, on their bit patterns
+// (for x >= 0 the unsigned order of the bits is the numeric order), so each
+// step is one v_max_u32 with a DPP operand.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dppu(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ float absmax8(float x) {
+  uint32_t u = __float_as_uint(x);
+  u = max(u, dppu<kDppXor1>(u));
+  u = max(u, dppu<kDppXor2>(u));
+  u = max(u, dppu<kDppHalfMirror>(u));
+  return __uint_as_float(u);
 }
 
 // ---------------------------------------------------------------------------
@@ -144,6 +161,16 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return u >> 16;
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 values to a packed bf16 pair (round to nearest even), one
+// v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
 __device__ __forceinline__ float f16_bits_to_f32(uint32_t b) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
 }
@@ -182,12 +209,9 @@ __device__ __forceinline__ void load_f32(const float* p, float (&f)[EPL]) {
   for (int i = 0; i < EPL; ++i) f[i] = __uint_as_float(w[i]);
 }
 
-// Dequantize EPL codes of one row slice: scale * code.
+// Dequantize EPL codes of one row slice held in words w: scale * code.
 template <int QB, int EPL>
-__device__ __forceinline__ void load_codes(const uint8_t* p, float s, float (&sh)[EPL]) {
-  constexpr int NB = EPL * QB / 8;
-  uint32_t w[NB / 4];
-  load_bytes<NB>(p, w);
+__device__ __forceinline__ void dequant_words(const uint32_t (&w)[EPL * QB / 32], float s, float (&sh)[EPL]) {
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
     int32_t c;
@@ -195,6 +219,13 @@ __device__ __forceinline__ void load_codes(const uint8_t* p, float s, float (&sh
     else c = (int32_t)(w[i >> 3] << (28 - 4 * (i & 7))) >> 28;
     sh[i] = s * (float)c;
   }
+}
+
+template <int QB, int EPL>
+__device__ __forceinline__ void load_codes(const uint8_t* p, float s, float (&sh)[EPL]) {
+  uint32_t w[EPL * QB / 32];
+  load_bytes<EPL * QB / 8>(p, w);
+  dequant_words<QB, EPL>(w, s, sh);
 }
 
 template <int QB, int EPL>
@@ -239,63 +270,82 @@ __device__ __forceinline__ void store_hp(uint8_t* p, int dt, const float (&f)[EP
     store_bytes<EPL * 4>(p, w);
   } else {
     uint32_t w[EPL / 2];
+    if (dt == 1) {
 #pragma unroll
-    for (int i = 0; i < EPL / 2; ++i) w[i] = 0u;
+      for (int i = 0; i < EPL / 2; ++i) w[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
+    } else {
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      const uint32_t b = (dt == 1) ? f32_to_bf16_bits(f[i]) : f32_to_f16_bits(f[i]);
-      w[i >> 1] |= b << (16 * (i & 1));
+      for (int i = 0; i < EPL / 2; ++i) w[i] = f32_to_f16_bits(f[2 * i]) | (f32_to_f16_bits(f[2 * i + 1]) << 16);
     }
     store_bytes<EPL * 2>(p, w);
   }
 }
 
 // ---------------------------------------------------------------------------
-// Row scale (value-axis grouping): scale = max / Q, inv = Q / max, both
-// correctly rounded; a zero row, or one whose inverse overflows, is zero.
+// Row scale (value-axis grouping): scale = max / Q and inv = Q / max, both
+// correctly rounded; invb = inv * 2^SRB (exact scaling) for stochastic
+// rounding with SRB random bits.  A zero row, or one whose inv (or invb)
+// overflows, is stored as zero.
 // ---------------------------------------------------------------------------
-template <int QB>
-__device__ __forceinline__ void row_scale(float m, float& scale, float& inv) {
+template <int QB, int SRB>
+__device__ __forceinline__ void row_scale(float m, float& scale, float& inv, float& invb) {
   constexpr float Q = (QB == 8) ? 127.0f : 7.0f;
   scale = 0.0f;
   inv = 0.0f;
+  invb = 0.0f;
   if (m > 0.0f) {
-    scale = m / Q;
-    inv = Q / m;
-    if (!__builtin_isfinite(inv)) {
-      scale = 0.0f;
-      inv = 0.0f;
+    const float s = m / Q;
+    const float i = Q / m;
+    const float ib = i * (float)(1u << SRB);
+    if (__builtin_isfinite(ib)) {
+      scale = s;
+      inv = i;
+      invb = ib;
     }
   }
 }
 
-// Round one element x = sp * inv to a code: nearest-even (RND 0) or
-// stochastic with random integer rb (RND 1: 16 bits, RND 2: 8 bits); with
-// BDR, a level on the wrong side of the old value (sh) by more than `bound`
-// is replaced by the neighbour of x toward the update; clamp to [-Q, Q].
-template <int QB, int RND>
-__device__ __forceinline__ int32_t round_elem(float sp, float sh, float inv, uint32_t rb, int bdr,
+// floor(x + 1/2) as an integer, one v_cvt_rpi_i32_f32 (exact for |x| < 2^23,
+// where x + 1/2 is representable).
+__device__ __forceinline__ int32_t cvt_rpi(float x) {
+  int32_t r;
+  asm("v_cvt_rpi_i32_f32 %0, %1" : "=v"(r) : "v"(x));
+  return r;
+}
+
+// Random bits per element for rounding mode RND (0 nearest, 1: 16, 2: 8).
+template <int RND>
+constexpr int sr_bits_of() { return RND == 1 ? 16 : (RND == 2 ? 8 : 0); }
+
+// Round one element to a code.  Nearest: rint(sp * inv), ties to even.
+// Stochastic (fixed point): X = floor(sp * invb + 1/2) is x rounded to SRB
+// fractional bits; the element's SRB-bit integer rb is added below the LSB
+// and the sum truncated, code = (X + rb) >> SRB.  BDR: with x = sp * inv and
+// xo = sh * inv (old value on the new grid), a code below xo - bound while
+// the element grew takes ceil(x); above xo + bound while it shrank takes
+// floor(x).  Codes are clamped to [-Q, Q].  A zero row (inv = 0) gives 0.
+template <int QB, int RND, int BDR>
+__device__ __forceinline__ int32_t round_elem(float sp, float sh, float inv, float invb, uint32_t rb,
                                               float bound) {
-  constexpr float Q = (QB == 8) ? 127.0f : 7.0f;
-  if (inv == 0.0f) return 0;
-  const float x = sp * inv;
-  float c;
+  constexpr int32_t Q = (QB == 8) ? 127 : 7;
+  int32_t c;
   if constexpr (RND == 0) {
-    c = rintf(x);
+    c = (int32_t)rintf(sp * inv);
   } else {
-    const float f = floorf(x);
-    const float r = x - f;
-    constexpr float sc = (RND == 1) ? 65536.0f : 256.0f;
-    c = ((float)rb < r * sc) ? f + 1.0f : f;
+    constexpr int SRB = sr_bits_of<RND>();
+    const int32_t X = cvt_rpi(sp * invb);
+    c = (X + (int32_t)rb) >> SRB;
   }
-  if (bdr) {
+  if constexpr (BDR) {
+    const float x = sp * inv;
     const float xo = sh * inv;
     const float d = sp - sh;
-    if (d > 0.0f && c < xo - bound) c = ceilf(x);
-    else if (d < 0.0f && c > xo + bound) c = floorf(x);
+    const float cf = (float)c;
+    const int32_t up = (int32_t)ceilf(x);
+    const int32_t dn = (int32_t)floorf(x);
+    c = (d > 0.0f && cf < xo - bound) ? up : ((d < 0.0f && cf > xo + bound) ? dn : c);
   }
-  c = fminf(fmaxf(c, -Q), Q);
-  return (int32_t)c;
+  return c < -Q ? -Q : (c > Q ? Q : c);
 }
 
 }  // namespace qs

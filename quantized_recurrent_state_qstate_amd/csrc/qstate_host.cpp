@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <numeric>
@@ -49,8 +50,35 @@ struct Plan {
   qstate_sizes sizes{};
   int family = qs::kFamDense;
   int row_chunks = 1;
+  int dense_rpl = 1;
+  int dense_threads = 256;
   uint32_t lds = 0;
+  uint64_t prot_mask = 0;       // dense family: protected heads
+  uint64_t code_hblk = 0, hp_hblk = 0;
 };
+
+// Rows per lane and row groups per workgroup of the dense kernel.  Default:
+// two rows per lane when a head has more than 32 rows; QSTATE_DENSE_RPL
+// (1, 2) and QSTATE_DENSE_GROUPS (8, 16, 32) override for tuning.
+int env_int(const char* name, int dflt) {
+  const char* e = std::getenv(name);
+  if (!e || !*e) return dflt;
+  char* end = nullptr;
+  long v = std::strtol(e, &end, 10);
+  return (end && *end == 0) ? (int)v : dflt;
+}
+
+void dense_shape(int dv, int* rpl, int* threads, int* chunks) {
+  int r = env_int("QSTATE_DENSE_RPL", dv > 32 ? 2 : 1);
+  if (r != 1 && r != 2) r = dv > 32 ? 2 : 1;
+  int ng = (dv + r - 1) / r;                 // row groups needed for one head
+  ng = std::min(32, (ng + 7) / 8 * 8);       // whole waves
+  const int ng_env = env_int("QSTATE_DENSE_GROUPS", 0);
+  if (ng_env == 8 || ng_env == 16 || ng_env == 32) ng = ng_env;
+  *rpl = r;
+  *threads = 8 * ng;
+  *chunks = (dv + ng * r - 1) / (ng * r);
+}
 
 bool protected_channel(const qstate_config* c, int h, int k) {
   if (c->map_mode == QS_MAP_NONE) return false;
@@ -135,12 +163,16 @@ qs_status make_plan(const qstate_config* c, Plan* p) {
   p->sizes.lrb_U = BH * (uint64_t)dk * r * 4u;
   p->sizes.lrb_n = r > 0 ? BH * 4u : 0u;
 
-  p->row_chunks = (dv + 31) / 32;
+  dense_shape(dv, &p->dense_rpl, &p->dense_threads, &p->row_chunks);
   if (c->lrb_rank > 0) {
     p->family = qs::kFamLrb;
     const uint64_t floats = (uint64_t)dv * r + (uint64_t)dk * r + 4u * (uint64_t)dv + 3u * (uint64_t)dk + 36u;
     p->lds = (uint32_t)(floats * 4u + 2u * (uint64_t)dk);
-  } else if (c->map_mode == QS_MAP_KEY) {
+  } else if (c->map_mode == QS_MAP_KEY ||
+             (c->map_mode == QS_MAP_HEAD && (c->hp_dtype == QS_FP32 || H > 64))) {
+    // key-channel maps, fp32 protected heads and head maps over more than 64
+    // heads run the LDS-staged kernel; the dense kernel handles whole-head
+    // maps with 16-bit protected heads (addressed from a 64-bit head mask)
     p->family = qs::kFamMixed;
     uint64_t mx = 0;
     for (int h = 0; h < H; ++h) {
@@ -152,11 +184,20 @@ qs_status make_plan(const qstate_config* c, Plan* p) {
     (void)any_mixed;
   } else {
     p->family = qs::kFamDense;
+    for (int h = 0; h < H && h < 64; ++h)
+      if (p->head_type[h] == qs::kHeadProt) p->prot_mask |= 1ull << h;
+    p->code_hblk = round16((uint64_t)dv * (((uint64_t)dk * (uint64_t)c->qbits + 7u) / 8u));
+    p->hp_hblk = round16((uint64_t)dv * (uint64_t)dk * hpb);
   }
   if (p->lds > kMaxLds)
     return fail(QS_EUNSUPPORTED, "a head needs %u bytes of LDS staging (max %u)", p->lds, kMaxLds);
   const uint64_t grid = BH * (p->family == qs::kFamDense ? (uint64_t)p->row_chunks : 1u);
   if (grid > 0x7FFFFFFFu) return fail(QS_EUNSUPPORTED, "B*H too large for one launch");
+  // the kernels form Philox block counters in 32 bits: element indices
+  // B*H*dv*dk must stay below 2^35
+  if (BH * (uint64_t)dv * (uint64_t)dk >= (1ull << 35))
+    return fail(QS_EUNSUPPORTED, "B*H*dv*dk = %llu elements (limit 2^35 per call)",
+                (unsigned long long)(BH * (uint64_t)dv * (uint64_t)dk));
   return QS_OK;
 }
 
@@ -219,6 +260,11 @@ qs::Args base_args(const qstate_handle* h, const qstate_tensors* st) {
   a.hp_bstride = h->plan.hp_bstride;
   a.t = h->t;
   a.row_chunks = h->plan.row_chunks;
+  a.dense_rpl = h->plan.dense_rpl;
+  a.dense_threads = h->plan.dense_threads;
+  a.prot_mask = h->plan.prot_mask;
+  a.code_hblk = h->plan.code_hblk;
+  a.hp_hblk = h->plan.hp_hblk;
   a.hp_dtype = c.hp_dtype == QS_FP32 ? 0 : (c.hp_dtype == QS_BF16 ? 1 : 2);
   a.in_bf16 = c.in_dtype == QS_BF16 ? 1 : 0;
   a.decay_key = c.decay_mode == QS_DECAY_KEY ? 1 : 0;

@@ -44,7 +44,12 @@ struct Args {
   int32_t B, H, dk, dv;
   uint64_t code_bstride, hp_bstride;
   DevTables t;
-  int32_t row_chunks;  // dense kernels: 32-row chunks per head
+  int32_t row_chunks;  // dense kernel: work items (row chunks) per head
+  int32_t dense_rpl;   // dense kernel: rows per lane (1, 2)
+  int32_t dense_threads;  // dense kernel: threads per workgroup (8 per row group)
+  uint64_t prot_mask;  // dense kernel: bit h set = head h protected (H <= 64 with a head map)
+  uint64_t code_hblk;  // dense kernel: bytes of one quantized head's code block
+  uint64_t hp_hblk;    // dense kernel: bytes of one protected head's block
   int32_t hp_dtype;    // 0 fp32, 1 bf16, 2 fp16
   int32_t in_bf16;     // q,k,v are bf16 (else fp32)
   int32_t decay_key;   // decay per key channel (else per head)
@@ -63,8 +68,10 @@ struct Args {
 // Kernel families chosen at init.
 enum StepFamily : int { kFamDense = 0, kFamMixed = 1, kFamLrb = 2 };
 
-// Launchers (defined in qstate_kernels.hip).  Return hipSuccess or the
+// Launchers (qstate_misc.hip; launch_step_qr<QB, RND> in qstate_step_q*_*.hip).  Return hipSuccess or the
 // launch error.  `rnd`: 0 nearest, 1 stochastic 16-bit, 2 stochastic 8-bit.
+template <int QB, int RND>
+hipError_t launch_step_qr(int family, int delta, const Args& a, hipStream_t s);
 hipError_t launch_step(int family, int qbits, int rnd, int delta, const Args& a,
                        hipStream_t s);
 hipError_t launch_quantize(const Args& a, hipStream_t s);

@@ -1,0 +1,204 @@
+// libqstate kernels off the decode path (quantize, dequantize, fill) and the
+// dispatch of the step launch to its qbits x rounding translation unit.
+#include <cstdio>
+
+#include "qstate_step_kernels.hpp"
+
+namespace qs {
+
+namespace {
+__device__ __forceinline__ const uint8_t* code_block_m(const Args& a, uint32_t b, uint32_t h) {
+  return a.codes + (uint64_t)b * a.code_bstride + a.t.code_off[h];
+}
+__device__ __forceinline__ const uint8_t* hp_block_m(const Args& a, uint32_t b, uint32_t h) {
+  return a.hp + (uint64_t)b * a.hp_bstride + a.t.hp_off[h];
+}
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Quantize / dequantize: one thread per row, channels in order (any layout).
+// Not on the decode path.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_quantize(const Args a) {
+  const uint64_t row = (uint64_t)blockIdx.x * 256u + threadIdx.x;
+  const uint64_t nrows = (uint64_t)a.B * (uint64_t)a.H * (uint64_t)a.dv;
+  if (row >= nrows) return;
+  const int dk = a.dk;
+  const uint64_t bh = row / (uint64_t)a.dv;
+  const uint32_t v = (uint32_t)(row % (uint64_t)a.dv);
+  const uint32_t h = (uint32_t)(bh % (uint64_t)a.H);
+  const uint32_t b = (uint32_t)(bh / (uint64_t)a.H);
+  const int nq = a.t.nq[h];
+  const int nhp = dk - nq;
+  const int hpb = hp_elem_bytes(a.hp_dtype);
+  const uint32_t rq = (uint32_t)(nq * a.qbits + 7) / 8u;
+  uint8_t* crow = const_cast<uint8_t*>(a.codes ? code_block_m(a, b, h) : nullptr);
+  if (crow) crow += (uint64_t)v * rq;
+  uint8_t* hrow = const_cast<uint8_t*>(a.hp ? hp_block_m(a, b, h) : nullptr);
+  if (hrow) hrow += (uint64_t)v * (uint64_t)nhp * (uint64_t)hpb;
+  const uint16_t* sl = a.t.slots + (uint64_t)h * dk;
+  const float* srow = a.S + row * (uint64_t)dk;
+  float m = 0.0f;
+  for (int k = 0; k < dk; ++k)
+    if (!(sl[k] & kSlotProt)) m = fmaxf(m, fabsf(srow[k]));
+  float scale, inv, invb;
+  const int srb = a.rounding ? a.sr_bits : 0;
+  if (a.qbits == 8) {
+    if (srb == 16) row_scale<8, 16>(m, scale, inv, invb);
+    else if (srb == 8) row_scale<8, 8>(m, scale, inv, invb);
+    else row_scale<8, 0>(m, scale, inv, invb);
+  } else {
+    if (srb == 16) row_scale<4, 16>(m, scale, inv, invb);
+    else if (srb == 8) row_scale<4, 8>(m, scale, inv, invb);
+    else row_scale<4, 0>(m, scale, inv, invb);
+  }
+  uint64_t cached = ~(uint64_t)0;
+  uint32_t x[4] = {0, 0, 0, 0};
+  uint32_t pend = 0;
+  for (int k = 0; k < dk; ++k) {
+    const uint32_t s = sl[k] & 0x7FFFu;
+    const float val = srow[k];
+    if (sl[k] & kSlotProt) {
+      if (a.hp_dtype == 0) reinterpret_cast<float*>(hrow)[s] = val;
+      else reinterpret_cast<uint16_t*>(hrow)[s] =
+          (uint16_t)((a.hp_dtype == 1) ? f32_to_bf16_bits(val) : f32_to_f16_bits(val));
+      continue;
+    }
+    uint32_t rbits = 0;
+    if (a.rounding) {
+      const uint64_t e = row * (uint64_t)dk + (uint64_t)k;
+      const uint64_t g = (a.sr_bits == 16) ? (e >> 3) : (e >> 4);
+      if (g != cached) {
+        x[0] = (uint32_t)g;
+        x[1] = (uint32_t)(g >> 32);
+        x[2] = a.step_lo;
+        x[3] = a.step_hi;
+        philox10(x, a.seed_lo, a.seed_hi);
+        cached = g;
+      }
+      rbits = (a.sr_bits == 16) ? ((e & 1u) ? (x[(e >> 1) & 3u] >> 16) : (x[(e >> 1) & 3u] & 0xFFFFu))
+                                : ((x[(e >> 2) & 3u] >> (8u * (uint32_t)(e & 3u))) & 0xFFu);
+    }
+    int32_t c;
+    if (a.qbits == 8) {
+      c = !a.rounding ? round_elem<8, 0, 0>(val, 0.0f, inv, invb, 0u, 0.0f)
+                      : (a.sr_bits == 16 ? round_elem<8, 1, 0>(val, 0.0f, inv, invb, rbits, 0.0f)
+                                         : round_elem<8, 2, 0>(val, 0.0f, inv, invb, rbits, 0.0f));
+      crow[s] = (uint8_t)c;
+    } else {
+      c = !a.rounding ? round_elem<4, 0, 0>(val, 0.0f, inv, invb, 0u, 0.0f)
+                      : (a.sr_bits == 16 ? round_elem<4, 1, 0>(val, 0.0f, inv, invb, rbits, 0.0f)
+                                         : round_elem<4, 2, 0>(val, 0.0f, inv, invb, rbits, 0.0f));
+      if ((s & 1u) == 0u) {
+        pend = (uint32_t)c & 0xFu;
+        if ((int)s == nq - 1) crow[s >> 1] = (uint8_t)pend;
+      } else {
+        crow[s >> 1] = (uint8_t)(pend | (((uint32_t)c & 0xFu) << 4));
+      }
+    }
+  }
+  a.scales[row] = scale;
+}
+
+__global__ __launch_bounds__(256) void k_dequantize(const Args a) {
+  const uint64_t row = (uint64_t)blockIdx.x * 256u + threadIdx.x;
+  const uint64_t nrows = (uint64_t)a.B * (uint64_t)a.H * (uint64_t)a.dv;
+  if (row >= nrows) return;
+  const int dk = a.dk;
+  const uint64_t bh = row / (uint64_t)a.dv;
+  const uint32_t v = (uint32_t)(row % (uint64_t)a.dv);
+  const uint32_t h = (uint32_t)(bh % (uint64_t)a.H);
+  const uint32_t b = (uint32_t)(bh / (uint64_t)a.H);
+  const int nq = a.t.nq[h];
+  const int nhp = dk - nq;
+  const int hpb = hp_elem_bytes(a.hp_dtype);
+  const uint32_t rq = (uint32_t)(nq * a.qbits + 7) / 8u;
+  const uint8_t* crow = a.codes ? code_block_m(a, b, h) + (uint64_t)v * rq : nullptr;
+  const uint8_t* hrow = a.hp ? hp_block_m(a, b, h) + (uint64_t)v * (uint64_t)nhp * (uint64_t)hpb : nullptr;
+  const uint16_t* sl = a.t.slots + (uint64_t)h * dk;
+  const float scale = a.scales ? a.scales[row] : 0.0f;
+  const int r = a.lrb_rank;
+  const int n = r > 0 ? a.n[bh] : 0;
+  const float* W = r > 0 ? a.W + (bh * (uint64_t)a.dv + v) * (uint64_t)r : nullptr;
+  const float* U = r > 0 ? a.U + bh * (uint64_t)dk * (uint64_t)r : nullptr;
+  float* orow = a.S_out + row * (uint64_t)dk;
+  for (int k = 0; k < dk; ++k) {
+    const uint32_t s = sl[k] & 0x7FFFu;
+    float val;
+    if (sl[k] & kSlotProt) {
+      if (a.hp_dtype == 0) val = reinterpret_cast<const float*>(hrow)[s];
+      else {
+        const uint32_t bits = reinterpret_cast<const uint16_t*>(hrow)[s];
+        val = (a.hp_dtype == 1) ? bf16_bits_to_f32(bits) : f16_bits_to_f32(bits);
+      }
+    } else {
+      int32_t c;
+      if (a.qbits == 8) c = (int32_t)(int8_t)crow[s];
+      else c = (int32_t)((uint32_t)crow[s >> 1] << (28 - 4 * (s & 1))) >> 28;
+      val = scale * (float)c;
+    }
+    if (n > 0) {
+      float col = 0.0f;
+      for (int j = 0; j < n; ++j) col = fmaf(W[j], U[(uint64_t)k * r + j], col);
+      val = val + col;
+    }
+    orow[k] = val;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_zero(uint32_t* p, uint64_t nwords) {
+  for (uint64_t i = (uint64_t)blockIdx.x * 256u + threadIdx.x; i < nwords; i += (uint64_t)gridDim.x * 256u)
+    p[i] = 0u;
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_step(int family, int qbits, int rnd, int delta, const Args& a, hipStream_t s) {
+  if (qbits == 8) {
+    switch (rnd) {
+      case 0: return launch_step_qr<8, 0>(family, delta, a, s);
+      case 1: return launch_step_qr<8, 1>(family, delta, a, s);
+      case 2: return launch_step_qr<8, 2>(family, delta, a, s);
+    }
+  } else {
+    switch (rnd) {
+      case 0: return launch_step_qr<4, 0>(family, delta, a, s);
+      case 1: return launch_step_qr<4, 1>(family, delta, a, s);
+      case 2: return launch_step_qr<4, 2>(family, delta, a, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_quantize(const Args& a, hipStream_t s) {
+  const uint64_t nrows = (uint64_t)a.B * (uint64_t)a.H * (uint64_t)a.dv;
+  if (nrows == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_quantize, dim3((uint32_t)((nrows + 255u) / 256u)), dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.lrb_rank == 0) return e;
+  const uint64_t bh = (uint64_t)a.B * (uint64_t)a.H;
+  const uint64_t nW = bh * (uint64_t)a.dv * (uint64_t)a.lrb_rank;
+  const uint64_t nU = bh * (uint64_t)a.dk * (uint64_t)a.lrb_rank;
+  hipLaunchKernelGGL(k_zero, dim3(1024), dim3(256), 0, s, reinterpret_cast<uint32_t*>(a.W), nW);
+  hipLaunchKernelGGL(k_zero, dim3(1024), dim3(256), 0, s, reinterpret_cast<uint32_t*>(a.U), nU);
+  hipLaunchKernelGGL(k_zero, dim3(64), dim3(256), 0, s, reinterpret_cast<uint32_t*>(a.n), bh);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequantize(const Args& a, hipStream_t s) {
+  const uint64_t nrows = (uint64_t)a.B * (uint64_t)a.H * (uint64_t)a.dv;
+  if (nrows == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_dequantize, dim3((uint32_t)((nrows + 255u) / 256u)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+const char* step_kernel_name(int family, int qbits, int rnd, int delta, int dk) {
+  static thread_local char buf[96];
+  const char* fam = family == kFamDense ? "dense" : (family == kFamMixed ? "mixed" : "lrb");
+  const char* rn = rnd == 0 ? "rtn" : (rnd == 1 ? "sr16" : "sr8");
+  snprintf(buf, sizeof(buf), "k_step_%s<int%d,%s,%s,dk%d>", fam, qbits, rn, delta ? "delta" : "additive", dk);
+  return buf;
+}
+
+}  // namespace qs

@@ -1,4 +1,5 @@
-// gfx950 kernels of libqstate: the fused quantized-state decode step.
+// gfx950 step kernels of libqstate (templates; instantiated per qbits and
+// rounding mode in qstate_step_q*_r*.hip): the fused quantized-state decode step.
 //
 // One decode step = dequantize -> decay + update -> readout -> requantize,
 // in one pass over the stored state (abstract of "Preserving Updates in
@@ -14,7 +15,8 @@
 // Every reduction of the step (delta-rule S k, readout S q, row max) is
 // over k inside one row, so it is three DPP steps inside the 8-lane group;
 // rows never exchange data.  A 256-thread workgroup covers 32 rows of one
-// head.
+// head per row a lane holds (two rows per lane when a head has more than 32).
+#pragma once
 #include "qstate_device.hpp"
 #include "qstate_internal.hpp"
 
@@ -47,87 +49,368 @@ __device__ __forceinline__ void load_decay(const Args& a, uint64_t bh, int k0, f
 
 // ---------------------------------------------------------------------------
 // Dense step: every head either fully quantized or fully protected
-// (precision map NONE or HEAD).
+// (precision map NONE or HEAD).  A workgroup has NG row groups of 8 lanes
+// (NG = blockDim / 8) and covers NG * RPL rows of one head: lane group g
+// holds rows g, g + NG, ... so the per-lane inputs (q, k, decay) are loaded
+// and widened once for RPL rows; every row's state load is issued before any
+// row is computed.
 // ---------------------------------------------------------------------------
-template <int QB, int RND, int DELTA, int EPL>
-__global__ __launch_bounds__(256) void k_step_dense(const Args a) {
+
+// Row scales of the RPL rows a lane group holds.  The 2*RPL correctly
+// rounded divisions (max/Q and Q/max per row) are spread over the group's
+// lanes -- lane j computes division j -- and gathered back with ds_bpermute,
+// instead of every lane computing all of them.
+template <int QB, int SRB, int RPL>
+__device__ __forceinline__ void group_row_scales(const float (&m)[RPL], int lane8, float (&scale)[RPL],
+                                                 float (&inv)[RPL], float (&invb)[RPL]) {
+  constexpr float Q = (QB == 8) ? 127.0f : 7.0f;
+  const int rr = (lane8 >> 1) & (RPL - 1);
+  float mr = m[0];
+#pragma unroll
+  for (int r = 1; r < RPL; ++r) mr = (rr == r) ? m[r] : mr;
+  const bool odd = lane8 & 1;
+  const float num = odd ? Q : mr;
+  const float den = odd ? mr : Q;
+  const float qv = num / den;               // even lane: max/Q, odd lane: Q/max
+  const int base = (int)(threadIdx.x & ~7u) & 63;
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) {
+    const float s = __shfl(qv, base + 2 * r, 64);
+    const float i = __shfl(qv, base + 2 * r + 1, 64);
+    const float ib = i * (float)(1u << SRB);
+    const bool ok = __builtin_isfinite(ib);   // max 0 gives Q/0 = inf: a zero row
+    scale[r] = ok ? s : 0.0f;
+    inv[r] = ok ? i : 0.0f;
+    invb[r] = ok ? ib : 0.0f;
+  }
+}
+
+// Pack four 32-bit words' byte B into one word (byte i from word i).
+template <int B>
+__device__ __forceinline__ uint32_t pack4(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3) {
+  constexpr uint32_t sel = 0x0c0c0000u | ((4u + B) << 8) | (uint32_t)B;
+  const uint32_t p01 = __builtin_amdgcn_perm(c1, c0, sel);
+  const uint32_t p23 = __builtin_amdgcn_perm(c3, c2, sel);
+  return __builtin_amdgcn_perm(p23, p01, 0x05040100u);
+}
+
+// Input words of a lane's EPL-element slice: bf16 (two per word) or fp32.
+template <int EPL, int INBF>
+constexpr int in_words() { return INBF ? EPL / 2 : EPL; }
+
+template <int INBF>
+__device__ __forceinline__ float load_in_scalar(const void* base, uint64_t idx) {
+  if constexpr (INBF) return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(base)[idx]);
+  else return reinterpret_cast<const float*>(base)[idx];
+}
+
+// max / Q, correctly rounded, as a multiply by fp32(1/Q) and one fused
+// correction step: equal to the IEEE quotient for every non-negative fp32
+// max (checked exhaustively for Q = 127 and Q = 7), in 3 instructions.
+template <int QB>
+__device__ __forceinline__ float div_by_q(float m) {
+  constexpr float Q = (QB == 8) ? 127.0f : 7.0f;
+  constexpr float RQ = 1.0f / Q;
+  const float q0 = m * RQ;
+  const float r = fmaf(-q0, Q, m);
+  return fmaf(r, RQ, q0);
+}
+
+// Row scale and inverse for one row: scale = max/Q, inv = Q/max (both
+// correctly rounded), invb = inv * 2^SRB; zero when inv*2^SRB overflows
+// (max 0 gives Q/0 = inf).
+template <int QB, int SRB>
+__device__ __forceinline__ void row_scale_fast(float m, float& scale, float& inv, float& invb) {
+  constexpr float Q = (QB == 8) ? 127.0f : 7.0f;
+  const float i = Q / m;
+  const float ib = i * (float)(1u << SRB);
+  const bool ok = __builtin_isfinite(ib);
+  scale = ok ? div_by_q<QB>(m) : 0.0f;
+  inv = ok ? i : 0.0f;
+  invb = ok ? ib : 0.0f;
+}
+
+// Stage the head's k and q slices into LDS as fp32 (one conversion per
+// value per workgroup instead of one per value and row-lane), then every lane
+// reads its EPL-wide slices.  Contains a workgroup barrier.
+template <int EPL, int INBF>
+__device__ __forceinline__ void stage_qk(const Args& a, uint64_t bh, int lane8, float* lds,
+                                         float (&kf)[EPL], float (&qf)[EPL]) {
   constexpr int DK = EPL * 8;
+  for (int t = threadIdx.x; t < 2 * DK; t += blockDim.x) {
+    const void* src = t < DK ? a.k : a.q;
+    const uint64_t idx = bh * DK + (uint64_t)(t < DK ? t : t - DK);
+    lds[t] = load_in_scalar<INBF>(src, idx);
+  }
+  __syncthreads();
+  const int k0 = lane8 * EPL;
+#pragma unroll
+  for (int i = 0; i < EPL; i += 4) {
+    const float4 kv = *reinterpret_cast<const float4*>(lds + k0 + i);
+    const float4 qv = *reinterpret_cast<const float4*>(lds + DK + k0 + i);
+    kf[i] = kv.x; kf[i + 1] = kv.y; kf[i + 2] = kv.z; kf[i + 3] = kv.w;
+    qf[i] = qv.x; qf[i + 1] = qv.y; qf[i + 2] = qv.z; qf[i + 3] = qv.w;
+  }
+}
+
+template <int QB, int RND, int DELTA, int EPL, int RPL, int BDR, int DKEY, int INBF>
+__device__ __forceinline__ void dense_quant_rows(const Args& a, uint8_t* blk, uint64_t bh, int v0, int ng,
+                                                 int lane8, float* lds) {
+  constexpr int DK = EPL * 8;
+  constexpr int RB = DK * QB / 8;           // code bytes per row
+  constexpr int NW = EPL * QB / 32;         // code words per lane and row
+  constexpr int SRB = sr_bits_of<RND>();
+  constexpr int32_t Q = (QB == 8) ? 127 : 7;
+  const int k0 = lane8 * EPL;
+  // every load first: state rows (HBM), then per-row scalars, then the head's inputs
+  uint32_t w[RPL][NW];
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) {
+    const int v = v0 + r * ng;
+    if (v < a.dv) load_bytes<EPL * QB / 8>(blk + (uint64_t)v * RB + k0 * QB / 8, w[r]);
+    else {
+#pragma unroll
+      for (int i = 0; i < NW; ++i) w[r][i] = 0u;
+    }
+  }
+  float s_old[RPL], vin[RPL];
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) {
+    const int v = v0 + r * ng;
+    const uint64_t row = bh * (uint64_t)a.dv + (uint64_t)(v < a.dv ? v : 0);
+    s_old[r] = a.scales[row];
+    vin[r] = load_in_scalar<INBF>(a.v, row);
+  }
+  float df[DKEY ? EPL : 1];
+  float dh = 1.0f;
+  if constexpr (DKEY) load_f32<EPL>(a.decay + (uint64_t)bh * DK + k0, df);
+  else dh = a.decay[bh];
+  const float beta = a.beta ? a.beta[bh] : 1.0f;
+  float kf[EPL], qf[EPL];
+  stage_qk<EPL, INBF>(a, bh, lane8, lds, kf, qf);
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) {
+    const int v = v0 + r * ng;
+    if (v >= a.dv) continue;   // whole 8-lane groups skip together
+    const uint64_t row = bh * (uint64_t)a.dv + (uint64_t)v;
+    // decay + update, readout, row maximum
+    float u;
+    if constexpr (DELTA) {
+      float wk = 0.0f;   // S_hat k = s * sum_k code_k k_k
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        float c;
+        if constexpr (QB == 8) c = (float)(int32_t)(int8_t)(w[r][i >> 2] >> (8 * (i & 3)));
+        else c = (float)((int32_t)(w[r][i >> 3] << (28 - 4 * (i & 7))) >> 28);
+        wk = fmaf(c, kf[i], wk);
+      }
+      wk = sum8(wk);
+      u = beta * (vin[r] - dh * (s_old[r] * wk));
+    } else {
+      u = beta * vin[r];
+    }
+    const float ds = dh * s_old[r];
+    float sp[EPL];
+    float o = 0.0f, mx = 0.0f;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      float c;
+      if constexpr (QB == 8) c = (float)(int32_t)(int8_t)(w[r][i >> 2] >> (8 * (i & 3)));
+      else c = (float)((int32_t)(w[r][i >> 3] << (28 - 4 * (i & 7))) >> 28);
+      sp[i] = fmaf(u, kf[i], (DKEY ? df[i] * s_old[r] : ds) * c);
+      o = fmaf(sp[i], qf[i], o);
+    }
+#pragma unroll
+    for (int i = 0; i < EPL; i += 2) mx = fmaxf(fmaxf(mx, fabsf(sp[i])), fabsf(sp[i + 1]));
+    o = sum8(o);
+    const float m = absmax8(mx);
+    if (lane8 == 0) a.out[row] = o;
+    float scale, inv, invb;
+    row_scale_fast<QB, SRB>(m, scale, inv, invb);
+    // requantize
+    uint32_t out[NW];
+    if constexpr (QB == 8 && !BDR) {
+      // byte B of y holds the code: nearest, y = clamp(rint(x)); stochastic,
+      // y = clamp(floor(x 2^SRB + 1/2), +-Q 2^SRB) + rb and code = y >> SRB
+      // (clamping before the add gives the same code as clamping after)
+      constexpr int BYTE = SRB / 8;
+      constexpr int PER = (RND == 1) ? 8 : 16;    // elements per Philox block
+      constexpr int NB = (RND == 0) ? 1 : (EPL + PER - 1) / PER;
+#pragma unroll
+      for (int gblk = 0; gblk < NB; ++gblk) {
+        uint32_t x[4] = {0u, 0u, 0u, 0u};
+        uint32_t sel = 0u;   // RND 2, EPL 8: which half of the 16-element block
+        if constexpr (RND != 0) {
+          // element indices stay below 2^35 (checked at init): the counter's
+          // high word is 0
+          const uint32_t e0 = (uint32_t)(row * DK) + (uint32_t)k0 + (uint32_t)(gblk * PER);
+          const uint64_t e0w = row * DK + (uint64_t)k0 + (uint64_t)(gblk * PER);
+          x[0] = (RND == 1) ? (uint32_t)(e0w >> 3) : (uint32_t)(e0w >> 4);
+          x[1] = 0u;
+          x[2] = a.step_lo;
+          x[3] = a.step_hi;
+          philox10(x, a.seed_lo, a.seed_hi);
+          if constexpr (RND == 2 && EPL < 16) sel = (e0 >> 3) & 1u;
+        }
+        constexpr int CNT = (RND == 0) ? EPL : ((PER < EPL) ? PER : EPL);
+        uint32_t y[CNT];
+#pragma unroll
+        for (int j = 0; j < CNT; ++j) {
+          const int i = gblk * PER + j;
+          if constexpr (RND == 0) {
+            const int32_t c = (int32_t)rintf(sp[i] * inv);
+            y[j] = (uint32_t)(c < -Q ? -Q : (c > Q ? Q : c));
+          } else {
+            uint32_t rbits;
+            if constexpr (RND == 1) rbits = (j & 1) ? (x[j >> 1] >> 16) : (x[j >> 1] & 0xFFFFu);
+            else {
+              const int jj = (EPL < 16) ? (j + 8 * (int)sel) : j;
+              const uint32_t word = (EPL < 16) ? (sel ? x[2 + (j >> 2)] : x[j >> 2]) : x[jj >> 2];
+              rbits = (word >> (8 * (jj & 3))) & 0xFFu;
+            }
+            constexpr int32_t QS = Q << SRB;
+            const int32_t X = cvt_rpi(sp[i] * invb);
+            y[j] = (uint32_t)((X < -QS ? -QS : (X > QS ? QS : X)) + (int32_t)rbits);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < CNT / 4; ++j)
+          out[(gblk * PER) / 4 + j] = pack4<BYTE>(y[4 * j], y[4 * j + 1], y[4 * j + 2], y[4 * j + 3]);
+      }
+    } else {
+      uint32_t rb[EPL];
+      if constexpr (RND != 0)
+        rand_bits<RND, EPL>(row * DK + (uint64_t)k0, a.seed_lo, a.seed_hi, a.step_lo, a.step_hi, rb);
+      int32_t code[EPL];
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        float shi = 0.0f;
+        if constexpr (BDR) {
+          if constexpr (QB == 8) shi = s_old[r] * (float)(int32_t)(int8_t)(w[r][i >> 2] >> (8 * (i & 3)));
+          else shi = s_old[r] * (float)((int32_t)(w[r][i >> 3] << (28 - 4 * (i & 7))) >> 28);
+        }
+        code[i] = round_elem<QB, RND, BDR>(sp[i], shi, inv, invb, (RND != 0) ? rb[i] : 0u, a.bdr_bound);
+      }
+#pragma unroll
+      for (int j = 0; j < NW; ++j) out[j] = 0u;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        if constexpr (QB == 8) out[i >> 2] |= ((uint32_t)code[i] & 0xFFu) << (8 * (i & 3));
+        else out[i >> 3] |= ((uint32_t)code[i] & 0xFu) << (4 * (i & 7));
+      }
+    }
+    store_bytes<EPL * QB / 8>(blk + (uint64_t)v * RB + k0 * QB / 8, out);
+    if (lane8 == 0) a.scales[row] = scale;
+  }
+}
+
+// Protected (16-bit) heads of a head map.
+template <int DELTA, int EPL, int RPL, int DKEY, int INBF>
+__device__ __forceinline__ void dense_prot_rows(const Args& a, uint8_t* blk, uint64_t bh, int v0, int ng,
+                                                int lane8, float* lds) {
+  constexpr int DK = EPL * 8;
+  const int k0 = lane8 * EPL;
+  uint32_t hw[RPL][EPL / 2];
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) {
+    const int v = v0 + r * ng;
+    if (v < a.dv) load_bytes<EPL * 2>(blk + ((uint64_t)v * DK + (uint64_t)k0) * 2u, hw[r]);
+    else {
+#pragma unroll
+      for (int i = 0; i < EPL / 2; ++i) hw[r][i] = 0u;
+    }
+  }
+  float vin[RPL];
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) {
+    const int v = v0 + r * ng;
+    vin[r] = load_in_scalar<INBF>(a.v, bh * (uint64_t)a.dv + (uint64_t)(v < a.dv ? v : 0));
+  }
+  float df[DKEY ? EPL : 1];
+  float dh = 1.0f;
+  if constexpr (DKEY) load_f32<EPL>(a.decay + (uint64_t)bh * DK + k0, df);
+  else dh = a.decay[bh];
+  const float beta = a.beta ? a.beta[bh] : 1.0f;
+  float kf[EPL], qf[EPL];
+  stage_qk<EPL, INBF>(a, bh, lane8, lds, kf, qf);
+  const bool is_bf16 = a.hp_dtype == 1;
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) {
+    const int v = v0 + r * ng;
+    if (v >= a.dv) continue;
+    const uint64_t row = bh * (uint64_t)a.dv + (uint64_t)v;
+    float u;
+    if constexpr (DELTA) {
+      float wk = 0.0f;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        const uint32_t bits = (hw[r][i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+        const float sh = is_bf16 ? bf16_bits_to_f32(bits) : f16_bits_to_f32(bits);
+        wk = fmaf(sh, kf[i], wk);
+      }
+      wk = sum8(wk);
+      u = beta * (vin[r] - dh * wk);
+    } else {
+      u = beta * vin[r];
+    }
+    float sp[EPL];
+    float o = 0.0f;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const uint32_t bits = (hw[r][i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+      const float sh = is_bf16 ? bf16_bits_to_f32(bits) : f16_bits_to_f32(bits);
+      sp[i] = fmaf(u, kf[i], (DKEY ? df[i] : dh) * sh);
+      o = fmaf(sp[i], qf[i], o);
+    }
+    o = sum8(o);
+    if (lane8 == 0) a.out[row] = o;
+    uint32_t ow[EPL / 2];
+#pragma unroll
+    for (int i = 0; i < EPL / 2; ++i)
+      ow[i] = is_bf16 ? pack_bf16x2(sp[2 * i], sp[2 * i + 1])
+                      : (f32_to_f16_bits(sp[2 * i]) | (f32_to_f16_bits(sp[2 * i + 1]) << 16));
+    store_bytes<EPL * 2>(blk + ((uint64_t)v * DK + (uint64_t)k0) * 2u, ow);
+  }
+}
+
+// Register budget (minimum waves per SIMD the body is compiled for), chosen
+// per shape as the highest occupancy at which it needs no spills: dk 128
+// takes 7 waves with one row per lane (72 VGPRs) and 5 with two, fewer with
+// BDR, per-key decay, fp32 inputs or the delta rule; dk 64 fits 8; dk 256 is
+// left to the compiler.
+template <int EPL, int RPL, int BDR, int DKEY, int INBF, int DELTA>
+constexpr int dense_min_waves() {
+  return EPL >= 32 ? 1
+                   : (EPL <= 8 ? (BDR ? 6 : 8)
+                               : (RPL == 1 ? 7 : 5) - (BDR ? 2 : 0) - (DKEY ? 1 : 0) - (INBF ? 0 : 1) -
+                                     (DELTA ? 1 : 0));
+}
+
+template <int QB, int RND, int DELTA, int EPL, int RPL, int BDR, int DKEY, int INBF>
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(dense_min_waves<EPL, RPL, BDR, DKEY, INBF, DELTA>(), 8)))
+void k_step_dense(const Args a) {
   const int lane8 = threadIdx.x & 7;
-  const int rloc = threadIdx.x >> 3;
+  const int g = threadIdx.x >> 3;
+  const int ng = blockDim.x >> 3;
   const uint32_t wg = blockIdx.x;
   const uint32_t chunk = wg % (uint32_t)a.row_chunks;
   const uint32_t bh = wg / (uint32_t)a.row_chunks;
   const uint32_t h = bh % (uint32_t)a.H;
   const uint32_t b = bh / (uint32_t)a.H;
-  const int v = (int)chunk * 32 + rloc;
-  if (v >= a.dv) return;   // whole 8-lane groups leave together
-  const int k0 = lane8 * EPL;
-  const uint64_t row = (uint64_t)bh * (uint64_t)a.dv + (uint64_t)v;
-  const bool quant = a.t.head_type[h] == kHeadQuant;
-
-  float kf[EPL], df[EPL];
-  load_in<EPL>(a.k, a.in_bf16, (uint64_t)bh * DK + k0, kf);
-  load_decay<EPL>(a, bh, k0, df);
-  const float beta = a.beta ? a.beta[bh] : 1.0f;
-  const float vin = load_in1(a.v, a.in_bf16, row);
-
-  // dequantize
-  float sh[EPL];
-  uint8_t* cp = nullptr;
-  uint8_t* hpp = nullptr;
-  if (quant) {
-    cp = const_cast<uint8_t*>(code_block(a, b, h)) + (uint64_t)v * (DK * QB / 8) + k0 * QB / 8;
-    load_codes<QB, EPL>(cp, a.scales[row], sh);
+  const int v0 = (int)chunk * ng * RPL + g;   // groups past dv stay for the barrier
+  __shared__ __align__(16) float lds[2 * EPL * 8];
+  // head storage from the protected-head mask: no table lookup stands
+  // between the launch and the state loads
+  const uint64_t below = (h >= 64u) ? 0ull : (a.prot_mask & ((1ull << h) - 1ull));
+  const uint32_t np = (uint32_t)__builtin_popcountll(below);
+  const bool prot = (h < 64u) && ((a.prot_mask >> h) & 1ull);
+  if (!prot) {
+    uint8_t* blk = a.codes + (uint64_t)b * a.code_bstride + (uint64_t)(h - np) * a.code_hblk;
+    dense_quant_rows<QB, RND, DELTA, EPL, RPL, BDR, DKEY, INBF>(a, blk, bh, v0, ng, lane8, lds);
   } else {
-    hpp = const_cast<uint8_t*>(hp_block(a, b, h)) +
-          ((uint64_t)v * DK + (uint64_t)k0) * (uint64_t)hp_elem_bytes(a.hp_dtype);
-    load_hp<EPL>(hpp, a.hp_dtype, sh);
-  }
-
-  // write vector u: beta v (additive) or beta (v - alpha S k) (delta rule)
-  float u;
-  if constexpr (DELTA) {
-    float w = 0.0f;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) w = fmaf(sh[i], kf[i], w);
-    w = sum8(w);
-    u = beta * (vin - df[0] * w);
-  } else {
-    u = beta * vin;
-  }
-
-  // decay + update
-  float sp[EPL];
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) sp[i] = fmaf(u, kf[i], df[i] * sh[i]);
-
-  // readout from the pre-rounding state
-  float qf[EPL];
-  load_in<EPL>(a.q, a.in_bf16, (uint64_t)bh * DK + k0, qf);
-  float o = 0.0f;
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) o = fmaf(sp[i], qf[i], o);
-  o = sum8(o);
-  if (lane8 == 0) a.out[row] = o;
-
-  // requantize
-  if (quant) {
-    float m = 0.0f;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) m = fmaxf(m, fabsf(sp[i]));
-    m = max8(m);
-    float scale, inv;
-    row_scale<QB>(m, scale, inv);
-    uint32_t rb[EPL];
-    if constexpr (RND != 0) rand_bits<RND, EPL>(row * DK + (uint64_t)k0, a.seed_lo, a.seed_hi, a.step_lo, a.step_hi, rb);
-    int32_t code[EPL];
-#pragma unroll
-    for (int i = 0; i < EPL; ++i)
-      code[i] = round_elem<QB, RND>(sp[i], sh[i], inv, (RND != 0) ? rb[i] : 0u, a.bdr, a.bdr_bound);
-    store_codes<QB, EPL>(cp, code);
-    if (lane8 == 0) a.scales[row] = scale;
-  } else {
-    store_hp<EPL>(hpp, a.hp_dtype, sp);
+    uint8_t* blk = a.hp + (uint64_t)b * a.hp_bstride + (uint64_t)np * a.hp_hblk;
+    dense_prot_rows<DELTA, EPL, RPL, DKEY, INBF>(a, blk, bh, v0, ng, lane8, lds);
   }
 }
 
@@ -181,7 +464,7 @@ __global__ __launch_bounds__(256) void k_step_mixed(const Args a) {
     const float vin = load_in1(a.v, a.in_bf16, row);
     uint8_t* crow = lcode + (uint32_t)v * rq;
     uint8_t* hrow = lhp + (uint32_t)v * (uint32_t)nhp * (uint32_t)hpb;
-    float sh[EPL];
+    float sh[EPL], dec[EPL];   // dequantized value; decayed value (d s) c or d h
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
       const uint32_t s = sl[i] & 0x7FFFu;
@@ -191,11 +474,13 @@ __global__ __launch_bounds__(256) void k_step_mixed(const Args a) {
           const uint32_t bits = *reinterpret_cast<const uint16_t*>(hrow + s * 2u);
           sh[i] = (a.hp_dtype == 1) ? bf16_bits_to_f32(bits) : f16_bits_to_f32(bits);
         }
+        dec[i] = df[i] * sh[i];
       } else {
         int32_t c;
         if constexpr (QB == 8) c = (int32_t)(int8_t)crow[s];
         else c = (int32_t)((uint32_t)crow[s >> 1] << (28 - 4 * (s & 1))) >> 28;
         sh[i] = s_old * (float)c;
+        dec[i] = (df[i] * s_old) * (float)c;
       }
     }
     float u;
@@ -210,7 +495,7 @@ __global__ __launch_bounds__(256) void k_step_mixed(const Args a) {
     }
     float sp[EPL];
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) sp[i] = fmaf(u, kf[i], df[i] * sh[i]);
+    for (int i = 0; i < EPL; ++i) sp[i] = fmaf(u, kf[i], dec[i]);
     float o = 0.0f;
 #pragma unroll
     for (int i = 0; i < EPL; ++i) o = fmaf(sp[i], qf[i], o);
@@ -222,14 +507,17 @@ __global__ __launch_bounds__(256) void k_step_mixed(const Args a) {
     for (int i = 0; i < EPL; ++i)
       if (!(sl[i] & kSlotProt)) m = fmaxf(m, fabsf(sp[i]));
     m = max8(m);
-    float scale, inv;
-    row_scale<QB>(m, scale, inv);
+    float scale, inv, invb;
+    row_scale<QB, sr_bits_of<RND>()>(m, scale, inv, invb);
     uint32_t rb[EPL];
     if constexpr (RND != 0) rand_bits<RND, EPL>(row * DK + (uint64_t)k0, a.seed_lo, a.seed_hi, a.step_lo, a.step_hi, rb);
     int32_t code[EPL];
 #pragma unroll
-    for (int i = 0; i < EPL; ++i)
-      code[i] = round_elem<QB, RND>(sp[i], sh[i], inv, (RND != 0) ? rb[i] : 0u, a.bdr, a.bdr_bound);
+    for (int i = 0; i < EPL; ++i) {
+      const uint32_t rbi = (RND != 0) ? rb[i] : 0u;
+      code[i] = a.bdr ? round_elem<QB, RND, 1>(sp[i], sh[i], inv, invb, rbi, a.bdr_bound)
+                      : round_elem<QB, RND, 0>(sp[i], sh[i], inv, invb, rbi, a.bdr_bound);
+    }
 
     // scatter: protected values and int8 codes are whole bytes of their own
 #pragma unroll
@@ -492,13 +780,21 @@ __global__ __launch_bounds__(256) void k_step_lrb(const Args a) {
   for (int v = rloc; v < dv; v += 32) {
     const uint64_t row = (uint64_t)bh * (uint64_t)dv + (uint64_t)v;
     uint8_t* cp = gcode + (uint64_t)v * (DK * QB / 8) + k0 * QB / 8;
-    float sh[EPL];
-    load_codes<QB, EPL>(cp, sol[v], sh);
+    uint32_t cw[EPL * QB / 32];
+    load_bytes<EPL * QB / 8>(cp, cw);
+    const float s_old = sol[v];
+    float sh[EPL], cf[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      if constexpr (QB == 8) cf[i] = (float)(int32_t)(int8_t)(cw[i >> 2] >> (8 * (i & 3)));
+      else cf[i] = (float)((int32_t)(cw[i >> 3] << (28 - 4 * (i & 7))) >> 28);
+      sh[i] = s_old * cf[i];
+    }
     const float uv = ul[v], upv = upl[v];
     float sp[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
-      float x = fmaf(smf[i] ? upv : uv, kf[i], df[i] * sh[i]);
+      float x = fmaf(smf[i] ? upv : uv, kf[i], (df[i] * s_old) * cf[i]);
       if (mgf[i]) {
         float col = 0.0f;
         for (int j = 0; j < n; ++j) col = fmaf(Wl[v * r + j], Ul[(k0 + i) * r + j], col);
@@ -515,246 +811,20 @@ __global__ __launch_bounds__(256) void k_step_lrb(const Args a) {
 #pragma unroll
     for (int i = 0; i < EPL; ++i) m = fmaxf(m, fabsf(sp[i]));
     m = max8(m);
-    float scale, inv;
-    row_scale<QB>(m, scale, inv);
+    float scale, inv, invb;
+    row_scale<QB, sr_bits_of<RND>()>(m, scale, inv, invb);
     uint32_t rb[EPL];
     if constexpr (RND != 0) rand_bits<RND, EPL>(row * DK + (uint64_t)k0, a.seed_lo, a.seed_hi, a.step_lo, a.step_hi, rb);
     int32_t code[EPL];
 #pragma unroll
-    for (int i = 0; i < EPL; ++i)
-      code[i] = round_elem<QB, RND>(sp[i], sh[i], inv, (RND != 0) ? rb[i] : 0u, a.bdr, a.bdr_bound);
+    for (int i = 0; i < EPL; ++i) {
+      const uint32_t rbi = (RND != 0) ? rb[i] : 0u;
+      code[i] = a.bdr ? round_elem<QB, RND, 1>(sp[i], sh[i], inv, invb, rbi, a.bdr_bound)
+                      : round_elem<QB, RND, 0>(sp[i], sh[i], inv, invb, rbi, a.bdr_bound);
+    }
     store_codes<QB, EPL>(cp, code);
     if (lane8 == 0) a.scales[row] = scale;
   }
-}
-
-// ---------------------------------------------------------------------------
-// Quantize / dequantize: one thread per row, channels in order (any layout).
-// Not on the decode path.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_quantize(const Args a) {
-  const uint64_t row = (uint64_t)blockIdx.x * 256u + threadIdx.x;
-  const uint64_t nrows = (uint64_t)a.B * (uint64_t)a.H * (uint64_t)a.dv;
-  if (row >= nrows) return;
-  const int dk = a.dk;
-  const uint64_t bh = row / (uint64_t)a.dv;
-  const uint32_t v = (uint32_t)(row % (uint64_t)a.dv);
-  const uint32_t h = (uint32_t)(bh % (uint64_t)a.H);
-  const uint32_t b = (uint32_t)(bh / (uint64_t)a.H);
-  const int nq = a.t.nq[h];
-  const int nhp = dk - nq;
-  const int hpb = hp_elem_bytes(a.hp_dtype);
-  const uint32_t rq = (uint32_t)(nq * a.qbits + 7) / 8u;
-  uint8_t* crow = const_cast<uint8_t*>(a.codes ? code_block(a, b, h) : nullptr);
-  if (crow) crow += (uint64_t)v * rq;
-  uint8_t* hrow = const_cast<uint8_t*>(a.hp ? hp_block(a, b, h) : nullptr);
-  if (hrow) hrow += (uint64_t)v * (uint64_t)nhp * (uint64_t)hpb;
-  const uint16_t* sl = a.t.slots + (uint64_t)h * dk;
-  const float* srow = a.S + row * (uint64_t)dk;
-  float m = 0.0f;
-  for (int k = 0; k < dk; ++k)
-    if (!(sl[k] & kSlotProt)) m = fmaxf(m, fabsf(srow[k]));
-  float scale, inv;
-  if (a.qbits == 8) row_scale<8>(m, scale, inv);
-  else row_scale<4>(m, scale, inv);
-  uint64_t cached = ~(uint64_t)0;
-  uint32_t x[4] = {0, 0, 0, 0};
-  uint32_t pend = 0;
-  for (int k = 0; k < dk; ++k) {
-    const uint32_t s = sl[k] & 0x7FFFu;
-    const float val = srow[k];
-    if (sl[k] & kSlotProt) {
-      if (a.hp_dtype == 0) reinterpret_cast<float*>(hrow)[s] = val;
-      else reinterpret_cast<uint16_t*>(hrow)[s] =
-          (uint16_t)((a.hp_dtype == 1) ? f32_to_bf16_bits(val) : f32_to_f16_bits(val));
-      continue;
-    }
-    uint32_t rbits = 0;
-    if (a.rounding) {
-      const uint64_t e = row * (uint64_t)dk + (uint64_t)k;
-      const uint64_t g = (a.sr_bits == 16) ? (e >> 3) : (e >> 4);
-      if (g != cached) {
-        x[0] = (uint32_t)g;
-        x[1] = (uint32_t)(g >> 32);
-        x[2] = a.step_lo;
-        x[3] = a.step_hi;
-        philox10(x, a.seed_lo, a.seed_hi);
-        cached = g;
-      }
-      rbits = (a.sr_bits == 16) ? ((e & 1u) ? (x[(e >> 1) & 3u] >> 16) : (x[(e >> 1) & 3u] & 0xFFFFu))
-                                : ((x[(e >> 2) & 3u] >> (8u * (uint32_t)(e & 3u))) & 0xFFu);
-    }
-    int32_t c;
-    if (a.qbits == 8) {
-      c = !a.rounding ? round_elem<8, 0>(val, 0.0f, inv, 0u, 0, 0.0f)
-                      : (a.sr_bits == 16 ? round_elem<8, 1>(val, 0.0f, inv, rbits, 0, 0.0f)
-                                         : round_elem<8, 2>(val, 0.0f, inv, rbits, 0, 0.0f));
-      crow[s] = (uint8_t)c;
-    } else {
-      c = !a.rounding ? round_elem<4, 0>(val, 0.0f, inv, 0u, 0, 0.0f)
-                      : (a.sr_bits == 16 ? round_elem<4, 1>(val, 0.0f, inv, rbits, 0, 0.0f)
-                                         : round_elem<4, 2>(val, 0.0f, inv, rbits, 0, 0.0f));
-      if ((s & 1u) == 0u) {
-        pend = (uint32_t)c & 0xFu;
-        if ((int)s == nq - 1) crow[s >> 1] = (uint8_t)pend;
-      } else {
-        crow[s >> 1] = (uint8_t)(pend | (((uint32_t)c & 0xFu) << 4));
-      }
-    }
-  }
-  a.scales[row] = scale;
-}
-
-__global__ __launch_bounds__(256) void k_dequantize(const Args a) {
-  const uint64_t row = (uint64_t)blockIdx.x * 256u + threadIdx.x;
-  const uint64_t nrows = (uint64_t)a.B * (uint64_t)a.H * (uint64_t)a.dv;
-  if (row >= nrows) return;
-  const int dk = a.dk;
-  const uint64_t bh = row / (uint64_t)a.dv;
-  const uint32_t v = (uint32_t)(row % (uint64_t)a.dv);
-  const uint32_t h = (uint32_t)(bh % (uint64_t)a.H);
-  const uint32_t b = (uint32_t)(bh / (uint64_t)a.H);
-  const int nq = a.t.nq[h];
-  const int nhp = dk - nq;
-  const int hpb = hp_elem_bytes(a.hp_dtype);
-  const uint32_t rq = (uint32_t)(nq * a.qbits + 7) / 8u;
-  const uint8_t* crow = a.codes ? code_block(a, b, h) + (uint64_t)v * rq : nullptr;
-  const uint8_t* hrow = a.hp ? hp_block(a, b, h) + (uint64_t)v * (uint64_t)nhp * (uint64_t)hpb : nullptr;
-  const uint16_t* sl = a.t.slots + (uint64_t)h * dk;
-  const float scale = a.scales ? a.scales[row] : 0.0f;
-  const int r = a.lrb_rank;
-  const int n = r > 0 ? a.n[bh] : 0;
-  const float* W = r > 0 ? a.W + (bh * (uint64_t)a.dv + v) * (uint64_t)r : nullptr;
-  const float* U = r > 0 ? a.U + bh * (uint64_t)dk * (uint64_t)r : nullptr;
-  float* orow = a.S_out + row * (uint64_t)dk;
-  for (int k = 0; k < dk; ++k) {
-    const uint32_t s = sl[k] & 0x7FFFu;
-    float val;
-    if (sl[k] & kSlotProt) {
-      if (a.hp_dtype == 0) val = reinterpret_cast<const float*>(hrow)[s];
-      else {
-        const uint32_t bits = reinterpret_cast<const uint16_t*>(hrow)[s];
-        val = (a.hp_dtype == 1) ? bf16_bits_to_f32(bits) : f16_bits_to_f32(bits);
-      }
-    } else {
-      int32_t c;
-      if (a.qbits == 8) c = (int32_t)(int8_t)crow[s];
-      else c = (int32_t)((uint32_t)crow[s >> 1] << (28 - 4 * (s & 1))) >> 28;
-      val = scale * (float)c;
-    }
-    if (n > 0) {
-      float col = 0.0f;
-      for (int j = 0; j < n; ++j) col = fmaf(W[j], U[(uint64_t)k * r + j], col);
-      val = val + col;
-    }
-    orow[k] = val;
-  }
-}
-
-__global__ __launch_bounds__(256) void k_zero(uint32_t* p, uint64_t nwords) {
-  for (uint64_t i = (uint64_t)blockIdx.x * 256u + threadIdx.x; i < nwords; i += (uint64_t)gridDim.x * 256u)
-    p[i] = 0u;
-}
-
-// ---------------------------------------------------------------------------
-// Launchers
-// ---------------------------------------------------------------------------
-namespace {
-
-template <int QB, int RND, int DELTA, int EPL>
-hipError_t launch_dense_t(const Args& a, hipStream_t s) {
-  const uint64_t grid = (uint64_t)a.B * (uint64_t)a.H * (uint64_t)a.row_chunks;
-  hipLaunchKernelGGL((k_step_dense<QB, RND, DELTA, EPL>), dim3((uint32_t)grid), dim3(256), 0, s, a);
-  return hipGetLastError();
-}
-
-template <int QB, int RND, int DELTA, int EPL>
-hipError_t launch_mixed_t(const Args& a, hipStream_t s) {
-  const uint64_t grid = (uint64_t)a.B * (uint64_t)a.H;
-  hipLaunchKernelGGL((k_step_mixed<QB, RND, DELTA, EPL>), dim3((uint32_t)grid), dim3(256), a.mixed_lds, s, a);
-  return hipGetLastError();
-}
-
-template <int QB, int RND, int EPL>
-hipError_t launch_lrb_t(const Args& a, hipStream_t s) {
-  const uint64_t grid = (uint64_t)a.B * (uint64_t)a.H;
-  hipLaunchKernelGGL((k_step_lrb<QB, RND, EPL>), dim3((uint32_t)grid), dim3(256), a.mixed_lds, s, a);
-  return hipGetLastError();
-}
-
-template <int QB, int RND, int DELTA>
-hipError_t launch_fam(int family, const Args& a, hipStream_t s) {
-  if (family == kFamDense) {
-    switch (a.dk) {
-      case 64: return launch_dense_t<QB, RND, DELTA, 8>(a, s);
-      case 128: return launch_dense_t<QB, RND, DELTA, 16>(a, s);
-      case 256: return launch_dense_t<QB, RND, DELTA, 32>(a, s);
-    }
-  } else if (family == kFamMixed) {
-    switch (a.dk) {
-      case 64: return launch_mixed_t<QB, RND, DELTA, 8>(a, s);
-      case 128: return launch_mixed_t<QB, RND, DELTA, 16>(a, s);
-      case 256: return launch_mixed_t<QB, RND, DELTA, 32>(a, s);
-    }
-  } else if (family == kFamLrb && !DELTA) {
-    switch (a.dk) {
-      case 64: return launch_lrb_t<QB, RND, 8>(a, s);
-      case 128: return launch_lrb_t<QB, RND, 16>(a, s);
-      case 256: return launch_lrb_t<QB, RND, 32>(a, s);
-    }
-  }
-  return hipErrorInvalidValue;
-}
-
-template <int QB, int RND>
-hipError_t launch_kind(int family, int delta, const Args& a, hipStream_t s) {
-  return delta ? launch_fam<QB, RND, 1>(family, a, s) : launch_fam<QB, RND, 0>(family, a, s);
-}
-
-template <int QB>
-hipError_t launch_rnd(int family, int rnd, int delta, const Args& a, hipStream_t s) {
-  switch (rnd) {
-    case 0: return launch_kind<QB, 0>(family, delta, a, s);
-    case 1: return launch_kind<QB, 1>(family, delta, a, s);
-    case 2: return launch_kind<QB, 2>(family, delta, a, s);
-  }
-  return hipErrorInvalidValue;
-}
-
-}  // namespace
-
-hipError_t launch_step(int family, int qbits, int rnd, int delta, const Args& a, hipStream_t s) {
-  return qbits == 8 ? launch_rnd<8>(family, rnd, delta, a, s) : launch_rnd<4>(family, rnd, delta, a, s);
-}
-
-hipError_t launch_quantize(const Args& a, hipStream_t s) {
-  const uint64_t nrows = (uint64_t)a.B * (uint64_t)a.H * (uint64_t)a.dv;
-  if (nrows == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_quantize, dim3((uint32_t)((nrows + 255u) / 256u)), dim3(256), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.lrb_rank == 0) return e;
-  const uint64_t bh = (uint64_t)a.B * (uint64_t)a.H;
-  const uint64_t nW = bh * (uint64_t)a.dv * (uint64_t)a.lrb_rank;
-  const uint64_t nU = bh * (uint64_t)a.dk * (uint64_t)a.lrb_rank;
-  hipLaunchKernelGGL(k_zero, dim3(1024), dim3(256), 0, s, reinterpret_cast<uint32_t*>(a.W), nW);
-  hipLaunchKernelGGL(k_zero, dim3(1024), dim3(256), 0, s, reinterpret_cast<uint32_t*>(a.U), nU);
-  hipLaunchKernelGGL(k_zero, dim3(64), dim3(256), 0, s, reinterpret_cast<uint32_t*>(a.n), bh);
-  return hipGetLastError();
-}
-
-hipError_t launch_dequantize(const Args& a, hipStream_t s) {
-  const uint64_t nrows = (uint64_t)a.B * (uint64_t)a.H * (uint64_t)a.dv;
-  if (nrows == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_dequantize, dim3((uint32_t)((nrows + 255u) / 256u)), dim3(256), 0, s, a);
-  return hipGetLastError();
-}
-
-const char* step_kernel_name(int family, int qbits, int rnd, int delta, int dk) {
-  static thread_local char buf[96];
-  const char* fam = family == kFamDense ? "dense" : (family == kFamMixed ? "mixed" : "lrb");
-  const char* rn = rnd == 0 ? "rtn" : (rnd == 1 ? "sr16" : "sr8");
-  snprintf(buf, sizeof(buf), "k_step_%s<int%d,%s,%s,dk%d>", fam, qbits, rn, delta ? "delta" : "additive", dk);
-  return buf;
 }
 
 }  // namespace qs

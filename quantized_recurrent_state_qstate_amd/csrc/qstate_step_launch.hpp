@@ -1,0 +1,91 @@
+// Step-kernel launchers of libqstate, templated on qbits and rounding mode;
+// each qstate_step_q*_r*.hip translation unit instantiates one pair so the
+// kernels compile in parallel.
+#pragma once
+#include "qstate_step_kernels.hpp"
+
+namespace qs {
+
+namespace {
+
+template <int QB, int RND, int DELTA, int EPL, int RPL, int INBF>
+hipError_t launch_dense_rpl(const Args& a, hipStream_t s) {
+  const uint64_t grid = (uint64_t)a.B * (uint64_t)a.H * (uint64_t)a.row_chunks;
+  const dim3 g((uint32_t)grid), blk((uint32_t)a.dense_threads);
+  if constexpr (DELTA) {
+    // the delta rule takes one decay per head
+    if (a.decay_key) return hipErrorInvalidValue;
+    if (a.bdr) hipLaunchKernelGGL((k_step_dense<QB, RND, DELTA, EPL, RPL, 1, 0, INBF>), g, blk, 0, s, a);
+    else hipLaunchKernelGGL((k_step_dense<QB, RND, DELTA, EPL, RPL, 0, 0, INBF>), g, blk, 0, s, a);
+  } else {
+    if (a.bdr) {
+      if (a.decay_key) hipLaunchKernelGGL((k_step_dense<QB, RND, DELTA, EPL, RPL, 1, 1, INBF>), g, blk, 0, s, a);
+      else hipLaunchKernelGGL((k_step_dense<QB, RND, DELTA, EPL, RPL, 1, 0, INBF>), g, blk, 0, s, a);
+    } else {
+      if (a.decay_key) hipLaunchKernelGGL((k_step_dense<QB, RND, DELTA, EPL, RPL, 0, 1, INBF>), g, blk, 0, s, a);
+      else hipLaunchKernelGGL((k_step_dense<QB, RND, DELTA, EPL, RPL, 0, 0, INBF>), g, blk, 0, s, a);
+    }
+  }
+  return hipGetLastError();
+}
+
+template <int QB, int RND, int DELTA, int EPL>
+hipError_t launch_dense_t(const Args& a, hipStream_t s) {
+  if (a.in_bf16) {
+    if (a.dense_rpl == 1) return launch_dense_rpl<QB, RND, DELTA, EPL, 1, 1>(a, s);
+    if (a.dense_rpl == 2) return launch_dense_rpl<QB, RND, DELTA, EPL, 2, 1>(a, s);
+  } else {
+    if (a.dense_rpl == 1) return launch_dense_rpl<QB, RND, DELTA, EPL, 1, 0>(a, s);
+    if (a.dense_rpl == 2) return launch_dense_rpl<QB, RND, DELTA, EPL, 2, 0>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int QB, int RND, int DELTA, int EPL>
+hipError_t launch_mixed_t(const Args& a, hipStream_t s) {
+  const uint64_t grid = (uint64_t)a.B * (uint64_t)a.H;
+  hipLaunchKernelGGL((k_step_mixed<QB, RND, DELTA, EPL>), dim3((uint32_t)grid), dim3(256), a.mixed_lds, s, a);
+  return hipGetLastError();
+}
+
+template <int QB, int RND, int EPL>
+hipError_t launch_lrb_t(const Args& a, hipStream_t s) {
+  const uint64_t grid = (uint64_t)a.B * (uint64_t)a.H;
+  hipLaunchKernelGGL((k_step_lrb<QB, RND, EPL>), dim3((uint32_t)grid), dim3(256), a.mixed_lds, s, a);
+  return hipGetLastError();
+}
+
+template <int QB, int RND, int DELTA>
+hipError_t launch_fam(int family, const Args& a, hipStream_t s) {
+  if (family == kFamDense) {
+    switch (a.dk) {
+      case 64: return launch_dense_t<QB, RND, DELTA, 8>(a, s);
+      case 128: return launch_dense_t<QB, RND, DELTA, 16>(a, s);
+      case 256: return launch_dense_t<QB, RND, DELTA, 32>(a, s);
+    }
+  } else if (family == kFamMixed) {
+    switch (a.dk) {
+      case 64: return launch_mixed_t<QB, RND, DELTA, 8>(a, s);
+      case 128: return launch_mixed_t<QB, RND, DELTA, 16>(a, s);
+      case 256: return launch_mixed_t<QB, RND, DELTA, 32>(a, s);
+    }
+  } else if constexpr (!DELTA) {
+    if (family == kFamLrb) {
+      switch (a.dk) {
+        case 64: return launch_lrb_t<QB, RND, 8>(a, s);
+        case 128: return launch_lrb_t<QB, RND, 16>(a, s);
+        case 256: return launch_lrb_t<QB, RND, 32>(a, s);
+      }
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+template <int QB, int RND>
+hipError_t launch_step_qr(int family, int delta, const Args& a, hipStream_t s) {
+  return delta ? launch_fam<QB, RND, 1>(family, a, s) : launch_fam<QB, RND, 0>(family, a, s);
+}
+
+}  // namespace qs

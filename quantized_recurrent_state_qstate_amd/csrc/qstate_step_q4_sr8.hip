@@ -1,0 +1,7 @@
+// Step kernels for int4 codes with sr8 rounding (one translation unit
+// per qbits x rounding mode so the instantiations compile in parallel).
+#include "qstate_step_launch.hpp"
+
+namespace qs {
+template hipError_t launch_step_qr<4, 2>(int family, int delta, const Args& a, hipStream_t s);
+}  // namespace qs

@@ -189,6 +189,52 @@ def test_quantize_dequantize_bitexact(name):
     assert np.array_equal(D, oracle.dequantize(ocfg, ost))
 
 
+@pytest.mark.parametrize("hp", ["bf16", "fp16"])
+@pytest.mark.parametrize("mode", ["head", "key"])
+def test_protected_rounding_special_values(hp, mode):
+    """Protected channels hold RNE bf16/fp16 of S_pre: subnormals, exact ties,
+    overflow to infinity and signed zeros, through the dense kernel (head map,
+    hardware conversion) and the LDS-staged kernel (key-channel map)."""
+    if mode == "head":
+        m = np.array([0, 1], np.uint8)
+    else:
+        m = np.zeros((2, 64), np.uint8)
+        m[1, :] = 1
+        m[0, :8] = 1
+    lcfg = StateConfig(B=2, H=2, dk=64, dv=16, map_mode=mode, map=m, hp_dtype=hp, in_dtype="fp32")
+    ocfg = oracle.Cfg(B=2, H=2, dk=64, dv=16, map_mode=mode, map=m, hp_dtype=hp)
+    r = np.random.default_rng(3)
+    bits = r.integers(0, 2 ** 32, (2, 2, 16, 64), dtype=np.uint64).astype(np.uint32)
+    tie_bf16 = (bits & np.uint32(0xFFFF0000)) | np.uint32(0x8000)
+    tie_fp16 = (bits & np.uint32(0x7FFFE000)) | np.uint32(0x1000)
+    sub = bits & np.uint32(0x807FFFFF)
+    S = np.where(r.random(bits.shape) < 0.3, tie_bf16 if hp == "bf16" else tie_fp16, bits)
+    S = np.where(r.random(bits.shape) < 0.2, sub, S).view(np.float32).copy()
+    S[~np.isfinite(S)] = 1.0
+    S[:, 1, 0, :4] = [0.0, -0.0, 65520.0 if hp == "fp16" else 3.4e38, -1e-45]
+    qs = QState(lcfg)
+    st = qs.new_state()
+    qs.quantize(torch.from_numpy(S).to(DEV), st, step=0)
+    torch.cuda.synchronize()
+    ost = oracle.new_state(ocfg)
+    oracle.quantize(ocfg, S, ost, step=0)
+    got = gpu_state_to_oracle(st, hp)
+    assert np.array_equal(got["hp"], ost["hp"])
+    assert np.array_equal(got["codes"], ost["codes"])
+    # one step with zero update and decay 1/2: S_pre = value / 2 (subnormals round)
+    z = torch.zeros(2, 2, 64, device=DEV)
+    inp = {"q": z, "k": z, "v": torch.zeros(2, 2, 16, device=DEV), "decay": torch.full((2, 2), 0.5, device=DEV),
+           "beta": None}
+    ref = gpu_state_to_oracle(st, hp)
+    oracle.step(ocfg, ref, q=np.zeros((2, 2, 64), np.float32), k=np.zeros((2, 2, 64), np.float32),
+                v=np.zeros((2, 2, 16), np.float32), decay=np.full((2, 2), 0.5, np.float32), step=1)
+    qs.step(st, **inp, step=1)
+    torch.cuda.synchronize()
+    got = gpu_state_to_oracle(st, hp)
+    assert np.array_equal(got["hp"], ref["hp"])
+    assert np.array_equal(got["codes"], ref["codes"])
+
+
 def test_dequantize_with_buffer():
     w = WORKLOADS["gla_int4"]
     B = 2

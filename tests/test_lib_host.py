@@ -85,6 +85,7 @@ BAD = [
     (dict(lrb_rank=4, lrb_period=0), _lib.QS_EINVAL),
     (dict(lrb_rank=4, lrb_theta=0.0), _lib.QS_EINVAL),
     (dict(lrb_rank=4, map_mode="head", map=np.zeros(2, np.uint8)), _lib.QS_EUNSUPPORTED),
+    (dict(B=1 << 20, H=2, dk=128, dv=128), _lib.QS_EUNSUPPORTED),    # 2^35 elements
 ]
 
 
