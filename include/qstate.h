@@ -51,16 +51,20 @@
  *     first lrb_n columns.
  *   All-zero buffers are the state S = 0.
  *
- * Rounding of a quantized element x = S_pre * (Q / max):
+ * Rounding of a quantized element x = S_pre * inv, inv = Q / max rounded
+ * toward zero (the largest fp32 with inv * max <= Q, so |x| <= Q; a row
+ * whose nearest Q / max, times 2^sr_bits under stochastic rounding,
+ * overflows is stored as zero):
  *   nearest: ties to even.  stochastic (fixed point, b = sr_bits):
  *   X = floor(x * 2^b + 1/2), code = floor((X + u) / 2^b), with u the
  *   element's b-bit Philox integer, key = seed, counter = (g as 64 bits,
  *   step as 64 bits); e = ((b*H+h)*dv+v)*dk+k is the logical element index;
  *   16 bits: g = e>>3, half (e&1) of word (e>>1)&3 (low half for even e);
- *   8 bits: g = e>>4, byte e&3 of word (e>>2)&3.  E[code] = X / 2^b.
- *   BDR: with D = S_pre - S_old and xo = S_old * (Q / max), an element with
+ *   8 bits: g = e>>4, byte e&3 of word (e>>2)&3.  E[code] = X / 2^b
+ *   (X uses invb = inv * 2^b).
+ *   BDR: with D = S_pre - S_old and xo = S_old * inv, an element with
  *   D > 0 and code < xo - bound takes ceil(x); with D < 0 and code > xo +
- *   bound takes floor(x).  Codes are clamped to [-Q, Q].  Protected values
+ *   bound takes floor(x).  Codes lie in [-Q, Q] by the choice of inv.  Protected values
  *   are stored as the nearest (ties to even) bf16/fp16.
  *   Element update: S_pre = fma(u_v, k_k, (d_k * s_v) * code) for a
  *   quantized channel, fma(u_v, k_k, d_k * value) for a protected one.

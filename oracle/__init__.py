@@ -39,6 +39,8 @@ def lib():
         L.orc_random_bits.restype = ctypes.c_uint32
         L.orc_sr_round.argtypes = [ctypes.c_float, ctypes.c_uint32, ctypes.c_int32]
         L.orc_sr_round.restype = ctypes.c_float
+        L.orc_inv_rtz.argtypes = [ctypes.c_float, ctypes.c_float]
+        L.orc_inv_rtz.restype = ctypes.c_float
         L.orc_to_bf16.argtypes = [ctypes.c_float]
         L.orc_to_bf16.restype = ctypes.c_uint16
         L.orc_to_fp16.argtypes = [ctypes.c_float]
@@ -248,6 +250,11 @@ def random_bits(cfg: Cfg, e: int, step: int) -> int:
 
 def sr_round(x: float, u: int, sr_bits: int = 16) -> float:
     return float(lib().orc_sr_round(x, u, sr_bits))
+
+
+def inv_rtz(q: float, m: float) -> float:
+    """q / m rounded toward zero to fp32 (q, m > 0, finite quotient)."""
+    return float(lib().orc_inv_rtz(q, m))
 
 
 def to_bf16(x: float) -> int:

@@ -73,6 +73,15 @@ uint32_t orc_random_bits(const orc_cfg* c, uint64_t e, uint64_t step) {
  * sum truncated: code = floor((X + u) / 2^sr_bits).  Integer arithmetic, so
  * the decision is exact; E[code] = X / 2^sr_bits, within 2^-(sr_bits+1) of
  * x.  `xb` is x * 2^sr_bits. */
+/* q / m rounded toward zero, for finite q, m > 0 whose quotient is finite:
+ * the nearest float, stepped down once when it exceeds the exact quotient.
+ * A product of two floats is exact in double, so the comparison is exact. */
+float orc_inv_rtz(float q, float m) {
+  float f = q / m;
+  if ((double)f * (double)m > (double)q) f = nextafterf(f, 0.0f);
+  return f;
+}
+
 float orc_sr_round(float xb, uint32_t u, int32_t sr_bits) {
   double X = floor((double)xb + 0.5);
   return (float)floor((X + (double)u) / ldexp(1.0, sr_bits));
@@ -332,9 +341,12 @@ static float requantize_row(const orc_cfg* c, const head_addr* a, int64_t bh, in
       float mag = fabsf(sp[k]);
       if (mag > m) m = mag;
     }
-  /* Scale and its inverse; a row whose inverse (times 2^sr_bits under
-   * stochastic rounding) overflows, i.e. max below about Q*2^16/FLT_MAX, is
-   * stored as zero. */
+  /* Scale and its inverse.  A row whose nearest inverse Q / max (times
+   * 2^sr_bits under stochastic rounding) overflows, i.e. max below about
+   * Q*2^16/FLT_MAX, is stored as zero.  The inverse used for rounding is
+   * Q / max rounded toward zero: the largest float inv with inv * max <= Q
+   * exactly, so |value * inv| <= Q for every element of the row and no code
+   * ever reaches the clamp below. */
   float scale = 0.0f, inv = 0.0f, invb = 0.0f;
   if (m > 0.0f) {
     scale = m / Q;
@@ -344,6 +356,9 @@ static float requantize_row(const orc_cfg* c, const head_addr* a, int64_t bh, in
       scale = 0.0f;
       inv = 0.0f;
       invb = 0.0f;
+    } else {
+      inv = orc_inv_rtz(Q, m);
+      invb = (c->rounding == 1) ? ldexpf(inv, c->sr_bits) : inv;
     }
   }
   for (int k = 0; k < dk; ++k) {

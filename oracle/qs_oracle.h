@@ -68,6 +68,7 @@ int  orc_layout(const orc_cfg* c, orc_sizes* s, uint64_t* code_off, uint64_t* hp
 void orc_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]);
 uint32_t orc_random_bits(const orc_cfg* c, uint64_t e, uint64_t step);
 float orc_sr_round(float xb, uint32_t rbits, int32_t sr_bits);  /* xb = x * 2^sr_bits */
+float orc_inv_rtz(float q, float m);   /* q / m rounded toward zero */
 uint16_t orc_to_bf16(float f);
 uint16_t orc_to_fp16(float f);
 float orc_from_bf16(uint16_t h);

@@ -113,19 +113,32 @@ __device__ __forceinline__ float absmax8(float x) {
 
 // ---------------------------------------------------------------------------
 // Vector memory access of N bytes (N = 4, 8 or a multiple of 16; p aligned).
+// NT = nontemporal: the stored state is streamed once per step, so its loads
+// and stores carry the streaming hint (no reuse expected in the caches).
 // ---------------------------------------------------------------------------
-template <int N>
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+template <typename T>
+__device__ __forceinline__ T ld_nt(const T* p) { return __builtin_nontemporal_load(p); }
+template <typename T>
+__device__ __forceinline__ void st_nt(T* p, T v) { __builtin_nontemporal_store(v, p); }
+
+template <int N, bool NT = false>
 __device__ __forceinline__ void load_bytes(const uint8_t* p, uint32_t (&w)[N / 4]) {
   if constexpr (N == 4) {
-    w[0] = *reinterpret_cast<const uint32_t*>(p);
+    const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+    w[0] = NT ? ld_nt(q) : *q;
   } else if constexpr (N == 8) {
-    const uint2 t = *reinterpret_cast<const uint2*>(p);
+    const u32x2_t* q = reinterpret_cast<const u32x2_t*>(p);
+    const u32x2_t t = NT ? ld_nt(q) : *q;
     w[0] = t.x;
     w[1] = t.y;
   } else {
 #pragma unroll
     for (int i = 0; i < N / 16; ++i) {
-      const uint4 t = reinterpret_cast<const uint4*>(p)[i];
+      const u32x4_t* q = reinterpret_cast<const u32x4_t*>(p) + i;
+      const u32x4_t t = NT ? ld_nt(q) : *q;
       w[4 * i + 0] = t.x;
       w[4 * i + 1] = t.y;
       w[4 * i + 2] = t.z;
@@ -134,16 +147,22 @@ __device__ __forceinline__ void load_bytes(const uint8_t* p, uint32_t (&w)[N / 4
   }
 }
 
-template <int N>
+template <int N, bool NT = false>
 __device__ __forceinline__ void store_bytes(uint8_t* p, const uint32_t (&w)[N / 4]) {
   if constexpr (N == 4) {
-    *reinterpret_cast<uint32_t*>(p) = w[0];
+    uint32_t* q = reinterpret_cast<uint32_t*>(p);
+    if constexpr (NT) st_nt(q, w[0]); else *q = w[0];
   } else if constexpr (N == 8) {
-    *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]);
+    u32x2_t* q = reinterpret_cast<u32x2_t*>(p);
+    const u32x2_t t = {w[0], w[1]};
+    if constexpr (NT) st_nt(q, t); else *q = t;
   } else {
 #pragma unroll
-    for (int i = 0; i < N / 16; ++i)
-      reinterpret_cast<uint4*>(p)[i] = make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
+    for (int i = 0; i < N / 16; ++i) {
+      u32x4_t* q = reinterpret_cast<u32x4_t*>(p) + i;
+      const u32x4_t t = {w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
+      if constexpr (NT) st_nt(q, t); else *q = t;
+    }
   }
 }
 
@@ -224,7 +243,7 @@ __device__ __forceinline__ void dequant_words(const uint32_t (&w)[EPL * QB / 32]
 template <int QB, int EPL>
 __device__ __forceinline__ void load_codes(const uint8_t* p, float s, float (&sh)[EPL]) {
   uint32_t w[EPL * QB / 32];
-  load_bytes<EPL * QB / 8>(p, w);
+  load_bytes<EPL * QB / 8, true>(p, w);
   dequant_words<QB, EPL>(w, s, sh);
 }
 
@@ -239,7 +258,7 @@ __device__ __forceinline__ void store_codes(uint8_t* p, const int32_t (&c)[EPL])
     if constexpr (QB == 8) w[i >> 2] |= ((uint32_t)c[i] & 0xFFu) << (8 * (i & 3));
     else w[i >> 3] |= ((uint32_t)c[i] & 0xFu) << (4 * (i & 7));
   }
-  store_bytes<NB>(p, w);
+  store_bytes<NB, true>(p, w);
 }
 
 // Protected row slice: widen / store in hp_dtype (0 fp32, 1 bf16, 2 fp16).
@@ -247,12 +266,12 @@ template <int EPL>
 __device__ __forceinline__ void load_hp(const uint8_t* p, int dt, float (&f)[EPL]) {
   if (dt == 0) {
     uint32_t w[EPL];
-    load_bytes<EPL * 4>(p, w);
+    load_bytes<EPL * 4, true>(p, w);
 #pragma unroll
     for (int i = 0; i < EPL; ++i) f[i] = __uint_as_float(w[i]);
   } else {
     uint32_t w[EPL / 2];
-    load_bytes<EPL * 2>(p, w);
+    load_bytes<EPL * 2, true>(p, w);
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
       const uint32_t b = (w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
@@ -267,7 +286,7 @@ __device__ __forceinline__ void store_hp(uint8_t* p, int dt, const float (&f)[EP
     uint32_t w[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) w[i] = __float_as_uint(f[i]);
-    store_bytes<EPL * 4>(p, w);
+    store_bytes<EPL * 4, true>(p, w);
   } else {
     uint32_t w[EPL / 2];
     if (dt == 1) {
@@ -277,16 +296,27 @@ __device__ __forceinline__ void store_hp(uint8_t* p, int dt, const float (&f)[EP
 #pragma unroll
       for (int i = 0; i < EPL / 2; ++i) w[i] = f32_to_f16_bits(f[2 * i]) | (f32_to_f16_bits(f[2 * i + 1]) << 16);
     }
-    store_bytes<EPL * 2>(p, w);
+    store_bytes<EPL * 2, true>(p, w);
   }
 }
 
 // ---------------------------------------------------------------------------
-// Row scale (value-axis grouping): scale = max / Q and inv = Q / max, both
-// correctly rounded; invb = inv * 2^SRB (exact scaling) for stochastic
-// rounding with SRB random bits.  A zero row, or one whose inv (or invb)
+// Row scale (value-axis grouping): scale = max / Q correctly rounded; the
+// rounding inverse inv = Q / max rounded toward zero (the largest fp32 with
+// inv * max <= Q, so every |x| = |value * inv| <= Q and no code needs a
+// clamp); invb = inv * 2^SRB (exact scaling) for stochastic rounding with
+// SRB random bits.  A zero row, or one whose nearest Q / max (times 2^SRB)
 // overflows, is stored as zero.
 // ---------------------------------------------------------------------------
+
+// q / m rounded toward zero from its nearest value rn (q, m > 0, rn finite):
+// the residual q - rn * m is exact in one fma, and a negative one means rn
+// lies above the quotient, so the next float down is taken.
+__device__ __forceinline__ float inv_toward_zero(float q, float m, float rn) {
+  const float e = fmaf(-rn, m, q);
+  return e < 0.0f ? __uint_as_float(__float_as_uint(rn) - 1u) : rn;
+}
+
 template <int QB, int SRB>
 __device__ __forceinline__ void row_scale(float m, float& scale, float& inv, float& invb) {
   constexpr float Q = (QB == 8) ? 127.0f : 7.0f;
@@ -299,8 +329,8 @@ __device__ __forceinline__ void row_scale(float m, float& scale, float& inv, flo
     const float ib = i * (float)(1u << SRB);
     if (__builtin_isfinite(ib)) {
       scale = s;
-      inv = i;
-      invb = ib;
+      inv = inv_toward_zero(Q, m, i);
+      invb = inv * (float)(1u << SRB);
     }
   }
 }
@@ -323,11 +353,11 @@ constexpr int sr_bits_of() { return RND == 1 ? 16 : (RND == 2 ? 8 : 0); }
 // and the sum truncated, code = (X + rb) >> SRB.  BDR: with x = sp * inv and
 // xo = sh * inv (old value on the new grid), a code below xo - bound while
 // the element grew takes ceil(x); above xo + bound while it shrank takes
-// floor(x).  Codes are clamped to [-Q, Q].  A zero row (inv = 0) gives 0.
+// floor(x).  |x| <= Q (inv rounded toward zero) keeps every code in
+// [-Q, Q].  A zero row (inv = 0) gives 0.
 template <int QB, int RND, int BDR>
 __device__ __forceinline__ int32_t round_elem(float sp, float sh, float inv, float invb, uint32_t rb,
                                               float bound) {
-  constexpr int32_t Q = (QB == 8) ? 127 : 7;
   int32_t c;
   if constexpr (RND == 0) {
     c = (int32_t)rintf(sp * inv);
@@ -345,7 +375,7 @@ __device__ __forceinline__ int32_t round_elem(float sp, float sh, float inv, flo
     const int32_t dn = (int32_t)floorf(x);
     c = (d > 0.0f && cf < xo - bound) ? up : ((d < 0.0f && cf > xo + bound) ? dn : c);
   }
-  return c < -Q ? -Q : (c > Q ? Q : c);
+  return c;
 }
 
 }  // namespace qs

@@ -116,18 +116,18 @@ __device__ __forceinline__ float div_by_q(float m) {
   return fmaf(r, RQ, q0);
 }
 
-// Row scale and inverse for one row: scale = max/Q, inv = Q/max (both
-// correctly rounded), invb = inv * 2^SRB; zero when inv*2^SRB overflows
-// (max 0 gives Q/0 = inf).
+// Row scale and inverse for one row, branch-free: scale = max/Q correctly
+// rounded, inv = Q/max rounded toward zero, invb = inv * 2^SRB; zero when the
+// nearest Q/max times 2^SRB overflows (max 0 gives Q/0 = inf).
 template <int QB, int SRB>
 __device__ __forceinline__ void row_scale_fast(float m, float& scale, float& inv, float& invb) {
   constexpr float Q = (QB == 8) ? 127.0f : 7.0f;
   const float i = Q / m;
-  const float ib = i * (float)(1u << SRB);
-  const bool ok = __builtin_isfinite(ib);
+  const bool ok = __builtin_isfinite(i * (float)(1u << SRB));
+  const float iz = inv_toward_zero(Q, m, i);
   scale = ok ? div_by_q<QB>(m) : 0.0f;
-  inv = ok ? i : 0.0f;
-  invb = ok ? ib : 0.0f;
+  inv = ok ? iz : 0.0f;
+  invb = ok ? iz * (float)(1u << SRB) : 0.0f;
 }
 
 // Stage the head's k and q slices into LDS as fp32 (one conversion per
@@ -160,14 +160,13 @@ __device__ __forceinline__ void dense_quant_rows(const Args& a, uint8_t* blk, ui
   constexpr int RB = DK * QB / 8;           // code bytes per row
   constexpr int NW = EPL * QB / 32;         // code words per lane and row
   constexpr int SRB = sr_bits_of<RND>();
-  constexpr int32_t Q = (QB == 8) ? 127 : 7;
   const int k0 = lane8 * EPL;
   // every load first: state rows (HBM), then per-row scalars, then the head's inputs
   uint32_t w[RPL][NW];
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
     const int v = v0 + r * ng;
-    if (v < a.dv) load_bytes<EPL * QB / 8>(blk + (uint64_t)v * RB + k0 * QB / 8, w[r]);
+    if (v < a.dv) load_bytes<EPL * QB / 8, true>(blk + (uint64_t)v * RB + k0 * QB / 8, w[r]);
     else {
 #pragma unroll
       for (int i = 0; i < NW; ++i) w[r][i] = 0u;
@@ -178,7 +177,7 @@ __device__ __forceinline__ void dense_quant_rows(const Args& a, uint8_t* blk, ui
   for (int r = 0; r < RPL; ++r) {
     const int v = v0 + r * ng;
     const uint64_t row = bh * (uint64_t)a.dv + (uint64_t)(v < a.dv ? v : 0);
-    s_old[r] = a.scales[row];
+    s_old[r] = ld_nt(a.scales + row);
     vin[r] = load_in_scalar<INBF>(a.v, row);
   }
   float df[DKEY ? EPL : 1];
@@ -224,15 +223,15 @@ __device__ __forceinline__ void dense_quant_rows(const Args& a, uint8_t* blk, ui
     for (int i = 0; i < EPL; i += 2) mx = fmaxf(fmaxf(mx, fabsf(sp[i])), fabsf(sp[i + 1]));
     o = sum8(o);
     const float m = absmax8(mx);
-    if (lane8 == 0) a.out[row] = o;
+    if (lane8 == 0) st_nt(a.out + row, o);
     float scale, inv, invb;
     row_scale_fast<QB, SRB>(m, scale, inv, invb);
     // requantize
     uint32_t out[NW];
     if constexpr (QB == 8 && !BDR) {
-      // byte B of y holds the code: nearest, y = clamp(rint(x)); stochastic,
-      // y = clamp(floor(x 2^SRB + 1/2), +-Q 2^SRB) + rb and code = y >> SRB
-      // (clamping before the add gives the same code as clamping after)
+      // byte B of y holds the code: nearest, y = rint(x); stochastic,
+      // y = floor(x 2^SRB + 1/2) + rb and code = y >> SRB (|x| <= Q, so no
+      // clamp)
       constexpr int BYTE = SRB / 8;
       constexpr int PER = (RND == 1) ? 8 : 16;    // elements per Philox block
       constexpr int NB = (RND == 0) ? 1 : (EPL + PER - 1) / PER;
@@ -258,8 +257,7 @@ __device__ __forceinline__ void dense_quant_rows(const Args& a, uint8_t* blk, ui
         for (int j = 0; j < CNT; ++j) {
           const int i = gblk * PER + j;
           if constexpr (RND == 0) {
-            const int32_t c = (int32_t)rintf(sp[i] * inv);
-            y[j] = (uint32_t)(c < -Q ? -Q : (c > Q ? Q : c));
+            y[j] = (uint32_t)(int32_t)rintf(sp[i] * inv);   // in [-Q, Q]
           } else {
             uint32_t rbits;
             if constexpr (RND == 1) rbits = (j & 1) ? (x[j >> 1] >> 16) : (x[j >> 1] & 0xFFFFu);
@@ -268,9 +266,9 @@ __device__ __forceinline__ void dense_quant_rows(const Args& a, uint8_t* blk, ui
               const uint32_t word = (EPL < 16) ? (sel ? x[2 + (j >> 2)] : x[j >> 2]) : x[jj >> 2];
               rbits = (word >> (8 * (jj & 3))) & 0xFFu;
             }
-            constexpr int32_t QS = Q << SRB;
+            // |X| <= Q 2^SRB: the code byte (X + rbits) >> SRB stays in [-Q, Q]
             const int32_t X = cvt_rpi(sp[i] * invb);
-            y[j] = (uint32_t)((X < -QS ? -QS : (X > QS ? QS : X)) + (int32_t)rbits);
+            y[j] = (uint32_t)(X + (int32_t)rbits);
           }
         }
 #pragma unroll
@@ -299,8 +297,8 @@ __device__ __forceinline__ void dense_quant_rows(const Args& a, uint8_t* blk, ui
         else out[i >> 3] |= ((uint32_t)code[i] & 0xFu) << (4 * (i & 7));
       }
     }
-    store_bytes<EPL * QB / 8>(blk + (uint64_t)v * RB + k0 * QB / 8, out);
-    if (lane8 == 0) a.scales[row] = scale;
+    store_bytes<EPL * QB / 8, true>(blk + (uint64_t)v * RB + k0 * QB / 8, out);
+    if (lane8 == 0) st_nt(a.scales + row, scale);
   }
 }
 
@@ -314,7 +312,7 @@ __device__ __forceinline__ void dense_prot_rows(const Args& a, uint8_t* blk, uin
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
     const int v = v0 + r * ng;
-    if (v < a.dv) load_bytes<EPL * 2>(blk + ((uint64_t)v * DK + (uint64_t)k0) * 2u, hw[r]);
+    if (v < a.dv) load_bytes<EPL * 2, true>(blk + ((uint64_t)v * DK + (uint64_t)k0) * 2u, hw[r]);
     else {
 #pragma unroll
       for (int i = 0; i < EPL / 2; ++i) hw[r][i] = 0u;
@@ -363,13 +361,13 @@ __device__ __forceinline__ void dense_prot_rows(const Args& a, uint8_t* blk, uin
       o = fmaf(sp[i], qf[i], o);
     }
     o = sum8(o);
-    if (lane8 == 0) a.out[row] = o;
+    if (lane8 == 0) st_nt(a.out + row, o);
     uint32_t ow[EPL / 2];
 #pragma unroll
     for (int i = 0; i < EPL / 2; ++i)
       ow[i] = is_bf16 ? pack_bf16x2(sp[2 * i], sp[2 * i + 1])
                       : (f32_to_f16_bits(sp[2 * i]) | (f32_to_f16_bits(sp[2 * i + 1]) << 16));
-    store_bytes<EPL * 2>(blk + ((uint64_t)v * DK + (uint64_t)k0) * 2u, ow);
+    store_bytes<EPL * 2, true>(blk + ((uint64_t)v * DK + (uint64_t)k0) * 2u, ow);
   }
 }
 
@@ -443,9 +441,9 @@ __global__ __launch_bounds__(256) void k_step_mixed(const Args a) {
   uint8_t* lhp = lds + code_bytes;
 
   for (uint32_t i = (uint32_t)tid * 16u; i < code_bytes; i += 256u * 16u)
-    *reinterpret_cast<uint4*>(lcode + i) = *reinterpret_cast<const uint4*>(gcode + i);
+    *reinterpret_cast<u32x4_t*>(lcode + i) = ld_nt(reinterpret_cast<const u32x4_t*>(gcode + i));
   for (uint32_t i = (uint32_t)tid * 16u; i < hp_bytes; i += 256u * 16u)
-    *reinterpret_cast<uint4*>(lhp + i) = *reinterpret_cast<const uint4*>(ghp + i);
+    *reinterpret_cast<u32x4_t*>(lhp + i) = ld_nt(reinterpret_cast<const u32x4_t*>(ghp + i));
 
   const int k0 = lane8 * EPL;
   uint16_t sl[EPL];
@@ -460,7 +458,7 @@ __global__ __launch_bounds__(256) void k_step_mixed(const Args a) {
 
   for (int v = rloc; v < a.dv; v += 32) {
     const uint64_t row = (uint64_t)bh * (uint64_t)a.dv + (uint64_t)v;
-    const float s_old = a.scales[row];
+    const float s_old = ld_nt(a.scales + row);
     const float vin = load_in1(a.v, a.in_bf16, row);
     uint8_t* crow = lcode + (uint32_t)v * rq;
     uint8_t* hrow = lhp + (uint32_t)v * (uint32_t)nhp * (uint32_t)hpb;
@@ -500,7 +498,7 @@ __global__ __launch_bounds__(256) void k_step_mixed(const Args a) {
 #pragma unroll
     for (int i = 0; i < EPL; ++i) o = fmaf(sp[i], qf[i], o);
     o = sum8(o);
-    if (lane8 == 0) a.out[row] = o;
+    if (lane8 == 0) st_nt(a.out + row, o);
 
     float m = 0.0f;
 #pragma unroll
@@ -570,13 +568,13 @@ __global__ __launch_bounds__(256) void k_step_mixed(const Args a) {
         }
       }
     }
-    if (lane8 == 0) a.scales[row] = scale;
+    if (lane8 == 0) st_nt(a.scales + row, scale);
   }
   __syncthreads();
   for (uint32_t i = (uint32_t)tid * 16u; i < code_bytes; i += 256u * 16u)
-    *reinterpret_cast<uint4*>(gcode + i) = *reinterpret_cast<const uint4*>(lcode + i);
+    st_nt(reinterpret_cast<u32x4_t*>(gcode + i), *reinterpret_cast<const u32x4_t*>(lcode + i));
   for (uint32_t i = (uint32_t)tid * 16u; i < hp_bytes; i += 256u * 16u)
-    *reinterpret_cast<uint4*>(ghp + i) = *reinterpret_cast<const uint4*>(lhp + i);
+    st_nt(reinterpret_cast<u32x4_t*>(ghp + i), *reinterpret_cast<const u32x4_t*>(lhp + i));
 }
 
 // ---------------------------------------------------------------------------
@@ -663,7 +661,7 @@ __global__ __launch_bounds__(256) void k_step_lrb(const Args a) {
   if (tid < dv) {
     const uint64_t row = (uint64_t)bh * (uint64_t)dv + (uint64_t)tid;
     ul[tid] = beta * load_in1(a.v, a.in_bf16, row);
-    sol[tid] = a.scales[row];
+    sol[tid] = ld_nt(a.scales + row);
   }
   if (tid < DK) {
     kl[tid] = load_in1(a.k, a.in_bf16, (uint64_t)bh * DK + tid);
@@ -781,7 +779,7 @@ __global__ __launch_bounds__(256) void k_step_lrb(const Args a) {
     const uint64_t row = (uint64_t)bh * (uint64_t)dv + (uint64_t)v;
     uint8_t* cp = gcode + (uint64_t)v * (DK * QB / 8) + k0 * QB / 8;
     uint32_t cw[EPL * QB / 32];
-    load_bytes<EPL * QB / 8>(cp, cw);
+    load_bytes<EPL * QB / 8, true>(cp, cw);
     const float s_old = sol[v];
     float sh[EPL], cf[EPL];
 #pragma unroll
@@ -806,7 +804,7 @@ __global__ __launch_bounds__(256) void k_step_lrb(const Args a) {
 #pragma unroll
     for (int i = 0; i < EPL; ++i) o = fmaf(sp[i], qf[i], o);
     o = sum8(o);
-    if (lane8 == 0) a.out[row] = o + lrl[v];
+    if (lane8 == 0) st_nt(a.out + row, o + lrl[v]);
     float m = 0.0f;
 #pragma unroll
     for (int i = 0; i < EPL; ++i) m = fmaxf(m, fabsf(sp[i]));
@@ -823,7 +821,7 @@ __global__ __launch_bounds__(256) void k_step_lrb(const Args a) {
                       : round_elem<QB, RND, 0>(sp[i], sh[i], inv, invb, rbi, a.bdr_bound);
     }
     store_codes<QB, EPL>(cp, code);
-    if (lane8 == 0) a.scales[row] = scale;
+    if (lane8 == 0) st_nt(a.scales + row, scale);
   }
 }
 

@@ -8,22 +8,27 @@ namespace qs {
 
 namespace {
 
+template <int QB, int RND, int DELTA, int EPL, int RPL, int BDR, int DKEY, int INBF>
+void launch_dense_one(const Args& a, hipStream_t s) {
+  const uint64_t grid = (uint64_t)a.B * (uint64_t)a.H * (uint64_t)a.row_chunks;
+  hipLaunchKernelGGL((k_step_dense<QB, RND, DELTA, EPL, RPL, BDR, DKEY, INBF>), dim3((uint32_t)grid),
+                     dim3((uint32_t)a.dense_threads), 0, s, a);
+}
+
 template <int QB, int RND, int DELTA, int EPL, int RPL, int INBF>
 hipError_t launch_dense_rpl(const Args& a, hipStream_t s) {
-  const uint64_t grid = (uint64_t)a.B * (uint64_t)a.H * (uint64_t)a.row_chunks;
-  const dim3 g((uint32_t)grid), blk((uint32_t)a.dense_threads);
   if constexpr (DELTA) {
     // the delta rule takes one decay per head
     if (a.decay_key) return hipErrorInvalidValue;
-    if (a.bdr) hipLaunchKernelGGL((k_step_dense<QB, RND, DELTA, EPL, RPL, 1, 0, INBF>), g, blk, 0, s, a);
-    else hipLaunchKernelGGL((k_step_dense<QB, RND, DELTA, EPL, RPL, 0, 0, INBF>), g, blk, 0, s, a);
+    if (a.bdr) launch_dense_one<QB, RND, DELTA, EPL, RPL, 1, 0, INBF>(a, s);
+    else launch_dense_one<QB, RND, DELTA, EPL, RPL, 0, 0, INBF>(a, s);
   } else {
     if (a.bdr) {
-      if (a.decay_key) hipLaunchKernelGGL((k_step_dense<QB, RND, DELTA, EPL, RPL, 1, 1, INBF>), g, blk, 0, s, a);
-      else hipLaunchKernelGGL((k_step_dense<QB, RND, DELTA, EPL, RPL, 1, 0, INBF>), g, blk, 0, s, a);
+      if (a.decay_key) launch_dense_one<QB, RND, DELTA, EPL, RPL, 1, 1, INBF>(a, s);
+      else launch_dense_one<QB, RND, DELTA, EPL, RPL, 1, 0, INBF>(a, s);
     } else {
-      if (a.decay_key) hipLaunchKernelGGL((k_step_dense<QB, RND, DELTA, EPL, RPL, 0, 1, INBF>), g, blk, 0, s, a);
-      else hipLaunchKernelGGL((k_step_dense<QB, RND, DELTA, EPL, RPL, 0, 0, INBF>), g, blk, 0, s, a);
+      if (a.decay_key) launch_dense_one<QB, RND, DELTA, EPL, RPL, 0, 1, INBF>(a, s);
+      else launch_dense_one<QB, RND, DELTA, EPL, RPL, 0, 0, INBF>(a, s);
     }
   }
   return hipGetLastError();

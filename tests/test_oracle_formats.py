@@ -9,7 +9,14 @@
   (halves up), within 2^-17 (2^-9) of x.
 * the map builder keeps the round-half-up(frac * n) units of smallest decay
   rate per group, ties to the lower index (hand-made statistics).
+* the row inverse Q / max rounded toward zero is the largest fp32 whose
+  product with max does not exceed Q (exact rational arithmetic), so every
+  element of the row scales into [-Q, Q] (and [-Q 2^b, Q 2^b] for
+  stochastic rounding) without clamping.
 """
+import math
+from fractions import Fraction
+
 import numpy as np
 import pytest
 import torch
@@ -90,3 +97,38 @@ def test_map_builder_hand_cases():
     # frac 0 and 1
     assert oracle.build_map(np.arange(4.0), 1, 4, 0.0).sum() == 0
     assert oracle.build_map(np.arange(4.0), 1, 4, 1.0).sum() == 4
+
+
+def _magnitudes():
+    rng = np.random.default_rng(11)
+    m = [rng.standard_normal(3000).astype(np.float32) * np.float32(10.0) ** rng.integers(-30, 30, 3000)]
+    m.append(rng.integers(0x00800000, 0x7F000000, 3000, dtype=np.uint64).astype(np.uint32).view(np.float32))
+    m.append(np.array([1.0, 127.0, 7.0, 0.5, 3.0, 1.0 / 3.0, 2.0 ** -100, 1e-30, 3.0e30], np.float32))
+    m = np.abs(np.concatenate(m)).astype(np.float32)
+    return m[(m > 0) & np.isfinite(m)]
+
+
+@pytest.mark.parametrize("q", [127.0, 7.0])
+def test_inverse_scale_rounds_toward_zero(q):
+    for m in _magnitudes():
+        m = float(m)
+        if q / m * 65536.0 >= 2.0 ** 127:      # inverse (times 2^16) near fp32 overflow
+            continue
+        f = oracle.inv_rtz(q, m)
+        assert Fraction(f) * Fraction(m) <= Fraction(q)
+        up = float(np.nextafter(np.float32(f), np.float32(np.inf)))
+        assert Fraction(up) * Fraction(m) > Fraction(q), (m, f)
+
+
+@pytest.mark.parametrize("q", [127.0, 7.0])
+def test_scaled_row_never_exceeds_q(q):
+    rng = np.random.default_rng(12)
+    for _ in range(300):
+        row = (rng.standard_normal(64) * 10.0 ** rng.uniform(-20, 20)).astype(np.float32)
+        m = float(np.abs(row).max())
+        inv = np.float32(oracle.inv_rtz(q, m))
+        for bits in (0, 8, 16):
+            invb = np.float32(inv * np.float32(2.0 ** bits))      # exact scaling
+            x = row * invb                                        # fp32 products, nearest
+            assert np.abs(x).max() <= q * 2.0 ** bits
+        assert np.abs(row * inv).max() >= q * (1 - 2.0 ** -22)  # the maximum reaches Q
