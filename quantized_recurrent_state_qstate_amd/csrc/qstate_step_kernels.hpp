@@ -56,35 +56,6 @@ __device__ __forceinline__ void load_decay(const Args& a, uint64_t bh, int k0, f
 // row is computed.
 // ---------------------------------------------------------------------------
 
-// Row scales of the RPL rows a lane group holds.  The 2*RPL correctly
-// rounded divisions (max/Q and Q/max per row) are spread over the group's
-// lanes -- lane j computes division j -- and gathered back with ds_bpermute,
-// instead of every lane computing all of them.
-template <int QB, int SRB, int RPL>
-__device__ __forceinline__ void group_row_scales(const float (&m)[RPL], int lane8, float (&scale)[RPL],
-                                                 float (&inv)[RPL], float (&invb)[RPL]) {
-  constexpr float Q = (QB == 8) ? 127.0f : 7.0f;
-  const int rr = (lane8 >> 1) & (RPL - 1);
-  float mr = m[0];
-#pragma unroll
-  for (int r = 1; r < RPL; ++r) mr = (rr == r) ? m[r] : mr;
-  const bool odd = lane8 & 1;
-  const float num = odd ? Q : mr;
-  const float den = odd ? mr : Q;
-  const float qv = num / den;               // even lane: max/Q, odd lane: Q/max
-  const int base = (int)(threadIdx.x & ~7u) & 63;
-#pragma unroll
-  for (int r = 0; r < RPL; ++r) {
-    const float s = __shfl(qv, base + 2 * r, 64);
-    const float i = __shfl(qv, base + 2 * r + 1, 64);
-    const float ib = i * (float)(1u << SRB);
-    const bool ok = __builtin_isfinite(ib);   // max 0 gives Q/0 = inf: a zero row
-    scale[r] = ok ? s : 0.0f;
-    inv[r] = ok ? i : 0.0f;
-    invb[r] = ok ? ib : 0.0f;
-  }
-}
-
 // Pack four 32-bit words' byte B into one word (byte i from word i).
 template <int B>
 __device__ __forceinline__ uint32_t pack4(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3) {
@@ -93,10 +64,6 @@ __device__ __forceinline__ uint32_t pack4(uint32_t c0, uint32_t c1, uint32_t c2,
   const uint32_t p23 = __builtin_amdgcn_perm(c3, c2, sel);
   return __builtin_amdgcn_perm(p23, p01, 0x05040100u);
 }
-
-// Input words of a lane's EPL-element slice: bf16 (two per word) or fp32.
-template <int EPL, int INBF>
-constexpr int in_words() { return INBF ? EPL / 2 : EPL; }
 
 template <int INBF>
 __device__ __forceinline__ float load_in_scalar(const void* base, uint64_t idx) {
