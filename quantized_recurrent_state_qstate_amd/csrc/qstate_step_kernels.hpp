@@ -358,11 +358,18 @@ void k_step_dense(const Args a) {
   const int lane8 = threadIdx.x & 7;
   const int g = threadIdx.x >> 3;
   const int ng = blockDim.x >> 3;
-  const uint32_t wg = blockIdx.x;
-  const uint32_t chunk = wg % (uint32_t)a.row_chunks;
-  const uint32_t bh = wg / (uint32_t)a.row_chunks;
-  const uint32_t h = bh % (uint32_t)a.H;
-  const uint32_t b = bh / (uint32_t)a.H;
+  // Workgroups are dealt to the XCDs round-robin, so with the plain order an
+  // XCD would only ever see the heads h = x (mod 8): under a head map some
+  // XCDs would hold only quantized heads (VALU-heavy) and others most of the
+  // 16-bit ones (traffic-heavy).  Rotating the (head, chunk) order by the
+  // batch index gives every XCD every head in turn.
+  const uint32_t per_b = (uint32_t)a.H * (uint32_t)a.row_chunks;
+  const uint32_t b = blockIdx.x / per_b;
+  uint32_t r = blockIdx.x - b * per_b + b % per_b;
+  r = r >= per_b ? r - per_b : r;
+  const uint32_t chunk = r % (uint32_t)a.row_chunks;
+  const uint32_t h = r / (uint32_t)a.row_chunks;
+  const uint32_t bh = b * (uint32_t)a.H + h;
   const int v0 = (int)chunk * ng * RPL + g;   // groups past dv stay for the barrier
   __shared__ __align__(16) float lds[2 * EPL * 8];
   // head storage from the protected-head mask: no table lookup stands
