@@ -51,9 +51,10 @@ __device__ __forceinline__ void load_decay(const Args& a, uint64_t bh, int k0, f
 // Dense step: every head either fully quantized or fully protected
 // (precision map NONE or HEAD).  A workgroup has NG row groups of 8 lanes
 // (NG = blockDim / 8) and covers NG * RPL rows of one head: lane group g
-// holds rows g, g + NG, ... so the per-lane inputs (q, k, decay) are loaded
-// and widened once for RPL rows; every row's state load is issued before any
-// row is computed.
+// holds the consecutive rows g*RPL .. g*RPL + RPL-1, so the per-lane inputs
+// (q, k, decay) are loaded and widened once for RPL rows and a wave's rows
+// are one contiguous stretch of the state, scales and outputs; every row's
+// state load is issued before any row is computed.
 // ---------------------------------------------------------------------------
 
 // Pack four 32-bit words' byte B into one word (byte i from word i).
@@ -120,6 +121,25 @@ __device__ __forceinline__ void stage_qk(const Args& a, uint64_t bh, int lane8, 
   }
 }
 
+// Outputs (and scales) of the RPL consecutive rows v0 .. v0+RPL-1 of a lane
+// group: lane r of the group stores row v0 + r, so a wave's 8 groups write
+// 8*RPL consecutive values with one store per array.
+template <int RPL>
+__device__ __forceinline__ void store_row_values(const Args& a, uint64_t bh, int v0, int lane8,
+                                                 const float (&o_row)[RPL], const float* s_row) {
+  float ov = o_row[0], sv = s_row ? s_row[0] : 0.0f;
+#pragma unroll
+  for (int r = 1; r < RPL; ++r) {
+    ov = lane8 == r ? o_row[r] : ov;
+    if (s_row) sv = lane8 == r ? s_row[r] : sv;
+  }
+  if (lane8 < RPL && v0 + lane8 < a.dv) {
+    const uint64_t row = bh * (uint64_t)a.dv + (uint64_t)(v0 + lane8);
+    st_nt(a.out + row, ov);
+    if (s_row) st_nt(a.scales + row, sv);
+  }
+}
+
 template <int QB, int RND, int DELTA, int EPL, int RPL, int BDR, int DKEY, int INBF>
 __device__ __forceinline__ void dense_quant_rows(const Args& a, uint8_t* blk, uint64_t bh, int v0, int ng,
                                                  int lane8, float* lds) {
@@ -132,7 +152,7 @@ __device__ __forceinline__ void dense_quant_rows(const Args& a, uint8_t* blk, ui
   uint32_t w[RPL][NW];
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
-    const int v = v0 + r * ng;
+    const int v = v0 + r;
     if (v < a.dv) load_bytes<EPL * QB / 8, true>(blk + (uint64_t)v * RB + k0 * QB / 8, w[r]);
     else {
 #pragma unroll
@@ -142,7 +162,7 @@ __device__ __forceinline__ void dense_quant_rows(const Args& a, uint8_t* blk, ui
   float s_old[RPL], vin[RPL];
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
-    const int v = v0 + r * ng;
+    const int v = v0 + r;
     const uint64_t row = bh * (uint64_t)a.dv + (uint64_t)(v < a.dv ? v : 0);
     s_old[r] = ld_nt(a.scales + row);
     vin[r] = load_in_scalar<INBF>(a.v, row);
@@ -154,9 +174,12 @@ __device__ __forceinline__ void dense_quant_rows(const Args& a, uint8_t* blk, ui
   const float beta = a.beta ? a.beta[bh] : 1.0f;
   float kf[EPL], qf[EPL];
   stage_qk<EPL, INBF>(a, bh, lane8, lds, kf, qf);
+  float o_row[RPL], s_row[RPL];
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
-    const int v = v0 + r * ng;
+    const int v = v0 + r;
+    o_row[r] = 0.0f;
+    s_row[r] = 0.0f;
     if (v >= a.dv) continue;   // whole 8-lane groups skip together
     const uint64_t row = bh * (uint64_t)a.dv + (uint64_t)v;
     // decay + update, readout, row maximum
@@ -190,9 +213,10 @@ __device__ __forceinline__ void dense_quant_rows(const Args& a, uint8_t* blk, ui
     for (int i = 0; i < EPL; i += 2) mx = fmaxf(fmaxf(mx, fabsf(sp[i])), fabsf(sp[i + 1]));
     o = sum8(o);
     const float m = absmax8(mx);
-    if (lane8 == 0) st_nt(a.out + row, o);
+    o_row[r] = o;
     float scale, inv, invb;
     row_scale_fast<QB, SRB>(m, scale, inv, invb);
+    s_row[r] = scale;
     // requantize
     uint32_t out[NW];
     if constexpr (QB == 8 && !BDR) {
@@ -265,8 +289,8 @@ __device__ __forceinline__ void dense_quant_rows(const Args& a, uint8_t* blk, ui
       }
     }
     store_bytes<EPL * QB / 8, true>(blk + (uint64_t)v * RB + k0 * QB / 8, out);
-    if (lane8 == 0) st_nt(a.scales + row, scale);
   }
+  store_row_values<RPL>(a, bh, v0, lane8, o_row, s_row);
 }
 
 // Protected (16-bit) heads of a head map.
@@ -278,7 +302,7 @@ __device__ __forceinline__ void dense_prot_rows(const Args& a, uint8_t* blk, uin
   uint32_t hw[RPL][EPL / 2];
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
-    const int v = v0 + r * ng;
+    const int v = v0 + r;
     if (v < a.dv) load_bytes<EPL * 2, true>(blk + ((uint64_t)v * DK + (uint64_t)k0) * 2u, hw[r]);
     else {
 #pragma unroll
@@ -288,7 +312,7 @@ __device__ __forceinline__ void dense_prot_rows(const Args& a, uint8_t* blk, uin
   float vin[RPL];
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
-    const int v = v0 + r * ng;
+    const int v = v0 + r;
     vin[r] = load_in_scalar<INBF>(a.v, bh * (uint64_t)a.dv + (uint64_t)(v < a.dv ? v : 0));
   }
   float df[DKEY ? EPL : 1];
@@ -299,9 +323,11 @@ __device__ __forceinline__ void dense_prot_rows(const Args& a, uint8_t* blk, uin
   float kf[EPL], qf[EPL];
   stage_qk<EPL, INBF>(a, bh, lane8, lds, kf, qf);
   const bool is_bf16 = a.hp_dtype == 1;
+  float o_row[RPL];
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
-    const int v = v0 + r * ng;
+    const int v = v0 + r;
+    o_row[r] = 0.0f;
     if (v >= a.dv) continue;
     const uint64_t row = bh * (uint64_t)a.dv + (uint64_t)v;
     float u;
@@ -327,8 +353,7 @@ __device__ __forceinline__ void dense_prot_rows(const Args& a, uint8_t* blk, uin
       sp[i] = fmaf(u, kf[i], (DKEY ? df[i] : dh) * sh);
       o = fmaf(sp[i], qf[i], o);
     }
-    o = sum8(o);
-    if (lane8 == 0) st_nt(a.out + row, o);
+    o_row[r] = sum8(o);
     uint32_t ow[EPL / 2];
 #pragma unroll
     for (int i = 0; i < EPL / 2; ++i)
@@ -336,6 +361,7 @@ __device__ __forceinline__ void dense_prot_rows(const Args& a, uint8_t* blk, uin
                       : (f32_to_f16_bits(sp[2 * i]) | (f32_to_f16_bits(sp[2 * i + 1]) << 16));
     store_bytes<EPL * 2, true>(blk + ((uint64_t)v * DK + (uint64_t)k0) * 2u, ow);
   }
+  store_row_values<RPL>(a, bh, v0, lane8, o_row, nullptr);
 }
 
 // Register budget (minimum waves per SIMD the body is compiled for), chosen
@@ -347,7 +373,7 @@ template <int EPL, int RPL, int BDR, int DKEY, int INBF, int DELTA>
 constexpr int dense_min_waves() {
   return EPL >= 32 ? 1
                    : (EPL <= 8 ? (BDR ? 6 : 8)
-                               : (RPL == 1 ? 7 : 5) - (BDR ? 2 : 0) - (DKEY ? 1 : 0) - (INBF ? 0 : 1) -
+                               : (RPL == 1 ? 7 : 6) - (BDR ? 2 : 0) - (DKEY ? 1 : 0) - (INBF ? 0 : 1) -
                                      (DELTA ? 1 : 0));
 }
 
@@ -370,7 +396,7 @@ void k_step_dense(const Args a) {
   const uint32_t chunk = r % (uint32_t)a.row_chunks;
   const uint32_t h = r / (uint32_t)a.row_chunks;
   const uint32_t bh = b * (uint32_t)a.H + h;
-  const int v0 = (int)chunk * ng * RPL + g;   // groups past dv stay for the barrier
+  const int v0 = ((int)chunk * ng + g) * RPL;   // groups past dv stay for the barrier
   __shared__ __align__(16) float lds[2 * EPL * 8];
   // head storage from the protected-head mask: no table lookup stands
   // between the launch and the state loads
