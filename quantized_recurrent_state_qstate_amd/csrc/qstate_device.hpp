@@ -96,6 +96,17 @@ __device__ __forceinline__ float max8(float x) {
   return x;
 }
 
+// The same reductions over a group of L = 4 or 8 lanes (4: the two quad
+// steps only).
+template <int L>
+__device__ __forceinline__ float red_sum(float x) {
+  static_assert(L == 4 || L == 8, "row groups of 4 or 8 lanes");
+  x = x + dppf<kDppXor1>(x);
+  x = x + dppf<kDppXor2>(x);
+  if constexpr (L == 8) x = x + dppf<kDppHalfMirror>(x);
+  return x;
+}
+
 // Maximum of non-negative floats over the row group, on their bit patterns
 // (for x >= 0 the unsigned order of the bits is the numeric order), so each
 // step is one v_max_u32 with a DPP operand.
@@ -108,6 +119,15 @@ __device__ __forceinline__ float absmax8(float x) {
   u = max(u, dppu<kDppXor1>(u));
   u = max(u, dppu<kDppXor2>(u));
   u = max(u, dppu<kDppHalfMirror>(u));
+  return __uint_as_float(u);
+}
+template <int L>
+__device__ __forceinline__ float red_absmax(float x) {
+  static_assert(L == 4 || L == 8, "row groups of 4 or 8 lanes");
+  uint32_t u = __float_as_uint(x);
+  u = max(u, dppu<kDppXor1>(u));
+  u = max(u, dppu<kDppXor2>(u));
+  if constexpr (L == 8) u = max(u, dppu<kDppHalfMirror>(u));
   return __uint_as_float(u);
 }
 
@@ -194,8 +214,19 @@ __device__ __forceinline__ float f16_bits_to_f32(uint32_t b) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
 }
 
-__device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+// fp32 -> fp16 bits with one v_cvt_f16_f32 (nearest even, subnormals kept).
+// Written as asm so that the compiler cannot fuse the fma that produced f
+// into a mixed-precision fma, which rounds once straight to fp16 instead of
+// to fp32 and then to fp16.
+__device__ __forceinline__ uint32_t cvt_f16_raw(float f) {
+  uint32_t r;
+  asm("v_cvt_f16_f32 %0, %1" : "=v"(r) : "v"(f));
+  return r;
+}
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float f) { return cvt_f16_raw(f) & 0xFFFFu; }
+// Two values packed, lo in the low half.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  return __builtin_amdgcn_perm(cvt_f16_raw(hi), cvt_f16_raw(lo), 0x05040100u);
 }
 
 // Scalar input element (bf16 or fp32).
@@ -294,7 +325,7 @@ __device__ __forceinline__ void store_hp(uint8_t* p, int dt, const float (&f)[EP
       for (int i = 0; i < EPL / 2; ++i) w[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
     } else {
 #pragma unroll
-      for (int i = 0; i < EPL / 2; ++i) w[i] = f32_to_f16_bits(f[2 * i]) | (f32_to_f16_bits(f[2 * i + 1]) << 16);
+      for (int i = 0; i < EPL / 2; ++i) w[i] = pack_f16x2(f[2 * i], f[2 * i + 1]);
     }
     store_bytes<EPL * 2, true>(p, w);
   }

@@ -51,15 +51,13 @@ struct Plan {
   int family = qs::kFamDense;
   int row_chunks = 1;
   int dense_rpl = 1;
+  int dense_lpr = 8;
   int dense_threads = 256;
   uint32_t lds = 0;
   uint64_t prot_mask = 0;       // dense family: protected heads
   uint64_t code_hblk = 0, hp_hblk = 0;
 };
 
-// Rows per lane and row groups per workgroup of the dense kernel.  Default:
-// two rows per lane when a head has more than 32 rows; QSTATE_DENSE_RPL
-// (1, 2) and QSTATE_DENSE_GROUPS (8, 16, 32) override for tuning.
 int env_int(const char* name, int dflt) {
   const char* e = std::getenv(name);
   if (!e || !*e) return dflt;
@@ -68,15 +66,27 @@ int env_int(const char* name, int dflt) {
   return (end && *end == 0) ? (int)v : dflt;
 }
 
-void dense_shape(int dv, int* rpl, int* threads, int* chunks) {
+// Shape of the dense kernel: lanes per row (4 for the delta rule at dk 128,
+// where the delta term makes the per-row work heavier and 32 keys per lane
+// measured faster; 8 otherwise), rows per lane (two with 8 lanes when a head
+// has more than 32 rows) and row groups per workgroup (whole waves, at most
+// 256 threads).  QSTATE_DENSE_LPR (4, 8; dk 128 only), QSTATE_DENSE_RPL
+// (1, 2) and QSTATE_DENSE_GROUPS override for tuning.
+void dense_shape(int kind, int dk, int dv, int* lpr, int* rpl, int* threads, int* chunks) {
+  int l = dk == 128 ? env_int("QSTATE_DENSE_LPR", kind == QS_KIND_DELTA ? 4 : 8) : 8;
+  if (l != 4 && l != 8) l = 8;
   int r = env_int("QSTATE_DENSE_RPL", dv > 32 ? 2 : 1);
   if (r != 1 && r != 2) r = dv > 32 ? 2 : 1;
+  if (l == 4) r = 1;                         // 32 keys per lane: one row per lane
+  const int gpw = 64 / l;                    // row groups per wave
+  const int gmax = 256 / l;                  // row groups per workgroup, at most
   int ng = (dv + r - 1) / r;                 // row groups needed for one head
-  ng = std::min(32, (ng + 7) / 8 * 8);       // whole waves
+  ng = std::min(gmax, (ng + gpw - 1) / gpw * gpw);   // whole waves
   const int ng_env = env_int("QSTATE_DENSE_GROUPS", 0);
-  if (ng_env == 8 || ng_env == 16 || ng_env == 32) ng = ng_env;
+  if (ng_env > 0 && ng_env <= gmax && ng_env % gpw == 0) ng = ng_env;
+  *lpr = l;
   *rpl = r;
-  *threads = 8 * ng;
+  *threads = l * ng;
   *chunks = (dv + ng * r - 1) / (ng * r);
 }
 
@@ -163,7 +173,7 @@ qs_status make_plan(const qstate_config* c, Plan* p) {
   p->sizes.lrb_U = BH * (uint64_t)dk * r * 4u;
   p->sizes.lrb_n = r > 0 ? BH * 4u : 0u;
 
-  dense_shape(dv, &p->dense_rpl, &p->dense_threads, &p->row_chunks);
+  dense_shape(c->kind, dk, dv, &p->dense_lpr, &p->dense_rpl, &p->dense_threads, &p->row_chunks);
   if (c->lrb_rank > 0) {
     p->family = qs::kFamLrb;
     const uint64_t floats = (uint64_t)dv * r + (uint64_t)dk * r + 4u * (uint64_t)dv + 3u * (uint64_t)dk + 36u;
@@ -261,6 +271,7 @@ qs::Args base_args(const qstate_handle* h, const qstate_tensors* st) {
   a.t = h->t;
   a.row_chunks = h->plan.row_chunks;
   a.dense_rpl = h->plan.dense_rpl;
+  a.dense_lpr = h->plan.dense_lpr;
   a.dense_threads = h->plan.dense_threads;
   a.prot_mask = h->plan.prot_mask;
   a.code_hblk = h->plan.code_hblk;

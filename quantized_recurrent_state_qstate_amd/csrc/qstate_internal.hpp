@@ -46,7 +46,8 @@ struct Args {
   DevTables t;
   int32_t row_chunks;  // dense kernel: work items (row chunks) per head
   int32_t dense_rpl;   // dense kernel: rows per lane (1, 2)
-  int32_t dense_threads;  // dense kernel: threads per workgroup (8 per row group)
+  int32_t dense_threads;  // dense kernel: threads per workgroup (dense_lpr per row group)
+  int32_t dense_lpr;   // dense kernel: lanes per row (8, or 4 for dk 128)
   uint64_t prot_mask;  // dense kernel: bit h set = head h protected (H <= 64 with a head map)
   uint64_t code_hblk;  // dense kernel: bytes of one quantized head's code block
   uint64_t hp_hblk;    // dense kernel: bytes of one protected head's block

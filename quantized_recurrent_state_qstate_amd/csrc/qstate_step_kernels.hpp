@@ -17,6 +17,8 @@
 // rows never exchange data.  A 256-thread workgroup covers 32 rows of one
 // head per row a lane holds (two rows per lane when a head has more than 32).
 #pragma once
+#include <type_traits>
+
 #include "qstate_device.hpp"
 #include "qstate_internal.hpp"
 
@@ -98,13 +100,30 @@ __device__ __forceinline__ void row_scale_fast(float m, float& scale, float& inv
   invb = ok ? iz * (float)(1u << SRB) : 0.0f;
 }
 
-// Stage the head's k and q slices into LDS as fp32 (one conversion per
-// value per workgroup instead of one per value and row-lane), then every lane
-// reads its EPL-wide slices.  Contains a workgroup barrier.
-template <int EPL, int INBF>
-__device__ __forceinline__ void stage_qk(const Args& a, uint64_t bh, int lane8, float* lds,
-                                         float (&kf)[EPL], float (&qf)[EPL]) {
-  constexpr int DK = EPL * 8;
+// A lane's k and q slices (EPL keys from k0).  REG: held in registers, for
+// lanes that compute several rows; otherwise read from the LDS copy where
+// they are used, which keeps 2*EPL registers free.
+template <int EPL, bool REG>
+struct KQ {
+  float kr[REG ? EPL : 1], qr[REG ? EPL : 1];
+  const float* kl;
+  const float* ql;
+  __device__ __forceinline__ float k(int i) const {
+    if constexpr (REG) return kr[i];
+    else return kl[i];
+  }
+  __device__ __forceinline__ float q(int i) const {
+    if constexpr (REG) return qr[i];
+    else return ql[i];
+  }
+};
+
+// Stage the head's k and q into LDS as fp32 (one conversion per value per
+// workgroup instead of one per value and row-lane), then point the lane at
+// its EPL-wide slices or load them.  Contains a workgroup barrier.
+template <int EPL, int LPR, int INBF, bool REG>
+__device__ __forceinline__ void stage_qk(const Args& a, uint64_t bh, int lane8, float* lds, KQ<EPL, REG>& kq) {
+  constexpr int DK = EPL * LPR;
   for (int t = threadIdx.x; t < 2 * DK; t += blockDim.x) {
     const void* src = t < DK ? a.k : a.q;
     const uint64_t idx = bh * DK + (uint64_t)(t < DK ? t : t - DK);
@@ -112,12 +131,16 @@ __device__ __forceinline__ void stage_qk(const Args& a, uint64_t bh, int lane8, 
   }
   __syncthreads();
   const int k0 = lane8 * EPL;
+  kq.kl = lds + k0;
+  kq.ql = lds + DK + k0;
+  if constexpr (REG) {
 #pragma unroll
-  for (int i = 0; i < EPL; i += 4) {
-    const float4 kv = *reinterpret_cast<const float4*>(lds + k0 + i);
-    const float4 qv = *reinterpret_cast<const float4*>(lds + DK + k0 + i);
-    kf[i] = kv.x; kf[i + 1] = kv.y; kf[i + 2] = kv.z; kf[i + 3] = kv.w;
-    qf[i] = qv.x; qf[i + 1] = qv.y; qf[i + 2] = qv.z; qf[i + 3] = qv.w;
+    for (int i = 0; i < EPL; i += 4) {
+      const float4 kv = *reinterpret_cast<const float4*>(lds + k0 + i);
+      const float4 qv = *reinterpret_cast<const float4*>(lds + DK + k0 + i);
+      kq.kr[i] = kv.x; kq.kr[i + 1] = kv.y; kq.kr[i + 2] = kv.z; kq.kr[i + 3] = kv.w;
+      kq.qr[i] = qv.x; kq.qr[i + 1] = qv.y; kq.qr[i + 2] = qv.z; kq.qr[i + 3] = qv.w;
+    }
   }
 }
 
@@ -140,10 +163,10 @@ __device__ __forceinline__ void store_row_values(const Args& a, uint64_t bh, int
   }
 }
 
-template <int QB, int RND, int DELTA, int EPL, int RPL, int BDR, int DKEY, int INBF>
+template <int QB, int RND, int DELTA, int EPL, int LPR, int RPL, int BDR, int DKEY, int INBF>
 __device__ __forceinline__ void dense_quant_rows(const Args& a, uint8_t* blk, uint64_t bh, int v0, int ng,
                                                  int lane8, float* lds) {
-  constexpr int DK = EPL * 8;
+  constexpr int DK = EPL * LPR;
   constexpr int RB = DK * QB / 8;           // code bytes per row
   constexpr int NW = EPL * QB / 32;         // code words per lane and row
   constexpr int SRB = sr_bits_of<RND>();
@@ -172,8 +195,8 @@ __device__ __forceinline__ void dense_quant_rows(const Args& a, uint8_t* blk, ui
   if constexpr (DKEY) load_f32<EPL>(a.decay + (uint64_t)bh * DK + k0, df);
   else dh = a.decay[bh];
   const float beta = a.beta ? a.beta[bh] : 1.0f;
-  float kf[EPL], qf[EPL];
-  stage_qk<EPL, INBF>(a, bh, lane8, lds, kf, qf);
+  KQ<EPL, (LPR == 8)> kq;
+  stage_qk<EPL, LPR, INBF>(a, bh, lane8, lds, kq);
   float o_row[RPL], s_row[RPL];
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
@@ -191,9 +214,9 @@ __device__ __forceinline__ void dense_quant_rows(const Args& a, uint8_t* blk, ui
         float c;
         if constexpr (QB == 8) c = (float)(int32_t)(int8_t)(w[r][i >> 2] >> (8 * (i & 3)));
         else c = (float)((int32_t)(w[r][i >> 3] << (28 - 4 * (i & 7))) >> 28);
-        wk = fmaf(c, kf[i], wk);
+        wk = fmaf(c, kq.k(i), wk);
       }
-      wk = sum8(wk);
+      wk = red_sum<LPR>(wk);
       u = beta * (vin[r] - dh * (s_old[r] * wk));
     } else {
       u = beta * vin[r];
@@ -206,13 +229,13 @@ __device__ __forceinline__ void dense_quant_rows(const Args& a, uint8_t* blk, ui
       float c;
       if constexpr (QB == 8) c = (float)(int32_t)(int8_t)(w[r][i >> 2] >> (8 * (i & 3)));
       else c = (float)((int32_t)(w[r][i >> 3] << (28 - 4 * (i & 7))) >> 28);
-      sp[i] = fmaf(u, kf[i], (DKEY ? df[i] * s_old[r] : ds) * c);
-      o = fmaf(sp[i], qf[i], o);
+      sp[i] = fmaf(u, kq.k(i), (DKEY ? df[i] * s_old[r] : ds) * c);
+      o = fmaf(sp[i], kq.q(i), o);
     }
 #pragma unroll
     for (int i = 0; i < EPL; i += 2) mx = fmaxf(fmaxf(mx, fabsf(sp[i])), fabsf(sp[i + 1]));
-    o = sum8(o);
-    const float m = absmax8(mx);
+    o = red_sum<LPR>(o);
+    const float m = red_absmax<LPR>(mx);
     o_row[r] = o;
     float scale, inv, invb;
     row_scale_fast<QB, SRB>(m, scale, inv, invb);
@@ -294,10 +317,10 @@ __device__ __forceinline__ void dense_quant_rows(const Args& a, uint8_t* blk, ui
 }
 
 // Protected (16-bit) heads of a head map.
-template <int DELTA, int EPL, int RPL, int DKEY, int INBF>
+template <int DELTA, int EPL, int LPR, int RPL, int DKEY, int INBF>
 __device__ __forceinline__ void dense_prot_rows(const Args& a, uint8_t* blk, uint64_t bh, int v0, int ng,
                                                 int lane8, float* lds) {
-  constexpr int DK = EPL * 8;
+  constexpr int DK = EPL * LPR;
   const int k0 = lane8 * EPL;
   uint32_t hw[RPL][EPL / 2];
 #pragma unroll
@@ -320,16 +343,17 @@ __device__ __forceinline__ void dense_prot_rows(const Args& a, uint8_t* blk, uin
   if constexpr (DKEY) load_f32<EPL>(a.decay + (uint64_t)bh * DK + k0, df);
   else dh = a.decay[bh];
   const float beta = a.beta ? a.beta[bh] : 1.0f;
-  float kf[EPL], qf[EPL];
-  stage_qk<EPL, INBF>(a, bh, lane8, lds, kf, qf);
-  const bool is_bf16 = a.hp_dtype == 1;
+  KQ<EPL, (LPR == 8)> kq;
+  stage_qk<EPL, LPR, INBF>(a, bh, lane8, lds, kq);
   float o_row[RPL];
+  // one body per 16-bit format (a uniform branch around the rows)
+  auto rows = [&](auto fmt) {
+    constexpr bool is_bf16 = decltype(fmt)::value;
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
     const int v = v0 + r;
     o_row[r] = 0.0f;
     if (v >= a.dv) continue;
-    const uint64_t row = bh * (uint64_t)a.dv + (uint64_t)v;
     float u;
     if constexpr (DELTA) {
       float wk = 0.0f;
@@ -337,9 +361,9 @@ __device__ __forceinline__ void dense_prot_rows(const Args& a, uint8_t* blk, uin
       for (int i = 0; i < EPL; ++i) {
         const uint32_t bits = (hw[r][i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
         const float sh = is_bf16 ? bf16_bits_to_f32(bits) : f16_bits_to_f32(bits);
-        wk = fmaf(sh, kf[i], wk);
+        wk = fmaf(sh, kq.k(i), wk);
       }
-      wk = sum8(wk);
+      wk = red_sum<LPR>(wk);
       u = beta * (vin[r] - dh * wk);
     } else {
       u = beta * vin[r];
@@ -350,40 +374,46 @@ __device__ __forceinline__ void dense_prot_rows(const Args& a, uint8_t* blk, uin
     for (int i = 0; i < EPL; ++i) {
       const uint32_t bits = (hw[r][i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
       const float sh = is_bf16 ? bf16_bits_to_f32(bits) : f16_bits_to_f32(bits);
-      sp[i] = fmaf(u, kf[i], (DKEY ? df[i] : dh) * sh);
-      o = fmaf(sp[i], qf[i], o);
+      sp[i] = fmaf(u, kq.k(i), (DKEY ? df[i] : dh) * sh);
+      o = fmaf(sp[i], kq.q(i), o);
     }
-    o_row[r] = sum8(o);
+    o_row[r] = red_sum<LPR>(o);
     uint32_t ow[EPL / 2];
 #pragma unroll
     for (int i = 0; i < EPL / 2; ++i)
       ow[i] = is_bf16 ? pack_bf16x2(sp[2 * i], sp[2 * i + 1])
-                      : (f32_to_f16_bits(sp[2 * i]) | (f32_to_f16_bits(sp[2 * i + 1]) << 16));
+                      : pack_f16x2(sp[2 * i], sp[2 * i + 1]);
     store_bytes<EPL * 2, true>(blk + ((uint64_t)v * DK + (uint64_t)k0) * 2u, ow);
   }
+  };
+  if (a.hp_dtype == 1) rows(std::true_type{});
+  else rows(std::false_type{});
   store_row_values<RPL>(a, bh, v0, lane8, o_row, nullptr);
 }
 
 // Register budget (minimum waves per SIMD the body is compiled for), chosen
-// per shape as the highest occupancy at which it needs no spills: dk 128
-// takes 7 waves with one row per lane (72 VGPRs) and 5 with two, fewer with
-// BDR, per-key decay, fp32 inputs or the delta rule; dk 64 fits 8; dk 256 is
-// left to the compiler.
-template <int EPL, int RPL, int BDR, int DKEY, int INBF, int DELTA>
+// per shape as the highest occupancy at which it needs no spills: with 8
+// lanes per row, dk 128 takes 7 waves with one row per lane (72 VGPRs) and 6
+// with two (80 VGPRs); with 4 lanes per row (32 keys per lane) 4 waves;
+// fewer with BDR, per-key decay, fp32 inputs or the delta rule; dk 64 fits
+// 8; dk 256 is left to the compiler.
+template <int EPL, int LPR, int RPL, int BDR, int DKEY, int INBF, int DELTA>
 constexpr int dense_min_waves() {
-  return EPL >= 32 ? 1
-                   : (EPL <= 8 ? (BDR ? 6 : 8)
-                               : (RPL == 1 ? 7 : 6) - (BDR ? 2 : 0) - (DKEY ? 1 : 0) - (INBF ? 0 : 1) -
-                                     (DELTA ? 1 : 0));
+  const int less = (BDR ? 2 : 0) + (DKEY ? 1 : 0) + (INBF ? 0 : 1) + (DELTA ? 1 : 0);
+  const int w = LPR == 4 ? 4 - less
+              : EPL >= 32 ? 1
+              : EPL <= 8 ? (BDR ? 6 : 8)
+              : (RPL == 1 ? 7 : 6) - less;
+  return w < 1 ? 1 : w;
 }
 
-template <int QB, int RND, int DELTA, int EPL, int RPL, int BDR, int DKEY, int INBF>
+template <int QB, int RND, int DELTA, int EPL, int LPR, int RPL, int BDR, int DKEY, int INBF>
 __global__ __launch_bounds__(256)
-__attribute__((amdgpu_waves_per_eu(dense_min_waves<EPL, RPL, BDR, DKEY, INBF, DELTA>(), 8)))
+__attribute__((amdgpu_waves_per_eu(dense_min_waves<EPL, LPR, RPL, BDR, DKEY, INBF, DELTA>(), 8)))
 void k_step_dense(const Args a) {
-  const int lane8 = threadIdx.x & 7;
-  const int g = threadIdx.x >> 3;
-  const int ng = blockDim.x >> 3;
+  const int lane8 = threadIdx.x & (LPR - 1);   // lane within the row group
+  const int g = threadIdx.x / LPR;
+  const int ng = blockDim.x / LPR;
   // Workgroups are dealt to the XCDs round-robin, so with the plain order an
   // XCD would only ever see the heads h = x (mod 8): under a head map some
   // XCDs would hold only quantized heads (VALU-heavy) and others most of the
@@ -397,7 +427,7 @@ void k_step_dense(const Args a) {
   const uint32_t h = r / (uint32_t)a.row_chunks;
   const uint32_t bh = b * (uint32_t)a.H + h;
   const int v0 = ((int)chunk * ng + g) * RPL;   // groups past dv stay for the barrier
-  __shared__ __align__(16) float lds[2 * EPL * 8];
+  __shared__ __align__(16) float lds[2 * EPL * LPR];
   // head storage from the protected-head mask: no table lookup stands
   // between the launch and the state loads
   const uint64_t below = (h >= 64u) ? 0ull : (a.prot_mask & ((1ull << h) - 1ull));
@@ -405,10 +435,10 @@ void k_step_dense(const Args a) {
   const bool prot = (h < 64u) && ((a.prot_mask >> h) & 1ull);
   if (!prot) {
     uint8_t* blk = a.codes + (uint64_t)b * a.code_bstride + (uint64_t)(h - np) * a.code_hblk;
-    dense_quant_rows<QB, RND, DELTA, EPL, RPL, BDR, DKEY, INBF>(a, blk, bh, v0, ng, lane8, lds);
+    dense_quant_rows<QB, RND, DELTA, EPL, LPR, RPL, BDR, DKEY, INBF>(a, blk, bh, v0, ng, lane8, lds);
   } else {
     uint8_t* blk = a.hp + (uint64_t)b * a.hp_bstride + (uint64_t)np * a.hp_hblk;
-    dense_prot_rows<DELTA, EPL, RPL, DKEY, INBF>(a, blk, bh, v0, ng, lane8, lds);
+    dense_prot_rows<DELTA, EPL, LPR, RPL, DKEY, INBF>(a, blk, bh, v0, ng, lane8, lds);
   }
 }
 
