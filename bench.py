@@ -59,9 +59,9 @@ def algorithmic_bytes(w, m) -> dict:
     nhp = prot.sum(1)
     nq = dk - nhp
     hpb = 4 if w.hp_dtype == "fp32" else 2
-    codes = B * int(sum(dv * ((int(n) * w.qbits + 7) // 8) for n in nq))
+    codes = B * int(sum(dv * (((int(n) * w.qbits + 7) // 8 + 3) // 4 * 4) for n in nq))   # rows padded to 4 B
     scales = B * int(sum(dv * 4 for n in nq if n > 0))
-    hp = B * int(sum(dv * int(n) * hpb for n in nhp))
+    hp = B * int(sum(dv * ((int(n) * hpb + 3) // 4 * 4) for n in nhp))
     state_rw = 2 * (codes + scales + hp)
     if w.lrb_rank:
         r = w.lrb_rank

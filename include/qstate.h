@@ -37,15 +37,17 @@
  *   it (map_mode HEAD: the whole head; KEY: that channel of that head).
  *   nq(h) = quantized channels of head h, nhp(h) = dk - nq(h).
  *   codes: per (b,h) a block of dv rows; a row holds the codes of the
- *     quantized channels in ascending k, ceil(nq*qbits/8) bytes
- *     (qbits 8: int8; qbits 4: two's-complement nibbles, even slot in the
- *     low nibble); the block is padded to a multiple of 16 bytes; blocks
- *     follow head order within a batch element, then batch order.
+ *     quantized channels in ascending k (slot j = the j-th quantized
+ *     channel), ceil(nq*qbits/8) bytes padded to a multiple of 4 (qbits 8:
+ *     int8; qbits 4: two's-complement nibbles, even slot in the low nibble);
+ *     the block is padded to a multiple of 16 bytes; blocks follow head order
+ *     within a batch element, then batch order.  Padding bytes stay zero.
  *   scales: fp32 [B][H][dv], one per row (value-axis grouping [LoReS]):
  *     scale = max_k |S_pre[v][k]| / Q over quantized k, Q = 127 (int8) or
  *     7 (int4); a row with max 0 has scale 0 and codes 0.
  *   hp: per (b,h) a block of dv rows of nhp(h) protected values in
- *     ascending k (bf16, fp16 or fp32 per hp_dtype), padded to 16 bytes.
+ *     ascending k (bf16, fp16 or fp32 per hp_dtype), each row padded to a
+ *     multiple of 4 bytes, the block to 16 bytes.
  *   lrb_W fp32 [B][H][dv][r], lrb_U fp32 [B][H][dk][r], lrb_n int32 [B][H]
  *     (LRB only): effective state = dequantized state + W U^T using the
  *     first lrb_n columns.
@@ -58,7 +60,8 @@
  *   nearest: ties to even.  stochastic (fixed point, b = sr_bits):
  *   X = floor(x * 2^b + 1/2), code = floor((X + u) / 2^b), with u the
  *   element's b-bit Philox integer, key = seed, counter = (g as 64 bits,
- *   step as 64 bits); e = ((b*H+h)*dv+v)*dk+k is the logical element index;
+ *   step as 64 bits); e = ((b*H+h)*dv+v)*dk+j, j the element's slot in its
+ *   stored code row (j = k when the whole head is quantized);
  *   16 bits: g = e>>3, half (e&1) of word (e>>1)&3 (low half for even e);
  *   8 bits: g = e>>4, byte e&3 of word (e>>2)&3.  E[code] = X / 2^b
  *   (X uses invb = inv * 2^b).

@@ -47,7 +47,7 @@ void orc_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t ou
   out[0] = x0; out[1] = x1; out[2] = x2; out[3] = x3;
 }
 
-/* Random integer for logical element e at decode step `step`.
+/* Random integer for element index e at decode step `step`.
  * Key = seed; counter = (element group as 64 bits, step as 64 bits).
  * 16-bit mode: 8 elements per Philox block, element e takes the low half of
  * word (e>>1)&3 when e is even, the high half when odd.
@@ -178,6 +178,17 @@ static int is_quantized(const orc_cfg* c, int h, int k) {
 static int hp_bytes(const orc_cfg* c) { return c->hp_dtype == 0 ? 4 : 2; }
 
 static uint64_t round16(uint64_t x) { return (x + 15u) & ~(uint64_t)15u; }
+static uint64_t round4(uint64_t x) { return (x + 3u) & ~(uint64_t)3u; }
+
+/* Bytes of one stored row: the quantized channels' codes, and the protected
+ * channels' values, each padded to a multiple of 4 bytes (a fully quantized
+ * or fully protected row already is one). */
+static uint64_t code_row_bytes(const orc_cfg* c, int nq) {
+  return round4(((uint64_t)nq * (uint64_t)c->qbits + 7u) / 8u);
+}
+static uint64_t hp_row_bytes(const orc_cfg* c, int nhp) {
+  return round4((uint64_t)nhp * (uint64_t)hp_bytes(c));
+}
 
 static int check_cfg(const orc_cfg* c) {
   if (c->kind != 0 && c->kind != 1) return -1;
@@ -207,9 +218,8 @@ int orc_layout(const orc_cfg* c, orc_sizes* s, uint64_t* code_off, uint64_t* hp_
     if (code_off) code_off[h] = coff;
     if (hp_off) hp_off[h] = hoff;
     if (nq_out) nq_out[h] = nq;
-    uint64_t row_bytes = ((uint64_t)nq * (uint64_t)c->qbits + 7u) / 8u;
-    coff += round16((uint64_t)c->dv * row_bytes);
-    hoff += round16((uint64_t)c->dv * (uint64_t)nhp * (uint64_t)hp_bytes(c));
+    coff += round16((uint64_t)c->dv * code_row_bytes(c, nq));
+    hoff += round16((uint64_t)c->dv * hp_row_bytes(c, nhp));
   }
   uint64_t BH = (uint64_t)c->B * (uint64_t)c->H;
   s->code_bstride = coff;
@@ -249,7 +259,8 @@ static void layout_free(layout_t* L) {
 typedef struct {
   uint8_t* code;
   uint8_t* hpb;
-  uint64_t row_bytes;
+  uint64_t row_bytes;      /* code row stride */
+  uint64_t hp_row_bytes;   /* protected row stride */
   int nq, nhp;
   int* slot;
 } head_addr;
@@ -260,7 +271,8 @@ static void head_address(const orc_cfg* c, const layout_t* L, const orc_state* s
   int h = (int)(bh % c->H);
   a->nq = L->nq[h];
   a->nhp = c->dk - a->nq;
-  a->row_bytes = ((uint64_t)a->nq * (uint64_t)c->qbits + 7u) / 8u;
+  a->row_bytes = code_row_bytes(c, a->nq);
+  a->hp_row_bytes = hp_row_bytes(c, a->nhp);
   a->code = st->codes ? st->codes + (uint64_t)b * L->s.code_bstride + L->code_off[h] : NULL;
   a->hpb = st->hp ? (uint8_t*)st->hp + (uint64_t)b * L->s.hp_bstride + L->hp_off[h] : NULL;
   int iq = 0, ih = 0;
@@ -289,25 +301,25 @@ static void put_code(const orc_cfg* c, const head_addr* a, int v, int slot, int3
 }
 
 static float get_hp(const orc_cfg* c, const head_addr* a, int v, int hslot) {
-  uint64_t idx = (uint64_t)v * (uint64_t)a->nhp + (uint64_t)hslot;
+  const uint8_t* row = a->hpb + (uint64_t)v * a->hp_row_bytes;
   if (c->hp_dtype == 0) {
     float f;
-    memcpy(&f, a->hpb + idx * 4u, 4);
+    memcpy(&f, row + (uint64_t)hslot * 4u, 4);
     return f;
   }
   uint16_t bits;
-  memcpy(&bits, a->hpb + idx * 2u, 2);
+  memcpy(&bits, row + (uint64_t)hslot * 2u, 2);
   return c->hp_dtype == 1 ? orc_from_bf16(bits) : orc_from_fp16(bits);
 }
 
 static void put_hp(const orc_cfg* c, const head_addr* a, int v, int hslot, float x) {
-  uint64_t idx = (uint64_t)v * (uint64_t)a->nhp + (uint64_t)hslot;
+  uint8_t* row = a->hpb + (uint64_t)v * a->hp_row_bytes;
   if (c->hp_dtype == 0) {
-    memcpy(a->hpb + idx * 4u, &x, 4);
+    memcpy(row + (uint64_t)hslot * 4u, &x, 4);
     return;
   }
   uint16_t bits = c->hp_dtype == 1 ? orc_to_bf16(x) : orc_to_fp16(x);
-  memcpy(a->hpb + idx * 2u, &bits, 2);
+  memcpy(row + (uint64_t)hslot * 2u, &bits, 2);
 }
 
 /* Dequantized value of element (v,k) of a head: scale times code for a
@@ -372,7 +384,9 @@ static float requantize_row(const orc_cfg* c, const head_addr* a, int64_t bh, in
     if (c->rounding == 0) {
       code = rintf(x);
     } else {
-      uint64_t e = ((uint64_t)bh * (uint64_t)c->dv + (uint64_t)v) * (uint64_t)dk + (uint64_t)k;
+      /* the element's index in the stored code rows: its slot, which is
+       * the key channel itself when the whole head is quantized */
+      uint64_t e = ((uint64_t)bh * (uint64_t)c->dv + (uint64_t)v) * (uint64_t)dk + (uint64_t)slot;
       code = orc_sr_round(sp[k] * invb, orc_random_bits(c, e, step), c->sr_bits);
     }
     if (c->bdr && old) {

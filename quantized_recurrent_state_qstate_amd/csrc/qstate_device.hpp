@@ -30,7 +30,7 @@ __device__ __forceinline__ void philox10(uint32_t (&x)[4], uint32_t k0, uint32_t
   }
 }
 
-// Random integers for EPL consecutive elements starting at logical index e0
+// Random integers for EPL consecutive elements starting at element index e0
 // (e0 a multiple of 8).  RND 1: 16 bits per element, block g = e>>3, low
 // half of word (e>>1)&3 for even e.  RND 2: 8 bits, block g = e>>4, byte
 // e&3 of word (e>>2)&3.  Counter = (g lo, g hi, step lo, step hi); element
@@ -67,6 +67,22 @@ __device__ __forceinline__ void rand_bits(uint64_t e0, uint32_t s0, uint32_t s1,
 #pragma unroll
       for (int j = 0; j < EPL; ++j) rb[j] = (((j < 4) ? w0 : w1) >> (8 * (j & 3))) & 0xFFu;
     }
+  }
+}
+
+// Random integer of one element e (same mapping as rand_bits), one Philox
+// block per call.
+template <int RND>
+__device__ __forceinline__ uint32_t rand_one(uint64_t e, uint32_t s0, uint32_t s1, uint32_t t0, uint32_t t1) {
+  if constexpr (RND == 1) {
+    uint32_t x[4] = {(uint32_t)(e >> 3), 0u, t0, t1};
+    philox10(x, s0, s1);
+    const uint32_t w = x[(e >> 1) & 3u];
+    return (e & 1u) ? (w >> 16) : (w & 0xFFFFu);
+  } else {
+    uint32_t x[4] = {(uint32_t)(e >> 4), 0u, t0, t1};
+    philox10(x, s0, s1);
+    return (x[(e >> 2) & 3u] >> (8u * (uint32_t)(e & 3u))) & 0xFFu;
   }
 }
 
@@ -130,6 +146,13 @@ __device__ __forceinline__ float red_absmax(float x) {
   if constexpr (L == 8) u = max(u, dppu<kDppHalfMirror>(u));
   return __uint_as_float(u);
 }
+
+// Stored row strides: the codes of nq quantized channels and the values of
+// nhp protected ones (hpb bytes each), each row padded to 4 bytes.
+__device__ __forceinline__ uint32_t code_row_bytes(int nq, int qbits) {
+  return (((uint32_t)(nq * qbits + 7) / 8u) + 3u) & ~3u;
+}
+__device__ __forceinline__ uint32_t hp_row_bytes(int nhp, int hpb) { return ((uint32_t)(nhp * hpb) + 3u) & ~3u; }
 
 // ---------------------------------------------------------------------------
 // Vector memory access of N bytes (N = 4, 8 or a multiple of 16; p aligned).

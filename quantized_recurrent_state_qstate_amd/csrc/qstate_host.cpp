@@ -40,6 +40,12 @@ constexpr int kMaxRank = 16;
 constexpr uint32_t kMaxLds = 64u * 1024u;
 
 uint64_t round16(uint64_t x) { return (x + 15u) & ~uint64_t(15); }
+uint64_t round4(uint64_t x) { return (x + 3u) & ~uint64_t(3); }
+
+// Stored row bytes: codes of the quantized channels, values of the protected
+// ones, each padded to a multiple of 4 bytes.
+uint64_t code_row(uint64_t nq, uint64_t qbits) { return round4((nq * qbits + 7u) / 8u); }
+uint64_t hp_row(uint64_t nhp, uint64_t hpb) { return round4(nhp * hpb); }
 
 struct Plan {
   std::vector<uint64_t> code_off, hp_off;
@@ -52,6 +58,7 @@ struct Plan {
   int row_chunks = 1;
   int dense_rpl = 1;
   int dense_lpr = 8;
+  int keymap_eh = 2;
   int dense_threads = 256;
   uint32_t lds = 0;
   uint64_t prot_mask = 0;       // dense family: protected heads
@@ -160,8 +167,8 @@ qs_status make_plan(const qstate_config* c, Plan* p) {
     any_mixed = any_mixed || p->head_type[h] == qs::kHeadMixed;
     p->code_off[h] = coff;
     p->hp_off[h] = hoff;
-    coff += round16((uint64_t)dv * (((uint64_t)iq * (uint64_t)c->qbits + 7u) / 8u));
-    hoff += round16((uint64_t)dv * (uint64_t)ip * hpb);
+    coff += round16((uint64_t)dv * code_row((uint64_t)iq, (uint64_t)c->qbits));
+    hoff += round16((uint64_t)dv * hp_row((uint64_t)ip, hpb));
   }
   p->code_bstride = coff;
   p->hp_bstride = hoff;
@@ -178,6 +185,16 @@ qs_status make_plan(const qstate_config* c, Plan* p) {
     p->family = qs::kFamLrb;
     const uint64_t floats = (uint64_t)dv * r + (uint64_t)dk * r + 4u * (uint64_t)dv + 3u * (uint64_t)dk + 36u;
     p->lds = (uint32_t)(floats * 4u + 2u * (uint64_t)dk);
+  } else if (c->map_mode == QS_MAP_KEY && c->hp_dtype != QS_FP32 && dk == 128) {
+    // key-channel maps with 16-bit protected values: rows in storage order,
+    // 16 code slots and keymap_eh protected slots per lane, 32 rows per
+    // workgroup
+    p->family = qs::kFamKeymap;
+    int maxhp = 0;
+    for (int h = 0; h < H; ++h) maxhp = std::max(maxhp, dk - p->nq[h]);
+    p->keymap_eh = 2;
+    while (p->keymap_eh * 8 < maxhp) p->keymap_eh *= 2;
+    p->row_chunks = (dv + 31) / 32;
   } else if (c->map_mode == QS_MAP_KEY ||
              (c->map_mode == QS_MAP_HEAD && (c->hp_dtype == QS_FP32 || H > 64))) {
     // key-channel maps, fp32 protected heads and head maps over more than 64
@@ -186,8 +203,8 @@ qs_status make_plan(const qstate_config* c, Plan* p) {
     p->family = qs::kFamMixed;
     uint64_t mx = 0;
     for (int h = 0; h < H; ++h) {
-      const uint64_t cb = round16((uint64_t)dv * (((uint64_t)p->nq[h] * (uint64_t)c->qbits + 7u) / 8u));
-      const uint64_t hb = round16((uint64_t)dv * (uint64_t)(dk - p->nq[h]) * hpb);
+      const uint64_t cb = round16((uint64_t)dv * code_row((uint64_t)p->nq[h], (uint64_t)c->qbits));
+      const uint64_t hb = round16((uint64_t)dv * hp_row((uint64_t)(dk - p->nq[h]), hpb));
       mx = std::max(mx, cb + hb);
     }
     p->lds = (uint32_t)std::min<uint64_t>(mx, 0xFFFFFFFFu);
@@ -196,12 +213,13 @@ qs_status make_plan(const qstate_config* c, Plan* p) {
     p->family = qs::kFamDense;
     for (int h = 0; h < H && h < 64; ++h)
       if (p->head_type[h] == qs::kHeadProt) p->prot_mask |= 1ull << h;
-    p->code_hblk = round16((uint64_t)dv * (((uint64_t)dk * (uint64_t)c->qbits + 7u) / 8u));
-    p->hp_hblk = round16((uint64_t)dv * (uint64_t)dk * hpb);
+    p->code_hblk = round16((uint64_t)dv * code_row((uint64_t)dk, (uint64_t)c->qbits));
+    p->hp_hblk = round16((uint64_t)dv * hp_row((uint64_t)dk, hpb));
   }
   if (p->lds > kMaxLds)
     return fail(QS_EUNSUPPORTED, "a head needs %u bytes of LDS staging (max %u)", p->lds, kMaxLds);
-  const uint64_t grid = BH * (p->family == qs::kFamDense ? (uint64_t)p->row_chunks : 1u);
+  const bool chunked = p->family == qs::kFamDense || p->family == qs::kFamKeymap;
+  const uint64_t grid = BH * (chunked ? (uint64_t)p->row_chunks : 1u);
   if (grid > 0x7FFFFFFFu) return fail(QS_EUNSUPPORTED, "B*H too large for one launch");
   // the kernels form Philox block counters in 32 bits: element indices
   // B*H*dv*dk must stay below 2^35
@@ -272,6 +290,7 @@ qs::Args base_args(const qstate_handle* h, const qstate_tensors* st) {
   a.row_chunks = h->plan.row_chunks;
   a.dense_rpl = h->plan.dense_rpl;
   a.dense_lpr = h->plan.dense_lpr;
+  a.keymap_eh = h->plan.keymap_eh;
   a.dense_threads = h->plan.dense_threads;
   a.prot_mask = h->plan.prot_mask;
   a.code_hblk = h->plan.code_hblk;

@@ -48,6 +48,7 @@ struct Args {
   int32_t dense_rpl;   // dense kernel: rows per lane (1, 2)
   int32_t dense_threads;  // dense kernel: threads per workgroup (dense_lpr per row group)
   int32_t dense_lpr;   // dense kernel: lanes per row (8, or 4 for dk 128)
+  int32_t keymap_eh;   // key-map kernel: protected slots per lane (2, 4, 8, 16)
   uint64_t prot_mask;  // dense kernel: bit h set = head h protected (H <= 64 with a head map)
   uint64_t code_hblk;  // dense kernel: bytes of one quantized head's code block
   uint64_t hp_hblk;    // dense kernel: bytes of one protected head's block
@@ -67,7 +68,7 @@ struct Args {
 };
 
 // Kernel families chosen at init.
-enum StepFamily : int { kFamDense = 0, kFamMixed = 1, kFamLrb = 2 };
+enum StepFamily : int { kFamDense = 0, kFamMixed = 1, kFamLrb = 2, kFamKeymap = 3 };
 
 // Launchers (qstate_misc.hip; launch_step_qr<QB, RND> in qstate_step_q*_*.hip).  Return hipSuccess or the
 // launch error.  `rnd`: 0 nearest, 1 stochastic 16-bit, 2 stochastic 8-bit.

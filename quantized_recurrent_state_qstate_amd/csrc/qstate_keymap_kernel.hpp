@@ -1,0 +1,247 @@
+// Step kernel for key-channel precision maps with 16-bit protected storage
+// (decay-based mixed precision per channel, abstract of "Quantizing
+// Recurrent Language Models Is Easier Than You Think").
+//
+// A row of a mixed head is stored as two packed rows: the codes of its nq
+// quantized channels in ascending key order (slot j = the j-th quantized
+// channel) and the 16-bit values of its nhp protected channels, each row
+// padded to 4 bytes.  The kernel works in that storage order instead of key
+// order: 8 lanes own a row, lane l holding code slots [l*EPL, l*EPL+EPL) and
+// protected slots [l*EH, l*EH+EH), so every lane reads and writes
+// consecutive dwords of both rows and runs the dense kernel's arithmetic on
+// them.  The per-key inputs (k, q, and the decay when it is per key) are
+// permuted into slot order once per workgroup in LDS; every sum of the step
+// (delta term, readout) and the row maximum are order-free, and an element's
+// Philox counter is its slot index, so nothing needs key order.
+#pragma once
+#include "qstate_step_kernels.hpp"
+
+namespace qs {
+
+namespace {
+
+// Up to N valid bytes (a multiple of 4) of a lane's slice at p: whole dwords,
+// never past the valid end; the rest of w is zero.
+template <int NW>
+__device__ __forceinline__ void load_dwords(const uint8_t* p, uint32_t nbytes, uint32_t (&w)[NW]) {
+  const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+#pragma unroll
+  for (int i = 0; i < NW; ++i) w[i] = (4u * (uint32_t)i < nbytes) ? ld_nt(q + i) : 0u;
+}
+template <int NW>
+__device__ __forceinline__ void store_dwords(uint8_t* p, uint32_t nbytes, const uint32_t (&w)[NW]) {
+  uint32_t* q = reinterpret_cast<uint32_t*>(p);
+#pragma unroll
+  for (int i = 0; i < NW; ++i)
+    if (4u * (uint32_t)i < nbytes) st_nt(q + i, w[i]);
+}
+
+}  // namespace
+
+// EPL code slots and EH protected slots per lane, one row per lane group.
+template <int QB, int RND, int DELTA, int EPL, int EH, int BDR, int DKEY>
+__global__ __launch_bounds__(256) void k_step_keymap(const Args a) {
+  constexpr int DK = EPL * 8;
+  constexpr int SRB = sr_bits_of<RND>();
+  constexpr int CW = EPL * QB / 32;        // code words per lane and row
+  constexpr int HW = EH / 2;               // 16-bit value words per lane and row
+  static_assert(EH % 2 == 0, "protected slots come in dword pairs");
+  const int lane = threadIdx.x & 7;
+  const int g = threadIdx.x >> 3;          // row group: one row of 32 per workgroup
+
+  // work item (b, h, chunk of 32 rows), head order rotated by b across XCDs
+  const uint32_t per_b = (uint32_t)a.H * (uint32_t)a.row_chunks;
+  const uint32_t b = blockIdx.x / per_b;
+  uint32_t r = blockIdx.x - b * per_b + b % per_b;
+  r = r >= per_b ? r - per_b : r;
+  const uint32_t chunk = r % (uint32_t)a.row_chunks;
+  const uint32_t h = r / (uint32_t)a.row_chunks;
+  const uint64_t bh = (uint64_t)b * (uint64_t)a.H + h;
+  const int v = (int)chunk * 32 + g;
+
+  const int nq = a.t.nq[h];
+  const int nhp = DK - nq;
+  const uint32_t rq = code_row_bytes(nq, QB);
+  const uint32_t rh = hp_row_bytes(nhp, 2);
+  const uint8_t* cblk = a.codes + (uint64_t)b * a.code_bstride + a.t.code_off[h];
+  const uint8_t* hblk = a.hp + (uint64_t)b * a.hp_bstride + a.t.hp_off[h];
+
+  // this lane's byte ranges in the two rows, and how many of them exist
+  constexpr uint32_t CB = EPL * QB / 8, HB = EH * 2;
+  const uint32_t coff = (uint32_t)lane * CB, hoff = (uint32_t)lane * HB;
+  const uint32_t cvalid = rq > coff ? (rq - coff < CB ? rq - coff : CB) : 0u;
+  const uint32_t hvalid = rh > hoff ? (rh - hoff < HB ? rh - hoff : HB) : 0u;
+
+  // state loads first
+  const bool row_ok = v < a.dv;
+  const int vr = row_ok ? v : 0;
+  uint32_t cw[CW], hw[HW > 0 ? HW : 1];
+  load_dwords<CW>(cblk + (uint64_t)vr * rq + coff, row_ok ? cvalid : 0u, cw);
+  load_dwords<HW>(hblk + (uint64_t)vr * rh + hoff, row_ok ? hvalid : 0u, hw);
+  const uint64_t row = bh * (uint64_t)a.dv + (uint64_t)vr;
+  const float s_old = ld_nt(a.scales + row);
+  const float vin = a.in_bf16 ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(a.v)[row])
+                              : reinterpret_cast<const float*>(a.v)[row];
+  const float dh = DKEY ? 1.0f : a.decay[bh];
+  const float beta = a.beta ? a.beta[bh] : 1.0f;
+
+  // k, q (and per-key decay) permuted into slot order: code slots in
+  // lc[0..DK), protected slots in lh[0..DK); slots past nq (nhp) hold 0
+  __shared__ __align__(16) float lc[3][DK];
+  __shared__ __align__(16) float lh[3][DK];
+  for (int t = threadIdx.x; t < DK; t += blockDim.x) {
+    const uint16_t sl = a.t.slots[(uint64_t)h * DK + t];
+    const uint64_t idx = bh * DK + (uint64_t)t;
+    const float kv = a.in_bf16 ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(a.k)[idx])
+                               : reinterpret_cast<const float*>(a.k)[idx];
+    const float qv = a.in_bf16 ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(a.q)[idx])
+                               : reinterpret_cast<const float*>(a.q)[idx];
+    const float dd = DKEY ? a.decay[idx] : 0.0f;
+    float(*dst)[DK] = (sl & kSlotProt) ? lh : lc;
+    const int s = sl & 0x7FFF;
+    dst[0][s] = kv;
+    dst[1][s] = qv;
+    if constexpr (DKEY) dst[2][s] = dd;
+    if (t >= nq) {
+      lc[0][t] = 0.0f;
+      lc[1][t] = 0.0f;
+      if constexpr (DKEY) lc[2][t] = 0.0f;
+    }
+    if (t >= nhp) {
+      lh[0][t] = 0.0f;
+      lh[1][t] = 0.0f;
+      if constexpr (DKEY) lh[2][t] = 0.0f;
+    }
+  }
+  __syncthreads();
+  if (!row_ok) return;   // after the barrier: whole row groups only
+
+  const float* kc = lc[0] + lane * EPL;
+  const float* qc = lc[1] + lane * EPL;
+  const float* dc = lc[2] + lane * EPL;
+  const float* kh = lh[0] + lane * EH;
+  const float* qh = lh[1] + lane * EH;
+  const float* dhk = lh[2] + lane * EH;
+  const bool is_bf16 = a.hp_dtype == 1;
+
+  // old values: codes (0 past nq: padding and unloaded dwords are zero)
+  auto code_at = [&](int i) -> float {
+    if constexpr (QB == 8) return (float)(int32_t)(int8_t)(cw[i >> 2] >> (8 * (i & 3)));
+    else return (float)((int32_t)(cw[i >> 3] << (28 - 4 * (i & 7))) >> 28);
+  };
+  auto hp_at = [&](int i) -> float {
+    const uint32_t bits = (hw[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+    return is_bf16 ? bf16_bits_to_f32(bits) : f16_bits_to_f32(bits);
+  };
+
+  float u;
+  if constexpr (DELTA) {
+    float wc = 0.0f, wh = 0.0f;   // S_hat k = s * sum code k + sum value k
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) wc = fmaf(code_at(i), kc[i], wc);
+#pragma unroll
+    for (int i = 0; i < EH; ++i) wh = fmaf(hp_at(i), kh[i], wh);
+    const float wk = red_sum<8>(fmaf(s_old, wc, wh));
+    u = beta * (vin - dh * wk);
+  } else {
+    u = beta * vin;
+  }
+
+  // protected slots: update, readout share, 16-bit store
+  float o = 0.0f;
+  {
+    float sp[EH];
+#pragma unroll
+    for (int i = 0; i < EH; ++i) {
+      sp[i] = fmaf(u, kh[i], (DKEY ? dhk[i] : dh) * hp_at(i));
+      o = fmaf(sp[i], qh[i], o);
+    }
+    uint32_t ow[HW > 0 ? HW : 1];
+#pragma unroll
+    for (int i = 0; i < HW; ++i)
+      ow[i] = is_bf16 ? pack_bf16x2(sp[2 * i], sp[2 * i + 1]) : pack_f16x2(sp[2 * i], sp[2 * i + 1]);
+    store_dwords<HW>(const_cast<uint8_t*>(hblk) + (uint64_t)v * rh + hoff, hvalid, ow);
+  }
+
+  // quantized slots: update, readout, row maximum, requantize
+  const float ds = dh * s_old;
+  float sp[EPL];
+  float mx = 0.0f;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    sp[i] = fmaf(u, kc[i], (DKEY ? dc[i] * s_old : ds) * code_at(i));
+    o = fmaf(sp[i], qc[i], o);
+  }
+#pragma unroll
+  for (int i = 0; i < EPL; i += 2) mx = fmaxf(fmaxf(mx, fabsf(sp[i])), fabsf(sp[i + 1]));
+  o = red_sum<8>(o);
+  const float m = red_absmax<8>(mx);
+  float scale, inv, invb;
+  row_scale_fast<QB, SRB>(m, scale, inv, invb);
+
+  uint32_t out[CW];
+  const uint64_t e0 = row * DK + (uint64_t)lane * EPL;   // slot-indexed element of the first slot
+  if constexpr (QB == 8 && !BDR) {
+    constexpr int BYTE = SRB / 8;
+    constexpr int PER = (RND == 1) ? 8 : 16;
+    constexpr int NB = (RND == 0) ? 1 : (EPL + PER - 1) / PER;
+#pragma unroll
+    for (int gblk = 0; gblk < NB; ++gblk) {
+      uint32_t x[4] = {0u, 0u, 0u, 0u};
+      uint32_t sel = 0u;
+      if constexpr (RND != 0) {
+        const uint64_t ew = e0 + (uint64_t)(gblk * PER);
+        x[0] = (RND == 1) ? (uint32_t)(ew >> 3) : (uint32_t)(ew >> 4);
+        x[1] = 0u;
+        x[2] = a.step_lo;
+        x[3] = a.step_hi;
+        philox10(x, a.seed_lo, a.seed_hi);
+        if constexpr (RND == 2 && EPL < 16) sel = (uint32_t)((ew >> 3) & 1u);
+      }
+      constexpr int CNT = (RND == 0) ? EPL : ((PER < EPL) ? PER : EPL);
+      uint32_t y[CNT];
+#pragma unroll
+      for (int j = 0; j < CNT; ++j) {
+        const int i = gblk * PER + j;
+        if constexpr (RND == 0) {
+          y[j] = (uint32_t)(int32_t)rintf(sp[i] * inv);
+        } else {
+          uint32_t rbits;
+          if constexpr (RND == 1) rbits = (j & 1) ? (x[j >> 1] >> 16) : (x[j >> 1] & 0xFFFFu);
+          else {
+            const int jj = (EPL < 16) ? (j + 8 * (int)sel) : j;
+            const uint32_t word = (EPL < 16) ? (sel ? x[2 + (j >> 2)] : x[j >> 2]) : x[jj >> 2];
+            rbits = (word >> (8 * (jj & 3))) & 0xFFu;
+          }
+          y[j] = (uint32_t)(cvt_rpi(sp[i] * invb) + (int32_t)rbits);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < CNT / 4; ++j)
+        out[(gblk * PER) / 4 + j] = pack4<BYTE>(y[4 * j], y[4 * j + 1], y[4 * j + 2], y[4 * j + 3]);
+    }
+  } else {
+    uint32_t rb[EPL];
+    if constexpr (RND != 0) rand_bits<RND, EPL>(e0, a.seed_lo, a.seed_hi, a.step_lo, a.step_hi, rb);
+    int32_t code[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const float shi = BDR ? s_old * code_at(i) : 0.0f;
+      code[i] = round_elem<QB, RND, BDR>(sp[i], shi, inv, invb, (RND != 0) ? rb[i] : 0u, a.bdr_bound);
+    }
+#pragma unroll
+    for (int j = 0; j < CW; ++j) out[j] = 0u;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      if constexpr (QB == 8) out[i >> 2] |= ((uint32_t)code[i] & 0xFFu) << (8 * (i & 3));
+      else out[i >> 3] |= ((uint32_t)code[i] & 0xFu) << (4 * (i & 7));
+    }
+  }
+  store_dwords<CW>(const_cast<uint8_t*>(cblk) + (uint64_t)v * rq + coff, cvalid, out);
+  if (lane == 0) {
+    st_nt(a.out + row, o);
+    st_nt(a.scales + row, scale);
+  }
+}
+
+}  // namespace qs

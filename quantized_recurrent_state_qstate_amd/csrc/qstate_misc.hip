@@ -31,11 +31,11 @@ __global__ __launch_bounds__(256) void k_quantize(const Args a) {
   const int nq = a.t.nq[h];
   const int nhp = dk - nq;
   const int hpb = hp_elem_bytes(a.hp_dtype);
-  const uint32_t rq = (uint32_t)(nq * a.qbits + 7) / 8u;
+  const uint32_t rq = code_row_bytes(nq, a.qbits);
   uint8_t* crow = const_cast<uint8_t*>(a.codes ? code_block_m(a, b, h) : nullptr);
   if (crow) crow += (uint64_t)v * rq;
   uint8_t* hrow = const_cast<uint8_t*>(a.hp ? hp_block_m(a, b, h) : nullptr);
-  if (hrow) hrow += (uint64_t)v * (uint64_t)nhp * (uint64_t)hpb;
+  if (hrow) hrow += (uint64_t)v * hp_row_bytes(nhp, hpb);
   const uint16_t* sl = a.t.slots + (uint64_t)h * dk;
   const float* srow = a.S + row * (uint64_t)dk;
   float m = 0.0f;
@@ -66,7 +66,7 @@ __global__ __launch_bounds__(256) void k_quantize(const Args a) {
     }
     uint32_t rbits = 0;
     if (a.rounding) {
-      const uint64_t e = row * (uint64_t)dk + (uint64_t)k;
+      const uint64_t e = row * (uint64_t)dk + (uint64_t)s;   // slot-indexed element
       const uint64_t g = (a.sr_bits == 16) ? (e >> 3) : (e >> 4);
       if (g != cached) {
         x[0] = (uint32_t)g;
@@ -112,9 +112,9 @@ __global__ __launch_bounds__(256) void k_dequantize(const Args a) {
   const int nq = a.t.nq[h];
   const int nhp = dk - nq;
   const int hpb = hp_elem_bytes(a.hp_dtype);
-  const uint32_t rq = (uint32_t)(nq * a.qbits + 7) / 8u;
+  const uint32_t rq = code_row_bytes(nq, a.qbits);
   const uint8_t* crow = a.codes ? code_block_m(a, b, h) + (uint64_t)v * rq : nullptr;
-  const uint8_t* hrow = a.hp ? hp_block_m(a, b, h) + (uint64_t)v * (uint64_t)nhp * (uint64_t)hpb : nullptr;
+  const uint8_t* hrow = a.hp ? hp_block_m(a, b, h) + (uint64_t)v * hp_row_bytes(nhp, hpb) : nullptr;
   const uint16_t* sl = a.t.slots + (uint64_t)h * dk;
   const float scale = a.scales ? a.scales[row] : 0.0f;
   const int r = a.lrb_rank;
@@ -195,7 +195,9 @@ hipError_t launch_dequantize(const Args& a, hipStream_t s) {
 
 const char* step_kernel_name(int family, int qbits, int rnd, int delta, int dk) {
   static thread_local char buf[96];
-  const char* fam = family == kFamDense ? "dense" : (family == kFamMixed ? "mixed" : "lrb");
+  const char* fam = family == kFamDense ? "dense"
+                    : family == kFamMixed ? "mixed"
+                    : family == kFamKeymap ? "keymap" : "lrb";
   const char* rn = rnd == 0 ? "rtn" : (rnd == 1 ? "sr16" : "sr8");
   snprintf(buf, sizeof(buf), "k_step_%s<int%d,%s,%s,dk%d>", fam, qbits, rn, delta ? "delta" : "additive", dk);
   return buf;

@@ -443,11 +443,13 @@ void k_step_dense(const Args a) {
 }
 
 // ---------------------------------------------------------------------------
-// Mixed step (precision map KEY): a row holds quantized and protected key
-// channels in two packed areas.  The head's code and protected blocks are
-// staged through LDS with 128-bit accesses; each lane gathers its logical
-// channels by slot, computes as the dense kernel, scatters back, and the
-// workgroup writes the blocks out.  One workgroup per head.
+// Mixed step, the general path for heads that mix quantized and protected
+// key channels (fp32 protected storage, dk other than 128, and head maps the
+// dense kernel does not take): a row holds the two kinds in two packed
+// areas.  The head's code and protected blocks are staged through LDS with
+// 128-bit accesses; each lane gathers its logical channels by slot, computes
+// as the dense kernel, scatters back, and the workgroup writes the blocks
+// out.  One workgroup per head.
 // ---------------------------------------------------------------------------
 template <int QB, int RND, int DELTA, int EPL>
 __global__ __launch_bounds__(256) void k_step_mixed(const Args a) {
@@ -462,9 +464,10 @@ __global__ __launch_bounds__(256) void k_step_mixed(const Args a) {
   const int nq = a.t.nq[h];
   const int nhp = DK - nq;
   const int hpb = hp_elem_bytes(a.hp_dtype);
-  const uint32_t rq = (uint32_t)(nq * QB + 7) / 8u;
+  const uint32_t rq = code_row_bytes(nq, QB);
+  const uint32_t rh = hp_row_bytes(nhp, hpb);
   const uint32_t code_bytes = ((uint32_t)a.dv * rq + 15u) & ~15u;
-  const uint32_t hp_bytes = ((uint32_t)a.dv * (uint32_t)nhp * (uint32_t)hpb + 15u) & ~15u;
+  const uint32_t hp_bytes = ((uint32_t)a.dv * rh + 15u) & ~15u;
   uint8_t* gcode = const_cast<uint8_t*>(code_block(a, b, h));
   uint8_t* ghp = const_cast<uint8_t*>(hp_block(a, b, h));
   uint8_t* lcode = lds;
@@ -491,7 +494,7 @@ __global__ __launch_bounds__(256) void k_step_mixed(const Args a) {
     const float s_old = ld_nt(a.scales + row);
     const float vin = load_in1(a.v, a.in_bf16, row);
     uint8_t* crow = lcode + (uint32_t)v * rq;
-    uint8_t* hrow = lhp + (uint32_t)v * (uint32_t)nhp * (uint32_t)hpb;
+    uint8_t* hrow = lhp + (uint32_t)v * rh;
     float sh[EPL], dec[EPL];   // dequantized value; decayed value (d s) c or d h
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
@@ -537,8 +540,21 @@ __global__ __launch_bounds__(256) void k_step_mixed(const Args a) {
     m = max8(m);
     float scale, inv, invb;
     row_scale<QB, sr_bits_of<RND>()>(m, scale, inv, invb);
+    // random bits by stored slot: rand_bits over the lane's keys when the
+    // whole head is quantized (slot = key), one Philox block per element
+    // otherwise
     uint32_t rb[EPL];
-    if constexpr (RND != 0) rand_bits<RND, EPL>(row * DK + (uint64_t)k0, a.seed_lo, a.seed_hi, a.step_lo, a.step_hi, rb);
+    if constexpr (RND != 0) {
+      if (nq == DK) {
+        rand_bits<RND, EPL>(row * DK + (uint64_t)k0, a.seed_lo, a.seed_hi, a.step_lo, a.step_hi, rb);
+      } else {
+#pragma unroll
+        for (int i = 0; i < EPL; ++i)
+          rb[i] = (sl[i] & kSlotProt) ? 0u
+                                      : rand_one<RND>(row * DK + (uint64_t)(sl[i] & 0x7FFFu), a.seed_lo, a.seed_hi,
+                                                      a.step_lo, a.step_hi);
+      }
+    }
     int32_t code[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {

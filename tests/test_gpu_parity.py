@@ -47,9 +47,9 @@ def _head_slices(ocfg):
     for bh in range(B * H):
         b, h = divmod(bh, H)
         nq = int(L["nq"][h])
-        cb = dv * ((nq * ocfg.qbits + 7) // 8)
+        cb = dv * (((nq * ocfg.qbits + 7) // 8 + 3) // 4 * 4)          # rows padded to 4 bytes
         c0 = b * L["code_bstride"] + int(L["code_off"][h])
-        hb = dv * (dk - nq)
+        hb = dv * (((dk - nq) * hp_item + 3) // 4 * 4) // hp_item
         h0 = (b * L["hp_bstride"] + int(L["hp_off"][h])) // hp_item
         out.append(dict(codes=slice(c0, c0 + cb), hp=slice(h0, h0 + hb), scales=slice(bh * dv, bh * dv + dv),
                         quant=nq > 0, W=slice(bh * dv * r, (bh + 1) * dv * r),
@@ -280,6 +280,17 @@ EDGE = {
     "sr_bdr_int8": dict(kind="additive", decay_mode="key", dk=128, dv=32, H=2, B=2, qbits=8, bdr=True),
     "lrb_headdecay_sr": dict(kind="additive", decay_mode="head", dk=64, dv=48, H=2, B=2, qbits=8,
                              lrb_rank=4, lrb_period=3),
+    # key maps in storage order: few, half and most channels protected
+    "keymap_fp16_delta_sparse": dict(kind="delta", decay_mode="head", dk=128, dv=128, H=2, B=2, qbits=8,
+                                     map_mode="key", hp_dtype="fp16", map_density=0.08),
+    "keymap_bf16_sr8_bdr_keydecay": dict(kind="additive", decay_mode="key", dk=128, dv=40, H=2, B=2, qbits=8,
+                                         sr_bits=8, bdr=True, map_mode="key", hp_dtype="bf16",
+                                         map_density=0.5),
+    "keymap_int4_rtn_bdr": dict(kind="additive", decay_mode="head", dk=128, dv=96, H=2, B=2, qbits=4,
+                                rounding="nearest", bdr=True, map_mode="key", hp_dtype="fp16",
+                                map_density=0.05),
+    "keymap_fp16_mostly_protected": dict(kind="additive", decay_mode="key", dk=128, dv=33, H=2, B=3, qbits=8,
+                                         map_mode="key", hp_dtype="fp16", map_density=0.9),
 }
 
 
@@ -303,12 +314,13 @@ def _edge_inputs(kw, t):
 @pytest.mark.parametrize("case", list(EDGE))
 def test_edge_cases(case):
     kw = dict(EDGE[case])
+    density = kw.pop("map_density", 0.2)
     r = np.random.default_rng(1)
     m = None
     if kw.get("map_mode") == "head":
         m = (np.arange(kw["H"]) % 2).astype(np.uint8)
     elif kw.get("map_mode") == "key":
-        m = (r.random((kw["H"], kw["dk"])) < 0.2).astype(np.uint8)
+        m = (r.random((kw["H"], kw["dk"])) < density).astype(np.uint8)
         m[0, :] = 0
         if kw["H"] > 2:
             m[2, :] = 1

@@ -50,13 +50,14 @@ def test_plan_random_key_maps(qbits, hp):
                                          map=m))
             blocks = np.diff(np.append(o["code_off"], o["code_bstride"])) + \
                 np.diff(np.append(o["hp_off"], o["hp_bstride"]))
+            staged = not (dk == 128 and hp != "fp32")   # other key maps stage a head through LDS
             try:
                 z = plan(StateConfig(B=3, H=H, dk=dk, dv=dv, qbits=qbits, hp_dtype=hp, map_mode="key", map=m))
             except _lib.QStateError as e:
-                # a head is staged whole through LDS: more than 64 KiB is unsupported
-                assert e.status == _lib.QS_EUNSUPPORTED and blocks.max() > 65536
+                # a head staged whole through LDS: more than 64 KiB is unsupported
+                assert e.status == _lib.QS_EUNSUPPORTED and staged and blocks.max() > 65536
                 continue
-            assert blocks.max() <= 65536
+            assert blocks.max() <= 65536 or not staged
             assert (z["codes"], z["scales"], z["hp"]) == (o["codes"], o["scales"], o["hp"])
 
 

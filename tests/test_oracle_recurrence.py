@@ -273,10 +273,16 @@ def test_layout_sizes_of_the_workloads():
     km = np.zeros((32, 128), np.uint8)
     km[:, :13] = 1
     z = sizes(B=1024, H=32, dk=128, dv=128, kind="delta", map_mode="key", map=km, hp_dtype="fp16")
-    assert (z["codes"], z["hp"]) == (1024 * 32 * 128 * 115, 1024 * 32 * 128 * 13 * 2)
-    # padding of a head block to 16 bytes: int4, 5 quantized channels -> 3 bytes per row
+    # rows padded to 4 bytes: 115 codes -> 116 bytes, 13 fp16 -> 28 bytes
+    assert (z["codes"], z["hp"]) == (1024 * 32 * 128 * 116, 1024 * 32 * 128 * 28)
+    # padding of rows to 4 bytes and head blocks to 16: int4, 5 quantized
+    # channels -> 3 bytes -> 4 per row; 3 bf16 -> 6 bytes -> 8 per row
     km = np.zeros((2, 8), np.uint8)
     km[0, :3] = 1
     z = sizes(B=1, H=2, dk=8, dv=3, qbits=4, map_mode="key", map=km, hp_dtype="bf16")
     assert z["code_off"].tolist() == [0, 16] and z["codes"] == 16 + 16
     assert z["hp_off"].tolist() == [0, 32] and z["hp"] == 32
+    km = np.zeros((1, 64), np.uint8)
+    km[0, :5] = 1                      # 59 int8 codes -> 60 bytes, 5 fp16 -> 12 bytes
+    z = sizes(B=2, H=1, dk=64, dv=5, map_mode="key", map=km, hp_dtype="fp16")
+    assert (z["code_bstride"], z["hp_bstride"]) == (304, 64)
