@@ -187,14 +187,18 @@ qs_status make_plan(const qstate_config* c, Plan* p) {
     p->lds = (uint32_t)(floats * 4u + 2u * (uint64_t)dk);
   } else if (c->map_mode == QS_MAP_KEY && c->hp_dtype != QS_FP32 && dk == 128) {
     // key-channel maps with 16-bit protected values: rows in storage order,
-    // 16 code slots and keymap_eh protected slots per lane, 32 rows per
-    // workgroup
+    // 8 lanes per row, each with 16 code slots and keymap_eh protected
+    // slots, 32 rows per workgroup (4 lanes per row measured slower)
     p->family = qs::kFamKeymap;
+    p->dense_lpr = 8;
+    p->dense_rpl = 1;
+    p->dense_threads = 256;
     int maxhp = 0;
     for (int h = 0; h < H; ++h) maxhp = std::max(maxhp, dk - p->nq[h]);
     p->keymap_eh = 2;
-    while (p->keymap_eh * 8 < maxhp) p->keymap_eh *= 2;
-    p->row_chunks = (dv + 31) / 32;
+    while (p->keymap_eh * p->dense_lpr < maxhp) p->keymap_eh *= 2;
+    const int rows = 256 / p->dense_lpr;
+    p->row_chunks = (dv + rows - 1) / rows;
   } else if (c->map_mode == QS_MAP_KEY ||
              (c->map_mode == QS_MAP_HEAD && (c->hp_dtype == QS_FP32 || H > 64))) {
     // key-channel maps, fp32 protected heads and head maps over more than 64

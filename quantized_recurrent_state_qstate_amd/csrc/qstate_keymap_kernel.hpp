@@ -6,7 +6,7 @@
 // quantized channels in ascending key order (slot j = the j-th quantized
 // channel) and the 16-bit values of its nhp protected channels, each row
 // padded to 4 bytes.  The kernel works in that storage order instead of key
-// order: 8 lanes own a row, lane l holding code slots [l*EPL, l*EPL+EPL) and
+// order: LPR lanes own a row, lane l holding code slots [l*EPL, l*EPL+EPL) and
 // protected slots [l*EH, l*EH+EH), so every lane reads and writes
 // consecutive dwords of both rows and runs the dense kernel's arithmetic on
 // them.  The per-key inputs (k, q, and the decay when it is per key) are
@@ -20,16 +20,44 @@ namespace qs {
 
 namespace {
 
-// Up to N valid bytes (a multiple of 4) of a lane's slice at p: whole dwords,
-// never past the valid end; the rest of w is zero.
+// 16 bytes at a dword-aligned address (global memory takes 128-bit accesses
+// at 4-byte alignment).
+typedef uint32_t u32x4a4_t __attribute__((ext_vector_type(4), aligned(4)));
+
+// Up to 4*NW valid bytes (nbytes, a multiple of 4) of a lane's slice at the
+// dword-aligned p: 128-bit accesses when the whole slice exists, else whole
+// dwords up to the valid end; the rest of w is zero.
 template <int NW>
 __device__ __forceinline__ void load_dwords(const uint8_t* p, uint32_t nbytes, uint32_t (&w)[NW]) {
+  if constexpr (NW % 4 == 0) {
+    if (nbytes == 4u * NW) {
+#pragma unroll
+      for (int i = 0; i < NW / 4; ++i) {
+        const u32x4a4_t t = ld_nt(reinterpret_cast<const u32x4a4_t*>(p) + i);
+        w[4 * i] = t.x;
+        w[4 * i + 1] = t.y;
+        w[4 * i + 2] = t.z;
+        w[4 * i + 3] = t.w;
+      }
+      return;
+    }
+  }
   const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
 #pragma unroll
   for (int i = 0; i < NW; ++i) w[i] = (4u * (uint32_t)i < nbytes) ? ld_nt(q + i) : 0u;
 }
 template <int NW>
 __device__ __forceinline__ void store_dwords(uint8_t* p, uint32_t nbytes, const uint32_t (&w)[NW]) {
+  if constexpr (NW % 4 == 0) {
+    if (nbytes == 4u * NW) {
+#pragma unroll
+      for (int i = 0; i < NW / 4; ++i) {
+        const u32x4a4_t t = {w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
+        st_nt(reinterpret_cast<u32x4a4_t*>(p) + i, t);
+      }
+      return;
+    }
+  }
   uint32_t* q = reinterpret_cast<uint32_t*>(p);
 #pragma unroll
   for (int i = 0; i < NW; ++i)
@@ -38,18 +66,20 @@ __device__ __forceinline__ void store_dwords(uint8_t* p, uint32_t nbytes, const 
 
 }  // namespace
 
-// EPL code slots and EH protected slots per lane, one row per lane group.
-template <int QB, int RND, int DELTA, int EPL, int EH, int BDR, int DKEY>
+// LPR lanes per row, EPL = dk/LPR code slots and EH protected slots per
+// lane, one row per lane group, 256/LPR rows per workgroup.
+template <int QB, int RND, int DELTA, int EPL, int LPR, int EH, int BDR, int DKEY>
 __global__ __launch_bounds__(256) void k_step_keymap(const Args a) {
-  constexpr int DK = EPL * 8;
+  constexpr int DK = EPL * LPR;
+  constexpr int RW = 256 / LPR;            // rows per workgroup
   constexpr int SRB = sr_bits_of<RND>();
   constexpr int CW = EPL * QB / 32;        // code words per lane and row
   constexpr int HW = EH / 2;               // 16-bit value words per lane and row
   static_assert(EH % 2 == 0, "protected slots come in dword pairs");
-  const int lane = threadIdx.x & 7;
-  const int g = threadIdx.x >> 3;          // row group: one row of 32 per workgroup
+  const int lane = threadIdx.x & (LPR - 1);
+  const int g = threadIdx.x / LPR;         // row group: one row per workgroup chunk
 
-  // work item (b, h, chunk of 32 rows), head order rotated by b across XCDs
+  // work item (b, h, chunk of RW rows), head order rotated by b across XCDs
   const uint32_t per_b = (uint32_t)a.H * (uint32_t)a.row_chunks;
   const uint32_t b = blockIdx.x / per_b;
   uint32_t r = blockIdx.x - b * per_b + b % per_b;
@@ -57,7 +87,7 @@ __global__ __launch_bounds__(256) void k_step_keymap(const Args a) {
   const uint32_t chunk = r % (uint32_t)a.row_chunks;
   const uint32_t h = r / (uint32_t)a.row_chunks;
   const uint64_t bh = (uint64_t)b * (uint64_t)a.H + h;
-  const int v = (int)chunk * 32 + g;
+  const int v = (int)chunk * RW + g;
 
   const int nq = a.t.nq[h];
   const int nhp = DK - nq;
@@ -141,7 +171,7 @@ __global__ __launch_bounds__(256) void k_step_keymap(const Args a) {
     for (int i = 0; i < EPL; ++i) wc = fmaf(code_at(i), kc[i], wc);
 #pragma unroll
     for (int i = 0; i < EH; ++i) wh = fmaf(hp_at(i), kh[i], wh);
-    const float wk = red_sum<8>(fmaf(s_old, wc, wh));
+    const float wk = red_sum<LPR>(fmaf(s_old, wc, wh));
     u = beta * (vin - dh * wk);
   } else {
     u = beta * vin;
@@ -174,8 +204,8 @@ __global__ __launch_bounds__(256) void k_step_keymap(const Args a) {
   }
 #pragma unroll
   for (int i = 0; i < EPL; i += 2) mx = fmaxf(fmaxf(mx, fabsf(sp[i])), fabsf(sp[i + 1]));
-  o = red_sum<8>(o);
-  const float m = red_absmax<8>(mx);
+  o = red_sum<LPR>(o);
+  const float m = red_absmax<LPR>(mx);
   float scale, inv, invb;
   row_scale_fast<QB, SRB>(m, scale, inv, invb);
 
