@@ -182,9 +182,9 @@ qs_status make_plan(const qstate_config* c, Plan* p) {
 
   dense_shape(c->kind, dk, dv, &p->dense_lpr, &p->dense_rpl, &p->dense_threads, &p->row_chunks);
   if (c->lrb_rank > 0) {
+    // one workgroup per head; the buffer and the head's vectors live in
+    // static LDS
     p->family = qs::kFamLrb;
-    const uint64_t floats = (uint64_t)dv * r + (uint64_t)dk * r + 4u * (uint64_t)dv + 3u * (uint64_t)dk + 36u;
-    p->lds = (uint32_t)(floats * 4u + 2u * (uint64_t)dk);
   } else if (c->map_mode == QS_MAP_KEY && c->hp_dtype != QS_FP32 && dk == 128) {
     // key-channel maps with 16-bit protected values: rows in storage order,
     // 8 lanes per row, each with 16 code slots and keymap_eh protected

@@ -1,0 +1,319 @@
+// Step kernel with the Low-Rank Bypass (abstract of "Preserving Updates in
+// Low-Bit Recurrent State Quantization": small updates accumulate in a
+// compact low-rank buffer whose sufficiently large elements are merged into
+// the state periodically).  Additive recurrences, map NONE.
+//
+// Buffer of one head: L = W U^T, W [dv][r] with orthonormal columns
+// 0..n-1, U [dk][r].  One workgroup of 256 threads per head (dv, dk <= 256):
+// thread t holds row t of W (t < dv) and row t of U (t < dk) in registers,
+// RANK >= r entries each.  Phase A follows the buffer steps (decay U, grow
+// the basis while n < r, project u on the basis, route the in-span part of
+// small key channels to U, merge on a merge step, buffer readout); the r
+// dot products of a projection are one vector reduction.  Phase B is the
+// row step of the dense kernel: 8 lanes per row, every row's codes loaded
+// first, u_perp on small channels, merged buffer columns added before
+// rounding.
+#pragma once
+#include "qstate_step_kernels.hpp"
+
+namespace qs {
+
+namespace {
+
+// Sum of the R-vector p over the wave: halving exchanges leave one
+// component per lane (component j in lanes with (lane / (64/R)) == j),
+// then a butterfly over the remaining lanes.  Returns the lane's component.
+template <int R>
+__device__ __forceinline__ float wave_sum_vec(float (&p)[R], int lane) {
+  static_assert(R == 8 || R == 16, "rank bound 8 or 16");
+  constexpr int LOGR = (R == 8) ? 3 : 4;
+#pragma unroll
+  for (int s = 0; s < LOGR; ++s) {
+    const int off = 32 >> s;
+    const int half = R >> (s + 1);
+    const bool up = (lane & off) != 0;
+#pragma unroll
+    for (int i = 0; i < half; ++i) {
+      const float keep = up ? p[i + half] : p[i];
+      const float send = up ? p[i] : p[i + half];
+      p[i] = keep + __shfl_xor(send, off, 64);
+    }
+  }
+  float x = p[0];
+#pragma unroll
+  for (int off = 32 >> LOGR; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+// Block sums of p (R values) and block max of mx: every thread gets them in
+// out[] and the return value.  red: 4 * (R + 1) floats of LDS.
+template <int R>
+__device__ __forceinline__ float block_sum_vec(float (&p)[R], float mx, float (&out)[R], float* red) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const float x = wave_sum_vec<R>(p, lane);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+  __syncthreads();   // red may still be read by an earlier reduction
+  if ((lane & (64 / R - 1)) == 0) red[w * (R + 1) + lane / (64 / R)] = x;
+  if (lane == 0) red[w * (R + 1) + R] = mx;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < R; ++j)
+    out[j] = (red[j] + red[(R + 1) + j]) + (red[2 * (R + 1) + j] + red[3 * (R + 1) + j]);
+  return fmaxf(fmaxf(red[R], red[2 * R + 1]), fmaxf(red[3 * R + 2], red[4 * R + 3]));
+}
+
+// Element j (runtime) of a register array, by selects.
+template <int R>
+__device__ __forceinline__ float pick(const float (&p)[R], int j) {
+  float x = p[0];
+#pragma unroll
+  for (int i = 1; i < R; ++i) x = (j == i) ? p[i] : x;
+  return x;
+}
+
+}  // namespace
+
+template <int QB, int RND, int EPL, int RANK, int BDR, int DKEY>
+__global__ __launch_bounds__(256) void k_step_lrb(const Args a) {
+  constexpr int DK = EPL * 8;
+  constexpr int SRB = sr_bits_of<RND>();
+  constexpr int CW = EPL * QB / 32;
+  const int tid = threadIdx.x;
+  const int dv = a.dv;
+  const int r = a.lrb_rank;
+  const uint32_t bh = blockIdx.x;
+  const uint32_t h = bh % (uint32_t)a.H;
+  const uint32_t b = bh / (uint32_t)a.H;
+  const float theta = a.lrb_theta;
+
+  __shared__ __align__(16) float Wt[RANK][256];   // W transposed, for merges and rows
+  __shared__ __align__(16) float Ut[RANK][DK];    // U rows of merged channels (before clearing)
+  __shared__ __align__(16) float ul[256], upl[256], sol[256], lrl[256];
+  __shared__ __align__(16) float kl[DK], ql[DK], dl[DK];
+  __shared__ float red[4 * (RANK + 1)];
+  __shared__ uint8_t smalll[DK], mflagl[DK];
+
+  float* Wg = a.W + (uint64_t)bh * (uint64_t)dv * (uint64_t)r;
+  float* Ug = a.U + (uint64_t)bh * (uint64_t)DK * (uint64_t)r;
+  const float beta = a.beta ? a.beta[bh] : 1.0f;
+  int n = a.n[bh];
+
+  // loads: this thread's W row (t < dv) and U row (t < dk), its u, s_old,
+  // k, q, decay
+  float Wr[RANK], Ur[RANK];
+  float uv = 0.0f, so = 0.0f, kk = 0.0f, qq = 0.0f, dd = 0.0f;
+#pragma unroll
+  for (int j = 0; j < RANK; ++j) {
+    Wr[j] = (tid < dv && j < r) ? Wg[tid * r + j] : 0.0f;
+    Ur[j] = (tid < DK && j < r) ? Ug[tid * r + j] : 0.0f;
+  }
+  if (tid < dv) {
+    const uint64_t row = (uint64_t)bh * (uint64_t)dv + (uint64_t)tid;
+    uv = beta * load_in1(a.v, a.in_bf16, row);
+    so = ld_nt(a.scales + row);
+  }
+  if (tid < DK) {
+    kk = load_in1(a.k, a.in_bf16, (uint64_t)bh * DK + tid);
+    qq = load_in1(a.q, a.in_bf16, (uint64_t)bh * DK + tid);
+    dd = DKEY ? a.decay[(uint64_t)bh * DK + tid] : a.decay[bh];
+  }
+
+  // 1. the buffer decays with the state (decay acts on the key side)
+#pragma unroll
+  for (int j = 0; j < RANK; ++j) Ur[j] = dd * Ur[j];
+
+  // 2. grow the basis while n < r (two Gram-Schmidt passes)
+  bool grown = false;
+  if (n < r) {
+    float y = uv;
+    for (int pass = 0; pass < 2; ++pass)
+      for (int j = 0; j < n; ++j) {
+        const float wv = pick<RANK>(Wr, j);
+        const float p = block_sum(wv * y, red);
+        y = fmaf(-p, wv, y);
+      }
+    const float ny = sqrtf(block_sum(y * y, red));
+    const float nu = sqrtf(block_sum(uv * uv, red));
+    if (ny > ldexpf(nu, -10)) {
+      const float wn = y / ny;
+#pragma unroll
+      for (int j = 0; j < RANK; ++j) Wr[j] = (j == n && tid < dv) ? wn : Wr[j];
+      n += 1;
+      grown = true;
+    }
+  }
+
+  // 3. coefficients c = W^T u (columns below n) and g = max_v |u_v| / s_v
+  float c[RANK];
+  float g;
+  {
+    float p[RANK];
+#pragma unroll
+    for (int j = 0; j < RANK; ++j) p[j] = (j < n) ? Wr[j] * uv : 0.0f;
+    const float au = fabsf(uv);
+    const float gv = (so > 0.0f) ? au / so : (au > 0.0f ? __builtin_inff() : 0.0f);
+    g = block_sum_vec<RANK>(p, tid < dv ? gv : 0.0f, c, red);
+  }
+  // remainder u_perp = u - W c, in column order
+  float up = uv;
+#pragma unroll
+  for (int j = 0; j < RANK; ++j) up = (j < n) ? fmaf(-c[j], Wr[j], up) : up;
+
+  // 4. small key channels send c k_k into U
+  bool sm = false;
+  if (tid < DK) {
+    sm = __builtin_isfinite(g) && (fabsf(kk) * g < theta);
+    if (sm) {
+#pragma unroll
+      for (int j = 0; j < RANK; ++j) Ur[j] = (j < n) ? fmaf(kk, c[j], Ur[j]) : Ur[j];
+    }
+  }
+  // W transposed into LDS for the merge test and the rows
+#pragma unroll
+  for (int j = 0; j < RANK; ++j) Wt[j][tid] = Wr[j];
+  if (tid < dv) {
+    ul[tid] = uv;
+    upl[tid] = up;
+    sol[tid] = so;
+  }
+  __syncthreads();
+
+  // 5. merge: a channel whose buffered column reaches theta LSB in some row
+  // is added to the state and cleared; a clear buffer resets the basis
+  bool merged = false;
+  int n_new = n;
+  const uint64_t step = ((uint64_t)a.step_hi << 32) | a.step_lo;
+  if (a.lrb_period > 0 && ((step + 1u) % (uint64_t)a.lrb_period) == 0u) {
+    int left = 0;
+    if (tid < DK) {
+      for (int v = 0; v < dv && !merged; ++v) {
+        float col = 0.0f;
+#pragma unroll
+        for (int j = 0; j < RANK; ++j)
+          if (j < n) col = fmaf(Wt[j][v], Ur[j], col);
+        if (col != 0.0f && fabsf(col) >= theta * sol[v]) merged = true;
+      }
+      if (merged) {
+#pragma unroll
+        for (int j = 0; j < RANK; ++j) {
+          Ut[j][tid] = Ur[j];
+          Ur[j] = 0.0f;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < RANK; ++j)
+        if (j < r && Ur[j] != 0.0f) left = 1;
+    }
+    if (!block_or(left, red)) n_new = 0;
+  }
+
+  // 6. buffer readout z = U^T q (merged channels are clear), lr = W z
+  float z[RANK];
+  {
+    float p[RANK];
+#pragma unroll
+    for (int j = 0; j < RANK; ++j) p[j] = (j < n_new && tid < DK) ? Ur[j] * qq : 0.0f;
+    (void)block_sum_vec<RANK>(p, 0.0f, z, red);
+  }
+  if (tid < dv) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int j = 0; j < RANK; ++j) acc = (j < n_new) ? fmaf(Wr[j], z[j], acc) : acc;
+    lrl[tid] = acc;
+  }
+  // write the buffer back
+  if (tid < DK) {
+#pragma unroll
+    for (int j = 0; j < RANK; ++j)
+      if (j < r) Ug[tid * r + j] = Ur[j];
+    kl[tid] = kk;
+    ql[tid] = qq;
+    dl[tid] = dd;
+    smalll[tid] = sm ? 1 : 0;
+    mflagl[tid] = merged ? 1 : 0;
+  }
+  if (grown && tid < dv) {
+#pragma unroll
+    for (int j = 0; j < RANK; ++j)
+      if (j < r) Wg[tid * r + j] = Wr[j];
+  }
+  if (tid == 0) a.n[bh] = n_new;
+  __syncthreads();
+
+  // Phase B: rows, 8 lanes per row, rows g, g + 32, ...
+  const int lane8 = tid & 7;
+  const int grp = tid >> 3;
+  const int k0 = lane8 * EPL;
+  float kf[EPL], qf[EPL], df[EPL];
+  uint32_t smask = 0u, mmask = 0u;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    kf[i] = kl[k0 + i];
+    qf[i] = ql[k0 + i];
+    df[i] = dl[k0 + i];
+    smask |= (smalll[k0 + i] ? 1u : 0u) << i;
+    mmask |= (mflagl[k0 + i] ? 1u : 0u) << i;
+  }
+  uint8_t* gcode = const_cast<uint8_t*>(code_block(a, b, h));
+  uint32_t cw_next[CW];
+  if (grp < dv) load_bytes<EPL * QB / 8, true>(gcode + (uint64_t)grp * (DK * QB / 8) + k0 * QB / 8, cw_next);
+  for (int v = grp; v < dv; v += 32) {
+    uint32_t cw[CW];
+#pragma unroll
+    for (int i = 0; i < CW; ++i) cw[i] = cw_next[i];
+    if (v + 32 < dv)   // next row's codes in flight while this one computes
+      load_bytes<EPL * QB / 8, true>(gcode + (uint64_t)(v + 32) * (DK * QB / 8) + k0 * QB / 8, cw_next);
+    const uint64_t row = (uint64_t)bh * (uint64_t)dv + (uint64_t)v;
+    const float s_old = sol[v];
+    const float uu = ul[v], upv = upl[v];
+    float sp[EPL], sh[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      float cf;
+      if constexpr (QB == 8) cf = (float)(int32_t)(int8_t)(cw[i >> 2] >> (8 * (i & 3)));
+      else cf = (float)((int32_t)(cw[i >> 3] << (28 - 4 * (i & 7))) >> 28);
+      sh[i] = s_old * cf;
+      sp[i] = fmaf(((smask >> i) & 1u) ? upv : uu, kf[i], (df[i] * s_old) * cf);
+    }
+    if (mmask) {
+#pragma unroll
+      for (int i = 0; i < EPL; ++i)
+        if ((mmask >> i) & 1u) {
+          float col = 0.0f;
+#pragma unroll
+          for (int j = 0; j < RANK; ++j)
+            if (j < n) col = fmaf(Wt[j][v], Ut[j][k0 + i], col);
+          sp[i] = sp[i] + col;
+        }
+    }
+    float o = 0.0f, mx = 0.0f;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      o = fmaf(sp[i], qf[i], o);
+      mx = fmaxf(mx, fabsf(sp[i]));
+    }
+    o = red_sum<8>(o);
+    const float m = red_absmax<8>(mx);
+    float scale, inv, invb;
+    row_scale_fast<QB, SRB>(m, scale, inv, invb);
+    uint32_t rb[EPL];
+    if constexpr (RND != 0) rand_bits<RND, EPL>(row * DK + (uint64_t)k0, a.seed_lo, a.seed_hi, a.step_lo, a.step_hi, rb);
+    uint32_t out[CW];
+#pragma unroll
+    for (int j = 0; j < CW; ++j) out[j] = 0u;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int32_t code = round_elem<QB, RND, BDR>(sp[i], sh[i], inv, invb, (RND != 0) ? rb[i] : 0u, a.bdr_bound);
+      if constexpr (QB == 8) out[i >> 2] |= ((uint32_t)code & 0xFFu) << (8 * (i & 3));
+      else out[i >> 3] |= ((uint32_t)code & 0xFu) << (4 * (i & 7));
+    }
+    store_bytes<EPL * QB / 8, true>(gcode + (uint64_t)v * (DK * QB / 8) + k0 * QB / 8, out);
+    if (lane8 == 0) {
+      st_nt(a.out + row, o + lrl[v]);
+      st_nt(a.scales + row, scale);
+    }
+  }
+}
+
+}  // namespace qs

@@ -632,11 +632,6 @@ __device__ __forceinline__ float wave_sum(float x) {
   for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
   return x;
 }
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
-  return x;
-}
 // Sum over the block; every thread gets the same value.  `red` holds 4 floats.
 __device__ __forceinline__ float block_sum(float x, float* red) {
   x = wave_sum(x);
@@ -644,13 +639,6 @@ __device__ __forceinline__ float block_sum(float x, float* red) {
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
   __syncthreads();
   return (red[0] + red[1]) + (red[2] + red[3]);
-}
-__device__ __forceinline__ float block_max(float x, float* red) {
-  x = wave_max(x);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
-  __syncthreads();
-  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 __device__ __forceinline__ int block_or(int x, float* red) {
   x = __any(x) ? 1 : 0;
@@ -660,215 +648,5 @@ __device__ __forceinline__ int block_or(int x, float* red) {
   return (red[0] + red[1] + red[2] + red[3]) > 0.0f;
 }
 }  // namespace
-
-// ---------------------------------------------------------------------------
-// Step with Low-Rank Bypass (additive recurrences, map NONE).  One
-// workgroup per head.  Phase A keeps the head's buffer (W [dv][r], U
-// [dk][r]) in LDS: decay U with the state, grow the orthonormal value basis
-// from the write vector while fewer than r columns exist, split u into its
-// in-span coefficients c and remainder u_perp, send c k_k into U for key
-// channels whose update is under theta LSB in every row, and on a merge step
-// flag buffer channels that reach theta LSB somewhere.  Phase B is the dense
-// row step with u_perp on small channels and the flagged buffer columns
-// added before rounding; the readout adds W (U^T q).
-// ---------------------------------------------------------------------------
-template <int QB, int RND, int EPL>
-__global__ __launch_bounds__(256) void k_step_lrb(const Args a) {
-  constexpr int DK = EPL * 8;
-  extern __shared__ __align__(16) uint8_t lds[];
-  const int tid = threadIdx.x;
-  const int dv = a.dv;
-  const int r = a.lrb_rank;
-  const uint32_t bh = blockIdx.x;
-  const uint32_t h = bh % (uint32_t)a.H;
-  const uint32_t b = bh / (uint32_t)a.H;
-  const float theta = a.lrb_theta;
-
-  float* Wl = reinterpret_cast<float*>(lds);           // [dv][r]
-  float* Ul = Wl + dv * r;                              // [DK][r]
-  float* ul = Ul + DK * r;                              // [dv]
-  float* upl = ul + dv;                                 // [dv]
-  float* sol = upl + dv;                                // [dv] scales on entry
-  float* lrl = sol + dv;                                // [dv] buffer readout
-  float* kl = lrl + dv;                                 // [DK]
-  float* ql = kl + DK;                                  // [DK]
-  float* dl = ql + DK;                                  // [DK]
-  float* cl = dl + DK;                                  // [16]
-  float* zl = cl + 16;                                  // [16]
-  float* red = zl + 16;                                 // [4]
-  uint8_t* small = reinterpret_cast<uint8_t*>(red + 4); // [DK]
-  uint8_t* mflag = small + DK;                          // [DK]
-
-  float* Wg = a.W + (uint64_t)bh * (uint64_t)dv * (uint64_t)r;
-  float* Ug = a.U + (uint64_t)bh * (uint64_t)DK * (uint64_t)r;
-  const float beta = a.beta ? a.beta[bh] : 1.0f;
-  int n = a.n[bh];
-
-  if (tid < dv) {
-    const uint64_t row = (uint64_t)bh * (uint64_t)dv + (uint64_t)tid;
-    ul[tid] = beta * load_in1(a.v, a.in_bf16, row);
-    sol[tid] = ld_nt(a.scales + row);
-  }
-  if (tid < DK) {
-    kl[tid] = load_in1(a.k, a.in_bf16, (uint64_t)bh * DK + tid);
-    ql[tid] = load_in1(a.q, a.in_bf16, (uint64_t)bh * DK + tid);
-    dl[tid] = a.decay_key ? a.decay[(uint64_t)bh * DK + tid] : a.decay[bh];
-  }
-  for (int i = tid; i < dv * r; i += 256) Wl[i] = Wg[i];
-  for (int i = tid; i < DK * r; i += 256) Ul[i] = Ug[i];
-  __syncthreads();
-
-  // 1. the buffer decays with the state (decay acts on the key side)
-  for (int i = tid; i < DK * r; i += 256) Ul[i] = dl[i / r] * Ul[i];
-
-  // 2. grow the basis (two Gram-Schmidt passes)
-  bool grown = false;
-  if (n < r) {
-    float y = (tid < dv) ? ul[tid] : 0.0f;
-    for (int pass = 0; pass < 2; ++pass)
-      for (int j = 0; j < n; ++j) {
-        const float wv = (tid < dv) ? Wl[tid * r + j] : 0.0f;
-        const float p = block_sum(wv * y, red);
-        if (tid < dv) y = fmaf(-p, wv, y);
-      }
-    const float ny = sqrtf(block_sum(y * y, red));
-    const float uu = (tid < dv) ? ul[tid] : 0.0f;
-    const float nu = sqrtf(block_sum(uu * uu, red));
-    if (ny > ldexpf(nu, -10)) {
-      if (tid < dv) Wl[tid * r + n] = y / ny;
-      n += 1;
-      grown = true;
-    }
-  }
-  __syncthreads();
-
-  // 3. project the write vector on the basis
-  for (int j = 0; j < n; ++j) {
-    const float c = block_sum((tid < dv) ? Wl[tid * r + j] * ul[tid] : 0.0f, red);
-    if (tid == 0) cl[j] = c;
-  }
-  __syncthreads();
-  float gv = 0.0f;
-  if (tid < dv) {
-    float t = ul[tid];
-    for (int j = 0; j < n; ++j) t = fmaf(-cl[j], Wl[tid * r + j], t);
-    upl[tid] = t;
-    const float au = fabsf(ul[tid]);
-    gv = (sol[tid] > 0.0f) ? au / sol[tid] : (au > 0.0f ? __builtin_inff() : 0.0f);
-  }
-  // 4. small key channels go to the buffer
-  const float g = block_max(gv, red);
-  if (tid < DK) {
-    const bool sm = __builtin_isfinite(g) && (fabsf(kl[tid]) * g < theta);
-    small[tid] = sm ? 1 : 0;
-    if (sm)
-      for (int j = 0; j < n; ++j) Ul[tid * r + j] = fmaf(kl[tid], cl[j], Ul[tid * r + j]);
-    mflag[tid] = 0;
-  }
-  __syncthreads();
-
-  // 5. merge
-  int n_new = n;
-  const uint64_t step = ((uint64_t)a.step_hi << 32) | a.step_lo;
-  if (a.lrb_period > 0 && ((step + 1u) % (uint64_t)a.lrb_period) == 0u) {
-    int left = 0;
-    if (tid < DK) {
-      int big = 0;
-      for (int v = 0; v < dv; ++v) {
-        float col = 0.0f;
-        for (int j = 0; j < n; ++j) col = fmaf(Wl[v * r + j], Ul[tid * r + j], col);
-        if (col != 0.0f && fabsf(col) >= theta * sol[v]) big = 1;
-      }
-      mflag[tid] = (uint8_t)big;
-      if (!big)
-        for (int j = 0; j < r; ++j)
-          if (Ul[tid * r + j] != 0.0f) left = 1;
-    }
-    if (!block_or(left, red)) n_new = 0;
-  }
-  __syncthreads();
-
-  // 6. buffer readout term z = U^T q over unmerged channels; lr = W z
-  for (int j = 0; j < n; ++j) {
-    const float zj = block_sum((tid < DK && !mflag[tid]) ? Ul[tid * r + j] * ql[tid] : 0.0f, red);
-    if (tid == 0) zl[j] = zj;
-  }
-  __syncthreads();
-  if (tid < dv) {
-    float acc = 0.0f;
-    for (int j = 0; j < n; ++j) acc = fmaf(Wl[tid * r + j], zl[j], acc);
-    lrl[tid] = acc;
-  }
-  // write the buffer back
-  for (int i = tid; i < DK * r; i += 256) Ug[i] = mflag[i / r] ? 0.0f : Ul[i];
-  if (grown)
-    for (int i = tid; i < dv * r; i += 256) Wg[i] = Wl[i];
-  if (tid == 0) a.n[bh] = n_new;
-  __syncthreads();
-
-  // Phase B: rows
-  const int lane8 = tid & 7;
-  const int rloc = tid >> 3;
-  const int k0 = lane8 * EPL;
-  float kf[EPL], df[EPL], qf[EPL];
-  bool smf[EPL], mgf[EPL];
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    kf[i] = kl[k0 + i];
-    df[i] = dl[k0 + i];
-    qf[i] = ql[k0 + i];
-    smf[i] = small[k0 + i] != 0;
-    mgf[i] = mflag[k0 + i] != 0;
-  }
-  uint8_t* gcode = const_cast<uint8_t*>(code_block(a, b, h));
-  for (int v = rloc; v < dv; v += 32) {
-    const uint64_t row = (uint64_t)bh * (uint64_t)dv + (uint64_t)v;
-    uint8_t* cp = gcode + (uint64_t)v * (DK * QB / 8) + k0 * QB / 8;
-    uint32_t cw[EPL * QB / 32];
-    load_bytes<EPL * QB / 8, true>(cp, cw);
-    const float s_old = sol[v];
-    float sh[EPL], cf[EPL];
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      if constexpr (QB == 8) cf[i] = (float)(int32_t)(int8_t)(cw[i >> 2] >> (8 * (i & 3)));
-      else cf[i] = (float)((int32_t)(cw[i >> 3] << (28 - 4 * (i & 7))) >> 28);
-      sh[i] = s_old * cf[i];
-    }
-    const float uv = ul[v], upv = upl[v];
-    float sp[EPL];
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      float x = fmaf(smf[i] ? upv : uv, kf[i], (df[i] * s_old) * cf[i]);
-      if (mgf[i]) {
-        float col = 0.0f;
-        for (int j = 0; j < n; ++j) col = fmaf(Wl[v * r + j], Ul[(k0 + i) * r + j], col);
-        x = x + col;
-      }
-      sp[i] = x;
-    }
-    float o = 0.0f;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) o = fmaf(sp[i], qf[i], o);
-    o = sum8(o);
-    if (lane8 == 0) st_nt(a.out + row, o + lrl[v]);
-    float m = 0.0f;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) m = fmaxf(m, fabsf(sp[i]));
-    m = max8(m);
-    float scale, inv, invb;
-    row_scale<QB, sr_bits_of<RND>()>(m, scale, inv, invb);
-    uint32_t rb[EPL];
-    if constexpr (RND != 0) rand_bits<RND, EPL>(row * DK + (uint64_t)k0, a.seed_lo, a.seed_hi, a.step_lo, a.step_hi, rb);
-    int32_t code[EPL];
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      const uint32_t rbi = (RND != 0) ? rb[i] : 0u;
-      code[i] = a.bdr ? round_elem<QB, RND, 1>(sp[i], sh[i], inv, invb, rbi, a.bdr_bound)
-                      : round_elem<QB, RND, 0>(sp[i], sh[i], inv, invb, rbi, a.bdr_bound);
-    }
-    store_codes<QB, EPL>(cp, code);
-    if (lane8 == 0) st_nt(a.scales + row, scale);
-  }
-}
 
 }  // namespace qs

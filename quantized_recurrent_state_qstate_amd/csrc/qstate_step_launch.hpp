@@ -3,6 +3,7 @@
 // kernels compile in parallel.
 #pragma once
 #include "qstate_keymap_kernel.hpp"
+#include "qstate_lrb_kernel.hpp"
 
 namespace qs {
 
@@ -60,11 +61,22 @@ hipError_t launch_mixed_t(const Args& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int QB, int RND, int EPL, int RANK>
+hipError_t launch_lrb_r(const Args& a, hipStream_t s) {
+  const dim3 grid((uint32_t)((uint64_t)a.B * (uint64_t)a.H));
+  if (a.bdr) {
+    if (a.decay_key) hipLaunchKernelGGL((k_step_lrb<QB, RND, EPL, RANK, 1, 1>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_step_lrb<QB, RND, EPL, RANK, 1, 0>), grid, dim3(256), 0, s, a);
+  } else {
+    if (a.decay_key) hipLaunchKernelGGL((k_step_lrb<QB, RND, EPL, RANK, 0, 1>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_step_lrb<QB, RND, EPL, RANK, 0, 0>), grid, dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
 template <int QB, int RND, int EPL>
 hipError_t launch_lrb_t(const Args& a, hipStream_t s) {
-  const uint64_t grid = (uint64_t)a.B * (uint64_t)a.H;
-  hipLaunchKernelGGL((k_step_lrb<QB, RND, EPL>), dim3((uint32_t)grid), dim3(256), a.mixed_lds, s, a);
-  return hipGetLastError();
+  return a.lrb_rank <= 8 ? launch_lrb_r<QB, RND, EPL, 8>(a, s) : launch_lrb_r<QB, RND, EPL, 16>(a, s);
 }
 
 template <int QB, int RND, int DELTA, int LPR, int EH>
