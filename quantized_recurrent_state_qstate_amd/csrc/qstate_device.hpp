@@ -412,24 +412,30 @@ constexpr int sr_bits_of() { return RND == 1 ? 16 : (RND == 2 ? 8 : 0); }
 template <int QB, int RND, int BDR>
 __device__ __forceinline__ int32_t round_elem(float sp, float sh, float inv, float invb, uint32_t rb,
                                               float bound) {
-  int32_t c;
   if constexpr (RND == 0) {
-    c = (int32_t)rintf(sp * inv);
+    // decided in float (ceil, floor and rint of |x| <= Q are exact), one
+    // conversion at the end
+    const float x = sp * inv;
+    float cf = rintf(x);
+    if constexpr (BDR) {
+      const float xo = sh * inv;
+      const float d = sp - sh;
+      cf = (d > 0.0f && cf < xo - bound) ? ceilf(x) : ((d < 0.0f && cf > xo + bound) ? floorf(x) : cf);
+    }
+    return (int32_t)cf;
   } else {
     constexpr int SRB = sr_bits_of<RND>();
-    const int32_t X = cvt_rpi(sp * invb);
-    c = (X + (int32_t)rb) >> SRB;
+    int32_t c = (cvt_rpi(sp * invb) + (int32_t)rb) >> SRB;
+    if constexpr (BDR) {
+      const float x = sp * inv;
+      const float xo = sh * inv;
+      const float d = sp - sh;
+      const float cf = (float)c;
+      const float nf = (d > 0.0f && cf < xo - bound) ? ceilf(x) : ((d < 0.0f && cf > xo + bound) ? floorf(x) : cf);
+      c = (int32_t)nf;
+    }
+    return c;
   }
-  if constexpr (BDR) {
-    const float x = sp * inv;
-    const float xo = sh * inv;
-    const float d = sp - sh;
-    const float cf = (float)c;
-    const int32_t up = (int32_t)ceilf(x);
-    const int32_t dn = (int32_t)floorf(x);
-    c = (d > 0.0f && cf < xo - bound) ? up : ((d < 0.0f && cf > xo + bound) ? dn : c);
-  }
-  return c;
 }
 
 }  // namespace qs

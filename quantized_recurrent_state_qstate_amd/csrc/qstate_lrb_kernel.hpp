@@ -20,47 +20,35 @@ namespace qs {
 
 namespace {
 
-// Sum of the R-vector p over the wave: halving exchanges leave one
-// component per lane (component j in lanes with (lane / (64/R)) == j),
-// then a butterfly over the remaining lanes.  Returns the lane's component.
+// Block sums of the R-vector p and block max of mx; every thread gets them
+// in out[] and the return value.  Through LDS: each thread writes its R
+// partial values to P [R][256], 256/R threads sum one component (a fixed
+// order), and a shuffle tree finishes it.  red: R + 4 floats.
 template <int R>
-__device__ __forceinline__ float wave_sum_vec(float (&p)[R], int lane) {
+__device__ __forceinline__ float block_sum_vec(const float (&p)[R], float mx, float (&out)[R], float* P,
+                                               float* red) {
   static_assert(R == 8 || R == 16, "rank bound 8 or 16");
-  constexpr int LOGR = (R == 8) ? 3 : 4;
-#pragma unroll
-  for (int s = 0; s < LOGR; ++s) {
-    const int off = 32 >> s;
-    const int half = R >> (s + 1);
-    const bool up = (lane & off) != 0;
-#pragma unroll
-    for (int i = 0; i < half; ++i) {
-      const float keep = up ? p[i + half] : p[i];
-      const float send = up ? p[i] : p[i + half];
-      p[i] = keep + __shfl_xor(send, off, 64);
-    }
-  }
-  float x = p[0];
-#pragma unroll
-  for (int off = 32 >> LOGR; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
-  return x;
-}
-
-// Block sums of p (R values) and block max of mx: every thread gets them in
-// out[] and the return value.  red: 4 * (R + 1) floats of LDS.
-template <int R>
-__device__ __forceinline__ float block_sum_vec(float (&p)[R], float mx, float (&out)[R], float* red) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const float x = wave_sum_vec<R>(p, lane);
+  constexpr int TPC = 256 / R;   // threads per component
+  constexpr int EPT = 256 / TPC; // entries each of them sums
+  const int t = threadIdx.x;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-  __syncthreads();   // red may still be read by an earlier reduction
-  if ((lane & (64 / R - 1)) == 0) red[w * (R + 1) + lane / (64 / R)] = x;
-  if (lane == 0) red[w * (R + 1) + R] = mx;
+  __syncthreads();   // P and red may still be read by an earlier reduction
+#pragma unroll
+  for (int j = 0; j < R; ++j) P[j * 256 + t] = p[j];
+  if ((t & 63) == 0) red[R + (t >> 6)] = mx;
+  __syncthreads();
+  const int j = t / TPC, part = t % TPC;
+  float sum = 0.0f;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) sum += P[j * 256 + part * EPT + e];
+#pragma unroll
+  for (int off = TPC / 2; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
+  if (part == 0) red[j] = sum;
   __syncthreads();
 #pragma unroll
-  for (int j = 0; j < R; ++j)
-    out[j] = (red[j] + red[(R + 1) + j]) + (red[2 * (R + 1) + j] + red[3 * (R + 1) + j]);
-  return fmaxf(fmaxf(red[R], red[2 * R + 1]), fmaxf(red[3 * R + 2], red[4 * R + 3]));
+  for (int i = 0; i < R; ++i) out[i] = red[i];
+  return fmaxf(fmaxf(red[R], red[R + 1]), fmaxf(red[R + 2], red[R + 3]));
 }
 
 // Element j (runtime) of a register array, by selects.
@@ -91,7 +79,8 @@ __global__ __launch_bounds__(256) void k_step_lrb(const Args a) {
   __shared__ __align__(16) float Ut[RANK][DK];    // U rows of merged channels (before clearing)
   __shared__ __align__(16) float ul[256], upl[256], sol[256], lrl[256];
   __shared__ __align__(16) float kl[DK], ql[DK], dl[DK];
-  __shared__ float red[4 * (RANK + 1)];
+  __shared__ __align__(16) float P[RANK * 256];   // reduction transpose
+  __shared__ float red[RANK + 4];
   __shared__ uint8_t smalll[DK], mflagl[DK];
 
   float* Wg = a.W + (uint64_t)bh * (uint64_t)dv * (uint64_t)r;
@@ -125,6 +114,7 @@ __global__ __launch_bounds__(256) void k_step_lrb(const Args a) {
 
   // 2. grow the basis while n < r (two Gram-Schmidt passes)
   bool grown = false;
+  float wnew = 0.0f;   // the new basis column's entry of this thread's row
   if (n < r) {
     float y = uv;
     for (int pass = 0; pass < 2; ++pass)
@@ -136,29 +126,35 @@ __global__ __launch_bounds__(256) void k_step_lrb(const Args a) {
     const float ny = sqrtf(block_sum(y * y, red));
     const float nu = sqrtf(block_sum(uv * uv, red));
     if (ny > ldexpf(nu, -10)) {
-      const float wn = y / ny;
+      wnew = tid < dv ? y / ny : 0.0f;
 #pragma unroll
-      for (int j = 0; j < RANK; ++j) Wr[j] = (j == n && tid < dv) ? wn : Wr[j];
+      for (int j = 0; j < RANK; ++j) Wr[j] = (j == n) ? wnew : Wr[j];
       n += 1;
       grown = true;
     }
   }
 
-  // 3. coefficients c = W^T u (columns below n) and g = max_v |u_v| / s_v
+  // Columns from n on are not part of the basis: zero them once here, so
+  // every sum below runs over all RANK columns (their terms add exact zeros)
+  // and no column test is needed.  U's columns from n on are zero already.
+#pragma unroll
+  for (int j = 0; j < RANK; ++j) Wr[j] = (j < n) ? Wr[j] : 0.0f;
+
+  // 3. coefficients c = W^T u and g = max_v |u_v| / s_v
   float c[RANK];
   float g;
   {
     float p[RANK];
 #pragma unroll
-    for (int j = 0; j < RANK; ++j) p[j] = (j < n) ? Wr[j] * uv : 0.0f;
+    for (int j = 0; j < RANK; ++j) p[j] = Wr[j] * uv;
     const float au = fabsf(uv);
     const float gv = (so > 0.0f) ? au / so : (au > 0.0f ? __builtin_inff() : 0.0f);
-    g = block_sum_vec<RANK>(p, tid < dv ? gv : 0.0f, c, red);
+    g = block_sum_vec<RANK>(p, tid < dv ? gv : 0.0f, c, P, red);
   }
   // remainder u_perp = u - W c, in column order
   float up = uv;
 #pragma unroll
-  for (int j = 0; j < RANK; ++j) up = (j < n) ? fmaf(-c[j], Wr[j], up) : up;
+  for (int j = 0; j < RANK; ++j) up = fmaf(-c[j], Wr[j], up);
 
   // 4. small key channels send c k_k into U
   bool sm = false;
@@ -166,7 +162,7 @@ __global__ __launch_bounds__(256) void k_step_lrb(const Args a) {
     sm = __builtin_isfinite(g) && (fabsf(kk) * g < theta);
     if (sm) {
 #pragma unroll
-      for (int j = 0; j < RANK; ++j) Ur[j] = (j < n) ? fmaf(kk, c[j], Ur[j]) : Ur[j];
+      for (int j = 0; j < RANK; ++j) Ur[j] = fmaf(kk, c[j], Ur[j]);
     }
   }
   // W transposed into LDS for the merge test and the rows
@@ -190,8 +186,7 @@ __global__ __launch_bounds__(256) void k_step_lrb(const Args a) {
       for (int v = 0; v < dv && !merged; ++v) {
         float col = 0.0f;
 #pragma unroll
-        for (int j = 0; j < RANK; ++j)
-          if (j < n) col = fmaf(Wt[j][v], Ur[j], col);
+        for (int j = 0; j < RANK; ++j) col = fmaf(Wt[j][v], Ur[j], col);
         if (col != 0.0f && fabsf(col) >= theta * sol[v]) merged = true;
       }
       if (merged) {
@@ -213,13 +208,13 @@ __global__ __launch_bounds__(256) void k_step_lrb(const Args a) {
   {
     float p[RANK];
 #pragma unroll
-    for (int j = 0; j < RANK; ++j) p[j] = (j < n_new && tid < DK) ? Ur[j] * qq : 0.0f;
-    (void)block_sum_vec<RANK>(p, 0.0f, z, red);
+    for (int j = 0; j < RANK; ++j) p[j] = Ur[j] * qq;   // all zero after a reset
+    (void)block_sum_vec<RANK>(p, 0.0f, z, P, red);
   }
   if (tid < dv) {
     float acc = 0.0f;
 #pragma unroll
-    for (int j = 0; j < RANK; ++j) acc = (j < n_new) ? fmaf(Wr[j], z[j], acc) : acc;
+    for (int j = 0; j < RANK; ++j) acc = fmaf(Wr[j], z[j], acc);
     lrl[tid] = acc;
   }
   // write the buffer back
@@ -233,11 +228,7 @@ __global__ __launch_bounds__(256) void k_step_lrb(const Args a) {
     smalll[tid] = sm ? 1 : 0;
     mflagl[tid] = merged ? 1 : 0;
   }
-  if (grown && tid < dv) {
-#pragma unroll
-    for (int j = 0; j < RANK; ++j)
-      if (j < r) Wg[tid * r + j] = Wr[j];
-  }
+  if (grown && tid < dv) Wg[tid * r + (n - 1)] = wnew;   // only the new column changed
   if (tid == 0) a.n[bh] = n_new;
   __syncthreads();
 
@@ -282,8 +273,7 @@ __global__ __launch_bounds__(256) void k_step_lrb(const Args a) {
         if ((mmask >> i) & 1u) {
           float col = 0.0f;
 #pragma unroll
-          for (int j = 0; j < RANK; ++j)
-            if (j < n) col = fmaf(Wt[j][v], Ut[j][k0 + i], col);
+          for (int j = 0; j < RANK; ++j) col = fmaf(Wt[j][v], Ut[j][k0 + i], col);
           sp[i] = sp[i] + col;
         }
     }
