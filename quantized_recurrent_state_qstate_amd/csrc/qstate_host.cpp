@@ -295,6 +295,7 @@ qs::Args base_args(const qstate_handle* h, const qstate_tensors* st) {
   a.dense_rpl = h->plan.dense_rpl;
   a.dense_lpr = h->plan.dense_lpr;
   a.keymap_eh = h->plan.keymap_eh;
+  a.load_prio = env_int("QSTATE_LOAD_PRIO", 1) ? 1 : 0;
   a.dense_threads = h->plan.dense_threads;
   a.prot_mask = h->plan.prot_mask;
   a.code_hblk = h->plan.code_hblk;

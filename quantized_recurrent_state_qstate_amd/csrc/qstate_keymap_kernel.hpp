@@ -76,6 +76,7 @@ __global__ __launch_bounds__(256) void k_step_keymap(const Args a) {
   constexpr int CW = EPL * QB / 32;        // code words per lane and row
   constexpr int HW = EH / 2;               // 16-bit value words per lane and row
   static_assert(EH % 2 == 0, "protected slots come in dword pairs");
+  if (a.load_prio) __builtin_amdgcn_s_setprio(3);   // raised until the loads are issued
   const int lane = threadIdx.x & (LPR - 1);
   const int g = threadIdx.x / LPR;         // row group: one row per workgroup chunk
 
@@ -144,6 +145,7 @@ __global__ __launch_bounds__(256) void k_step_keymap(const Args a) {
     }
   }
   __syncthreads();
+  if (a.load_prio) __builtin_amdgcn_s_setprio(0);
   if (!row_ok) return;   // after the barrier: whole row groups only
 
   const float* kc = lc[0] + lane * EPL;

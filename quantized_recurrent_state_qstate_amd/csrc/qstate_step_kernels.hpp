@@ -197,6 +197,7 @@ __device__ __forceinline__ void dense_quant_rows(const Args& a, uint8_t* blk, ui
   const float beta = a.beta ? a.beta[bh] : 1.0f;
   KQ<EPL, (LPR == 8)> kq;
   stage_qk<EPL, LPR, INBF>(a, bh, lane8, lds, kq);
+  if (a.load_prio) __builtin_amdgcn_s_setprio(0);
   float o_row[RPL], s_row[RPL];
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
@@ -345,6 +346,7 @@ __device__ __forceinline__ void dense_prot_rows(const Args& a, uint8_t* blk, uin
   const float beta = a.beta ? a.beta[bh] : 1.0f;
   KQ<EPL, (LPR == 8)> kq;
   stage_qk<EPL, LPR, INBF>(a, bh, lane8, lds, kq);
+  if (a.load_prio) __builtin_amdgcn_s_setprio(0);
   float o_row[RPL];
   // one body per 16-bit format (a uniform branch around the rows)
   auto rows = [&](auto fmt) {
@@ -411,6 +413,10 @@ template <int QB, int RND, int DELTA, int EPL, int LPR, int RPL, int BDR, int DK
 __global__ __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(dense_min_waves<EPL, LPR, RPL, BDR, DKEY, INBF, DELTA>(), 8)))
 void k_step_dense(const Args a) {
+  // A starting wave runs at raised priority until its loads are issued, so
+  // its address arithmetic is not queued behind the rounding work of older
+  // waves and the memory pipeline stays fed.
+  if (a.load_prio) __builtin_amdgcn_s_setprio(3);
   const int lane8 = threadIdx.x & (LPR - 1);   // lane within the row group
   const int g = threadIdx.x / LPR;
   const int ng = blockDim.x / LPR;
