@@ -28,6 +28,10 @@
  *   delta rule (Gated DeltaNet), alpha = the (scalar) decay d:
  *       S <- alpha (S - beta S k k^T) + beta v k^T
  *          = alpha S + u k^T,      u = beta * (v - alpha * (S k))
+ *   delta rule with a decay per key channel (channel-gated, Kimi-Linear):
+ *       D = S diag(d),  S <- D - beta (D k) k^T + beta v k^T
+ *          = D + u k^T,            u = beta * (v - D k), D's entries being
+ *       the decayed values of the element update below
  *   readout: o = S_pre q, from the updated state before it is rounded.
  * Every step dequantizes the state, applies decay and update, computes o,
  * and requantizes (one fused kernel, one pass over the state in HBM).
@@ -108,7 +112,7 @@ typedef enum { QS_ROUND_NEAREST = 0, QS_ROUND_STOCHASTIC = 1 } qs_rounding;
 typedef struct {
   uint32_t abi_version;   /* QSTATE_ABI_VERSION */
   int32_t kind;           /* qs_kind */
-  int32_t decay_mode;     /* qs_decay_mode; the delta rule takes HEAD only */
+  int32_t decay_mode;     /* qs_decay_mode (both kinds) */
   int32_t B, H;           /* batch (>= 0; 0 = every call is a no-op), heads (>= 1);
                              B*H*dv*dk must stay below 2^35 */
   int32_t dk;             /* key dim: 64, 128 or 256 */

@@ -10,6 +10,9 @@ k = key channel):
 * delta rule (Gated DeltaNet):
   S_t = alpha_t (S_{t-1} - beta_t S_{t-1} k_t k_t^T) + beta_t v_t k_t^T,
   o_t = S_t q_t
+* delta rule with a decay per key channel (the channel-gated delta rule of
+  Kimi-Linear): with D = S_{t-1} diag(d_t),
+  S_t = D - beta_t (D k_t) k_t^T + beta_t v_t k_t^T; a scalar d is alpha above
 
 Shapes: S [..., dv, dk]; q, k [..., dk]; v [..., dv]; d [...] or [..., dk];
 beta, alpha [...].
@@ -34,10 +37,16 @@ def additive_step(S, q, k, v, d, beta=None):
 def delta_step(S, q, k, v, alpha, beta):
     S = np.asarray(S, np.float64)
     k = np.asarray(k, np.float64)
-    a = np.asarray(alpha, np.float64)[..., None, None]
+    alpha = np.asarray(alpha, np.float64)
     b = np.asarray(beta, np.float64)[..., None, None]
-    Sk = np.einsum("...vk,...k->...v", S, k)
-    S = a * (S - b * Sk[..., :, None] * k[..., None, :]) + b * np.asarray(v, np.float64)[..., :, None] * k[..., None, :]
+    if alpha.ndim == k.ndim:              # one decay per key channel
+        D = S * alpha[..., None, :]
+        Dk = np.einsum("...vk,...k->...v", D, k)
+        S = D - b * Dk[..., :, None] * k[..., None, :] + b * np.asarray(v, np.float64)[..., :, None] * k[..., None, :]
+    else:
+        a = alpha[..., None, None]
+        Sk = np.einsum("...vk,...k->...v", S, k)
+        S = a * (S - b * Sk[..., :, None] * k[..., None, :]) + b * np.asarray(v, np.float64)[..., :, None] * k[..., None, :]
     o = np.einsum("...vk,...k->...v", S, np.asarray(q, np.float64))
     return S, o
 

@@ -193,7 +193,6 @@ static uint64_t hp_row_bytes(const orc_cfg* c, int nhp) {
 static int check_cfg(const orc_cfg* c) {
   if (c->kind != 0 && c->kind != 1) return -1;
   if (c->decay_mode != 0 && c->decay_mode != 1) return -1;
-  if (c->kind == 1 && c->decay_mode != 0) return -1;
   if (c->B < 0 || c->H <= 0 || c->dk <= 0 || c->dv <= 0) return -1;
   if (c->qbits != 8 && c->qbits != 4) return -1;
   if (c->hp_dtype < 0 || c->hp_dtype > 2) return -1;
@@ -612,13 +611,25 @@ static void head_step(const orc_cfg* c, const layout_t* L, orc_state* st, int64_
     s_old[v] = scales[v];
     for (int k = 0; k < dk; ++k) sh[v * dk + k] = dequant_elem(c, &a, s_old[v], v, k);
   }
-  /* write vector */
+  /* write vector.  Delta rule with one decay per head (Gated DeltaNet):
+   * u = beta (v - alpha (S_hat k)).  With a decay per key channel (the
+   * channel-gated delta rule of Kimi-Linear, named in the LoReS abstract):
+   * u = beta (v - (S_hat diag(d)) k), the decayed values being exactly the
+   * ones the update adds u k^T to: (d_k s_v) code, or d_k value. */
   for (int v = 0; v < dv; ++v) {
     if (c->kind == 0) {
       u[v] = bt * vh[v];
-    } else {
+    } else if (c->decay_mode == 0) {
       float w = (float)dot_d(sh + (uint64_t)v * dk, kh, dk);
       u[v] = bt * (vh[v] - d[0] * w);
+    } else {
+      double w = 0.0;
+      for (int k = 0; k < dk; ++k) {
+        float dec = (a.slot[k] >= 0) ? (d[k] * s_old[v]) * (float)get_code(c, &a, v, a.slot[k])
+                                     : d[k] * sh[v * dk + k];
+        w += (double)dec * (double)kh[k];
+      }
+      u[v] = bt * (vh[v] - (float)w);
     }
   }
   /* low-rank bypass */

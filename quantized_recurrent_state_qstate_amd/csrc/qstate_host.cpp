@@ -110,8 +110,6 @@ qs_status validate(const qstate_config* c) {
   if (c->kind != QS_KIND_ADDITIVE && c->kind != QS_KIND_DELTA) return fail(QS_EINVAL, "kind %d", c->kind);
   if (c->decay_mode != QS_DECAY_HEAD && c->decay_mode != QS_DECAY_KEY)
     return fail(QS_EINVAL, "decay_mode %d", c->decay_mode);
-  if (c->kind == QS_KIND_DELTA && c->decay_mode != QS_DECAY_HEAD)
-    return fail(QS_EUNSUPPORTED, "the delta rule takes one decay per head");
   if (c->B < 0) return fail(QS_EINVAL, "B = %d", c->B);
   if (c->H < 1) return fail(QS_EINVAL, "H = %d", c->H);
   if (c->dk < 1 || c->dv < 1) return fail(QS_EINVAL, "dk = %d, dv = %d", c->dk, c->dv);

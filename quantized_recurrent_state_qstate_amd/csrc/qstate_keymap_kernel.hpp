@@ -168,13 +168,19 @@ __global__ __launch_bounds__(256) void k_step_keymap(const Args a) {
 
   float u;
   if constexpr (DELTA) {
-    float wc = 0.0f, wh = 0.0f;   // S_hat k = s * sum code k + sum value k
+    // head decay: S_hat k = s * sum code k + sum value k, u = beta (v - alpha
+    // S_hat k); key decay: u = beta (v - sum decayed k)
+    float wc = 0.0f, wh = 0.0f;
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) wc = fmaf(code_at(i), kc[i], wc);
+    for (int i = 0; i < EPL; ++i) wc = fmaf(DKEY ? (dc[i] * s_old) * code_at(i) : code_at(i), kc[i], wc);
 #pragma unroll
-    for (int i = 0; i < EH; ++i) wh = fmaf(hp_at(i), kh[i], wh);
-    const float wk = red_sum<LPR>(fmaf(s_old, wc, wh));
-    u = beta * (vin - dh * wk);
+    for (int i = 0; i < EH; ++i) wh = fmaf(DKEY ? dhk[i] * hp_at(i) : hp_at(i), kh[i], wh);
+    if constexpr (DKEY) {
+      u = beta * (vin - red_sum<LPR>(wc + wh));
+    } else {
+      const float wk = red_sum<LPR>(fmaf(s_old, wc, wh));
+      u = beta * (vin - dh * wk);
+    }
   } else {
     u = beta * vin;
   }

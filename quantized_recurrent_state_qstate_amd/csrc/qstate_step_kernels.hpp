@@ -209,16 +209,18 @@ __device__ __forceinline__ void dense_quant_rows(const Args& a, uint8_t* blk, ui
     // decay + update, readout, row maximum
     float u;
     if constexpr (DELTA) {
-      float wk = 0.0f;   // S_hat k = s * sum_k code_k k_k
+      // head decay: S_hat k = s * sum_k code_k k_k, u = beta (v - alpha S_hat k);
+      // key decay: u = beta (v - sum_k ((d_k s) code_k) k_k)
+      float wk = 0.0f;
 #pragma unroll
       for (int i = 0; i < EPL; ++i) {
         float c;
         if constexpr (QB == 8) c = (float)(int32_t)(int8_t)(w[r][i >> 2] >> (8 * (i & 3)));
         else c = (float)((int32_t)(w[r][i >> 3] << (28 - 4 * (i & 7))) >> 28);
-        wk = fmaf(c, kq.k(i), wk);
+        wk = fmaf(DKEY ? (df[i] * s_old[r]) * c : c, kq.k(i), wk);
       }
       wk = red_sum<LPR>(wk);
-      u = beta * (vin[r] - dh * (s_old[r] * wk));
+      u = DKEY ? beta * (vin[r] - wk) : beta * (vin[r] - dh * (s_old[r] * wk));
     } else {
       u = beta * vin[r];
     }
@@ -358,15 +360,15 @@ __device__ __forceinline__ void dense_prot_rows(const Args& a, uint8_t* blk, uin
     if (v >= a.dv) continue;
     float u;
     if constexpr (DELTA) {
-      float wk = 0.0f;
+      float wk = 0.0f;   // key decay: sum_k (d_k value_k) k_k
 #pragma unroll
       for (int i = 0; i < EPL; ++i) {
         const uint32_t bits = (hw[r][i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
         const float sh = is_bf16 ? bf16_bits_to_f32(bits) : f16_bits_to_f32(bits);
-        wk = fmaf(sh, kq.k(i), wk);
+        wk = fmaf(DKEY ? df[i] * sh : sh, kq.k(i), wk);
       }
       wk = red_sum<LPR>(wk);
-      u = beta * (vin[r] - dh * wk);
+      u = DKEY ? beta * (vin[r] - wk) : beta * (vin[r] - dh * wk);
     } else {
       u = beta * vin[r];
     }
@@ -522,11 +524,13 @@ __global__ __launch_bounds__(256) void k_step_mixed(const Args a) {
     }
     float u;
     if constexpr (DELTA) {
+      // head decay: u = beta (v - alpha S_hat k); key decay: u = beta (v -
+      // sum_k decayed_k k_k)
       float w = 0.0f;
 #pragma unroll
-      for (int i = 0; i < EPL; ++i) w = fmaf(sh[i], kf[i], w);
+      for (int i = 0; i < EPL; ++i) w = fmaf(a.decay_key ? dec[i] : sh[i], kf[i], w);
       w = sum8(w);
-      u = beta * (vin - df[0] * w);
+      u = a.decay_key ? beta * (vin - w) : beta * (vin - df[0] * w);
     } else {
       u = beta * vin;
     }

@@ -18,19 +18,12 @@ void launch_dense_one(const Args& a, hipStream_t s) {
 
 template <int QB, int RND, int DELTA, int EPL, int LPR, int RPL, int INBF>
 hipError_t launch_dense_rpl(const Args& a, hipStream_t s) {
-  if constexpr (DELTA) {
-    // the delta rule takes one decay per head
-    if (a.decay_key) return hipErrorInvalidValue;
-    if (a.bdr) launch_dense_one<QB, RND, DELTA, EPL, LPR, RPL, 1, 0, INBF>(a, s);
-    else launch_dense_one<QB, RND, DELTA, EPL, LPR, RPL, 0, 0, INBF>(a, s);
+  if (a.bdr) {
+    if (a.decay_key) launch_dense_one<QB, RND, DELTA, EPL, LPR, RPL, 1, 1, INBF>(a, s);
+    else launch_dense_one<QB, RND, DELTA, EPL, LPR, RPL, 1, 0, INBF>(a, s);
   } else {
-    if (a.bdr) {
-      if (a.decay_key) launch_dense_one<QB, RND, DELTA, EPL, LPR, RPL, 1, 1, INBF>(a, s);
-      else launch_dense_one<QB, RND, DELTA, EPL, LPR, RPL, 1, 0, INBF>(a, s);
-    } else {
-      if (a.decay_key) launch_dense_one<QB, RND, DELTA, EPL, LPR, RPL, 0, 1, INBF>(a, s);
-      else launch_dense_one<QB, RND, DELTA, EPL, LPR, RPL, 0, 0, INBF>(a, s);
-    }
+    if (a.decay_key) launch_dense_one<QB, RND, DELTA, EPL, LPR, RPL, 0, 1, INBF>(a, s);
+    else launch_dense_one<QB, RND, DELTA, EPL, LPR, RPL, 0, 0, INBF>(a, s);
   }
   return hipGetLastError();
 }
@@ -83,18 +76,12 @@ template <int QB, int RND, int DELTA, int LPR, int EH>
 hipError_t launch_keymap_eh(const Args& a, hipStream_t s) {
   constexpr int EPL = 128 / LPR;
   const dim3 grid((uint32_t)((uint64_t)a.B * (uint64_t)a.H * (uint64_t)a.row_chunks));
-  if constexpr (DELTA) {
-    if (a.decay_key) return hipErrorInvalidValue;
-    if (a.bdr) hipLaunchKernelGGL((k_step_keymap<QB, RND, DELTA, EPL, LPR, EH, 1, 0>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((k_step_keymap<QB, RND, DELTA, EPL, LPR, EH, 0, 0>), grid, dim3(256), 0, s, a);
+  if (a.bdr) {
+    if (a.decay_key) hipLaunchKernelGGL((k_step_keymap<QB, RND, DELTA, EPL, LPR, EH, 1, 1>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_step_keymap<QB, RND, DELTA, EPL, LPR, EH, 1, 0>), grid, dim3(256), 0, s, a);
   } else {
-    if (a.bdr) {
-      if (a.decay_key) hipLaunchKernelGGL((k_step_keymap<QB, RND, DELTA, EPL, LPR, EH, 1, 1>), grid, dim3(256), 0, s, a);
-      else hipLaunchKernelGGL((k_step_keymap<QB, RND, DELTA, EPL, LPR, EH, 1, 0>), grid, dim3(256), 0, s, a);
-    } else {
-      if (a.decay_key) hipLaunchKernelGGL((k_step_keymap<QB, RND, DELTA, EPL, LPR, EH, 0, 1>), grid, dim3(256), 0, s, a);
-      else hipLaunchKernelGGL((k_step_keymap<QB, RND, DELTA, EPL, LPR, EH, 0, 0>), grid, dim3(256), 0, s, a);
-    }
+    if (a.decay_key) hipLaunchKernelGGL((k_step_keymap<QB, RND, DELTA, EPL, LPR, EH, 0, 1>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_step_keymap<QB, RND, DELTA, EPL, LPR, EH, 0, 0>), grid, dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }

@@ -64,7 +64,6 @@ def test_plan_random_key_maps(qbits, hp):
 BAD = [
     (dict(kind=5), _lib.QS_EINVAL),
     (dict(decay_mode=3), _lib.QS_EINVAL),
-    (dict(kind="delta", decay_mode="key"), _lib.QS_EUNSUPPORTED),
     (dict(B=-1), _lib.QS_EINVAL),
     (dict(H=0), _lib.QS_EINVAL),
     (dict(dk=96), _lib.QS_EUNSUPPORTED),

@@ -87,6 +87,36 @@ def test_gated_deltanet_transition_product():
         np.testing.assert_allclose(outs[t], S @ q[t], rtol=1e-11, atol=1e-12)
 
 
+def test_channel_gated_delta_transition_product():
+    """Delta rule with a decay per key channel: S_t = S_{t-1} M_t + beta_t v_t k_t^T
+    with M_t = diag(d_t) (I - beta_t k_t k_t^T), checked against the dense product."""
+    r = _rng(13)
+    T, dv, dk = 7, 4, 6
+    q, v = r.standard_normal((T, dk)), r.standard_normal((T, dv))
+    k = r.standard_normal((T, dk))
+    k /= np.linalg.norm(k, axis=1, keepdims=True)
+    d = 1 / (1 + np.exp(-r.standard_normal((T, dk)) - 2))
+    be = 1 / (1 + np.exp(-r.standard_normal(T)))
+    S0 = r.standard_normal((dv, dk))
+    states, outs = fp64.run("delta", S0, q, k, v, d, betas=be)
+    M = [np.diag(d[t]) @ (np.eye(dk) - be[t] * np.outer(k[t], k[t])) for t in range(T)]
+    for t in range(T):
+        S = S0.copy()
+        for tau in range(t + 1):
+            S = S @ M[tau]
+        for s in range(t + 1):
+            term = be[s] * np.outer(v[s], k[s])
+            for tau in range(s + 1, t + 1):
+                term = term @ M[tau]
+            S = S + term
+        np.testing.assert_allclose(states[t], S, rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(outs[t], S @ q[t], rtol=1e-11, atol=1e-12)
+    # equal channel decays reduce to the scalar-decay delta rule
+    Sa, oa = fp64.delta_step(S0, q[0], k[0], v[0], np.full(dk, 0.7), be[0])
+    Sb, ob = fp64.delta_step(S0, q[0], k[0], v[0], 0.7, be[0])
+    np.testing.assert_allclose(Sa, Sb, rtol=1e-13, atol=1e-14)
+
+
 def test_delta_special_cases():
     r = _rng(4)
     dv, dk = 4, 6
@@ -114,6 +144,9 @@ CASES = {
                                 map_mode="key", hp_dtype="fp16"),
     "gdn_int4_keymap_bdr": dict(kind="delta", decay_mode="head", rounding="sr", qbits=4, bdr=True,
                                 map_mode="key", hp_dtype="bf16"),
+    "kda_sr": dict(kind="delta", decay_mode="key", rounding="sr"),
+    "kda_keymap_fp16_rtn": dict(kind="delta", decay_mode="key", rounding="rtn", map_mode="key",
+                                hp_dtype="fp16"),
 }
 
 
@@ -138,7 +171,8 @@ def _inputs(cfg, r, t):
     v = r.standard_normal((B, H, dv)).astype(np.float32)
     if cfg.kind == "delta":
         k = (k / np.linalg.norm(k, axis=-1, keepdims=True)).astype(np.float32)
-        d = (1 / (1 + np.exp(-r.standard_normal((B, H)) - 3))).astype(np.float32)
+        shape = (B, H, dk) if cfg.decay_mode == "key" else (B, H)
+        d = (1 / (1 + np.exp(-r.standard_normal(shape) - 3))).astype(np.float32)
         beta = (1 / (1 + np.exp(-r.standard_normal((B, H))))).astype(np.float32)
     else:
         shape = (B, H, dk) if cfg.decay_mode == "key" else (B, H)
