@@ -76,6 +76,21 @@
  *   Element update: S_pre = fma(u_v, k_k, (d_k * s_v) * code) for a
  *   quantized channel, fma(u_v, k_k, d_k * value) for a protected one.
  *
+ * Low-Rank Bypass [PU] (lrb_rank r > 0, map NONE, both kinds), per (b,h),
+ * with s_v the row scales on entry and n the basis size:
+ *   1. U[k][:] *= d_k (the buffer decays with the state);
+ *   2. delta rule only: u = beta * (v - w), w the decayed effective state
+ *      times k: (decayed S_hat) k + W (U^T k);
+ *   3. while n < r: the part of u orthogonal to W's n columns (two
+ *      Gram-Schmidt passes) becomes column n, normalised, when its norm
+ *      exceeds 2^-10 |u|;
+ *   4. c = W^T u; key channel k is small when |k_k| * max_v |u_v| / s_v <
+ *      theta: it adds k_k c to U[k] and only (u - W c) k_k to S_pre;
+ *   5. when (step+1) % period == 0, a channel whose buffered column
+ *      reaches theta * s_v in some row is added to S_pre and cleared; an
+ *      all-clear buffer resets n to 0;
+ *   6. o gains W (U^T q); requantization sees S_pre with the merged columns.
+ *
  * Conventions: every call is asynchronous on `stream` (a hipStream_t; NULL
  * = the null stream).  The return code reports errors found on the host
  * (arguments) and launch failures; a fault inside a kernel surfaces at the
@@ -127,7 +142,7 @@ typedef struct {
   int32_t sr_bits;        /* stochastic rounding: 16 or 8 random bits per element */
   int32_t bdr;            /* 1 = bounded directional rounding [PU] */
   float bdr_bound;        /* tolerated reversal in LSB (>= 0) */
-  int32_t lrb_rank;       /* 0 = off; 1..16 = low-rank bypass rank [PU] (additive, map NONE) */
+  int32_t lrb_rank;       /* 0 = off; 1..16 = low-rank bypass rank [PU] (map NONE) */
   int32_t lrb_period;     /* merge when (step+1) % period == 0 */
   float lrb_theta;        /* merge / smallness threshold in LSB (> 0) */
   uint64_t seed;          /* Philox key for stochastic rounding */

@@ -201,8 +201,7 @@ static int check_cfg(const orc_cfg* c) {
   if (c->rounding != 0 && c->rounding != 1) return -1;
   if (c->rounding == 1 && c->sr_bits != 16 && c->sr_bits != 8) return -1;
   if (c->lrb_rank < 0) return -1;
-  if (c->lrb_rank > 0 && (c->kind != 0 || c->map_mode != 0 || c->lrb_period <= 0))
-    return -1;
+  if (c->lrb_rank > 0 && (c->map_mode != 0 || c->lrb_period <= 0)) return -1;
   return 0;
 }
 
@@ -478,10 +477,13 @@ static double dot_d(const float* a, const float* b, int n) {
 /* ------------------------------------------------------------------------ */
 /* Low-Rank Bypass (abstract of the page on preserving updates: small        */
 /* updates accumulate in a compact low-rank buffer whose sufficiently large  */
-/* elements are merged into the state periodically).  Additive recurrences   */
-/* only.  Buffer of one head: L = W U^T, W [dv][r] with orthonormal columns  */
-/* 0..n-1, U [dk][r].  Reading taken (the page gives one sentence):          */
-/*  1. the buffer decays with the state: U[k][:] *= d[k];                    */
+/* elements are merged into the state periodically).  The page names Gated  */
+/* DeltaNet, GLA, Mamba2 and RetNet, so both kinds.  Buffer of one head:     */
+/* L = W U^T, W [dv][r] with orthonormal columns 0..n-1, U [dk][r].  Reading */
+/* taken (the page gives one sentence):                                      */
+/*  1. the buffer decays with the state: U[k][:] *= d[k] (lrb_decay, done    */
+/*     before the write vector, which for the delta rule reads the decayed   */
+/*     buffer);                                                              */
 /*  2. while n < r, the write vector u (Gram-Schmidt, two passes, against the */
 /*     basis) adds a basis column when its new part is above 2^-10 |u|;      */
 /*  3. coefficients c = W^T u, remainder u_perp = u - W c;                   */
@@ -493,15 +495,19 @@ static double dot_d(const float* a, const float* b, int n) {
 /*     whole buffer is clear the basis is reset (n = 0).                     */
 /* Outputs: per-channel flags, u_perp, merged columns [dv][dk] (0 if none). */
 /* ------------------------------------------------------------------------ */
+static void lrb_decay(const orc_cfg* c, float* U, const float* d) {
+  const int dk = c->dk, r = c->lrb_rank;
+  for (int k = 0; k < dk; ++k)
+    for (int j = 0; j < r; ++j) U[k * r + j] = d[k] * U[k * r + j];
+}
+
+/* Steps 2-5 (the buffer has decayed already). */
 static void lrb_phase(const orc_cfg* c, float* W, float* U, int32_t* np_, const float* u,
-                      const float* kk, const float* d, const float* s_old, uint64_t step,
+                      const float* kk, const float* s_old, uint64_t step,
                       int* small, float* u_perp, float* merged, int* merge_flag) {
   const int dk = c->dk, dv = c->dv, r = c->lrb_rank;
   const float theta = c->lrb_theta;
   int n = *np_;
-  /* 1. decay */
-  for (int k = 0; k < dk; ++k)
-    for (int j = 0; j < r; ++j) U[k * r + j] = d[k] * U[k * r + j];
   /* 2. grow the basis */
   if (n < r) {
     float* y = (float*)malloc(sizeof(float) * (size_t)dv);
@@ -611,17 +617,38 @@ static void head_step(const orc_cfg* c, const layout_t* L, orc_state* st, int64_
     s_old[v] = scales[v];
     for (int k = 0; k < dk; ++k) sh[v * dk + k] = dequant_elem(c, &a, s_old[v], v, k);
   }
+  /* the low-rank buffer decays first: the delta rule reads it decayed */
+  float* W = NULL;
+  float* U = NULL;
+  float* wb = (float*)calloc((size_t)dv, sizeof(float));
+  if (r > 0) {
+    W = st->W + (uint64_t)bh * dv * r;
+    U = st->U + (uint64_t)bh * dk * r;
+    lrb_decay(c, U, d);
+    /* buffer part of the decayed effective state times k:
+     * wb_v = sum_j W[v][j] zk_j, zk = U^T k (fp64 sums, rounded once) */
+    if (c->kind == 1) {
+      const int n = st->n[bh];
+      for (int j = 0; j < n; ++j) {
+        double zk = 0.0;
+        for (int k = 0; k < dk; ++k) zk += (double)U[k * r + j] * (double)kh[k];
+        for (int v = 0; v < dv; ++v) wb[v] = fmaf(W[v * r + j], (float)zk, wb[v]);
+      }
+    }
+  }
   /* write vector.  Delta rule with one decay per head (Gated DeltaNet):
    * u = beta (v - alpha (S_hat k)).  With a decay per key channel (the
    * channel-gated delta rule of Kimi-Linear, named in the LoReS abstract):
    * u = beta (v - (S_hat diag(d)) k), the decayed values being exactly the
-   * ones the update adds u k^T to: (d_k s_v) code, or d_k value. */
+   * ones the update adds u k^T to: (d_k s_v) code, or d_k value.  With the
+   * low-rank buffer the rule acts on the effective state: wb is added to the
+   * decayed state's product with k. */
   for (int v = 0; v < dv; ++v) {
     if (c->kind == 0) {
       u[v] = bt * vh[v];
     } else if (c->decay_mode == 0) {
       float w = (float)dot_d(sh + (uint64_t)v * dk, kh, dk);
-      u[v] = bt * (vh[v] - d[0] * w);
+      u[v] = (r > 0) ? bt * (vh[v] - (d[0] * w + wb[v])) : bt * (vh[v] - d[0] * w);
     } else {
       double w = 0.0;
       for (int k = 0; k < dk; ++k) {
@@ -629,21 +656,17 @@ static void head_step(const orc_cfg* c, const layout_t* L, orc_state* st, int64_
                                      : d[k] * sh[v * dk + k];
         w += (double)dec * (double)kh[k];
       }
-      u[v] = bt * (vh[v] - (float)w);
+      u[v] = (r > 0) ? bt * (vh[v] - ((float)w + wb[v])) : bt * (vh[v] - (float)w);
     }
   }
-  /* low-rank bypass */
+  /* low-rank bypass, steps 2-5 */
   int* small = (int*)calloc((size_t)dk, sizeof(int));
   int* mflag = (int*)calloc((size_t)dk, sizeof(int));
   float* u_perp = (float*)malloc(sizeof(float) * (size_t)dv);
   float* merged = NULL;
-  float* W = NULL;
-  float* U = NULL;
   if (r > 0) {
-    W = st->W + (uint64_t)bh * dv * r;
-    U = st->U + (uint64_t)bh * dk * r;
     merged = (float*)malloc(sizeof(float) * (size_t)dv * (size_t)dk);
-    lrb_phase(c, W, U, &st->n[bh], u, kh, d, s_old, step, small, u_perp, merged, mflag);
+    lrb_phase(c, W, U, &st->n[bh], u, kh, s_old, step, small, u_perp, merged, mflag);
   }
   /* decay + update (+ merged buffer columns).  The decay multiplies the
    * row scale before the code: (d_k * s_v) * code for a quantized channel,
@@ -678,6 +701,7 @@ static void head_step(const orc_cfg* c, const layout_t* L, orc_state* st, int64_
     scales[v] = requantize_row(c, &a, bh, v, sp + (uint64_t)v * dk, sh + (uint64_t)v * dk, step);
 
   free(z);
+  free(wb);
   free(merged);
   free(u_perp);
   free(small);

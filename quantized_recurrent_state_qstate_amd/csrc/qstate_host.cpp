@@ -134,7 +134,6 @@ qs_status validate(const qstate_config* c) {
   if (c->lrb_rank < 0) return fail(QS_EINVAL, "lrb_rank %d", c->lrb_rank);
   if (c->lrb_rank > 0) {
     if (c->lrb_rank > kMaxRank) return fail(QS_EUNSUPPORTED, "lrb_rank %d (max %d)", c->lrb_rank, kMaxRank);
-    if (c->kind != QS_KIND_ADDITIVE) return fail(QS_EUNSUPPORTED, "low-rank bypass needs the additive kind");
     if (c->map_mode != QS_MAP_NONE) return fail(QS_EUNSUPPORTED, "low-rank bypass needs map_mode NONE");
     if (c->lrb_period < 1) return fail(QS_EINVAL, "lrb_period %d", c->lrb_period);
     if (!std::isfinite(c->lrb_theta) || c->lrb_theta <= 0.0f) return fail(QS_EINVAL, "lrb_theta %g", c->lrb_theta);

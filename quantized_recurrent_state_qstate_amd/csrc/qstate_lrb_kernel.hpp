@@ -1,7 +1,8 @@
 // Step kernel with the Low-Rank Bypass (abstract of "Preserving Updates in
 // Low-Bit Recurrent State Quantization": small updates accumulate in a
 // compact low-rank buffer whose sufficiently large elements are merged into
-// the state periodically).  Additive recurrences, map NONE.
+// the state periodically).  Both kinds the page names (additive: GLA,
+// Mamba2, RetNet; delta rule: Gated DeltaNet), map NONE.
 //
 // Buffer of one head: L = W U^T, W [dv][r] with orthonormal columns
 // 0..n-1, U [dk][r].  One workgroup of 256 threads per head (dv, dk <= 256):
@@ -9,7 +10,10 @@
 // RANK >= r entries each.  Phase A follows the buffer steps (decay U, grow
 // the basis while n < r, project u on the basis, route the in-span part of
 // small key channels to U, merge on a merge step, buffer readout); the r
-// dot products of a projection are one vector reduction.  Phase B is the
+// dot products of a projection are one vector reduction.  For the delta
+// rule a phase before A forms the write vector from the decayed effective
+// state: each row's codes give w_v = (decayed S_hat k)_v, the decayed buffer
+// adds W (U^T k), and u = beta (v - that).  Phase B is the
 // row step of the dense kernel: 8 lanes per row, every row's codes loaded
 // first, u_perp on small channels, merged buffer columns added before
 // rounding.
@@ -62,7 +66,7 @@ __device__ __forceinline__ float pick(const float (&p)[R], int j) {
 
 }  // namespace
 
-template <int QB, int RND, int EPL, int RANK, int BDR, int DKEY>
+template <int QB, int RND, int DELTA, int EPL, int RANK, int BDR, int DKEY>
 __global__ __launch_bounds__(256) void k_step_lrb(const Args a) {
   constexpr int DK = EPL * 8;
   constexpr int SRB = sr_bits_of<RND>();
@@ -78,6 +82,7 @@ __global__ __launch_bounds__(256) void k_step_lrb(const Args a) {
   __shared__ __align__(16) float Wt[RANK][256];   // W transposed, for merges and rows
   __shared__ __align__(16) float Ut[RANK][DK];    // U rows of merged channels (before clearing)
   __shared__ __align__(16) float ul[256], upl[256], sol[256], lrl[256];
+  __shared__ __align__(16) float wl[DELTA ? 256 : 1];   // delta rule: decayed S_hat k per row
   __shared__ __align__(16) float kl[DK], ql[DK], dl[DK];
   __shared__ __align__(16) float P[RANK * 256];   // reduction transpose
   __shared__ float red[RANK + 4];
@@ -99,7 +104,8 @@ __global__ __launch_bounds__(256) void k_step_lrb(const Args a) {
   }
   if (tid < dv) {
     const uint64_t row = (uint64_t)bh * (uint64_t)dv + (uint64_t)tid;
-    uv = beta * load_in1(a.v, a.in_bf16, row);
+    uv = load_in1(a.v, a.in_bf16, row);
+    if constexpr (!DELTA) uv = beta * uv;
     so = ld_nt(a.scales + row);
   }
   if (tid < DK) {
@@ -108,9 +114,71 @@ __global__ __launch_bounds__(256) void k_step_lrb(const Args a) {
     dd = DKEY ? a.decay[(uint64_t)bh * DK + tid] : a.decay[bh];
   }
 
+  if constexpr (DELTA) {
+    // rows: w_v = sum_k (decayed S_hat)[v][k] k_k, 8 lanes per row, four
+    // rows' codes in flight at a time.  With one decay per head the sum is
+    // over S_hat and alpha multiplies it below.
+    if (tid < DK) {
+      kl[tid] = kk;
+      dl[tid] = dd;
+    }
+    if (tid < dv) sol[tid] = so;
+    __syncthreads();
+    const int lane8 = tid & 7;
+    const int k0 = lane8 * EPL;
+    float kf[EPL], df[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      kf[i] = kl[k0 + i];
+      df[i] = dl[k0 + i];
+    }
+    const uint8_t* gc = code_block(a, b, h);
+    for (int v0 = tid >> 3; v0 < dv; v0 += 128) {
+      uint32_t cw[4][CW];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+        if (v0 + 32 * rr < dv)
+          load_bytes<EPL * QB / 8, false>(gc + (uint64_t)(v0 + 32 * rr) * (DK * QB / 8) + k0 * QB / 8, cw[rr]);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int v = v0 + 32 * rr;
+        if (v < dv) {   // uniform over the 8 lanes of a row
+          const float s = sol[v];
+          float w = 0.0f;
+#pragma unroll
+          for (int i = 0; i < EPL; ++i) {
+            float cf;
+            if constexpr (QB == 8) cf = (float)(int32_t)(int8_t)(cw[rr][i >> 2] >> (8 * (i & 3)));
+            else cf = (float)((int32_t)(cw[rr][i >> 3] << (28 - 4 * (i & 7))) >> 28);
+            const float dec = DKEY ? (df[i] * s) * cf : s * cf;
+            w = fmaf(dec, kf[i], w);
+          }
+          w = red_sum<8>(w);
+          if (lane8 == 0) wl[v] = w;
+        }
+      }
+    }
+  }
+
   // 1. the buffer decays with the state (decay acts on the key side)
 #pragma unroll
   for (int j = 0; j < RANK; ++j) Ur[j] = dd * Ur[j];
+
+  if constexpr (DELTA) {
+    // the decayed buffer's part: W (U^T k); U's columns from n on are zero,
+    // so their coefficients are exact zeros.  Then u = beta (v - w_eff).
+    float p[RANK], zk[RANK];
+#pragma unroll
+    for (int j = 0; j < RANK; ++j) p[j] = Ur[j] * kk;
+    (void)block_sum_vec<RANK>(p, 0.0f, zk, P, red);   // its barriers also publish wl
+    if (tid < dv) {
+      float wb = 0.0f;
+#pragma unroll
+      for (int j = 0; j < RANK; ++j) wb = fmaf(Wr[j], zk[j], wb);
+      const float w = wl[tid];
+      uv = DKEY ? beta * (uv - (w + wb)) : beta * (uv - (a.decay[bh] * w + wb));
+    }
+  }
 
   // 2. grow the basis while n < r (two Gram-Schmidt passes)
   bool grown = false;

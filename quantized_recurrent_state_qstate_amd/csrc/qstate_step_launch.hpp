@@ -54,22 +54,23 @@ hipError_t launch_mixed_t(const Args& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int QB, int RND, int EPL, int RANK>
+template <int QB, int RND, int DELTA, int EPL, int RANK>
 hipError_t launch_lrb_r(const Args& a, hipStream_t s) {
   const dim3 grid((uint32_t)((uint64_t)a.B * (uint64_t)a.H));
   if (a.bdr) {
-    if (a.decay_key) hipLaunchKernelGGL((k_step_lrb<QB, RND, EPL, RANK, 1, 1>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((k_step_lrb<QB, RND, EPL, RANK, 1, 0>), grid, dim3(256), 0, s, a);
+    if (a.decay_key) hipLaunchKernelGGL((k_step_lrb<QB, RND, DELTA, EPL, RANK, 1, 1>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_step_lrb<QB, RND, DELTA, EPL, RANK, 1, 0>), grid, dim3(256), 0, s, a);
   } else {
-    if (a.decay_key) hipLaunchKernelGGL((k_step_lrb<QB, RND, EPL, RANK, 0, 1>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((k_step_lrb<QB, RND, EPL, RANK, 0, 0>), grid, dim3(256), 0, s, a);
+    if (a.decay_key) hipLaunchKernelGGL((k_step_lrb<QB, RND, DELTA, EPL, RANK, 0, 1>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_step_lrb<QB, RND, DELTA, EPL, RANK, 0, 0>), grid, dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }
 
-template <int QB, int RND, int EPL>
+template <int QB, int RND, int DELTA, int EPL>
 hipError_t launch_lrb_t(const Args& a, hipStream_t s) {
-  return a.lrb_rank <= 8 ? launch_lrb_r<QB, RND, EPL, 8>(a, s) : launch_lrb_r<QB, RND, EPL, 16>(a, s);
+  return a.lrb_rank <= 8 ? launch_lrb_r<QB, RND, DELTA, EPL, 8>(a, s)
+                         : launch_lrb_r<QB, RND, DELTA, EPL, 16>(a, s);
 }
 
 template <int QB, int RND, int DELTA, int LPR, int EH>
@@ -116,13 +117,11 @@ hipError_t launch_fam(int family, const Args& a, hipStream_t s) {
       case 128: return launch_mixed_t<QB, RND, DELTA, 16>(a, s);
       case 256: return launch_mixed_t<QB, RND, DELTA, 32>(a, s);
     }
-  } else if constexpr (!DELTA) {
-    if (family == kFamLrb) {
-      switch (a.dk) {
-        case 64: return launch_lrb_t<QB, RND, 8>(a, s);
-        case 128: return launch_lrb_t<QB, RND, 16>(a, s);
-        case 256: return launch_lrb_t<QB, RND, 32>(a, s);
-      }
+  } else if (family == kFamLrb) {
+    switch (a.dk) {
+      case 64: return launch_lrb_t<QB, RND, DELTA, 8>(a, s);
+      case 128: return launch_lrb_t<QB, RND, DELTA, 16>(a, s);
+      case 256: return launch_lrb_t<QB, RND, DELTA, 32>(a, s);
     }
   }
   return hipErrorInvalidValue;

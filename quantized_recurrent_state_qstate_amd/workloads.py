@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for the five decode workloads.
+"""Seeded synthetic inputs for the six decode workloads.
 
 Input generation only: random draws with the stated laws, the Mamba2
 discretization (decay = exp(dt * A), beta = dt) that forms the step's
@@ -27,6 +27,9 @@ Workloads (S[v][k] orientation; v = value / output channel, k = key):
   gdn_large   Gated DeltaNet B=1024 H=32 dk=dv=128 T=256, inputs as gdn;
               per head the 10% slowest key channels (13 of 128) in fp16,
               others int8, SR.
+  gdn_int4    Gated DeltaNet B=64 H=32 dk=dv=128 T=1024, inputs as gdn;
+              int4 + low-rank bypass (rank 8, merge every 64 steps, 0.5 LSB)
+              + BDR over nearest rounding, as gla_int4.
 """
 from __future__ import annotations
 
@@ -144,4 +147,7 @@ WORKLOADS = {
                          lrb_theta=0.5, decay_mu=5.0, seed_base=1004),
     "gdn_large": Workload("gdn_large", "gdn", B=1024, H=32, dk=128, dv=128, T=256, in_dtype="bf16",
                           map_mode="key", map_frac=0.10, hp_dtype="fp16", seed_base=1005),
+    "gdn_int4": Workload("gdn_int4", "gdn", B=64, H=32, dk=128, dv=128, T=1024, in_dtype="bf16",
+                         qbits=4, rounding="nearest", bdr=True, lrb_rank=8, lrb_period=64,
+                         lrb_theta=0.5, seed_base=1006),
 }

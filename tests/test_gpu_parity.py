@@ -142,6 +142,7 @@ SMALL = {
     "mamba2": dict(B=3, T=6),
     "gla_int4": dict(B=2, T=6),
     "gdn_large": dict(B=2, T=6),
+    "gdn_int4": dict(B=2, T=6),
 }
 
 
@@ -153,10 +154,11 @@ def test_step_teacher_forced_small(name):
     run_teacher_forced(w, p["B"], p["T"], warm=4 if name != "gla_small" else 0)
 
 
-def test_gla_int4_merge_steps():
-    """Low-rank bypass across a merge (period 64: steps 63 and 127)."""
-    w = WORKLOADS["gla_int4"]
-    _log("[parity] gla_int4 merge steps 60..66")
+@pytest.mark.parametrize("name", ["gla_int4", "gdn_int4"])
+def test_lrb_merge_steps(name):
+    """Low-rank bypass across a merge (period 64: step 63)."""
+    w = WORKLOADS[name]
+    _log(f"[parity] {name} merge steps 60..66")
     run_teacher_forced(w, 2, 7, warm=60)
 
 
@@ -262,10 +264,10 @@ def test_dequantize_with_buffer():
 
 
 # Full size, in the benchmark's launch configuration, sampled heads.
-FULL_STEPS = {"gdn": 2, "mamba2": 2, "gla_int4": 2, "gdn_large": 1}
+FULL_STEPS = {"gdn": 2, "mamba2": 2, "gla_int4": 2, "gdn_large": 1, "gdn_int4": 2}
 
 
-@pytest.mark.parametrize("name", ["gdn", "mamba2", "gla_int4", "gdn_large"])
+@pytest.mark.parametrize("name", ["gdn", "mamba2", "gla_int4", "gdn_large", "gdn_int4"])
 def test_full_size_sampled_heads(name):
     w = WORKLOADS[name]
     r = np.random.default_rng(5)
@@ -291,6 +293,16 @@ EDGE = {
     "sr_bdr_int8": dict(kind="additive", decay_mode="key", dk=128, dv=32, H=2, B=2, qbits=8, bdr=True),
     "lrb_headdecay_sr": dict(kind="additive", decay_mode="head", dk=64, dv=48, H=2, B=2, qbits=8,
                              lrb_rank=4, lrb_period=3),
+    # low-rank bypass under the delta rule: growth, buffered channels and
+    # merges within the 8 steps; rank bounds 8 and 16, dk 64 / 128 / 256
+    "lrb_delta_int4_bdr": dict(kind="delta", decay_mode="head", dk=128, dv=128, H=2, B=2, qbits=4,
+                               rounding="nearest", bdr=True, lrb_rank=8, lrb_period=3),
+    "lrb_delta_keydecay_sr_r12": dict(kind="delta", decay_mode="key", dk=64, dv=48, H=2, B=2, qbits=8,
+                                      lrb_rank=12, lrb_period=4),
+    "lrb_delta_dk256_dv200": dict(kind="delta", decay_mode="head", dk=256, dv=200, H=2, B=1, qbits=4,
+                                  rounding="nearest", lrb_rank=8, lrb_period=5),
+    "lrb_delta_keydecay_int4_sr_bdr_r16": dict(kind="delta", decay_mode="key", dk=128, dv=64, H=2, B=2,
+                                               qbits=4, bdr=True, lrb_rank=16, lrb_period=3),
     # key maps in storage order: few, half and most channels protected
     "keymap_fp16_delta_sparse": dict(kind="delta", decay_mode="head", dk=128, dv=128, H=2, B=2, qbits=8,
                                      map_mode="key", hp_dtype="fp16", map_density=0.08),

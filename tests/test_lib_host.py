@@ -81,7 +81,6 @@ BAD = [
     (dict(bdr_bound=float("nan")), _lib.QS_EINVAL),
     (dict(lrb_rank=-1), _lib.QS_EINVAL),
     (dict(lrb_rank=17), _lib.QS_EUNSUPPORTED),
-    (dict(lrb_rank=4, kind="delta"), _lib.QS_EUNSUPPORTED),
     (dict(lrb_rank=4, lrb_period=0), _lib.QS_EINVAL),
     (dict(lrb_rank=4, lrb_theta=0.0), _lib.QS_EINVAL),
     (dict(lrb_rank=4, map_mode="head", map=np.zeros(2, np.uint8)), _lib.QS_EUNSUPPORTED),
