@@ -16,6 +16,10 @@
 // over k inside one row, so it is three DPP steps inside the 8-lane group;
 // rows never exchange data.  A 256-thread workgroup covers 32 rows of one
 // head per row a lane holds (two rows per lane when a head has more than 32).
+// Within a wave the row groups take consecutive rows (group g row g, g + 8,
+// ...), so each state load of the wave covers one contiguous stretch of
+// rows, and a 16-bit row is split into 128-byte pieces that 8 lanes cover
+// whole (lane j: bytes 16j + 128i); every access moves whole cache lines.
 #pragma once
 #include <type_traits>
 
@@ -100,29 +104,39 @@ __device__ __forceinline__ void row_scale_fast(float m, float& scale, float& inv
   invb = ok ? iz * (float)(1u << SRB) : 0.0f;
 }
 
-// A lane's k and q slices (EPL keys from k0).  REG: held in registers, for
-// lanes that compute several rows; otherwise read from the LDS copy where
-// they are used, which keeps 2*EPL registers free.
-template <int EPL, bool REG>
+// A lane's k and q slices (EPL keys from k0, or the split slice of a 16-bit
+// row: keys 64 (i / 8) + 8 lane + i % 8).  REG: held in registers, for lanes
+// that compute several rows; otherwise read from the LDS copy where they are
+// used, which keeps 2*EPL registers free.
+template <int EPL, bool REG, bool SPLIT = false>
 struct KQ {
   float kr[REG ? EPL : 1], qr[REG ? EPL : 1];
-  const float* kl;
+  const float* kl;   // the lane's first key in LDS
   const float* ql;
+  static __device__ __forceinline__ int off(int i) { return SPLIT ? 64 * (i >> 3) + (i & 7) : i; }
   __device__ __forceinline__ float k(int i) const {
     if constexpr (REG) return kr[i];
-    else return kl[i];
+    else return kl[off(i)];
   }
   __device__ __forceinline__ float q(int i) const {
     if constexpr (REG) return qr[i];
-    else return ql[i];
+    else return ql[off(i)];
   }
 };
+
+// Key of element i of a lane's slice: contiguous (k0 + i), or, for 16-bit
+// rows split into 128-byte pieces (SPLIT), 64 (i / 8) + 8 lane + i % 8.
+template <int EPL, bool SPLIT>
+__device__ __forceinline__ int slice_key(int lane8, int i) {
+  return SPLIT ? 64 * (i >> 3) + 8 * lane8 + (i & 7) : lane8 * EPL + i;
+}
 
 // Stage the head's k and q into LDS as fp32 (one conversion per value per
 // workgroup instead of one per value and row-lane), then point the lane at
 // its EPL-wide slices or load them.  Contains a workgroup barrier.
-template <int EPL, int LPR, int INBF, bool REG>
-__device__ __forceinline__ void stage_qk(const Args& a, uint64_t bh, int lane8, float* lds, KQ<EPL, REG>& kq) {
+template <int EPL, int LPR, int INBF, bool SPLIT, bool REG>
+__device__ __forceinline__ void stage_qk(const Args& a, uint64_t bh, int lane8, float* lds,
+                                         KQ<EPL, REG, SPLIT>& kq) {
   constexpr int DK = EPL * LPR;
   for (int t = threadIdx.x; t < 2 * DK; t += blockDim.x) {
     const void* src = t < DK ? a.k : a.q;
@@ -130,43 +144,51 @@ __device__ __forceinline__ void stage_qk(const Args& a, uint64_t bh, int lane8, 
     lds[t] = load_in_scalar<INBF>(src, idx);
   }
   __syncthreads();
-  const int k0 = lane8 * EPL;
+  const int k0 = slice_key<EPL, SPLIT>(lane8, 0);
   kq.kl = lds + k0;
   kq.ql = lds + DK + k0;
   if constexpr (REG) {
 #pragma unroll
     for (int i = 0; i < EPL; i += 4) {
-      const float4 kv = *reinterpret_cast<const float4*>(lds + k0 + i);
-      const float4 qv = *reinterpret_cast<const float4*>(lds + DK + k0 + i);
+      const int kk = slice_key<EPL, SPLIT>(lane8, i);
+      const float4 kv = *reinterpret_cast<const float4*>(lds + kk);
+      const float4 qv = *reinterpret_cast<const float4*>(lds + DK + kk);
       kq.kr[i] = kv.x; kq.kr[i + 1] = kv.y; kq.kr[i + 2] = kv.z; kq.kr[i + 3] = kv.w;
       kq.qr[i] = qv.x; kq.qr[i + 1] = qv.y; kq.qr[i + 2] = qv.z; kq.qr[i + 3] = qv.w;
     }
   }
 }
 
-// Outputs (and scales) of the RPL consecutive rows v0 .. v0+RPL-1 of a lane
-// group: lane r of the group stores row v0 + r, so a wave's 8 groups write
-// 8*RPL consecutive values with one store per array.
-template <int RPL>
-__device__ __forceinline__ void store_row_values(const Args& a, uint64_t bh, int v0, int lane8,
+// Outputs (and scales) of a wave's GPW*RPL rows wrow0 .. (group gi holds
+// rows wrow0 + gi + GPW r): lane r of a group takes its group's row r, then
+// one lane permute hands lane L the value of row wrow0 + L, so each array
+// gets one contiguous store per wave.  Called with every lane active.
+template <int RPL, int LPR>
+__device__ __forceinline__ void store_row_values(const Args& a, uint64_t bh, int wrow0, int lane8,
                                                  const float (&o_row)[RPL], const float* s_row) {
+  constexpr int GPW = 64 / LPR;
   float ov = o_row[0], sv = s_row ? s_row[0] : 0.0f;
 #pragma unroll
   for (int r = 1; r < RPL; ++r) {
     ov = lane8 == r ? o_row[r] : ov;
     if (s_row) sv = lane8 == r ? s_row[r] : sv;
   }
-  if (lane8 < RPL && v0 + lane8 < a.dv) {
-    const uint64_t row = bh * (uint64_t)a.dv + (uint64_t)(v0 + lane8);
+  const int lane = (int)(threadIdx.x & 63u);
+  const int src = (LPR * (lane % GPW) + lane / GPW) * 4;   // byte address of the source lane
+  ov = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(ov)));
+  if (s_row) sv = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(sv)));
+  if (lane < GPW * RPL && wrow0 + lane < a.dv) {
+    const uint64_t row = bh * (uint64_t)a.dv + (uint64_t)(wrow0 + lane);
     st_nt(a.out + row, ov);
     if (s_row) st_nt(a.scales + row, sv);
   }
 }
 
 template <int QB, int RND, int DELTA, int EPL, int LPR, int RPL, int BDR, int DKEY, int INBF>
-__device__ __forceinline__ void dense_quant_rows(const Args& a, uint8_t* blk, uint64_t bh, int v0, int ng,
+__device__ __forceinline__ void dense_quant_rows(const Args& a, uint8_t* blk, uint64_t bh, int v0, int wrow0,
                                                  int lane8, float* lds) {
   constexpr int DK = EPL * LPR;
+  constexpr int GPW = 64 / LPR;             // row groups per wave: rows v0 + GPW r
   constexpr int RB = DK * QB / 8;           // code bytes per row
   constexpr int NW = EPL * QB / 32;         // code words per lane and row
   constexpr int SRB = sr_bits_of<RND>();
@@ -175,7 +197,7 @@ __device__ __forceinline__ void dense_quant_rows(const Args& a, uint8_t* blk, ui
   uint32_t w[RPL][NW];
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
-    const int v = v0 + r;
+    const int v = v0 + GPW * r;
     if (v < a.dv) load_bytes<EPL * QB / 8, true>(blk + (uint64_t)v * RB + k0 * QB / 8, w[r]);
     else {
 #pragma unroll
@@ -185,7 +207,7 @@ __device__ __forceinline__ void dense_quant_rows(const Args& a, uint8_t* blk, ui
   float s_old[RPL], vin[RPL];
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
-    const int v = v0 + r;
+    const int v = v0 + GPW * r;
     const uint64_t row = bh * (uint64_t)a.dv + (uint64_t)(v < a.dv ? v : 0);
     s_old[r] = ld_nt(a.scales + row);
     vin[r] = load_in_scalar<INBF>(a.v, row);
@@ -196,12 +218,12 @@ __device__ __forceinline__ void dense_quant_rows(const Args& a, uint8_t* blk, ui
   else dh = a.decay[bh];
   const float beta = a.beta ? a.beta[bh] : 1.0f;
   KQ<EPL, (LPR == 8)> kq;
-  stage_qk<EPL, LPR, INBF>(a, bh, lane8, lds, kq);
+  stage_qk<EPL, LPR, INBF, false>(a, bh, lane8, lds, kq);
   if (a.load_prio) __builtin_amdgcn_s_setprio(0);
   float o_row[RPL], s_row[RPL];
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
-    const int v = v0 + r;
+    const int v = v0 + GPW * r;
     o_row[r] = 0.0f;
     s_row[r] = 0.0f;
     if (v >= a.dv) continue;   // whole 8-lane groups skip together
@@ -316,21 +338,36 @@ __device__ __forceinline__ void dense_quant_rows(const Args& a, uint8_t* blk, ui
     }
     store_bytes<EPL * QB / 8, true>(blk + (uint64_t)v * RB + k0 * QB / 8, out);
   }
-  store_row_values<RPL>(a, bh, v0, lane8, o_row, s_row);
+  store_row_values<RPL, LPR>(a, bh, wrow0, lane8, o_row, s_row);
 }
 
-// Protected (16-bit) heads of a head map.
+// Protected (16-bit) heads of a head map.  With 8 lanes per row a row is
+// split into 128-byte pieces, lane j holding bytes 16j + 128i of each (keys
+// 64i + 8j .. 64i + 8j + 7), so every load and store of the wave covers
+// whole cache lines; with 4 lanes per row a lane holds 32 consecutive keys.
 template <int DELTA, int EPL, int LPR, int RPL, int DKEY, int INBF>
-__device__ __forceinline__ void dense_prot_rows(const Args& a, uint8_t* blk, uint64_t bh, int v0, int ng,
+__device__ __forceinline__ void dense_prot_rows(const Args& a, uint8_t* blk, uint64_t bh, int v0, int wrow0,
                                                 int lane8, float* lds) {
   constexpr int DK = EPL * LPR;
-  const int k0 = lane8 * EPL;
+  constexpr int GPW = 64 / LPR;
+  constexpr bool SPLIT = (LPR == 8);
+  constexpr int NPC = EPL / 8;               // 16-byte pieces per lane and row (SPLIT)
+  // byte offset of the lane's piece i within a row
+  auto piece = [&](int i) -> uint32_t {
+    return SPLIT ? (uint32_t)(128 * i + 16 * lane8) : (uint32_t)(lane8 * EPL * 2 + 16 * i);
+  };
   uint32_t hw[RPL][EPL / 2];
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
-    const int v = v0 + r;
-    if (v < a.dv) load_bytes<EPL * 2, true>(blk + ((uint64_t)v * DK + (uint64_t)k0) * 2u, hw[r]);
-    else {
+    const int v = v0 + GPW * r;
+    if (v < a.dv) {
+      const uint8_t* rowp = blk + (uint64_t)v * (DK * 2);
+#pragma unroll
+      for (int i = 0; i < NPC; ++i) {
+        const u32x4_t t = ld_nt(reinterpret_cast<const u32x4_t*>(rowp + piece(i)));
+        hw[r][4 * i] = t.x; hw[r][4 * i + 1] = t.y; hw[r][4 * i + 2] = t.z; hw[r][4 * i + 3] = t.w;
+      }
+    } else {
 #pragma unroll
       for (int i = 0; i < EPL / 2; ++i) hw[r][i] = 0u;
     }
@@ -338,16 +375,23 @@ __device__ __forceinline__ void dense_prot_rows(const Args& a, uint8_t* blk, uin
   float vin[RPL];
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
-    const int v = v0 + r;
+    const int v = v0 + GPW * r;
     vin[r] = load_in_scalar<INBF>(a.v, bh * (uint64_t)a.dv + (uint64_t)(v < a.dv ? v : 0));
   }
   float df[DKEY ? EPL : 1];
   float dh = 1.0f;
-  if constexpr (DKEY) load_f32<EPL>(a.decay + (uint64_t)bh * DK + k0, df);
-  else dh = a.decay[bh];
+  if constexpr (DKEY) {
+#pragma unroll
+    for (int i = 0; i < EPL; i += 4) {
+      const float4 t = *reinterpret_cast<const float4*>(a.decay + (uint64_t)bh * DK + slice_key<EPL, SPLIT>(lane8, i));
+      df[i] = t.x; df[i + 1] = t.y; df[i + 2] = t.z; df[i + 3] = t.w;
+    }
+  } else {
+    dh = a.decay[bh];
+  }
   const float beta = a.beta ? a.beta[bh] : 1.0f;
-  KQ<EPL, (LPR == 8)> kq;
-  stage_qk<EPL, LPR, INBF>(a, bh, lane8, lds, kq);
+  KQ<EPL, false, SPLIT> kq;   // one pass over the rows' k and q: read from LDS where used
+  stage_qk<EPL, LPR, INBF, SPLIT>(a, bh, lane8, lds, kq);
   if (a.load_prio) __builtin_amdgcn_s_setprio(0);
   float o_row[RPL];
   // one body per 16-bit format (a uniform branch around the rows)
@@ -355,7 +399,7 @@ __device__ __forceinline__ void dense_prot_rows(const Args& a, uint8_t* blk, uin
     constexpr bool is_bf16 = decltype(fmt)::value;
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
-    const int v = v0 + r;
+    const int v = v0 + GPW * r;
     o_row[r] = 0.0f;
     if (v >= a.dv) continue;
     float u;
@@ -387,12 +431,17 @@ __device__ __forceinline__ void dense_prot_rows(const Args& a, uint8_t* blk, uin
     for (int i = 0; i < EPL / 2; ++i)
       ow[i] = is_bf16 ? pack_bf16x2(sp[2 * i], sp[2 * i + 1])
                       : pack_f16x2(sp[2 * i], sp[2 * i + 1]);
-    store_bytes<EPL * 2, true>(blk + ((uint64_t)v * DK + (uint64_t)k0) * 2u, ow);
+    uint8_t* rowp = blk + (uint64_t)v * (DK * 2);
+#pragma unroll
+    for (int i = 0; i < NPC; ++i) {
+      const u32x4_t t = {ow[4 * i], ow[4 * i + 1], ow[4 * i + 2], ow[4 * i + 3]};
+      st_nt(reinterpret_cast<u32x4_t*>(rowp + piece(i)), t);
+    }
   }
   };
   if (a.hp_dtype == 1) rows(std::true_type{});
   else rows(std::false_type{});
-  store_row_values<RPL>(a, bh, v0, lane8, o_row, nullptr);
+  store_row_values<RPL, LPR>(a, bh, wrow0, lane8, o_row, nullptr);
 }
 
 // Register budget (minimum waves per SIMD the body is compiled for), chosen
@@ -434,7 +483,11 @@ void k_step_dense(const Args a) {
   const uint32_t chunk = r % (uint32_t)a.row_chunks;
   const uint32_t h = r / (uint32_t)a.row_chunks;
   const uint32_t bh = b * (uint32_t)a.H + h;
-  const int v0 = ((int)chunk * ng + g) * RPL;   // groups past dv stay for the barrier
+  // rows: a wave owns GPW * RPL consecutive rows from wrow0, its group gi the
+  // rows wrow0 + gi + GPW r; groups past dv stay for the barrier
+  constexpr int GPW = 64 / LPR;
+  const int wrow0 = ((int)chunk * ng + (g / GPW) * GPW) * RPL;
+  const int v0 = wrow0 + g % GPW;
   __shared__ __align__(16) float lds[2 * EPL * LPR];
   // head storage from the protected-head mask: no table lookup stands
   // between the launch and the state loads
@@ -443,10 +496,10 @@ void k_step_dense(const Args a) {
   const bool prot = (h < 64u) && ((a.prot_mask >> h) & 1ull);
   if (!prot) {
     uint8_t* blk = a.codes + (uint64_t)b * a.code_bstride + (uint64_t)(h - np) * a.code_hblk;
-    dense_quant_rows<QB, RND, DELTA, EPL, LPR, RPL, BDR, DKEY, INBF>(a, blk, bh, v0, ng, lane8, lds);
+    dense_quant_rows<QB, RND, DELTA, EPL, LPR, RPL, BDR, DKEY, INBF>(a, blk, bh, v0, wrow0, lane8, lds);
   } else {
     uint8_t* blk = a.hp + (uint64_t)b * a.hp_bstride + (uint64_t)np * a.hp_hblk;
-    dense_prot_rows<DELTA, EPL, LPR, RPL, DKEY, INBF>(a, blk, bh, v0, ng, lane8, lds);
+    dense_prot_rows<DELTA, EPL, LPR, RPL, DKEY, INBF>(a, blk, bh, v0, wrow0, lane8, lds);
   }
 }
 
