@@ -59,6 +59,7 @@ struct Plan {
   int dense_rpl = 1;
   int dense_lpr = 8;
   int keymap_eh = 2;
+  int keymap_rpl = 1;
   int dense_threads = 256;
   uint32_t lds = 0;
   uint64_t prot_mask = 0;       // dense family: protected heads
@@ -185,7 +186,7 @@ qs_status make_plan(const qstate_config* c, Plan* p) {
   } else if (c->map_mode == QS_MAP_KEY && c->hp_dtype != QS_FP32 && dk == 128) {
     // key-channel maps with 16-bit protected values: rows in storage order,
     // 8 lanes per row, each with 16 code slots and keymap_eh protected
-    // slots, 32 rows per workgroup (4 lanes per row measured slower)
+    // slots, keymap_rpl rows per lane group (4 lanes per row measured slower)
     p->family = qs::kFamKeymap;
     p->dense_lpr = 8;
     p->dense_rpl = 1;
@@ -194,7 +195,10 @@ qs_status make_plan(const qstate_config* c, Plan* p) {
     for (int h = 0; h < H; ++h) maxhp = std::max(maxhp, dk - p->nq[h]);
     p->keymap_eh = 2;
     while (p->keymap_eh * p->dense_lpr < maxhp) p->keymap_eh *= 2;
-    const int rows = 256 / p->dense_lpr;
+    int krpl = env_int("QSTATE_KEYMAP_RPL", 2);
+    if (krpl != 1 && krpl != 2 && krpl != 4) krpl = 2;
+    p->keymap_rpl = krpl;
+    const int rows = 256 / p->dense_lpr * krpl;
     p->row_chunks = (dv + rows - 1) / rows;
   } else if (c->map_mode == QS_MAP_KEY ||
              (c->map_mode == QS_MAP_HEAD && (c->hp_dtype == QS_FP32 || H > 64))) {
@@ -292,6 +296,7 @@ qs::Args base_args(const qstate_handle* h, const qstate_tensors* st) {
   a.dense_rpl = h->plan.dense_rpl;
   a.dense_lpr = h->plan.dense_lpr;
   a.keymap_eh = h->plan.keymap_eh;
+  a.keymap_rpl = h->plan.keymap_rpl;
   a.load_prio = env_int("QSTATE_LOAD_PRIO", 1) ? 1 : 0;
   a.dense_threads = h->plan.dense_threads;
   a.prot_mask = h->plan.prot_mask;

@@ -67,28 +67,34 @@ __device__ __forceinline__ void store_dwords(uint8_t* p, uint32_t nbytes, const 
 }  // namespace
 
 // LPR lanes per row, EPL = dk/LPR code slots and EH protected slots per
-// lane, one row per lane group, 256/LPR rows per workgroup.
-template <int QB, int RND, int DELTA, int EPL, int LPR, int EH, int BDR, int DKEY>
+// lane; a lane group holds RPL rows, 256/LPR*RPL rows per workgroup.  Within
+// a wave the groups take consecutive rows (group gi rows wrow0 + gi + GPW r),
+// so each state access of the wave covers one contiguous stretch; the
+// workgroup's per-row outputs and scales are collected in LDS and stored as
+// whole cache lines.
+template <int QB, int RND, int DELTA, int EPL, int LPR, int EH, int BDR, int DKEY, int RPL>
 __global__ __launch_bounds__(256) void k_step_keymap(const Args a) {
   constexpr int DK = EPL * LPR;
-  constexpr int RW = 256 / LPR;            // rows per workgroup
+  constexpr int GPW = 64 / LPR;            // row groups per wave
+  constexpr int RW = 256 / LPR * RPL;      // rows per workgroup
   constexpr int SRB = sr_bits_of<RND>();
   constexpr int CW = EPL * QB / 32;        // code words per lane and row
   constexpr int HW = EH / 2;               // 16-bit value words per lane and row
   static_assert(EH % 2 == 0, "protected slots come in dword pairs");
   if (a.load_prio) __builtin_amdgcn_s_setprio(3);   // raised until the loads are issued
   const int lane = threadIdx.x & (LPR - 1);
-  const int g = threadIdx.x / LPR;         // row group: one row per workgroup chunk
+  const int g = threadIdx.x / LPR;         // row group
 
   // work item (b, h, chunk of RW rows), head order rotated by b across XCDs
   const uint32_t per_b = (uint32_t)a.H * (uint32_t)a.row_chunks;
   const uint32_t b = blockIdx.x / per_b;
-  uint32_t r = blockIdx.x - b * per_b + b % per_b;
-  r = r >= per_b ? r - per_b : r;
-  const uint32_t chunk = r % (uint32_t)a.row_chunks;
-  const uint32_t h = r / (uint32_t)a.row_chunks;
+  uint32_t r0 = blockIdx.x - b * per_b + b % per_b;
+  r0 = r0 >= per_b ? r0 - per_b : r0;
+  const uint32_t chunk = r0 % (uint32_t)a.row_chunks;
+  const uint32_t h = r0 / (uint32_t)a.row_chunks;
   const uint64_t bh = (uint64_t)b * (uint64_t)a.H + h;
-  const int v = (int)chunk * RW + g;
+  const int crow0 = (int)chunk * RW;                          // first row of the workgroup
+  const int v0 = crow0 + (g / GPW) * GPW * RPL + g % GPW;     // rows v0 + GPW r
 
   const int nq = a.t.nq[h];
   const int nhp = DK - nq;
@@ -104,15 +110,24 @@ __global__ __launch_bounds__(256) void k_step_keymap(const Args a) {
   const uint32_t hvalid = rh > hoff ? (rh - hoff < HB ? rh - hoff : HB) : 0u;
 
   // state loads first
-  const bool row_ok = v < a.dv;
-  const int vr = row_ok ? v : 0;
-  uint32_t cw[CW], hw[HW > 0 ? HW : 1];
-  load_dwords<CW>(cblk + (uint64_t)vr * rq + coff, row_ok ? cvalid : 0u, cw);
-  load_dwords<HW>(hblk + (uint64_t)vr * rh + hoff, row_ok ? hvalid : 0u, hw);
-  const uint64_t row = bh * (uint64_t)a.dv + (uint64_t)vr;
-  const float s_old = ld_nt(a.scales + row);
-  const float vin = a.in_bf16 ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(a.v)[row])
-                              : reinterpret_cast<const float*>(a.v)[row];
+  uint32_t cw[RPL][CW], hw[RPL][HW > 0 ? HW : 1];
+  float s_old[RPL], vin[RPL];
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) {
+    const int v = v0 + GPW * r;
+    const bool ok = v < a.dv;
+    const int vr = ok ? v : 0;
+    load_dwords<CW>(cblk + (uint64_t)vr * rq + coff, ok ? cvalid : 0u, cw[r]);
+    load_dwords<HW>(hblk + (uint64_t)vr * rh + hoff, ok ? hvalid : 0u, hw[r]);
+  }
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) {
+    const int v = v0 + GPW * r;
+    const uint64_t row = bh * (uint64_t)a.dv + (uint64_t)(v < a.dv ? v : 0);
+    s_old[r] = ld_nt(a.scales + row);
+    vin[r] = a.in_bf16 ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(a.v)[row])
+                       : reinterpret_cast<const float*>(a.v)[row];
+  }
   const float dh = DKEY ? 1.0f : a.decay[bh];
   const float beta = a.beta ? a.beta[bh] : 1.0f;
 
@@ -146,7 +161,6 @@ __global__ __launch_bounds__(256) void k_step_keymap(const Args a) {
   }
   __syncthreads();
   if (a.load_prio) __builtin_amdgcn_s_setprio(0);
-  if (!row_ok) return;   // after the barrier: whole row groups only
 
   const float* kc = lc[0] + lane * EPL;
   const float* qc = lc[1] + lane * EPL;
@@ -155,14 +169,21 @@ __global__ __launch_bounds__(256) void k_step_keymap(const Args a) {
   const float* qh = lh[1] + lane * EH;
   const float* dhk = lh[2] + lane * EH;
   const bool is_bf16 = a.hp_dtype == 1;
+  // per-row outputs and scales of the workgroup, stored at the end
+  __shared__ float ol[RW], sl_[RW];
 
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) {
+  const int v = v0 + GPW * r;
+  if (v < a.dv) {   // whole row groups
+  const uint64_t row = bh * (uint64_t)a.dv + (uint64_t)v;
   // old values: codes (0 past nq: padding and unloaded dwords are zero)
   auto code_at = [&](int i) -> float {
-    if constexpr (QB == 8) return (float)(int32_t)(int8_t)(cw[i >> 2] >> (8 * (i & 3)));
-    else return (float)((int32_t)(cw[i >> 3] << (28 - 4 * (i & 7))) >> 28);
+    if constexpr (QB == 8) return (float)(int32_t)(int8_t)(cw[r][i >> 2] >> (8 * (i & 3)));
+    else return (float)((int32_t)(cw[r][i >> 3] << (28 - 4 * (i & 7))) >> 28);
   };
   auto hp_at = [&](int i) -> float {
-    const uint32_t bits = (hw[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+    const uint32_t bits = (hw[r][i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
     return is_bf16 ? bf16_bits_to_f32(bits) : f16_bits_to_f32(bits);
   };
 
@@ -172,17 +193,17 @@ __global__ __launch_bounds__(256) void k_step_keymap(const Args a) {
     // S_hat k); key decay: u = beta (v - sum decayed k)
     float wc = 0.0f, wh = 0.0f;
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) wc = fmaf(DKEY ? (dc[i] * s_old) * code_at(i) : code_at(i), kc[i], wc);
+    for (int i = 0; i < EPL; ++i) wc = fmaf(DKEY ? (dc[i] * s_old[r]) * code_at(i) : code_at(i), kc[i], wc);
 #pragma unroll
     for (int i = 0; i < EH; ++i) wh = fmaf(DKEY ? dhk[i] * hp_at(i) : hp_at(i), kh[i], wh);
     if constexpr (DKEY) {
-      u = beta * (vin - red_sum<LPR>(wc + wh));
+      u = beta * (vin[r] - red_sum<LPR>(wc + wh));
     } else {
-      const float wk = red_sum<LPR>(fmaf(s_old, wc, wh));
-      u = beta * (vin - dh * wk);
+      const float wk = red_sum<LPR>(fmaf(s_old[r], wc, wh));
+      u = beta * (vin[r] - dh * wk);
     }
   } else {
-    u = beta * vin;
+    u = beta * vin[r];
   }
 
   // protected slots: update, readout share, 16-bit store
@@ -202,12 +223,12 @@ __global__ __launch_bounds__(256) void k_step_keymap(const Args a) {
   }
 
   // quantized slots: update, readout, row maximum, requantize
-  const float ds = dh * s_old;
+  const float ds = dh * s_old[r];
   float sp[EPL];
   float mx = 0.0f;
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
-    sp[i] = fmaf(u, kc[i], (DKEY ? dc[i] * s_old : ds) * code_at(i));
+    sp[i] = fmaf(u, kc[i], (DKEY ? dc[i] * s_old[r] : ds) * code_at(i));
     o = fmaf(sp[i], qc[i], o);
   }
 #pragma unroll
@@ -216,7 +237,6 @@ __global__ __launch_bounds__(256) void k_step_keymap(const Args a) {
   const float m = red_absmax<LPR>(mx);
   float scale, inv, invb;
   row_scale_fast<QB, SRB>(m, scale, inv, invb);
-
   uint32_t out[CW];
   const uint64_t e0 = row * DK + (uint64_t)lane * EPL;   // slot-indexed element of the first slot
   if constexpr (QB == 8 && !BDR) {
@@ -264,7 +284,7 @@ __global__ __launch_bounds__(256) void k_step_keymap(const Args a) {
     int32_t code[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
-      const float shi = BDR ? s_old * code_at(i) : 0.0f;
+      const float shi = BDR ? s_old[r] * code_at(i) : 0.0f;
       code[i] = round_elem<QB, RND, BDR>(sp[i], shi, inv, invb, (RND != 0) ? rb[i] : 0u, a.bdr_bound);
     }
 #pragma unroll
@@ -277,8 +297,17 @@ __global__ __launch_bounds__(256) void k_step_keymap(const Args a) {
   }
   store_dwords<CW>(const_cast<uint8_t*>(cblk) + (uint64_t)v * rq + coff, cvalid, out);
   if (lane == 0) {
-    st_nt(a.out + row, o);
-    st_nt(a.scales + row, scale);
+    ol[v - crow0] = o;
+    sl_[v - crow0] = scale;
+  }
+  }   // v < dv
+  }   // rows
+  __syncthreads();
+  const int t = (int)threadIdx.x;
+  if (t < RW && crow0 + t < a.dv) {
+    const uint64_t row0 = bh * (uint64_t)a.dv + (uint64_t)(crow0 + t);
+    st_nt(a.out + row0, ol[t]);
+    st_nt(a.scales + row0, sl_[t]);
   }
 }
 

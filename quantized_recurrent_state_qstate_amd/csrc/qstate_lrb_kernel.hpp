@@ -83,6 +83,7 @@ __global__ __launch_bounds__(256) void k_step_lrb(const Args a) {
   __shared__ __align__(16) float Ut[RANK][DK];    // U rows of merged channels (before clearing)
   __shared__ __align__(16) float ul[256], upl[256], sol[256], lrl[256];
   __shared__ __align__(16) float wl[DELTA ? 256 : 1];   // delta rule: decayed S_hat k per row
+  __shared__ __align__(16) float ol[256], sl_[256];      // per-row outputs and scales
   __shared__ __align__(16) float kl[DK], ql[DK], dl[DK];
   __shared__ __align__(16) float P[RANK * 256];   // reduction transpose
   __shared__ float red[RANK + 4];
@@ -367,10 +368,16 @@ __global__ __launch_bounds__(256) void k_step_lrb(const Args a) {
       else out[i >> 3] |= ((uint32_t)code & 0xFu) << (4 * (i & 7));
     }
     store_bytes<EPL * QB / 8, true>(gcode + (uint64_t)v * (DK * QB / 8) + k0 * QB / 8, out);
-    if (lane8 == 0) {
-      st_nt(a.out + row, o + lrl[v]);
-      st_nt(a.scales + row, scale);
+    if (lane8 == 0) {   // collected in LDS, stored below as whole cache lines
+      ol[v] = o + lrl[v];
+      sl_[v] = scale;
     }
+  }
+  __syncthreads();
+  if (tid < dv) {
+    const uint64_t row = (uint64_t)bh * (uint64_t)dv + (uint64_t)tid;
+    st_nt(a.out + row, ol[tid]);
+    st_nt(a.scales + row, sl_[tid]);
   }
 }
 

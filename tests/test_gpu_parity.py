@@ -314,6 +314,13 @@ EDGE = {
                                 map_density=0.05),
     "keymap_fp16_mostly_protected": dict(kind="additive", decay_mode="key", dk=128, dv=33, H=2, B=3, qbits=8,
                                          map_mode="key", hp_dtype="fp16", map_density=0.9),
+    # key-map kernel with 1 and 4 rows per lane group (ragged last chunk)
+    "keymap_rows1_delta": dict(kind="delta", decay_mode="head", dk=128, dv=72, H=2, B=2, qbits=8,
+                               map_mode="key", hp_dtype="fp16", map_density=0.1, keymap_rows=1),
+    "keymap_rows4_delta_bf16": dict(kind="delta", decay_mode="head", dk=128, dv=200, H=2, B=2, qbits=8,
+                                    map_mode="key", hp_dtype="bf16", map_density=0.3, keymap_rows=4),
+    "keymap_rows4_int4_sr8": dict(kind="additive", decay_mode="key", dk=128, dv=40, H=3, B=2, qbits=4,
+                                  sr_bits=8, map_mode="key", hp_dtype="fp16", keymap_rows=4),
     # delta rule with a decay per key channel (channel-gated, Kimi-Linear)
     "kda_dk128": dict(kind="delta", decay_mode="key", dk=128, dv=64, H=2, B=2, qbits=8),
     "kda_dk128_8lanes_fp32_in": dict(kind="delta", decay_mode="key", dk=128, dv=96, H=2, B=2, qbits=8,
@@ -354,6 +361,9 @@ def test_edge_cases(case, monkeypatch):
     lanes = kw.pop("lanes", None)         # lanes per row of the dense kernel, when not the default
     if lanes is not None:
         monkeypatch.setenv("QSTATE_DENSE_LPR", str(lanes))
+    krows = kw.pop("keymap_rows", None)   # rows per lane group of the key-map kernel
+    if krows is not None:
+        monkeypatch.setenv("QSTATE_KEYMAP_RPL", str(krows))
     r = np.random.default_rng(1)
     m = None
     if kw.get("map_mode") == "head":
