@@ -131,17 +131,40 @@ __device__ __forceinline__ int slice_key(int lane8, int i) {
   return SPLIT ? 64 * (i >> 3) + 8 * lane8 + (i & 7) : lane8 * EPL + i;
 }
 
-// Stage the head's k and q into LDS as fp32 (one conversion per value per
-// workgroup instead of one per value and row-lane), then point the lane at
-// its EPL-wide slices or load them.  Contains a workgroup barrier.
+// Staging of the head's k and q into LDS as fp32 (one conversion per value
+// per workgroup instead of one per value and row-lane), in two parts so the
+// loads go out with the state loads: qk_load reads this thread's first
+// values (unconditionally, from clamped indices: a load inside a branch makes
+// the compiler wait for it where the branch joins); stage_qk stores them,
+// loads any rest (workgroups smaller than 2*dk threads), synchronizes the
+// workgroup, and points the lane at its slices or loads them.
+template <int DK>
+constexpr int qk_first() { return (2 * DK + 255) / 256; }
+
+template <int DK, int INBF>
+__device__ __forceinline__ void qk_load(const Args& a, uint64_t bh, float (&f)[qk_first<DK>()]) {
+#pragma unroll
+  for (int i = 0; i < qk_first<DK>(); ++i) {
+    const int t = (int)threadIdx.x + i * (int)blockDim.x;
+    const int tc = t < 2 * DK ? t : 0;
+    const void* src = tc < DK ? a.k : a.q;
+    f[i] = load_in_scalar<INBF>(src, bh * DK + (uint64_t)(tc < DK ? tc : tc - DK));
+  }
+}
+
 template <int EPL, int LPR, int INBF, bool SPLIT, bool REG>
 __device__ __forceinline__ void stage_qk(const Args& a, uint64_t bh, int lane8, float* lds,
-                                         KQ<EPL, REG, SPLIT>& kq) {
+                                         const float (&f)[qk_first<EPL * LPR>()], KQ<EPL, REG, SPLIT>& kq) {
   constexpr int DK = EPL * LPR;
-  for (int t = threadIdx.x; t < 2 * DK; t += blockDim.x) {
+  constexpr int NF = qk_first<DK>();
+#pragma unroll
+  for (int i = 0; i < NF; ++i) {
+    const int t = (int)threadIdx.x + i * (int)blockDim.x;
+    if (t < 2 * DK) lds[t] = f[i];
+  }
+  for (int t = (int)threadIdx.x + NF * (int)blockDim.x; t < 2 * DK; t += (int)blockDim.x) {
     const void* src = t < DK ? a.k : a.q;
-    const uint64_t idx = bh * DK + (uint64_t)(t < DK ? t : t - DK);
-    lds[t] = load_in_scalar<INBF>(src, idx);
+    lds[t] = load_in_scalar<INBF>(src, bh * DK + (uint64_t)(t < DK ? t : t - DK));
   }
   __syncthreads();
   const int k0 = slice_key<EPL, SPLIT>(lane8, 0);
@@ -189,20 +212,19 @@ __device__ __forceinline__ void dense_quant_rows(const Args& a, uint8_t* blk, ui
                                                  int lane8, float* lds) {
   constexpr int DK = EPL * LPR;
   constexpr int GPW = 64 / LPR;             // row groups per wave: rows v0 + GPW r
+  constexpr bool KQREG = (LPR == 8) && !(QB == 8 && RND != 0 && !BDR);   // see below
   constexpr int RB = DK * QB / 8;           // code bytes per row
   constexpr int NW = EPL * QB / 32;         // code words per lane and row
   constexpr int SRB = sr_bits_of<RND>();
   const int k0 = lane8 * EPL;
-  // every load first: state rows (HBM), then per-row scalars, then the head's inputs
+  // every load first: state rows (HBM), then per-row scalars, then the
+  // head's inputs; rows past dv read row 0 and are not used (no branch
+  // around a load: the compiler would wait for it where the branch joins)
   uint32_t w[RPL][NW];
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
     const int v = v0 + GPW * r;
-    if (v < a.dv) load_bytes<EPL * QB / 8, true>(blk + (uint64_t)v * RB + k0 * QB / 8, w[r]);
-    else {
-#pragma unroll
-      for (int i = 0; i < NW; ++i) w[r][i] = 0u;
-    }
+    load_bytes<EPL * QB / 8, true>(blk + (uint64_t)(v < a.dv ? v : 0) * RB + k0 * QB / 8, w[r]);
   }
   float s_old[RPL], vin[RPL];
 #pragma unroll
@@ -217,9 +239,36 @@ __device__ __forceinline__ void dense_quant_rows(const Args& a, uint8_t* blk, ui
   if constexpr (DKEY) load_f32<EPL>(a.decay + (uint64_t)bh * DK + k0, df);
   else dh = a.decay[bh];
   const float beta = a.beta ? a.beta[bh] : 1.0f;
-  KQ<EPL, (LPR == 8)> kq;
-  stage_qk<EPL, LPR, INBF, false>(a, bh, lane8, lds, kq);
+  float qkf[qk_first<DK>()];
+  qk_load<DK, INBF>(a, bh, qkf);
   if (a.load_prio) __builtin_amdgcn_s_setprio(0);
+  // Stochastic rounding's Philox blocks depend only on the element index and
+  // the step, not on the state: computed while the state loads are in flight
+  // (the empty asm keeps them ahead of the barrier that waits for the loads).
+  constexpr int PER = (RND == 1) ? 8 : 16;                 // elements per Philox block
+  constexpr int NB = (RND == 0) ? 1 : (EPL + PER - 1) / PER;
+  constexpr bool PRE = (RND != 0) && QB == 8 && !BDR;
+  uint32_t px[PRE ? RPL : 1][NB][4];
+  if constexpr (PRE) {
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+      const uint64_t row = bh * (uint64_t)a.dv + (uint64_t)(v0 + GPW * r);   // rows past dv: unused
+#pragma unroll
+      for (int gblk = 0; gblk < NB; ++gblk) {
+        // element indices stay below 2^35 (checked at init): the counter's
+        // high word is 0
+        const uint64_t e0w = row * DK + (uint64_t)k0 + (uint64_t)(gblk * PER);
+        px[r][gblk][0] = (RND == 1) ? (uint32_t)(e0w >> 3) : (uint32_t)(e0w >> 4);
+        px[r][gblk][1] = 0u;
+        px[r][gblk][2] = a.step_lo;
+        px[r][gblk][3] = a.step_hi;
+        philox10(px[r][gblk], a.seed_lo, a.seed_hi);
+        asm volatile("" : "+v"(px[r][gblk][0]), "+v"(px[r][gblk][1]), "+v"(px[r][gblk][2]), "+v"(px[r][gblk][3]));
+      }
+    }
+  }
+  KQ<EPL, KQREG> kq;
+  stage_qk<EPL, LPR, INBF, false>(a, bh, lane8, lds, qkf, kq);
   float o_row[RPL], s_row[RPL];
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
@@ -272,22 +321,14 @@ __device__ __forceinline__ void dense_quant_rows(const Args& a, uint8_t* blk, ui
       // y = floor(x 2^SRB + 1/2) + rb and code = y >> SRB (|x| <= Q, so no
       // clamp)
       constexpr int BYTE = SRB / 8;
-      constexpr int PER = (RND == 1) ? 8 : 16;    // elements per Philox block
-      constexpr int NB = (RND == 0) ? 1 : (EPL + PER - 1) / PER;
 #pragma unroll
       for (int gblk = 0; gblk < NB; ++gblk) {
         uint32_t x[4] = {0u, 0u, 0u, 0u};
         uint32_t sel = 0u;   // RND 2, EPL 8: which half of the 16-element block
         if constexpr (RND != 0) {
-          // element indices stay below 2^35 (checked at init): the counter's
-          // high word is 0
+#pragma unroll
+          for (int j = 0; j < 4; ++j) x[j] = px[r][gblk][j];
           const uint32_t e0 = (uint32_t)(row * DK) + (uint32_t)k0 + (uint32_t)(gblk * PER);
-          const uint64_t e0w = row * DK + (uint64_t)k0 + (uint64_t)(gblk * PER);
-          x[0] = (RND == 1) ? (uint32_t)(e0w >> 3) : (uint32_t)(e0w >> 4);
-          x[1] = 0u;
-          x[2] = a.step_lo;
-          x[3] = a.step_hi;
-          philox10(x, a.seed_lo, a.seed_hi);
           if constexpr (RND == 2 && EPL < 16) sel = (e0 >> 3) & 1u;
         }
         constexpr int CNT = (RND == 0) ? EPL : ((PER < EPL) ? PER : EPL);
@@ -360,16 +401,11 @@ __device__ __forceinline__ void dense_prot_rows(const Args& a, uint8_t* blk, uin
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
     const int v = v0 + GPW * r;
-    if (v < a.dv) {
-      const uint8_t* rowp = blk + (uint64_t)v * (DK * 2);
+    const uint8_t* rowp = blk + (uint64_t)(v < a.dv ? v : 0) * (DK * 2);   // rows past dv: unused
 #pragma unroll
-      for (int i = 0; i < NPC; ++i) {
-        const u32x4_t t = ld_nt(reinterpret_cast<const u32x4_t*>(rowp + piece(i)));
-        hw[r][4 * i] = t.x; hw[r][4 * i + 1] = t.y; hw[r][4 * i + 2] = t.z; hw[r][4 * i + 3] = t.w;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < EPL / 2; ++i) hw[r][i] = 0u;
+    for (int i = 0; i < NPC; ++i) {
+      const u32x4_t t = ld_nt(reinterpret_cast<const u32x4_t*>(rowp + piece(i)));
+      hw[r][4 * i] = t.x; hw[r][4 * i + 1] = t.y; hw[r][4 * i + 2] = t.z; hw[r][4 * i + 3] = t.w;
     }
   }
   float vin[RPL];
@@ -390,9 +426,11 @@ __device__ __forceinline__ void dense_prot_rows(const Args& a, uint8_t* blk, uin
     dh = a.decay[bh];
   }
   const float beta = a.beta ? a.beta[bh] : 1.0f;
-  KQ<EPL, false, SPLIT> kq;   // one pass over the rows' k and q: read from LDS where used
-  stage_qk<EPL, LPR, INBF, SPLIT>(a, bh, lane8, lds, kq);
+  float qkf[qk_first<DK>()];
+  qk_load<DK, INBF>(a, bh, qkf);
   if (a.load_prio) __builtin_amdgcn_s_setprio(0);
+  KQ<EPL, false, SPLIT> kq;   // one pass over the rows' k and q: read from LDS where used
+  stage_qk<EPL, LPR, INBF, SPLIT>(a, bh, lane8, lds, qkf, kq);
   float o_row[RPL];
   // one body per 16-bit format (a uniform branch around the rows)
   auto rows = [&](auto fmt) {
