@@ -195,8 +195,8 @@ qs_status make_plan(const qstate_config* c, Plan* p) {
     for (int h = 0; h < H; ++h) maxhp = std::max(maxhp, dk - p->nq[h]);
     p->keymap_eh = 2;
     while (p->keymap_eh * p->dense_lpr < maxhp) p->keymap_eh *= 2;
-    int krpl = env_int("QSTATE_KEYMAP_RPL", 2);
-    if (krpl != 1 && krpl != 2 && krpl != 4) krpl = 2;
+    int krpl = env_int("QSTATE_KEYMAP_RPL", dv > 32 ? 2 : 1);
+    if (krpl != 1 && krpl != 2) krpl = dv > 32 ? 2 : 1;
     p->keymap_rpl = krpl;
     const int rows = 256 / p->dense_lpr * krpl;
     p->row_chunks = (dv + rows - 1) / rows;

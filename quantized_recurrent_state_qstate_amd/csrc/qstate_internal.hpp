@@ -49,7 +49,7 @@ struct Args {
   int32_t dense_threads;  // dense kernel: threads per workgroup (dense_lpr per row group)
   int32_t dense_lpr;   // dense kernel: lanes per row (8, or 4 for dk 128)
   int32_t keymap_eh;   // key-map kernel: protected slots per lane (2, 4, 8, 16)
-  int32_t keymap_rpl;  // key-map kernel: rows per lane group (1, 2, 4)
+  int32_t keymap_rpl;  // key-map kernel: rows per lane group (1, 2)
   int32_t load_prio;   // dense kernel: raised wave priority until the loads are issued
   uint64_t prot_mask;  // dense kernel: bit h set = head h protected (H <= 64 with a head map)
   uint64_t code_hblk;  // dense kernel: bytes of one quantized head's code block

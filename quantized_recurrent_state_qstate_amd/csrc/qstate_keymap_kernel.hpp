@@ -23,29 +23,70 @@ namespace {
 // 16 bytes at a dword-aligned address (global memory takes 128-bit accesses
 // at 4-byte alignment).
 typedef uint32_t u32x4a4_t __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint32_t u32x2a4_t __attribute__((ext_vector_type(2), aligned(4)));
 
-// Up to 4*NW valid bytes (nbytes, a multiple of 4) of a lane's slice at the
-// dword-aligned p: 128-bit accesses when the whole slice exists, else whole
-// dwords up to the valid end; the rest of w is zero.
+// A lane's slice of a stored row: the NW dwords at byte `off` of the row that
+// starts at byte `rowo` of its head block (rowbytes long, a multiple of 4),
+// of which the first nb exist.  Read in pieces of up to 16 bytes with no
+// branch (a load inside a lane-dependent branch makes the compiler wait for
+// it where the branch joins): a whole piece from its own address; a partial
+// one from the piece-sized window that ends at the row end, moved up to the
+// block start when the row is shorter than a piece (a non-empty block is a
+// whole number of 16-byte units, so the window stays inside it); a missing
+// one from `so` bytes past the block (the start of whichever of the head's
+// two blocks is non-empty).  slice_fix, applied once the loads have landed,
+// moves the valid dwords down and zeroes the rest.
 template <int NW>
-__device__ __forceinline__ void load_dwords(const uint8_t* p, uint32_t nbytes, uint32_t (&w)[NW]) {
-  if constexpr (NW % 4 == 0) {
-    if (nbytes == 4u * NW) {
+constexpr int slice_pw() { return NW >= 4 ? 4 : NW; }   // dwords per piece
+
+template <int NW>
+__device__ __forceinline__ void slice_load(const uint8_t* blk, uint32_t rowo, uint32_t rowbytes, uint32_t off,
+                                           int64_t so, uint32_t (&w)[NW], uint32_t (&sh)[NW / slice_pw<NW>()],
+                                           uint32_t (&nbv)[NW / slice_pw<NW>()]) {
+  constexpr int PW = slice_pw<NW>();
+  constexpr uint32_t PB = 4u * PW;
 #pragma unroll
-      for (int i = 0; i < NW / 4; ++i) {
-        const u32x4a4_t t = ld_nt(reinterpret_cast<const u32x4a4_t*>(p) + i);
-        w[4 * i] = t.x;
-        w[4 * i + 1] = t.y;
-        w[4 * i + 2] = t.z;
-        w[4 * i + 3] = t.w;
-      }
-      return;
+  for (int c = 0; c < NW / PW; ++c) {
+    const uint32_t po = off + PB * (uint32_t)c;
+    const uint32_t nb = rowbytes > po ? (rowbytes - po < PB ? rowbytes - po : PB) : 0u;
+    const uint32_t end = rowo + rowbytes;                       // row end within the block
+    const uint32_t win = end >= PB ? end - PB : 0u;             // window ending there, clamped
+    const uint32_t o = nb == PB ? rowo + po : win;
+    const uint8_t* a = blk + (nb > 0u ? (int64_t)o : so);
+    nbv[c] = nb;
+    sh[c] = nb > 0u ? (rowo + po - o) / 4u : 0u;
+    if constexpr (PW == 4) {
+      const u32x4a4_t v = ld_nt(reinterpret_cast<const u32x4a4_t*>(a));
+      w[4 * c] = v.x; w[4 * c + 1] = v.y; w[4 * c + 2] = v.z; w[4 * c + 3] = v.w;
+    } else if constexpr (PW == 2) {
+      const u32x2a4_t v = ld_nt(reinterpret_cast<const u32x2a4_t*>(a));
+      w[2 * c] = v.x; w[2 * c + 1] = v.y;
+    } else {
+      w[c] = ld_nt(reinterpret_cast<const uint32_t*>(a));
     }
   }
-  const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
-#pragma unroll
-  for (int i = 0; i < NW; ++i) w[i] = (4u * (uint32_t)i < nbytes) ? ld_nt(q + i) : 0u;
 }
+
+template <int NW>
+__device__ __forceinline__ void slice_fix(uint32_t (&w)[NW], const uint32_t (&sh)[NW / slice_pw<NW>()],
+                                          const uint32_t (&nbv)[NW / slice_pw<NW>()]) {
+  constexpr int PW = slice_pw<NW>();
+#pragma unroll
+  for (int c = 0; c < NW / PW; ++c) {
+    uint32_t t[PW];
+#pragma unroll
+    for (int i = 0; i < PW; ++i) t[i] = w[PW * c + i];
+#pragma unroll
+    for (int i = 0; i < PW; ++i) {
+      uint32_t x = t[i];
+#pragma unroll
+      for (int d = 1; d < PW; ++d)
+        if (i + d < PW) x = sh[c] == (uint32_t)d ? t[i + d] : x;
+      w[PW * c + i] = 4u * (uint32_t)i < nbv[c] ? x : 0u;
+    }
+  }
+}
+
 template <int NW>
 __device__ __forceinline__ void store_dwords(uint8_t* p, uint32_t nbytes, const uint32_t (&w)[NW]) {
   if constexpr (NW % 4 == 0) {
@@ -72,7 +113,7 @@ __device__ __forceinline__ void store_dwords(uint8_t* p, uint32_t nbytes, const 
 // so each state access of the wave covers one contiguous stretch; the
 // workgroup's per-row outputs and scales are collected in LDS and stored as
 // whole cache lines.
-template <int QB, int RND, int DELTA, int EPL, int LPR, int EH, int BDR, int DKEY, int RPL>
+template <int QB, int RND, int DELTA, int EPL, int LPR, int EH, int BDR, int DKEY, int RPL, int INBF>
 __global__ __launch_bounds__(256) void k_step_keymap(const Args a) {
   constexpr int DK = EPL * LPR;
   constexpr int GPW = 64 / LPR;            // row groups per wave
@@ -80,7 +121,8 @@ __global__ __launch_bounds__(256) void k_step_keymap(const Args a) {
   constexpr int SRB = sr_bits_of<RND>();
   constexpr int CW = EPL * QB / 32;        // code words per lane and row
   constexpr int HW = EH / 2;               // 16-bit value words per lane and row
-  static_assert(EH % 2 == 0, "protected slots come in dword pairs");
+  static_assert(EH % 2 == 0 && EH >= 2, "protected slots come in dword pairs");
+  static_assert(DK <= 256, "one key per thread in the slot permutation");
   if (a.load_prio) __builtin_amdgcn_s_setprio(3);   // raised until the loads are issued
   const int lane = threadIdx.x & (LPR - 1);
   const int g = threadIdx.x / LPR;         // row group
@@ -96,12 +138,18 @@ __global__ __launch_bounds__(256) void k_step_keymap(const Args a) {
   const int crow0 = (int)chunk * RW;                          // first row of the workgroup
   const int v0 = crow0 + (g / GPW) * GPW * RPL + g % GPW;     // rows v0 + GPW r
 
-  const int nq = a.t.nq[h];
+  // per-head layout: read-only tables at a uniform index, read through the
+  // constant address space (scalar loads, all three issued together)
+  typedef const int32_t __attribute__((address_space(4)))* cint_p;
+  typedef const uint64_t __attribute__((address_space(4)))* cu64_p;
+  const int nq = ((cint_p)a.t.nq)[h];
+  const uint64_t coff_h = ((cu64_p)a.t.code_off)[h];
+  const uint64_t hoff_h = ((cu64_p)a.t.hp_off)[h];
   const int nhp = DK - nq;
   const uint32_t rq = code_row_bytes(nq, QB);
   const uint32_t rh = hp_row_bytes(nhp, 2);
-  const uint8_t* cblk = a.codes + (uint64_t)b * a.code_bstride + a.t.code_off[h];
-  const uint8_t* hblk = a.hp + (uint64_t)b * a.hp_bstride + a.t.hp_off[h];
+  const uint8_t* cblk = a.codes + (uint64_t)b * a.code_bstride + coff_h;
+  const uint8_t* hblk = a.hp + (uint64_t)b * a.hp_bstride + hoff_h;
 
   // this lane's byte ranges in the two rows, and how many of them exist
   constexpr uint32_t CB = EPL * QB / 8, HB = EH * 2;
@@ -109,40 +157,48 @@ __global__ __launch_bounds__(256) void k_step_keymap(const Args a) {
   const uint32_t cvalid = rq > coff ? (rq - coff < CB ? rq - coff : CB) : 0u;
   const uint32_t hvalid = rh > hoff ? (rh - hoff < HB ? rh - hoff : HB) : 0u;
 
-  // state loads first
-  uint32_t cw[RPL][CW], hw[RPL][HW > 0 ? HW : 1];
+  // state loads first, then the per-row and per-head inputs: all issued
+  // before anything waits (rows past dv read row 0 and are not used; a head
+  // has at least one of its two blocks, whose start is readable)
+  const uint8_t* sblk = rq > 0u ? cblk : hblk;
+  const int64_t cso = sblk - cblk, hso = sblk - hblk;   // the readable block start, from each block
+  uint32_t cw[RPL][CW], hw[RPL][HW];
+  uint32_t csh[RPL][CW / slice_pw<CW>()], cnb[RPL][CW / slice_pw<CW>()];
+  uint32_t hsh[RPL][HW / slice_pw<HW>()], hnb[RPL][HW / slice_pw<HW>()];
   float s_old[RPL], vin[RPL];
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
     const int v = v0 + GPW * r;
-    const bool ok = v < a.dv;
-    const int vr = ok ? v : 0;
-    load_dwords<CW>(cblk + (uint64_t)vr * rq + coff, ok ? cvalid : 0u, cw[r]);
-    load_dwords<HW>(hblk + (uint64_t)vr * rh + hoff, ok ? hvalid : 0u, hw[r]);
+    const uint32_t vr = (uint32_t)(v < a.dv ? v : 0);
+    slice_load<CW>(cblk, vr * rq, rq, coff, cso, cw[r], csh[r], cnb[r]);
+    slice_load<HW>(hblk, vr * rh, rh, hoff, hso, hw[r], hsh[r], hnb[r]);
   }
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
     const int v = v0 + GPW * r;
     const uint64_t row = bh * (uint64_t)a.dv + (uint64_t)(v < a.dv ? v : 0);
     s_old[r] = ld_nt(a.scales + row);
-    vin[r] = a.in_bf16 ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(a.v)[row])
-                       : reinterpret_cast<const float*>(a.v)[row];
+    vin[r] = load_in_scalar<INBF>(a.v, row);
   }
   const float dh = DKEY ? 1.0f : a.decay[bh];
   const float beta = a.beta ? a.beta[bh] : 1.0f;
+  // this thread's k, q (and per-key decay) value for the slot permutation
+  const int tk = (int)threadIdx.x < DK ? (int)threadIdx.x : 0;
+  const uint64_t kidx = bh * DK + (uint64_t)tk;
+  const float kv0 = load_in_scalar<INBF>(a.k, kidx);
+  const float qv0 = load_in_scalar<INBF>(a.q, kidx);
+  const float dd0 = DKEY ? a.decay[kidx] : 0.0f;
+  const uint16_t sl0 = a.t.slots[(uint64_t)h * DK + tk];
+  if (a.load_prio) __builtin_amdgcn_s_setprio(0);
 
   // k, q (and per-key decay) permuted into slot order: code slots in
   // lc[0..DK), protected slots in lh[0..DK); slots past nq (nhp) hold 0
   __shared__ __align__(16) float lc[3][DK];
   __shared__ __align__(16) float lh[3][DK];
-  for (int t = threadIdx.x; t < DK; t += blockDim.x) {
-    const uint16_t sl = a.t.slots[(uint64_t)h * DK + t];
-    const uint64_t idx = bh * DK + (uint64_t)t;
-    const float kv = a.in_bf16 ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(a.k)[idx])
-                               : reinterpret_cast<const float*>(a.k)[idx];
-    const float qv = a.in_bf16 ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(a.q)[idx])
-                               : reinterpret_cast<const float*>(a.q)[idx];
-    const float dd = DKEY ? a.decay[idx] : 0.0f;
+  if ((int)threadIdx.x < DK) {   // 256 threads, dk 128: one key each
+    const int t = (int)threadIdx.x;
+    const uint16_t sl = sl0;
+    const float kv = kv0, qv = qv0, dd = dd0;
     float(*dst)[DK] = (sl & kSlotProt) ? lh : lc;
     const int s = sl & 0x7FFF;
     dst[0][s] = kv;
@@ -160,7 +216,11 @@ __global__ __launch_bounds__(256) void k_step_keymap(const Args a) {
     }
   }
   __syncthreads();
-  if (a.load_prio) __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) {
+    slice_fix<CW>(cw[r], csh[r], cnb[r]);
+    slice_fix<HW>(hw[r], hsh[r], hnb[r]);
+  }
 
   const float* kc = lc[0] + lane * EPL;
   const float* qc = lc[1] + lane * EPL;

@@ -73,16 +73,16 @@ hipError_t launch_lrb_t(const Args& a, hipStream_t s) {
                          : launch_lrb_r<QB, RND, DELTA, EPL, 16>(a, s);
 }
 
-template <int QB, int RND, int DELTA, int LPR, int EH, int RPL>
+template <int QB, int RND, int DELTA, int LPR, int EH, int RPL, int INBF>
 hipError_t launch_keymap_eh(const Args& a, hipStream_t s) {
   constexpr int EPL = 128 / LPR;
   const dim3 grid((uint32_t)((uint64_t)a.B * (uint64_t)a.H * (uint64_t)a.row_chunks));
   if (a.bdr) {
-    if (a.decay_key) hipLaunchKernelGGL((k_step_keymap<QB, RND, DELTA, EPL, LPR, EH, 1, 1, RPL>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((k_step_keymap<QB, RND, DELTA, EPL, LPR, EH, 1, 0, RPL>), grid, dim3(256), 0, s, a);
+    if (a.decay_key) hipLaunchKernelGGL((k_step_keymap<QB, RND, DELTA, EPL, LPR, EH, 1, 1, RPL, INBF>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_step_keymap<QB, RND, DELTA, EPL, LPR, EH, 1, 0, RPL, INBF>), grid, dim3(256), 0, s, a);
   } else {
-    if (a.decay_key) hipLaunchKernelGGL((k_step_keymap<QB, RND, DELTA, EPL, LPR, EH, 0, 1, RPL>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((k_step_keymap<QB, RND, DELTA, EPL, LPR, EH, 0, 0, RPL>), grid, dim3(256), 0, s, a);
+    if (a.decay_key) hipLaunchKernelGGL((k_step_keymap<QB, RND, DELTA, EPL, LPR, EH, 0, 1, RPL, INBF>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_step_keymap<QB, RND, DELTA, EPL, LPR, EH, 0, 0, RPL, INBF>), grid, dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }
@@ -90,15 +90,16 @@ hipError_t launch_keymap_eh(const Args& a, hipStream_t s) {
 template <int QB, int RND, int DELTA, int EH>
 hipError_t launch_keymap_rpl(const Args& a, hipStream_t s) {
   switch (a.keymap_rpl) {
-    case 1: return launch_keymap_eh<QB, RND, DELTA, 8, EH, 1>(a, s);
-    case 2: return launch_keymap_eh<QB, RND, DELTA, 8, EH, 2>(a, s);
-    case 4: return launch_keymap_eh<QB, RND, DELTA, 8, EH, 4>(a, s);
+    case 1: return a.in_bf16 ? launch_keymap_eh<QB, RND, DELTA, 8, EH, 1, 1>(a, s)
+                             : launch_keymap_eh<QB, RND, DELTA, 8, EH, 1, 0>(a, s);
+    case 2: return a.in_bf16 ? launch_keymap_eh<QB, RND, DELTA, 8, EH, 2, 1>(a, s)
+                             : launch_keymap_eh<QB, RND, DELTA, 8, EH, 2, 0>(a, s);
   }
   return hipErrorInvalidValue;
 }
 
 // dk 128: 8 lanes per row (16 code slots each); keymap_eh protected slots
-// per lane, keymap_rpl rows per lane group
+// per lane, keymap_rpl (1 or 2) rows per lane group
 template <int QB, int RND, int DELTA>
 hipError_t launch_keymap_t(const Args& a, hipStream_t s) {
   switch (a.keymap_eh) {

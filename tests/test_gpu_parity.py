@@ -314,13 +314,16 @@ EDGE = {
                                 map_density=0.05),
     "keymap_fp16_mostly_protected": dict(kind="additive", decay_mode="key", dk=128, dv=33, H=2, B=3, qbits=8,
                                          map_mode="key", hp_dtype="fp16", map_density=0.9),
-    # key-map kernel with 1 and 4 rows per lane group (ragged last chunk)
+    # key-map kernel with 1 and 2 rows per lane group (ragged last chunk),
+    # fp32 inputs, rows shorter than 16 bytes
     "keymap_rows1_delta": dict(kind="delta", decay_mode="head", dk=128, dv=72, H=2, B=2, qbits=8,
                                map_mode="key", hp_dtype="fp16", map_density=0.1, keymap_rows=1),
-    "keymap_rows4_delta_bf16": dict(kind="delta", decay_mode="head", dk=128, dv=200, H=2, B=2, qbits=8,
-                                    map_mode="key", hp_dtype="bf16", map_density=0.3, keymap_rows=4),
-    "keymap_rows4_int4_sr8": dict(kind="additive", decay_mode="key", dk=128, dv=40, H=3, B=2, qbits=4,
-                                  sr_bits=8, map_mode="key", hp_dtype="fp16", keymap_rows=4),
+    "keymap_rows2_delta_bf16_dv200": dict(kind="delta", decay_mode="head", dk=128, dv=200, H=2, B=2, qbits=8,
+                                          map_mode="key", hp_dtype="bf16", map_density=0.3),
+    "keymap_int4_sr8_dv24": dict(kind="additive", decay_mode="key", dk=128, dv=24, H=3, B=2, qbits=4,
+                                 sr_bits=8, map_mode="key", hp_dtype="fp16"),
+    "keymap_fp32_in_short_rows": dict(kind="delta", decay_mode="key", dk=128, dv=48, H=3, B=2, qbits=8,
+                                      in_dtype="fp32", map_mode="key", hp_dtype="fp16", map_density=0.93),
     # delta rule with a decay per key channel (channel-gated, Kimi-Linear)
     "kda_dk128": dict(kind="delta", decay_mode="key", dk=128, dv=64, H=2, B=2, qbits=8),
     "kda_dk128_8lanes_fp32_in": dict(kind="delta", decay_mode="key", dk=128, dv=96, H=2, B=2, qbits=8,
