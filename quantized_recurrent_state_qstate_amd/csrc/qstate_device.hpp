@@ -258,6 +258,24 @@ __device__ __forceinline__ float load_in1(const void* base, int bf16, uint64_t i
   return reinterpret_cast<const float*>(base)[idx];
 }
 
+// One input element (bf16 or fp32 by a runtime flag) read with no branch:
+// the 16-bit word at element idx (inside the array either way) and the
+// 32-bit word at element idx, or at element 0 for bf16 input (so it stays
+// inside the array); in_raw_value picks and widens, once the loads landed.
+struct InRaw {
+  uint16_t h;
+  uint32_t w;
+};
+__device__ __forceinline__ InRaw in_raw_load(const void* base, int bf16, uint64_t idx) {
+  InRaw r;
+  r.h = reinterpret_cast<const uint16_t*>(base)[idx];
+  r.w = reinterpret_cast<const uint32_t*>(base)[bf16 ? 0 : idx];
+  return r;
+}
+__device__ __forceinline__ float in_raw_value(const InRaw& r, int bf16) {
+  return bf16 ? bf16_bits_to_f32(r.h) : __uint_as_float(r.w);
+}
+
 // EPL consecutive input elements (bf16 or fp32) starting at element idx.
 template <int EPL>
 __device__ __forceinline__ void load_in(const void* base, int bf16, uint64_t idx, float (&f)[EPL]) {

@@ -94,26 +94,50 @@ __global__ __launch_bounds__(256) void k_step_lrb(const Args a) {
   const float beta = a.beta ? a.beta[bh] : 1.0f;
   int n = a.n[bh];
 
-  // loads: this thread's W row (t < dv) and U row (t < dk), its u, s_old,
-  // k, q, decay
+  // Every load at entry, in one burst with no lane-dependent branch (a load
+  // inside such a branch makes the compiler wait for it where the branch
+  // joins): this thread's W row (t < dv) and U row (t < dk), its v, s_old,
+  // k, q, decay (inputs read as raw 16- or 32-bit words, widened later),
+  // and the codes of its lane group's first NPF rows, which phase B (and
+  // the delta rule's row pass) use after the buffer steps.
+  const int lane8 = tid & 7;
+  const int grp = tid >> 3;
+  const int k0 = lane8 * EPL;
+  constexpr int NPF = 4;                       // rows grp + 32 i, i < NPF
+  const uint8_t* gc = code_block(a, b, h);
+  uint32_t pf[NPF][CW];
+#pragma unroll
+  for (int i = 0; i < NPF; ++i) {
+    const int v = grp + 32 * i;
+    load_bytes<EPL * QB / 8, true>(gc + (uint64_t)(v < dv ? v : 0) * (DK * QB / 8) + k0 * QB / 8, pf[i]);
+  }
+  const int tv = tid < dv ? tid : 0, tk = tid < DK ? tid : 0;
   float Wr[RANK], Ur[RANK];
-  float uv = 0.0f, so = 0.0f, kk = 0.0f, qq = 0.0f, dd = 0.0f;
 #pragma unroll
   for (int j = 0; j < RANK; ++j) {
-    Wr[j] = (tid < dv && j < r) ? Wg[tid * r + j] : 0.0f;
-    Ur[j] = (tid < DK && j < r) ? Ug[tid * r + j] : 0.0f;
+    Wr[j] = j < r ? Wg[tv * r + j] : 0.0f;   // j < r: uniform
+    Ur[j] = j < r ? Ug[tk * r + j] : 0.0f;
   }
-  if (tid < dv) {
-    const uint64_t row = (uint64_t)bh * (uint64_t)dv + (uint64_t)tid;
-    uv = load_in1(a.v, a.in_bf16, row);
-    if constexpr (!DELTA) uv = beta * uv;
-    so = ld_nt(a.scales + row);
+  const uint64_t trow = (uint64_t)bh * (uint64_t)dv + (uint64_t)tv;
+  const uint64_t tkey = (uint64_t)bh * DK + (uint64_t)tk;
+  const InRaw vraw = in_raw_load(a.v, a.in_bf16, trow);
+  const float so_raw = ld_nt(a.scales + trow);
+  const InRaw kraw = in_raw_load(a.k, a.in_bf16, tkey);
+  const InRaw qraw = in_raw_load(a.q, a.in_bf16, tkey);
+  const float dd_raw = DKEY ? a.decay[tkey] : a.decay[bh];
+  // widen and mask, after the burst
+  const bool tv_ok = tid < dv, tk_ok = tid < DK;
+#pragma unroll
+  for (int j = 0; j < RANK; ++j) {
+    Wr[j] = tv_ok ? Wr[j] : 0.0f;
+    Ur[j] = tk_ok ? Ur[j] : 0.0f;
   }
-  if (tid < DK) {
-    kk = load_in1(a.k, a.in_bf16, (uint64_t)bh * DK + tid);
-    qq = load_in1(a.q, a.in_bf16, (uint64_t)bh * DK + tid);
-    dd = DKEY ? a.decay[(uint64_t)bh * DK + tid] : a.decay[bh];
-  }
+  float uv = tv_ok ? in_raw_value(vraw, a.in_bf16) : 0.0f;
+  if constexpr (!DELTA) uv = beta * uv;
+  const float so = tv_ok ? so_raw : 0.0f;
+  const float kk = tk_ok ? in_raw_value(kraw, a.in_bf16) : 0.0f;
+  const float qq = tk_ok ? in_raw_value(qraw, a.in_bf16) : 0.0f;
+  const float dd = tk_ok ? dd_raw : 0.0f;
 
   if constexpr (DELTA) {
     // rows: w_v = sum_k (decayed S_hat)[v][k] k_k, 8 lanes per row, four
@@ -125,23 +149,26 @@ __global__ __launch_bounds__(256) void k_step_lrb(const Args a) {
     }
     if (tid < dv) sol[tid] = so;
     __syncthreads();
-    const int lane8 = tid & 7;
-    const int k0 = lane8 * EPL;
     float kf[EPL], df[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
       kf[i] = kl[k0 + i];
       df[i] = dl[k0 + i];
     }
-    const uint8_t* gc = code_block(a, b, h);
-    for (int v0 = tid >> 3; v0 < dv; v0 += 128) {
-      uint32_t cw[4][CW];
+    for (int v0 = grp; v0 < dv; v0 += 32 * NPF) {
+      uint32_t cw[NPF][CW];
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
-        if (v0 + 32 * rr < dv)
-          load_bytes<EPL * QB / 8, false>(gc + (uint64_t)(v0 + 32 * rr) * (DK * QB / 8) + k0 * QB / 8, cw[rr]);
+      for (int rr = 0; rr < NPF; ++rr) {
+        if (v0 == grp) {   // uniform: the prefetched rows
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
+          for (int j = 0; j < CW; ++j) cw[rr][j] = pf[rr][j];
+        } else {
+          const int v = v0 + 32 * rr;
+          load_bytes<EPL * QB / 8, false>(gc + (uint64_t)(v < dv ? v : 0) * (DK * QB / 8) + k0 * QB / 8, cw[rr]);
+        }
+      }
+#pragma unroll
+      for (int rr = 0; rr < NPF; ++rr) {
         const int v = v0 + 32 * rr;
         if (v < dv) {   // uniform over the 8 lanes of a row
           const float s = sol[v];
@@ -301,10 +328,7 @@ __global__ __launch_bounds__(256) void k_step_lrb(const Args a) {
   if (tid == 0) a.n[bh] = n_new;
   __syncthreads();
 
-  // Phase B: rows, 8 lanes per row, rows g, g + 32, ...
-  const int lane8 = tid & 7;
-  const int grp = tid >> 3;
-  const int k0 = lane8 * EPL;
+  // Phase B: rows, 8 lanes per row, rows grp, grp + 32, ...
   float kf[EPL], qf[EPL], df[EPL];
   uint32_t smask = 0u, mmask = 0u;
 #pragma unroll
@@ -315,15 +339,8 @@ __global__ __launch_bounds__(256) void k_step_lrb(const Args a) {
     smask |= (smalll[k0 + i] ? 1u : 0u) << i;
     mmask |= (mflagl[k0 + i] ? 1u : 0u) << i;
   }
-  uint8_t* gcode = const_cast<uint8_t*>(code_block(a, b, h));
-  uint32_t cw_next[CW];
-  if (grp < dv) load_bytes<EPL * QB / 8, true>(gcode + (uint64_t)grp * (DK * QB / 8) + k0 * QB / 8, cw_next);
-  for (int v = grp; v < dv; v += 32) {
-    uint32_t cw[CW];
-#pragma unroll
-    for (int i = 0; i < CW; ++i) cw[i] = cw_next[i];
-    if (v + 32 < dv)   // next row's codes in flight while this one computes
-      load_bytes<EPL * QB / 8, true>(gcode + (uint64_t)(v + 32) * (DK * QB / 8) + k0 * QB / 8, cw_next);
+  uint8_t* gcode = const_cast<uint8_t*>(gc);
+  auto row_step = [&](const int v, const uint32_t (&cw)[CW]) {
     const uint64_t row = (uint64_t)bh * (uint64_t)dv + (uint64_t)v;
     const float s_old = sol[v];
     const float uu = ul[v], upv = upl[v];
@@ -372,6 +389,14 @@ __global__ __launch_bounds__(256) void k_step_lrb(const Args a) {
       ol[v] = o + lrl[v];
       sl_[v] = scale;
     }
+  };
+#pragma unroll
+  for (int i = 0; i < NPF; ++i)
+    if (grp + 32 * i < dv) row_step(grp + 32 * i, pf[i]);   // whole row groups
+  for (int v = grp + 32 * NPF; v < dv; v += 32) {            // dv > 32 NPF only
+    uint32_t cw[CW];
+    load_bytes<EPL * QB / 8, true>(gcode + (uint64_t)v * (DK * QB / 8) + k0 * QB / 8, cw);
+    row_step(v, cw);
   }
   __syncthreads();
   if (tid < dv) {
