@@ -206,6 +206,26 @@ qs_status qstate_decode_step(qstate_handle* h, const qstate_tensors* state,
                              const qstate_inputs* in, float* out, uint64_t step,
                              void* stream);
 
+/* One decode step for a batch of n sequences whose states live in a pool
+ * of B state slots (the handle's B), as a server with continuous batching
+ * keeps them; the operation on each (sequence, head) is that of
+ * qstate_decode_step [LoReS, PU].
+ *   pool: the stored state of all B slots, in place.
+ *   in, out: the batch's inputs and outputs, laid out as for
+ *     qstate_decode_step with B replaced by n (batch element b first).
+ *   slot: device int32 [n]; batch element b reads and writes state slot
+ *     slot[b].  An element whose slot lies outside [0, B) is skipped: no
+ *     state is touched and its outputs are not written.  Two elements with
+ *     the same slot race.
+ *   step: device uint64 [n]; element b's step: its Philox counter word (with
+ *     the element index taken in the pool, e = ((slot*H+h)*dv+v)*dk+j, so
+ *     its random bits do not depend on its batch position) and the LRB merge
+ *     clock.
+ * n = 0 is a no-op; n > B is QS_EINVAL.  Never allocates or synchronizes. */
+qs_status qstate_decode_step_batch(qstate_handle* h, const qstate_tensors* pool,
+                                   const qstate_inputs* in, float* out, int32_t n,
+                                   const int32_t* slot, const uint64_t* step, void* stream);
+
 /* Stored state -> fp32 effective state S [B][H][dv][dk] (device):
  * scale * code for quantized channels, the widened value for protected
  * ones, plus W U^T when LRB is on. */

@@ -60,6 +60,9 @@ def lib():
         L.orc_step.argtypes = [c_cfg, P(_State), fp, fp, fp, fp, fp, fp, ctypes.c_uint64, fp,
                                P(ctypes.c_int64), ctypes.c_int64]
         L.orc_step.restype = ctypes.c_int
+        L.orc_step_batch.argtypes = [c_cfg, P(_State), fp, fp, fp, fp, fp, fp, ctypes.c_int32,
+                                     P(ctypes.c_int32), P(ctypes.c_uint64)]
+        L.orc_step_batch.restype = ctypes.c_int
         _LIB = L
     return _LIB
 
@@ -233,6 +236,34 @@ def step(cfg: Cfg, st: dict, q, k, v, decay, beta=None, step: int = 0, heads=Non
     if rc:
         raise ValueError("oracle step failed")
     return (out, sp) if want_sp else out
+
+
+def step_batch(cfg: Cfg, st: dict, q, k, v, decay, beta, slot, steps, out=None):
+    """A step for n = len(slot) sequences whose states sit in slots of ``st``
+    (the config's B states); inputs [n,H,...]; element b uses state slot
+    slot[b] and step steps[b].  Returns o [n,H,dv]."""
+    H, dk, dv = cfg.H, cfg.dk, cfg.dv
+    slot = np.ascontiguousarray(slot, dtype=np.int32)
+    steps = np.ascontiguousarray(steps, dtype=np.uint64)
+    n = slot.size
+    q = _f32(q, (n, H, dk))
+    k = _f32(k, (n, H, dk))
+    v = _f32(v, (n, H, dv))
+    decay = _f32(decay, (n, H) if cfg.decay_mode == "head" else (n, H, dk))
+    beta_p = None
+    if beta is not None:
+        beta = _f32(beta, (n, H))
+        beta_p = _fp(beta)
+    if out is None:
+        out = np.zeros((n, H, dv), np.float32)
+    c = cfg.c()
+    s = _state_struct(st)
+    rc = lib().orc_step_batch(ctypes.byref(c), ctypes.byref(s), _fp(q), _fp(k), _fp(v), _fp(decay), beta_p,
+                              _fp(out), n, slot.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                              steps.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)))
+    if rc:
+        raise ValueError("oracle batch step failed")
+    return out
 
 
 def philox(ctr, key):

@@ -587,24 +587,27 @@ static void lrb_phase(const orc_cfg* c, float* W, float* U, int32_t* np_, const 
 /*   delta rule (Gated DeltaNet):   S <- alpha S + u k^T,                     */
 /*                                   u = beta (v - alpha S k)                 */
 /* i.e. alpha (S - beta S k k^T) + beta v k^T written in factored form.      */
+/* bh indexes the head's state (and its Philox element indices), bi its     */
+/* inputs and output: equal for a plain step, slot and batch position for a  */
+/* batched one.                                                              */
 /* Element update: Sp = fmaf(u_v, k_k, (d_k * s_v) * code) for a quantized   */
 /* channel (the decay scales the row scale), fmaf(u_v, k_k, d_k * value) for */
 /* a protected one; readout o_v = sum_k Sp[v][k] q_k (+ buffer term).        */
 /* ------------------------------------------------------------------------ */
-static void head_step(const orc_cfg* c, const layout_t* L, orc_state* st, int64_t bh,
+static void head_step(const orc_cfg* c, const layout_t* L, orc_state* st, int64_t bh, int64_t bi,
                       const float* q, const float* kin, const float* vin, const float* decay,
                       const float* beta, float* out, uint64_t step, float* sp_dbg) {
   const int dk = c->dk, dv = c->dv, r = c->lrb_rank;
   int* slot = (int*)malloc(sizeof(int) * (size_t)dk);
   head_addr a;
   head_address(c, L, st, bh, &a, slot);
-  const float* qh = q + (uint64_t)bh * dk;
-  const float* kh = kin + (uint64_t)bh * dk;
-  const float* vh = vin + (uint64_t)bh * dv;
+  const float* qh = q + (uint64_t)bi * dk;
+  const float* kh = kin + (uint64_t)bi * dk;
+  const float* vh = vin + (uint64_t)bi * dv;
   float* d = (float*)malloc(sizeof(float) * (size_t)dk);
   for (int k = 0; k < dk; ++k)
-    d[k] = (c->decay_mode == 0) ? decay[bh] : decay[(uint64_t)bh * dk + k];
-  const float bt = beta ? beta[bh] : 1.0f;
+    d[k] = (c->decay_mode == 0) ? decay[bi] : decay[(uint64_t)bi * dk + k];
+  const float bt = beta ? beta[bi] : 1.0f;
   float* scales = st->scales + (uint64_t)bh * dv;
 
   float* sh = (float*)malloc(sizeof(float) * (size_t)dv * (size_t)dk);
@@ -693,9 +696,9 @@ static void head_step(const orc_cfg* c, const layout_t* L, orc_state* st, int64_
     double acc = dot_d(sp + (uint64_t)v * dk, qh, dk);
     if (r > 0)
       for (int j = 0; j < st->n[bh]; ++j) acc += (double)W[v * r + j] * z[j];
-    out[(uint64_t)bh * dv + v] = (float)acc;
+    out[(uint64_t)bi * dv + v] = (float)acc;
   }
-  if (sp_dbg) memcpy(sp_dbg + (uint64_t)bh * dv * dk, sp, sizeof(float) * (size_t)dv * (size_t)dk);
+  if (sp_dbg) memcpy(sp_dbg + (uint64_t)bi * dv * dk, sp, sizeof(float) * (size_t)dv * (size_t)dk);
   /* requantize */
   for (int v = 0; v < dv; ++v)
     scales[v] = requantize_row(c, &a, bh, v, sp + (uint64_t)v * dk, sh + (uint64_t)v * dk, step);
@@ -729,11 +732,33 @@ int orc_step(const orc_cfg* c, orc_state* st, const float* q, const float* k, co
         layout_free(&L);
         return -1;
       }
-      head_step(c, &L, st, heads[i], q, k, v, decay, beta, out, step, sp_dbg);
+      head_step(c, &L, st, heads[i], heads[i], q, k, v, decay, beta, out, step, sp_dbg);
     }
   } else {
     for (int64_t bh = 0; bh < BH; ++bh)
-      head_step(c, &L, st, bh, q, k, v, decay, beta, out, step, sp_dbg);
+      head_step(c, &L, st, bh, bh, q, k, v, decay, beta, out, step, sp_dbg);
+  }
+  layout_free(&L);
+  return 0;
+}
+
+/* A step for a batch of n sequences held in slots of the state pool (the
+ * config's B states): batch element b reads its inputs and writes its
+ * output at b and its state at slot[b], with its own step.  An element
+ * whose slot lies outside [0, B) is skipped. */
+int orc_step_batch(const orc_cfg* c, orc_state* st, const float* q, const float* k, const float* v,
+                   const float* decay, const float* beta, float* out, int32_t n, const int32_t* slot,
+                   const uint64_t* step) {
+  layout_t L;
+  if (n < 0 || n > c->B || layout_make(c, &L)) {
+    if (n >= 0 && n <= c->B) layout_free(&L);
+    return -1;
+  }
+  for (int32_t b = 0; b < n; ++b) {
+    if (slot[b] < 0 || slot[b] >= c->B) continue;
+    for (int32_t h = 0; h < c->H; ++h)
+      head_step(c, &L, st, (int64_t)slot[b] * c->H + h, (int64_t)b * c->H + h, q, k, v, decay, beta, out,
+                step[b], NULL);
   }
   layout_free(&L);
   return 0;

@@ -80,6 +80,12 @@ int  orc_dequantize(const orc_cfg* c, const orc_state* st, float* S);
 int  orc_step(const orc_cfg* c, orc_state* st, const float* q, const float* k,
               const float* v, const float* decay, const float* beta, float* out,
               uint64_t step, float* sp_dbg, const int64_t* heads, int64_t nheads);
+/* A step for n sequences held in slots of the pool (the config's B states):
+ * element b's inputs and output at b, its state at slot[b] (skipped when
+ * outside [0, B)), its step step[b].  Returns 0, or -1 for n outside [0, B]. */
+int  orc_step_batch(const orc_cfg* c, orc_state* st, const float* q, const float* k,
+                    const float* v, const float* decay, const float* beta, float* out,
+                    int32_t n, const int32_t* slot, const uint64_t* step);
 
 #ifdef __cplusplus
 }

@@ -22,7 +22,7 @@ MAP = {"none": 0, "head": 1, "key": 2}
 ROUNDING = {"nearest": 0, "stochastic": 1}
 
 EXPORTS = (
-    "qstate_plan", "qstate_init", "qstate_quantize", "qstate_decode_step",
+    "qstate_plan", "qstate_init", "qstate_quantize", "qstate_decode_step", "qstate_decode_step_batch",
     "qstate_dequantize", "qstate_build_map", "qstate_destroy", "qstate_strerror",
     "qstate_last_error", "qstate_kernel_name",
 )
@@ -80,10 +80,11 @@ def lib() -> ctypes.CDLL:
         L.qstate_init.argtypes = [P(Config), P(vp), P(Sizes)]
         L.qstate_quantize.argtypes = [vp, vp, P(Tensors), ctypes.c_uint64, vp]
         L.qstate_decode_step.argtypes = [vp, P(Tensors), P(Inputs), vp, ctypes.c_uint64, vp]
+        L.qstate_decode_step_batch.argtypes = [vp, P(Tensors), P(Inputs), vp, ctypes.c_int32, vp, vp, vp]
         L.qstate_dequantize.argtypes = [vp, P(Tensors), vp, vp]
         L.qstate_build_map.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, vp]
         for f in ("qstate_plan", "qstate_init", "qstate_quantize", "qstate_decode_step",
-                  "qstate_dequantize", "qstate_build_map"):
+                  "qstate_decode_step_batch", "qstate_dequantize", "qstate_build_map"):
             getattr(L, f).restype = ctypes.c_int
         L.qstate_destroy.argtypes = [vp]
         L.qstate_destroy.restype = None

@@ -170,3 +170,22 @@ class QState:
         _lib.check(_lib.lib().qstate_decode_step(self._h, ctypes.byref(t), ctypes.byref(inp), _ptr(out), step,
                                                  self._stream(stream)), "qstate_decode_step")
         return out
+
+    def step_batch(self, pool: dict, slot, step, q, k, v, decay, beta=None, out=None, stream=None):
+        """One decode step for n = len(slot) sequences whose states sit in the
+        slots `slot` (int32 [n], device) of `pool` (this handle's B slots),
+        each with its own step (uint64 stored as int64 [n], device); inputs
+        [n,H,...]; returns o [n,H,dv] fp32."""
+        import torch
+        c = self.cfg
+        n = int(slot.numel())
+        if slot.dtype != torch.int32 or step.dtype not in (torch.int64, torch.uint64) or step.numel() != n:
+            raise ValueError("slot must be int32 [n] and step 64-bit [n]")
+        if out is None:
+            out = torch.empty((n, c.H, c.dv), dtype=torch.float32, device=self.device)
+        t = self._tensors(pool)
+        inp = _lib.Inputs(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(beta))
+        _lib.check(_lib.lib().qstate_decode_step_batch(self._h, ctypes.byref(t), ctypes.byref(inp), _ptr(out), n,
+                                                       _ptr(slot), _ptr(step), self._stream(stream)),
+                   "qstate_decode_step_batch")
+        return out

@@ -316,6 +316,7 @@ qs::Args base_args(const qstate_handle* h, const qstate_tensors* st) {
   a.seed_lo = (uint32_t)c.seed;
   a.seed_hi = (uint32_t)(c.seed >> 32);
   a.mixed_lds = h->plan.lds;
+  a.nslots = c.B;
   return a;
 }
 
@@ -430,6 +431,40 @@ qs_status qstate_decode_step(qstate_handle* h, const qstate_tensors* state, cons
   hipError_t e = qs::launch_step(h->plan.family, h->cfg.qbits, h->rnd, h->cfg.kind == QS_KIND_DELTA, a,
                                  reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(QS_EHIP, "step launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+qs_status qstate_decode_step_batch(qstate_handle* h, const qstate_tensors* pool, const qstate_inputs* in,
+                                   float* out, int32_t n, const int32_t* slot, const uint64_t* step,
+                                   void* stream) {
+  if (!h) return fail(QS_EINVAL, "handle is NULL");
+  qs_status s = check_tensors(h, pool);
+  if (s != QS_OK) return s;
+  if (!in) return fail(QS_EINVAL, "inputs are NULL");
+  if (n < 0 || n > h->cfg.B) return fail(QS_EINVAL, "batch size %d (pool of %d states)", n, h->cfg.B);
+  if (n == 0) return ok();
+  if (!slot || !aligned(slot, 4)) return fail(QS_EINVAL, "slot NULL or misaligned");
+  if (!step || !aligned(step, 8)) return fail(QS_EINVAL, "step NULL or misaligned");
+  if (!in->q || !in->k || !in->v || !in->decay) return fail(QS_EINVAL, "q, k, v or decay is NULL");
+  if (!aligned(in->q, 16) || !aligned(in->k, 16) || !aligned(in->v, 16) || !aligned(in->decay, 16))
+    return fail(QS_EINVAL, "q, k, v and decay must be 16-byte aligned");
+  if (in->beta && !aligned(in->beta, 4)) return fail(QS_EINVAL, "beta misaligned");
+  if (!out || !aligned(out, 4)) return fail(QS_EINVAL, "out NULL or misaligned");
+  if ((s = check_device(h)) != QS_OK) return s;
+  qs::Args a = base_args(h, pool);
+  a.B = n;                 // the grid covers the batch; the state is addressed through slot
+  a.nslots = h->cfg.B;
+  a.slot = slot;
+  a.seq_step = step;
+  a.q = in->q;
+  a.k = in->k;
+  a.v = in->v;
+  a.decay = in->decay;
+  a.beta = in->beta;
+  a.out = out;
+  hipError_t e = qs::launch_step(h->plan.family, h->cfg.qbits, h->rnd, h->cfg.kind == QS_KIND_DELTA, a,
+                                 reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(QS_EHIP, "batch step launch: %s", hipGetErrorString(e));
   return ok();
 }
 

@@ -67,6 +67,20 @@ struct Args {
   uint32_t seed_lo, seed_hi;
   uint32_t step_lo, step_hi;
   uint32_t mixed_lds;  // mixed kernel: dynamic LDS bytes
+  // batched entry point: batch element b reads its inputs and writes its
+  // outputs at b, and its state at slot[b] of a pool of nslots states, with
+  // its own step; null = the plain step (slot b, step above)
+  const int32_t* slot;
+  const uint64_t* seq_step;
+  int32_t nslots;
+};
+
+// One (batch element, head) of a step: index of its inputs and outputs
+// (b*H + h), index of its state (slot*H + h), and its step (Philox counter
+// word and merge clock).
+struct HeadIx {
+  uint64_t in, st;
+  uint32_t step_lo, step_hi;
 };
 
 // Kernel families chosen at init.

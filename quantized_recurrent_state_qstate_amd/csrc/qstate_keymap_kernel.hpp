@@ -134,7 +134,11 @@ __global__ __launch_bounds__(256) void k_step_keymap(const Args a) {
   r0 = r0 >= per_b ? r0 - per_b : r0;
   const uint32_t chunk = r0 % (uint32_t)a.row_chunks;
   const uint32_t h = r0 / (uint32_t)a.row_chunks;
-  const uint64_t bh = (uint64_t)b * (uint64_t)a.H + h;
+  bool ok;
+  const HeadIx ix = head_ix(a, b, h, ok);
+  if (!ok) return;   // uniform: a batch element with no valid state slot
+  const uint64_t bh = ix.in;                               // inputs and outputs
+  const uint32_t bs = (uint32_t)(ix.st / (uint64_t)a.H);   // state slot
   const int crow0 = (int)chunk * RW;                          // first row of the workgroup
   const int v0 = crow0 + (g / GPW) * GPW * RPL + g % GPW;     // rows v0 + GPW r
 
@@ -148,8 +152,8 @@ __global__ __launch_bounds__(256) void k_step_keymap(const Args a) {
   const int nhp = DK - nq;
   const uint32_t rq = code_row_bytes(nq, QB);
   const uint32_t rh = hp_row_bytes(nhp, 2);
-  const uint8_t* cblk = a.codes + (uint64_t)b * a.code_bstride + coff_h;
-  const uint8_t* hblk = a.hp + (uint64_t)b * a.hp_bstride + hoff_h;
+  const uint8_t* cblk = a.codes + (uint64_t)bs * a.code_bstride + coff_h;
+  const uint8_t* hblk = a.hp + (uint64_t)bs * a.hp_bstride + hoff_h;
 
   // this lane's byte ranges in the two rows, and how many of them exist
   constexpr uint32_t CB = EPL * QB / 8, HB = EH * 2;
@@ -176,9 +180,9 @@ __global__ __launch_bounds__(256) void k_step_keymap(const Args a) {
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
     const int v = v0 + GPW * r;
-    const uint64_t row = bh * (uint64_t)a.dv + (uint64_t)(v < a.dv ? v : 0);
-    s_old[r] = ld_nt(a.scales + row);
-    vin[r] = load_in_scalar<INBF>(a.v, row);
+    const uint64_t vc = (uint64_t)(v < a.dv ? v : 0);
+    s_old[r] = ld_nt(a.scales + ix.st * (uint64_t)a.dv + vc);
+    vin[r] = load_in_scalar<INBF>(a.v, bh * (uint64_t)a.dv + vc);
   }
   const float dh = DKEY ? 1.0f : a.decay[bh];
   const float beta = a.beta ? a.beta[bh] : 1.0f;
@@ -236,7 +240,7 @@ __global__ __launch_bounds__(256) void k_step_keymap(const Args a) {
   for (int r = 0; r < RPL; ++r) {
   const int v = v0 + GPW * r;
   if (v < a.dv) {   // whole row groups
-  const uint64_t row = bh * (uint64_t)a.dv + (uint64_t)v;
+  const uint64_t row = ix.st * (uint64_t)a.dv + (uint64_t)v;   // state row (Philox counter)
   // old values: codes (0 past nq: padding and unloaded dwords are zero)
   auto code_at = [&](int i) -> float {
     if constexpr (QB == 8) return (float)(int32_t)(int8_t)(cw[r][i >> 2] >> (8 * (i & 3)));
@@ -311,8 +315,8 @@ __global__ __launch_bounds__(256) void k_step_keymap(const Args a) {
         const uint64_t ew = e0 + (uint64_t)(gblk * PER);
         x[0] = (RND == 1) ? (uint32_t)(ew >> 3) : (uint32_t)(ew >> 4);
         x[1] = 0u;
-        x[2] = a.step_lo;
-        x[3] = a.step_hi;
+        x[2] = ix.step_lo;
+        x[3] = ix.step_hi;
         philox10(x, a.seed_lo, a.seed_hi);
         if constexpr (RND == 2 && EPL < 16) sel = (uint32_t)((ew >> 3) & 1u);
       }
@@ -340,7 +344,7 @@ __global__ __launch_bounds__(256) void k_step_keymap(const Args a) {
     }
   } else {
     uint32_t rb[EPL];
-    if constexpr (RND != 0) rand_bits<RND, EPL>(e0, a.seed_lo, a.seed_hi, a.step_lo, a.step_hi, rb);
+    if constexpr (RND != 0) rand_bits<RND, EPL>(e0, a.seed_lo, a.seed_hi, ix.step_lo, ix.step_hi, rb);
     int32_t code[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
@@ -365,9 +369,9 @@ __global__ __launch_bounds__(256) void k_step_keymap(const Args a) {
   __syncthreads();
   const int t = (int)threadIdx.x;
   if (t < RW && crow0 + t < a.dv) {
-    const uint64_t row0 = bh * (uint64_t)a.dv + (uint64_t)(crow0 + t);
-    st_nt(a.out + row0, ol[t]);
-    st_nt(a.scales + row0, sl_[t]);
+    const uint64_t vt = (uint64_t)(crow0 + t);
+    st_nt(a.out + bh * (uint64_t)a.dv + vt, ol[t]);
+    st_nt(a.scales + ix.st * (uint64_t)a.dv + vt, sl_[t]);
   }
 }
 

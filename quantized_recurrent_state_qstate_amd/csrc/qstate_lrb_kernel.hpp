@@ -74,9 +74,13 @@ __global__ __launch_bounds__(256) void k_step_lrb(const Args a) {
   const int tid = threadIdx.x;
   const int dv = a.dv;
   const int r = a.lrb_rank;
-  const uint32_t bh = blockIdx.x;
-  const uint32_t h = bh % (uint32_t)a.H;
-  const uint32_t b = bh / (uint32_t)a.H;
+  const uint32_t h = blockIdx.x % (uint32_t)a.H;
+  bool ok;
+  const HeadIx ix = head_ix(a, blockIdx.x / (uint32_t)a.H, h, ok);
+  if (!ok) return;   // uniform: a batch element with no valid state slot
+  const uint64_t bh = ix.in;                               // inputs and outputs
+  const uint64_t bhs = ix.st;                              // state: buffer, scales, codes
+  const uint32_t bs = (uint32_t)(bhs / (uint64_t)a.H);
   const float theta = a.lrb_theta;
 
   __shared__ __align__(16) float Wt[RANK][256];   // W transposed, for merges and rows
@@ -89,10 +93,10 @@ __global__ __launch_bounds__(256) void k_step_lrb(const Args a) {
   __shared__ float red[RANK + 4];
   __shared__ uint8_t smalll[DK], mflagl[DK];
 
-  float* Wg = a.W + (uint64_t)bh * (uint64_t)dv * (uint64_t)r;
-  float* Ug = a.U + (uint64_t)bh * (uint64_t)DK * (uint64_t)r;
+  float* Wg = a.W + bhs * (uint64_t)dv * (uint64_t)r;
+  float* Ug = a.U + bhs * (uint64_t)DK * (uint64_t)r;
   const float beta = a.beta ? a.beta[bh] : 1.0f;
-  int n = a.n[bh];
+  int n = a.n[bhs];
 
   // Every load at entry, in one burst with no lane-dependent branch (a load
   // inside such a branch makes the compiler wait for it where the branch
@@ -104,7 +108,7 @@ __global__ __launch_bounds__(256) void k_step_lrb(const Args a) {
   const int grp = tid >> 3;
   const int k0 = lane8 * EPL;
   constexpr int NPF = 4;                       // rows grp + 32 i, i < NPF
-  const uint8_t* gc = code_block(a, b, h);
+  const uint8_t* gc = code_block(a, bs, h);
   uint32_t pf[NPF][CW];
 #pragma unroll
   for (int i = 0; i < NPF; ++i) {
@@ -118,10 +122,10 @@ __global__ __launch_bounds__(256) void k_step_lrb(const Args a) {
     Wr[j] = j < r ? Wg[tv * r + j] : 0.0f;   // j < r: uniform
     Ur[j] = j < r ? Ug[tk * r + j] : 0.0f;
   }
-  const uint64_t trow = (uint64_t)bh * (uint64_t)dv + (uint64_t)tv;
-  const uint64_t tkey = (uint64_t)bh * DK + (uint64_t)tk;
+  const uint64_t trow = bh * (uint64_t)dv + (uint64_t)tv;
+  const uint64_t tkey = bh * DK + (uint64_t)tk;
   const InRaw vraw = in_raw_load(a.v, a.in_bf16, trow);
-  const float so_raw = ld_nt(a.scales + trow);
+  const float so_raw = ld_nt(a.scales + bhs * (uint64_t)dv + (uint64_t)tv);
   const InRaw kraw = in_raw_load(a.k, a.in_bf16, tkey);
   const InRaw qraw = in_raw_load(a.q, a.in_bf16, tkey);
   const float dd_raw = DKEY ? a.decay[tkey] : a.decay[bh];
@@ -275,7 +279,7 @@ __global__ __launch_bounds__(256) void k_step_lrb(const Args a) {
   // is added to the state and cleared; a clear buffer resets the basis
   bool merged = false;
   int n_new = n;
-  const uint64_t step = ((uint64_t)a.step_hi << 32) | a.step_lo;
+  const uint64_t step = ((uint64_t)ix.step_hi << 32) | ix.step_lo;
   if (a.lrb_period > 0 && ((step + 1u) % (uint64_t)a.lrb_period) == 0u) {
     int left = 0;
     if (tid < DK) {
@@ -325,7 +329,7 @@ __global__ __launch_bounds__(256) void k_step_lrb(const Args a) {
     mflagl[tid] = merged ? 1 : 0;
   }
   if (grown && tid < dv) Wg[tid * r + (n - 1)] = wnew;   // only the new column changed
-  if (tid == 0) a.n[bh] = n_new;
+  if (tid == 0) a.n[bhs] = n_new;
   __syncthreads();
 
   // Phase B: rows, 8 lanes per row, rows grp, grp + 32, ...
@@ -341,7 +345,7 @@ __global__ __launch_bounds__(256) void k_step_lrb(const Args a) {
   }
   uint8_t* gcode = const_cast<uint8_t*>(gc);
   auto row_step = [&](const int v, const uint32_t (&cw)[CW]) {
-    const uint64_t row = (uint64_t)bh * (uint64_t)dv + (uint64_t)v;
+    const uint64_t row = bhs * (uint64_t)dv + (uint64_t)v;   // state row (Philox counter)
     const float s_old = sol[v];
     const float uu = ul[v], upv = upl[v];
     float sp[EPL], sh[EPL];
@@ -374,7 +378,7 @@ __global__ __launch_bounds__(256) void k_step_lrb(const Args a) {
     float scale, inv, invb;
     row_scale_fast<QB, SRB>(m, scale, inv, invb);
     uint32_t rb[EPL];
-    if constexpr (RND != 0) rand_bits<RND, EPL>(row * DK + (uint64_t)k0, a.seed_lo, a.seed_hi, a.step_lo, a.step_hi, rb);
+    if constexpr (RND != 0) rand_bits<RND, EPL>(row * DK + (uint64_t)k0, a.seed_lo, a.seed_hi, ix.step_lo, ix.step_hi, rb);
     uint32_t out[CW];
 #pragma unroll
     for (int j = 0; j < CW; ++j) out[j] = 0u;
@@ -400,9 +404,8 @@ __global__ __launch_bounds__(256) void k_step_lrb(const Args a) {
   }
   __syncthreads();
   if (tid < dv) {
-    const uint64_t row = (uint64_t)bh * (uint64_t)dv + (uint64_t)tid;
-    st_nt(a.out + row, ol[tid]);
-    st_nt(a.scales + row, sl_[tid]);
+    st_nt(a.out + bh * (uint64_t)dv + (uint64_t)tid, ol[tid]);
+    st_nt(a.scales + bhs * (uint64_t)dv + (uint64_t)tid, sl_[tid]);
   }
 }
 

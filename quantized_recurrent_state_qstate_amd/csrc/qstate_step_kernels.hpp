@@ -38,6 +38,33 @@ __device__ __forceinline__ const uint8_t* hp_block(const Args& a, uint32_t b, ui
 }
 __device__ __forceinline__ int hp_elem_bytes(int dt) { return dt == 0 ? 4 : 2; }
 
+// Head indices of batch element b, head h: state slot and step from the
+// batch tables when given (read as scalar loads: b is uniform), else b and
+// the launch's step.  ok = false for a slot outside the pool: that element
+// is skipped (its state and outputs untouched).
+__device__ __forceinline__ HeadIx head_ix(const Args& a, uint32_t b, uint32_t h, bool& ok) {
+  typedef const int32_t __attribute__((address_space(4)))* cint_p;
+  typedef const uint64_t __attribute__((address_space(4)))* cu64_p;
+  HeadIx x;
+  uint32_t bs = b;
+  ok = true;
+  if (a.slot) {
+    const int32_t sl = ((cint_p)a.slot)[b];
+    ok = sl >= 0 && sl < a.nslots;
+    bs = ok ? (uint32_t)sl : 0u;
+  }
+  x.in = (uint64_t)b * (uint64_t)a.H + h;
+  x.st = (uint64_t)bs * (uint64_t)a.H + h;
+  x.step_lo = a.step_lo;
+  x.step_hi = a.step_hi;
+  if (a.seq_step) {
+    const uint64_t st = ((cu64_p)a.seq_step)[b];
+    x.step_lo = (uint32_t)st;
+    x.step_hi = (uint32_t)(st >> 32);
+  }
+  return x;
+}
+
 // Per-lane decay factors of a head: one per key channel, or the head's
 // scalar broadcast.
 template <int EPL>
@@ -187,7 +214,7 @@ __device__ __forceinline__ void stage_qk(const Args& a, uint64_t bh, int lane8, 
 // one lane permute hands lane L the value of row wrow0 + L, so each array
 // gets one contiguous store per wave.  Called with every lane active.
 template <int RPL, int LPR>
-__device__ __forceinline__ void store_row_values(const Args& a, uint64_t bh, int wrow0, int lane8,
+__device__ __forceinline__ void store_row_values(const Args& a, const HeadIx& ix, int wrow0, int lane8,
                                                  const float (&o_row)[RPL], const float* s_row) {
   constexpr int GPW = 64 / LPR;
   float ov = o_row[0], sv = s_row ? s_row[0] : 0.0f;
@@ -201,15 +228,16 @@ __device__ __forceinline__ void store_row_values(const Args& a, uint64_t bh, int
   ov = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(ov)));
   if (s_row) sv = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(sv)));
   if (lane < GPW * RPL && wrow0 + lane < a.dv) {
-    const uint64_t row = bh * (uint64_t)a.dv + (uint64_t)(wrow0 + lane);
-    st_nt(a.out + row, ov);
-    if (s_row) st_nt(a.scales + row, sv);
+    const uint64_t v = (uint64_t)(wrow0 + lane);
+    st_nt(a.out + ix.in * (uint64_t)a.dv + v, ov);
+    if (s_row) st_nt(a.scales + ix.st * (uint64_t)a.dv + v, sv);
   }
 }
 
 template <int QB, int RND, int DELTA, int EPL, int LPR, int RPL, int BDR, int DKEY, int INBF>
-__device__ __forceinline__ void dense_quant_rows(const Args& a, uint8_t* blk, uint64_t bh, int v0, int wrow0,
+__device__ __forceinline__ void dense_quant_rows(const Args& a, uint8_t* blk, const HeadIx& ix, int v0, int wrow0,
                                                  int lane8, float* lds) {
+  const uint64_t bh = ix.in;   // inputs and outputs; the state (scales, Philox counter) at ix.st
   constexpr int DK = EPL * LPR;
   constexpr int GPW = 64 / LPR;             // row groups per wave: rows v0 + GPW r
   constexpr bool KQREG = (LPR == 8) && !(QB == 8 && RND != 0 && !BDR);   // see below
@@ -230,9 +258,9 @@ __device__ __forceinline__ void dense_quant_rows(const Args& a, uint8_t* blk, ui
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
     const int v = v0 + GPW * r;
-    const uint64_t row = bh * (uint64_t)a.dv + (uint64_t)(v < a.dv ? v : 0);
-    s_old[r] = ld_nt(a.scales + row);
-    vin[r] = load_in_scalar<INBF>(a.v, row);
+    const uint64_t vc = (uint64_t)(v < a.dv ? v : 0);
+    s_old[r] = ld_nt(a.scales + ix.st * (uint64_t)a.dv + vc);
+    vin[r] = load_in_scalar<INBF>(a.v, bh * (uint64_t)a.dv + vc);
   }
   float df[DKEY ? EPL : 1];
   float dh = 1.0f;
@@ -252,7 +280,7 @@ __device__ __forceinline__ void dense_quant_rows(const Args& a, uint8_t* blk, ui
   if constexpr (PRE) {
 #pragma unroll
     for (int r = 0; r < RPL; ++r) {
-      const uint64_t row = bh * (uint64_t)a.dv + (uint64_t)(v0 + GPW * r);   // rows past dv: unused
+      const uint64_t row = ix.st * (uint64_t)a.dv + (uint64_t)(v0 + GPW * r);   // rows past dv: unused
 #pragma unroll
       for (int gblk = 0; gblk < NB; ++gblk) {
         // element indices stay below 2^35 (checked at init): the counter's
@@ -260,8 +288,8 @@ __device__ __forceinline__ void dense_quant_rows(const Args& a, uint8_t* blk, ui
         const uint64_t e0w = row * DK + (uint64_t)k0 + (uint64_t)(gblk * PER);
         px[r][gblk][0] = (RND == 1) ? (uint32_t)(e0w >> 3) : (uint32_t)(e0w >> 4);
         px[r][gblk][1] = 0u;
-        px[r][gblk][2] = a.step_lo;
-        px[r][gblk][3] = a.step_hi;
+        px[r][gblk][2] = ix.step_lo;
+        px[r][gblk][3] = ix.step_hi;
         philox10(px[r][gblk], a.seed_lo, a.seed_hi);
         asm volatile("" : "+v"(px[r][gblk][0]), "+v"(px[r][gblk][1]), "+v"(px[r][gblk][2]), "+v"(px[r][gblk][3]));
       }
@@ -276,7 +304,7 @@ __device__ __forceinline__ void dense_quant_rows(const Args& a, uint8_t* blk, ui
     o_row[r] = 0.0f;
     s_row[r] = 0.0f;
     if (v >= a.dv) continue;   // whole 8-lane groups skip together
-    const uint64_t row = bh * (uint64_t)a.dv + (uint64_t)v;
+    const uint64_t row = ix.st * (uint64_t)a.dv + (uint64_t)v;   // the element's state row
     // decay + update, readout, row maximum
     float u;
     if constexpr (DELTA) {
@@ -358,7 +386,7 @@ __device__ __forceinline__ void dense_quant_rows(const Args& a, uint8_t* blk, ui
     } else {
       uint32_t rb[EPL];
       if constexpr (RND != 0)
-        rand_bits<RND, EPL>(row * DK + (uint64_t)k0, a.seed_lo, a.seed_hi, a.step_lo, a.step_hi, rb);
+        rand_bits<RND, EPL>(row * DK + (uint64_t)k0, a.seed_lo, a.seed_hi, ix.step_lo, ix.step_hi, rb);
       int32_t code[EPL];
 #pragma unroll
       for (int i = 0; i < EPL; ++i) {
@@ -379,7 +407,7 @@ __device__ __forceinline__ void dense_quant_rows(const Args& a, uint8_t* blk, ui
     }
     store_bytes<EPL * QB / 8, true>(blk + (uint64_t)v * RB + k0 * QB / 8, out);
   }
-  store_row_values<RPL, LPR>(a, bh, wrow0, lane8, o_row, s_row);
+  store_row_values<RPL, LPR>(a, ix, wrow0, lane8, o_row, s_row);
 }
 
 // Protected (16-bit) heads of a head map.  With 8 lanes per row a row is
@@ -387,8 +415,9 @@ __device__ __forceinline__ void dense_quant_rows(const Args& a, uint8_t* blk, ui
 // 64i + 8j .. 64i + 8j + 7), so every load and store of the wave covers
 // whole cache lines; with 4 lanes per row a lane holds 32 consecutive keys.
 template <int DELTA, int EPL, int LPR, int RPL, int DKEY, int INBF>
-__device__ __forceinline__ void dense_prot_rows(const Args& a, uint8_t* blk, uint64_t bh, int v0, int wrow0,
+__device__ __forceinline__ void dense_prot_rows(const Args& a, uint8_t* blk, const HeadIx& ix, int v0, int wrow0,
                                                 int lane8, float* lds) {
+  const uint64_t bh = ix.in;   // inputs and outputs
   constexpr int DK = EPL * LPR;
   constexpr int GPW = 64 / LPR;
   constexpr bool SPLIT = (LPR == 8);
@@ -479,7 +508,7 @@ __device__ __forceinline__ void dense_prot_rows(const Args& a, uint8_t* blk, uin
   };
   if (a.hp_dtype == 1) rows(std::true_type{});
   else rows(std::false_type{});
-  store_row_values<RPL, LPR>(a, bh, wrow0, lane8, o_row, nullptr);
+  store_row_values<RPL, LPR>(a, ix, wrow0, lane8, o_row, nullptr);
 }
 
 // Register budget (minimum waves per SIMD the body is compiled for), chosen
@@ -520,7 +549,10 @@ void k_step_dense(const Args a) {
   r = r >= per_b ? r - per_b : r;
   const uint32_t chunk = r % (uint32_t)a.row_chunks;
   const uint32_t h = r / (uint32_t)a.row_chunks;
-  const uint32_t bh = b * (uint32_t)a.H + h;
+  bool ok;
+  const HeadIx ix = head_ix(a, b, h, ok);
+  if (!ok) return;   // uniform: a batch element with no valid state slot
+  const uint32_t bs = (uint32_t)(ix.st / (uint64_t)a.H);   // state slot
   // rows: a wave owns GPW * RPL consecutive rows from wrow0, its group gi the
   // rows wrow0 + gi + GPW r; groups past dv stay for the barrier
   constexpr int GPW = 64 / LPR;
@@ -533,11 +565,11 @@ void k_step_dense(const Args a) {
   const uint32_t np = (uint32_t)__builtin_popcountll(below);
   const bool prot = (h < 64u) && ((a.prot_mask >> h) & 1ull);
   if (!prot) {
-    uint8_t* blk = a.codes + (uint64_t)b * a.code_bstride + (uint64_t)(h - np) * a.code_hblk;
-    dense_quant_rows<QB, RND, DELTA, EPL, LPR, RPL, BDR, DKEY, INBF>(a, blk, bh, v0, wrow0, lane8, lds);
+    uint8_t* blk = a.codes + (uint64_t)bs * a.code_bstride + (uint64_t)(h - np) * a.code_hblk;
+    dense_quant_rows<QB, RND, DELTA, EPL, LPR, RPL, BDR, DKEY, INBF>(a, blk, ix, v0, wrow0, lane8, lds);
   } else {
-    uint8_t* blk = a.hp + (uint64_t)b * a.hp_bstride + (uint64_t)np * a.hp_hblk;
-    dense_prot_rows<DELTA, EPL, LPR, RPL, DKEY, INBF>(a, blk, bh, v0, wrow0, lane8, lds);
+    uint8_t* blk = a.hp + (uint64_t)bs * a.hp_bstride + (uint64_t)np * a.hp_hblk;
+    dense_prot_rows<DELTA, EPL, LPR, RPL, DKEY, INBF>(a, blk, ix, v0, wrow0, lane8, lds);
   }
 }
 
@@ -557,9 +589,13 @@ __global__ __launch_bounds__(256) void k_step_mixed(const Args a) {
   const int tid = threadIdx.x;
   const int lane8 = tid & 7;
   const int rloc = tid >> 3;
-  const uint32_t bh = blockIdx.x;
-  const uint32_t h = bh % (uint32_t)a.H;
-  const uint32_t b = bh / (uint32_t)a.H;
+  const uint32_t h = blockIdx.x % (uint32_t)a.H;
+  const uint32_t b = blockIdx.x / (uint32_t)a.H;
+  bool ok;
+  const HeadIx ix = head_ix(a, b, h, ok);
+  if (!ok) return;   // uniform: a batch element with no valid state slot
+  const uint64_t bh = ix.in;                               // inputs and outputs
+  const uint32_t bs = (uint32_t)(ix.st / (uint64_t)a.H);   // state slot
   const int nq = a.t.nq[h];
   const int nhp = DK - nq;
   const int hpb = hp_elem_bytes(a.hp_dtype);
@@ -567,8 +603,8 @@ __global__ __launch_bounds__(256) void k_step_mixed(const Args a) {
   const uint32_t rh = hp_row_bytes(nhp, hpb);
   const uint32_t code_bytes = ((uint32_t)a.dv * rq + 15u) & ~15u;
   const uint32_t hp_bytes = ((uint32_t)a.dv * rh + 15u) & ~15u;
-  uint8_t* gcode = const_cast<uint8_t*>(code_block(a, b, h));
-  uint8_t* ghp = const_cast<uint8_t*>(hp_block(a, b, h));
+  uint8_t* gcode = const_cast<uint8_t*>(code_block(a, bs, h));
+  uint8_t* ghp = const_cast<uint8_t*>(hp_block(a, bs, h));
   uint8_t* lcode = lds;
   uint8_t* lhp = lds + code_bytes;
 
@@ -589,9 +625,10 @@ __global__ __launch_bounds__(256) void k_step_mixed(const Args a) {
   __syncthreads();
 
   for (int v = rloc; v < a.dv; v += 32) {
-    const uint64_t row = (uint64_t)bh * (uint64_t)a.dv + (uint64_t)v;
+    const uint64_t row = ix.st * (uint64_t)a.dv + (uint64_t)v;      // state row
+    const uint64_t orow = bh * (uint64_t)a.dv + (uint64_t)v;        // input / output row
     const float s_old = ld_nt(a.scales + row);
-    const float vin = load_in1(a.v, a.in_bf16, row);
+    const float vin = load_in1(a.v, a.in_bf16, orow);
     uint8_t* crow = lcode + (uint32_t)v * rq;
     uint8_t* hrow = lhp + (uint32_t)v * rh;
     float sh[EPL], dec[EPL];   // dequantized value; decayed value (d s) c or d h
@@ -632,7 +669,7 @@ __global__ __launch_bounds__(256) void k_step_mixed(const Args a) {
 #pragma unroll
     for (int i = 0; i < EPL; ++i) o = fmaf(sp[i], qf[i], o);
     o = sum8(o);
-    if (lane8 == 0) st_nt(a.out + row, o);
+    if (lane8 == 0) st_nt(a.out + orow, o);
 
     float m = 0.0f;
 #pragma unroll
@@ -647,13 +684,13 @@ __global__ __launch_bounds__(256) void k_step_mixed(const Args a) {
     uint32_t rb[EPL];
     if constexpr (RND != 0) {
       if (nq == DK) {
-        rand_bits<RND, EPL>(row * DK + (uint64_t)k0, a.seed_lo, a.seed_hi, a.step_lo, a.step_hi, rb);
+        rand_bits<RND, EPL>(row * DK + (uint64_t)k0, a.seed_lo, a.seed_hi, ix.step_lo, ix.step_hi, rb);
       } else {
 #pragma unroll
         for (int i = 0; i < EPL; ++i)
           rb[i] = (sl[i] & kSlotProt) ? 0u
                                       : rand_one<RND>(row * DK + (uint64_t)(sl[i] & 0x7FFFu), a.seed_lo, a.seed_hi,
-                                                      a.step_lo, a.step_hi);
+                                                      ix.step_lo, ix.step_hi);
       }
     }
     int32_t code[EPL];

@@ -431,3 +431,81 @@ def test_misaligned_pointer_is_rejected():
     with pytest.raises(_lib.QStateError) as e:
         qs.step(st, buf[1:], buf, buf, buf)
     assert e.value.status == _lib.QS_EINVAL
+
+
+# Batched step over a pool of state slots ------------------------------------
+BATCH_CASES = {
+    "dense_headmap_bf16_sr": dict(kind="additive", decay_mode="head", dk=128, dv=64, H=4, qbits=8,
+                                  map_mode="head", hp_dtype="bf16"),
+    "dense_delta_4lanes": dict(kind="delta", decay_mode="head", dk=128, dv=128, H=2, qbits=8),
+    "keymap_fp16_delta": dict(kind="delta", decay_mode="head", dk=128, dv=72, H=2, qbits=8, map_mode="key",
+                              hp_dtype="fp16"),
+    "mixed_fp32_keymap": dict(kind="additive", decay_mode="key", dk=64, dv=48, H=3, qbits=8, map_mode="key",
+                              hp_dtype="fp32"),
+    "lrb_delta_int4": dict(kind="delta", decay_mode="head", dk=128, dv=128, H=2, qbits=4, rounding="nearest",
+                           bdr=True, lrb_rank=8, lrb_period=4),
+}
+POOL = 6
+BATCH_SLOTS = [5, 1, 3, -1, 0]                       # -1: outside the pool, skipped
+BATCH_STEPS = [3, (1 << 33) + 5, 7, 0, 11]
+
+
+@pytest.mark.parametrize("case", list(BATCH_CASES))
+def test_batch_step_matches_oracle(case):
+    kw = dict(BATCH_CASES[case])
+    r = np.random.default_rng(3)
+    m = None
+    if kw.get("map_mode") == "head":
+        m = (np.arange(kw["H"]) % 2).astype(np.uint8)
+    elif kw.get("map_mode") == "key":
+        m = (r.random((kw["H"], kw["dk"])) < 0.2).astype(np.uint8)
+    lkw = dict(kw)
+    lkw.setdefault("rounding", "stochastic")
+    lcfg = StateConfig(B=POOL, map=m, seed=0x1234_5678_9ABC, **lkw)
+    okw = {k_: v_ for k_, v_ in kw.items()}
+    okw["rounding"] = "rtn" if lkw["rounding"] == "nearest" else "sr"
+    ocfg = oracle.Cfg(B=POOL, map=m, seed=0x1234_5678_9ABC, **okw)
+    qs = QState(lcfg)
+    st = qs.new_state()
+    _log(f"[parity] batch {case}")
+    n = len(BATCH_SLOTS)
+    for t in range(3):   # a non-trivial pool first (plain steps)
+        full = dict(kw, B=POOL)
+        qs.step(st, **_dev_inputs(_edge_inputs(full, 40 + t)), step=t)
+    slots = torch.tensor(BATCH_SLOTS, dtype=torch.int32, device=DEV)
+    valid = [b for b, s in enumerate(BATCH_SLOTS) if 0 <= s < POOL]
+    exact = kw["kind"] == "additive" and not kw.get("lrb_rank")
+    for t in range(4):
+        steps = [s + t for s in BATCH_STEPS]
+        inp = _edge_inputs(dict(kw, B=n), 60 + t)
+        ref = gpu_state_to_oracle(st, ocfg.hp_dtype)
+        o_ref = oracle.step_batch(ocfg, ref, **inputs_f32(inp), slot=np.array(BATCH_SLOTS, np.int32),
+                                  steps=np.array(steps, np.uint64))
+        out = torch.full((n, kw["H"], kw["dv"]), float("nan"), device=DEV)
+        qs.step_batch(st, slots, torch.tensor(steps, dtype=torch.int64, device=DEV), **_dev_inputs(inp), out=out)
+        torch.cuda.synchronize()
+        zero = np.zeros((POOL * kw["H"], kw["dv"]), np.float32)
+        compare(ocfg, exact, ref, gpu_state_to_oracle(st, ocfg.hp_dtype), zero, zero, what=f"batch {case} t={t}")
+        og = out.cpu().numpy().astype(np.float64)
+        orf = o_ref.astype(np.float64)
+        for b in range(n):
+            if b in valid:
+                for h in range(kw["H"]):
+                    nr = np.linalg.norm(orf[b, h])
+                    assert np.linalg.norm(og[b, h] - orf[b, h]) <= 1e-3 * nr + 1e-30, f"{case} t={t} out {b},{h}"
+            else:
+                assert np.isnan(og[b]).all(), f"{case}: output of a skipped element was written"
+    qs.close()
+
+
+def test_batch_step_rejects_bad_arguments():
+    from quantized_recurrent_state_qstate_amd import _lib
+    qs = QState(StateConfig(B=2, H=1, dk=64, dv=8, in_dtype="fp32"))
+    st = qs.new_state()
+    x = torch.zeros(4096, device=DEV)
+    slot3 = torch.zeros(3, dtype=torch.int32, device=DEV)
+    step3 = torch.zeros(3, dtype=torch.int64, device=DEV)
+    with pytest.raises(_lib.QStateError) as e:      # n = 3 > pool of 2
+        qs.step_batch(st, slot3, step3, x, x, x, x)
+    assert e.value.status == _lib.QS_EINVAL
+    qs.close()
