@@ -427,31 +427,35 @@ constexpr int sr_bits_of() { return RND == 1 ? 16 : (RND == 2 ? 8 : 0); }
 // the element grew takes ceil(x); above xo + bound while it shrank takes
 // floor(x).  |x| <= Q (inv rounded toward zero) keeps every code in
 // [-Q, Q].  A zero row (inv = 0) gives 0.
+// BDR as one clamp.  The rule: an element that grew (sp > sh, so x >= xo:
+// rounding is monotone) whose code c fell below t = xo - bound takes ceil(x);
+// one that shrank whose code rose above xo + bound takes floor(x).  Both
+// codes here (nearest, or stochastic from x rounded to sr_bits fractional
+// bits) lie in {floor(x), floor(x) + 1}; so c < t <= x forces c = floor(x)
+// with t in (c, c + 1), where ceil(x) = c + 1 = ceil(t), and c >= t means
+// c >= ceil(t).  Hence the rule is c' = max(c, ceil(t)) for a grown element,
+// and likewise min(c, floor(xo + bound)) for a shrunk one: med3 of c and the
+// two limits (infinite when they do not apply).
+__device__ __forceinline__ float bdr_clamp(float cf, float sp, float sh, float inv, float bound) {
+  const float xo = sh * inv;
+  const float lo = sp > sh ? ceilf(xo - bound) : -__builtin_inff();
+  const float hi = sp < sh ? floorf(xo + bound) : __builtin_inff();
+  return __builtin_amdgcn_fmed3f(cf, lo, hi);
+}
+
 template <int QB, int RND, int BDR>
 __device__ __forceinline__ int32_t round_elem(float sp, float sh, float inv, float invb, uint32_t rb,
                                               float bound) {
   if constexpr (RND == 0) {
     // decided in float (ceil, floor and rint of |x| <= Q are exact), one
     // conversion at the end
-    const float x = sp * inv;
-    float cf = rintf(x);
-    if constexpr (BDR) {
-      const float xo = sh * inv;
-      const float d = sp - sh;
-      cf = (d > 0.0f && cf < xo - bound) ? ceilf(x) : ((d < 0.0f && cf > xo + bound) ? floorf(x) : cf);
-    }
+    float cf = rintf(sp * inv);
+    if constexpr (BDR) cf = bdr_clamp(cf, sp, sh, inv, bound);
     return (int32_t)cf;
   } else {
     constexpr int SRB = sr_bits_of<RND>();
     int32_t c = (cvt_rpi(sp * invb) + (int32_t)rb) >> SRB;
-    if constexpr (BDR) {
-      const float x = sp * inv;
-      const float xo = sh * inv;
-      const float d = sp - sh;
-      const float cf = (float)c;
-      const float nf = (d > 0.0f && cf < xo - bound) ? ceilf(x) : ((d < 0.0f && cf > xo + bound) ? floorf(x) : cf);
-      c = (int32_t)nf;
-    }
+    if constexpr (BDR) c = (int32_t)bdr_clamp((float)c, sp, sh, inv, bound);
     return c;
   }
 }

@@ -66,8 +66,18 @@ __device__ __forceinline__ float pick(const float (&p)[R], int j) {
 
 }  // namespace
 
+// Register budget: 5 waves per SIMD (the limit the ~28 KiB of LDS per
+// workgroup sets) for int4 codes with nearest rounding at rank bound 8, where
+// it needs no spills (except with the delta rule and a per-key decay
+// together); otherwise the compiler's choice.
+template <int QB, int RND, int RANK, int DELTA, int DKEY>
+constexpr int lrb_min_waves() {
+  return (QB == 4 && RND == 0 && RANK == 8 && !(DELTA && DKEY)) ? 5 : 1;
+}
+
 template <int QB, int RND, int DELTA, int EPL, int RANK, int BDR, int DKEY>
-__global__ __launch_bounds__(256) void k_step_lrb(const Args a) {
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(lrb_min_waves<QB, RND, RANK, DELTA, DKEY>(), 8))) void k_step_lrb(const Args a) {
   constexpr int DK = EPL * 8;
   constexpr int SRB = sr_bits_of<RND>();
   constexpr int CW = EPL * QB / 32;
@@ -333,13 +343,14 @@ __global__ __launch_bounds__(256) void k_step_lrb(const Args a) {
   __syncthreads();
 
   // Phase B: rows, 8 lanes per row, rows grp, grp + 32, ...
-  float kf[EPL], qf[EPL], df[EPL];
+  // k, q and the decay of the lane's keys are read from LDS where used
+  // (registers for more resident waves, which hide the buffer steps)
+  const float* kf = kl + k0;
+  const float* qf = ql + k0;
+  const float* df = dl + k0;
   uint32_t smask = 0u, mmask = 0u;
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
-    kf[i] = kl[k0 + i];
-    qf[i] = ql[k0 + i];
-    df[i] = dl[k0 + i];
     smask |= (smalll[k0 + i] ? 1u : 0u) << i;
     mmask |= (mflagl[k0 + i] ? 1u : 0u) << i;
   }
