@@ -66,10 +66,9 @@ __device__ __forceinline__ float pick(const float (&p)[R], int j) {
 
 }  // namespace
 
-// Register budget: 5 waves per SIMD (the limit the ~28 KiB of LDS per
-// workgroup sets) for int4 codes with nearest rounding at rank bound 8, where
-// it needs no spills (except with the delta rule and a per-key decay
-// together); otherwise the compiler's choice.
+// Register budget: 5 waves per SIMD for int4 codes with nearest rounding at
+// rank bound 8, where it needs no spills (except with the delta rule and a
+// per-key decay together); otherwise the compiler's choice.
 template <int QB, int RND, int RANK, int DELTA, int DKEY>
 constexpr int lrb_min_waves() {
   return (QB == 4 && RND == 0 && RANK == 8 && !(DELTA && DKEY)) ? 5 : 1;
@@ -96,10 +95,15 @@ __attribute__((amdgpu_waves_per_eu(lrb_min_waves<QB, RND, RANK, DELTA, DKEY>(), 
   __shared__ __align__(16) float Wt[RANK][256];   // W transposed, for merges and rows
   __shared__ __align__(16) float Ut[RANK][DK];    // U rows of merged channels (before clearing)
   __shared__ __align__(16) float ul[256], upl[256], sol[256], lrl[256];
-  __shared__ __align__(16) float wl[DELTA ? 256 : 1];   // delta rule: decayed S_hat k per row
-  __shared__ __align__(16) float ol[256], sl_[256];      // per-row outputs and scales
   __shared__ __align__(16) float kl[DK], ql[DK], dl[DK];
   __shared__ __align__(16) float P[RANK * 256];   // reduction transpose
+  // Arrays whose lives do not overlap share LDS (less LDS per workgroup, more
+  // resident heads): the delta rule's per-row S_hat k is read before the
+  // buffer readout lrl is written, and the per-row outputs and scales of the
+  // row pass are written after the last reduction through P.
+  float* const wl = lrl;
+  float* const ol = P;
+  float* const sl_ = P + 256;
   __shared__ float red[RANK + 4];
   __shared__ uint8_t smalll[DK], mflagl[DK];
 
