@@ -271,12 +271,15 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8+bf16 state, fp32 arithmetic" if w.qbits == 8 else "int4 state, fp32 arithmetic",
+        "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": f"{w.name}: {w.recurrence}, B={w.B}, H={w.H}, dk={w.dk}, dv={w.dv}, "
                                f"{'int%d' % w.qbits}, map={w.map_mode}:{w.map_frac}, {w.rounding}"
                                + (f" {w.sr_bits}-bit" if w.rounding == "stochastic" else "")
                                + (", bdr" if w.bdr else "") + (f", lrb r={w.lrb_rank}" if w.lrb_rank else ""),
+                   "state": "int%d codes" % w.qbits + ("" if w.map_mode == "none" else
+                                                        f" + {w.hp_dtype} protected "
+                                                        + ("heads" if w.map_mode == "head" else "key channels")),
                    "mode": args.mode, "replicas": R, "graph": bool(graph is not None),
                    "tokens_per_s": round(steps_per_s * w.B, 1)},
         "state_GBps": round(state_gbps, 1),
