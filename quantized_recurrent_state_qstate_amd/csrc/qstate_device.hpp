@@ -319,19 +319,7 @@ __device__ __forceinline__ void load_codes(const uint8_t* p, float s, float (&sh
   dequant_words<QB, EPL>(w, s, sh);
 }
 
-template <int QB, int EPL>
-__device__ __forceinline__ void store_codes(uint8_t* p, const int32_t (&c)[EPL]) {
-  constexpr int NB = EPL * QB / 8;
-  uint32_t w[NB / 4];
-#pragma unroll
-  for (int i = 0; i < NB / 4; ++i) w[i] = 0u;
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    if constexpr (QB == 8) w[i >> 2] |= ((uint32_t)c[i] & 0xFFu) << (8 * (i & 3));
-    else w[i >> 3] |= ((uint32_t)c[i] & 0xFu) << (4 * (i & 7));
-  }
-  store_bytes<NB, true>(p, w);
-}
+
 
 // Protected row slice: widen / store in hp_dtype (0 fp32, 1 bf16, 2 fp16).
 template <int EPL>
@@ -436,10 +424,15 @@ constexpr int sr_bits_of() { return RND == 1 ? 16 : (RND == 2 ? 8 : 0); }
 // c >= ceil(t).  Hence the rule is c' = max(c, ceil(t)) for a grown element,
 // and likewise min(c, floor(xo + bound)) for a shrunk one: med3 of c and the
 // two limits (infinite when they do not apply).
+// BDR 2 is the same rule for a bound known to be zero (xo -/+ 0 is xo up to
+// the sign of a zero, which no code depends on), two instructions fewer.
+template <int BDR>
 __device__ __forceinline__ float bdr_clamp(float cf, float sp, float sh, float inv, float bound) {
   const float xo = sh * inv;
-  const float lo = sp > sh ? ceilf(xo - bound) : -__builtin_inff();
-  const float hi = sp < sh ? floorf(xo + bound) : __builtin_inff();
+  const float tl = (BDR == 2) ? xo : xo - bound;
+  const float th = (BDR == 2) ? xo : xo + bound;
+  const float lo = sp > sh ? ceilf(tl) : -__builtin_inff();
+  const float hi = sp < sh ? floorf(th) : __builtin_inff();
   return __builtin_amdgcn_fmed3f(cf, lo, hi);
 }
 
@@ -450,13 +443,39 @@ __device__ __forceinline__ int32_t round_elem(float sp, float sh, float inv, flo
     // decided in float (ceil, floor and rint of |x| <= Q are exact), one
     // conversion at the end
     float cf = rintf(sp * inv);
-    if constexpr (BDR) cf = bdr_clamp(cf, sp, sh, inv, bound);
+    if constexpr (BDR) cf = bdr_clamp<BDR>(cf, sp, sh, inv, bound);
     return (int32_t)cf;
   } else {
     constexpr int SRB = sr_bits_of<RND>();
     int32_t c = (cvt_rpi(sp * invb) + (int32_t)rb) >> SRB;
-    if constexpr (BDR) c = (int32_t)bdr_clamp((float)c, sp, sh, inv, bound);
+    if constexpr (BDR) c = (int32_t)bdr_clamp<BDR>((float)c, sp, sh, inv, bound);
     return c;
+  }
+}
+
+// N codes packed into N * QB / 32 words, code i at bits QB*i.. of the
+// stream (low bits first).  int8: byte i & 3 of word i >> 2.  int4, codes
+// in [-8, 7]: each offset code c + 8 is a digit in [0, 15], so the word of
+// offset codes is the plain sum of (c_i + 8) 16^i, with no carry between
+// digits; in wrapping 32-bit arithmetic that is 0x88888888 + sum c_i 16^i,
+// one shift-add per code, and xor 0x88888888 turns every digit c + 8 back
+// into c mod 16 (c >= 0: c + 8 has bit 3 set; c < 0: it has not, and
+// c + 8 + 8 = c + 16).  Unused digits of a partial word come out 0.
+template <int QB, int N>
+__device__ __forceinline__ void pack_codes(const int32_t (&c)[N], uint32_t (&w)[(N * QB + 31) / 32]) {
+  constexpr int NW = (N * QB + 31) / 32;
+  if constexpr (QB == 8) {
+#pragma unroll
+    for (int j = 0; j < NW; ++j) w[j] = 0u;
+#pragma unroll
+    for (int i = 0; i < N; ++i) w[i >> 2] |= ((uint32_t)c[i] & 0xFFu) << (8 * (i & 3));
+  } else {
+#pragma unroll
+    for (int j = 0; j < NW; ++j) w[j] = 0x88888888u;
+#pragma unroll
+    for (int i = 0; i < N; ++i) w[i >> 3] += (uint32_t)c[i] << (4 * (i & 7));
+#pragma unroll
+    for (int j = 0; j < NW; ++j) w[j] ^= 0x88888888u;
   }
 }
 

@@ -351,13 +351,7 @@ __global__ __launch_bounds__(256) void k_step_keymap(const Args a) {
       const float shi = BDR ? s_old[r] * code_at(i) : 0.0f;
       code[i] = round_elem<QB, RND, BDR>(sp[i], shi, inv, invb, (RND != 0) ? rb[i] : 0u, a.bdr_bound);
     }
-#pragma unroll
-    for (int j = 0; j < CW; ++j) out[j] = 0u;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      if constexpr (QB == 8) out[i >> 2] |= ((uint32_t)code[i] & 0xFFu) << (8 * (i & 3));
-      else out[i >> 3] |= ((uint32_t)code[i] & 0xFu) << (4 * (i & 7));
-    }
+    pack_codes<QB, EPL>(code, out);
   }
   store_dwords<CW>(const_cast<uint8_t*>(cblk) + (uint64_t)v * rq + coff, cvalid, out);
   if (lane == 0) {

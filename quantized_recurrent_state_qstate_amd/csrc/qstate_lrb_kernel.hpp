@@ -394,15 +394,12 @@ __attribute__((amdgpu_waves_per_eu(lrb_min_waves<QB, RND, RANK, DELTA, DKEY>(), 
     row_scale_fast<QB, SRB>(m, scale, inv, invb);
     uint32_t rb[EPL];
     if constexpr (RND != 0) rand_bits<RND, EPL>(row * DK + (uint64_t)k0, a.seed_lo, a.seed_hi, ix.step_lo, ix.step_hi, rb);
+    int32_t code[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      code[i] = round_elem<QB, RND, BDR>(sp[i], sh[i], inv, invb, (RND != 0) ? rb[i] : 0u, a.bdr_bound);
     uint32_t out[CW];
-#pragma unroll
-    for (int j = 0; j < CW; ++j) out[j] = 0u;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      const int32_t code = round_elem<QB, RND, BDR>(sp[i], sh[i], inv, invb, (RND != 0) ? rb[i] : 0u, a.bdr_bound);
-      if constexpr (QB == 8) out[i >> 2] |= ((uint32_t)code & 0xFFu) << (8 * (i & 3));
-      else out[i >> 3] |= ((uint32_t)code & 0xFu) << (4 * (i & 7));
-    }
+    pack_codes<QB, EPL>(code, out);
     store_bytes<EPL * QB / 8, true>(gcode + (uint64_t)v * (DK * QB / 8) + k0 * QB / 8, out);
     if (lane8 == 0) {   // collected in LDS, stored below as whole cache lines
       ol[v] = o + lrl[v];

@@ -397,13 +397,7 @@ __device__ __forceinline__ void dense_quant_rows(const Args& a, uint8_t* blk, co
         }
         code[i] = round_elem<QB, RND, BDR>(sp[i], shi, inv, invb, (RND != 0) ? rb[i] : 0u, a.bdr_bound);
       }
-#pragma unroll
-      for (int j = 0; j < NW; ++j) out[j] = 0u;
-#pragma unroll
-      for (int i = 0; i < EPL; ++i) {
-        if constexpr (QB == 8) out[i >> 2] |= ((uint32_t)code[i] & 0xFFu) << (8 * (i & 3));
-        else out[i >> 3] |= ((uint32_t)code[i] & 0xFu) << (4 * (i & 7));
-      }
+      pack_codes<QB, EPL>(code, out);
     }
     store_bytes<EPL * QB / 8, true>(blk + (uint64_t)v * RB + k0 * QB / 8, out);
   }

@@ -57,7 +57,10 @@ hipError_t launch_mixed_t(const Args& a, hipStream_t s) {
 template <int QB, int RND, int DELTA, int EPL, int RANK>
 hipError_t launch_lrb_r(const Args& a, hipStream_t s) {
   const dim3 grid((uint32_t)((uint64_t)a.B * (uint64_t)a.H));
-  if (a.bdr) {
+  if (a.bdr && a.bdr_bound == 0.0f) {   // the rule's zero-bound form
+    if (a.decay_key) hipLaunchKernelGGL((k_step_lrb<QB, RND, DELTA, EPL, RANK, 2, 1>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_step_lrb<QB, RND, DELTA, EPL, RANK, 2, 0>), grid, dim3(256), 0, s, a);
+  } else if (a.bdr) {
     if (a.decay_key) hipLaunchKernelGGL((k_step_lrb<QB, RND, DELTA, EPL, RANK, 1, 1>), grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((k_step_lrb<QB, RND, DELTA, EPL, RANK, 1, 0>), grid, dim3(256), 0, s, a);
   } else {

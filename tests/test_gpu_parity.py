@@ -303,6 +303,14 @@ EDGE = {
                                   rounding="nearest", lrb_rank=8, lrb_period=5),
     "lrb_delta_keydecay_int4_sr_bdr_r16": dict(kind="delta", decay_mode="key", dk=128, dv=64, H=2, B=2,
                                                qbits=4, bdr=True, lrb_rank=16, lrb_period=3),
+    # BDR with a nonzero bound (the other BDR cases use bound 0, which the
+    # low-rank-bypass kernel runs in a zero-bound form)
+    "lrb_int4_bdr_bound": dict(kind="additive", decay_mode="key", dk=128, dv=64, H=2, B=2, qbits=4,
+                               rounding="nearest", bdr=True, bdr_bound=0.3, lrb_rank=8, lrb_period=3),
+    "lrb_delta_int4_bdr_bound": dict(kind="delta", decay_mode="head", dk=128, dv=96, H=2, B=2, qbits=4,
+                                     rounding="nearest", bdr=True, bdr_bound=0.6, lrb_rank=8, lrb_period=4),
+    "int4_rtn_bdr_bound": dict(kind="additive", decay_mode="head", dk=128, dv=64, H=2, B=2, qbits=4,
+                               rounding="nearest", bdr=True, bdr_bound=0.3),
     # key maps in storage order: few, half and most channels protected
     "keymap_fp16_delta_sparse": dict(kind="delta", decay_mode="head", dk=128, dv=128, H=2, B=2, qbits=8,
                                      map_mode="key", hp_dtype="fp16", map_density=0.08),
