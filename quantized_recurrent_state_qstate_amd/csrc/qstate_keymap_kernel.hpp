@@ -56,10 +56,12 @@ __device__ __forceinline__ void slice_load(const uint8_t* blk, uint32_t rowo, ui
     nbv[c] = nb;
     sh[c] = nb > 0u ? (rowo + po - o) / 4u : 0u;
     if constexpr (PW == 4) {
-      const u32x4a4_t v = ld_nt(reinterpret_cast<const u32x4a4_t*>(a));
+      // the builtin keeps the 4-byte alignment of the type (a template
+      // parameter would not)
+      const u32x4a4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4a4_t*>(a));
       w[4 * c] = v.x; w[4 * c + 1] = v.y; w[4 * c + 2] = v.z; w[4 * c + 3] = v.w;
     } else if constexpr (PW == 2) {
-      const u32x2a4_t v = ld_nt(reinterpret_cast<const u32x2a4_t*>(a));
+      const u32x2a4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2a4_t*>(a));
       w[2 * c] = v.x; w[2 * c + 1] = v.y;
     } else {
       w[c] = ld_nt(reinterpret_cast<const uint32_t*>(a));
@@ -94,7 +96,7 @@ __device__ __forceinline__ void store_dwords(uint8_t* p, uint32_t nbytes, const 
 #pragma unroll
       for (int i = 0; i < NW / 4; ++i) {
         const u32x4a4_t t = {w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
-        st_nt(reinterpret_cast<u32x4a4_t*>(p) + i, t);
+        __builtin_nontemporal_store(t, reinterpret_cast<u32x4a4_t*>(p) + i);
       }
       return;
     }
