@@ -82,6 +82,56 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+_STATE_DTYPE = {"codes": "uint8", "scales": "float32", "hp": "uint8", "lrb_W": "float32",
+                "lrb_U": "float32", "lrb_n": "int32"}
+
+
+def check_tensor(name: str, t, dtype, numel: int, device, at_least: bool = False) -> None:
+    """Host-side argument check before a pointer crosses the C ABI: the kernels
+    read and write exactly the planned extents, so a tensor of the wrong dtype,
+    size, memory layout or device would make them read or write out of bounds
+    or get wrong results.  Raises ValueError (checks in that order)."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name}: expected a torch.Tensor, got {type(t).__name__}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if (t.numel() < numel) if at_least else (t.numel() != numel):
+        raise ValueError(f"{name}: {t.numel()} elements, expected {'at least ' if at_least else ''}{numel}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: not contiguous")
+    if t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+
+
+def check_state(cfg: "StateConfig", sizes: dict, st: dict, device) -> None:
+    """Every buffer the plan sizes > 0 must be present, typed and large enough."""
+    import torch
+    for n, dt in _STATE_DTYPE.items():
+        nbytes = sizes[n]
+        if nbytes == 0:
+            continue
+        dtype = getattr(torch, dt)
+        item = torch.empty((), dtype=dtype).element_size()
+        check_tensor(f"state[{n!r}]", st.get(n), dtype, nbytes // item, device, at_least=True)
+
+
+def check_inputs(cfg: "StateConfig", n: int, device, q, k, v, decay, beta, out) -> None:
+    """Inputs of a step for n batch elements: q, k [n,H,dk] and v [n,H,dv] in
+    the configured input dtype, decay fp32 [n,H] (or [n,H,dk] per key), beta
+    fp32 [n,H] or None, out fp32 [n,H,dv]."""
+    import torch
+    ind = torch.bfloat16 if cfg.in_dtype == "bf16" else torch.float32
+    nh = n * cfg.H
+    check_tensor("q", q, ind, nh * cfg.dk, device)
+    check_tensor("k", k, ind, nh * cfg.dk, device)
+    check_tensor("v", v, ind, nh * cfg.dv, device)
+    check_tensor("decay", decay, torch.float32, nh * (cfg.dk if cfg.decay_mode == "key" else 1), device)
+    if beta is not None:
+        check_tensor("beta", beta, torch.float32, nh, device)
+    check_tensor("out", out, torch.float32, nh * cfg.dv, device)
+
+
 class QState:
     """A libqstate handle for one configuration on the current HIP device."""
 
@@ -145,6 +195,10 @@ class QState:
         return stream.cuda_stream
 
     def quantize(self, S, st: dict, step: int = 0, stream=None) -> None:
+        import torch
+        c = self.cfg
+        check_tensor("S", S, torch.float32, c.B * c.H * c.dv * c.dk, self.device)
+        check_state(c, self.sizes, st, self.device)
         t = self._tensors(st)
         _lib.check(_lib.lib().qstate_quantize(self._h, _ptr(S), ctypes.byref(t), step, self._stream(stream)),
                    "qstate_quantize")
@@ -154,6 +208,8 @@ class QState:
         c = self.cfg
         if out is None:
             out = torch.empty((c.B, c.H, c.dv, c.dk), dtype=torch.float32, device=self.device)
+        check_tensor("out", out, torch.float32, c.B * c.H * c.dv * c.dk, self.device)
+        check_state(c, self.sizes, st, self.device)
         t = self._tensors(st)
         _lib.check(_lib.lib().qstate_dequantize(self._h, ctypes.byref(t), _ptr(out), self._stream(stream)),
                    "qstate_dequantize")
@@ -165,6 +221,8 @@ class QState:
         c = self.cfg
         if out is None:
             out = torch.empty((c.B, c.H, c.dv), dtype=torch.float32, device=self.device)
+        check_inputs(c, c.B, self.device, q, k, v, decay, beta, out)
+        check_state(c, self.sizes, st, self.device)
         t = self._tensors(st)
         inp = _lib.Inputs(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(beta))
         _lib.check(_lib.lib().qstate_decode_step(self._h, ctypes.byref(t), ctypes.byref(inp), _ptr(out), step,
@@ -181,8 +239,12 @@ class QState:
         n = int(slot.numel())
         if slot.dtype != torch.int32 or step.dtype not in (torch.int64, torch.uint64) or step.numel() != n:
             raise ValueError("slot must be int32 [n] and step 64-bit [n]")
+        check_tensor("slot", slot, torch.int32, n, self.device)
+        check_tensor("step", step, step.dtype, n, self.device)
         if out is None:
             out = torch.empty((n, c.H, c.dv), dtype=torch.float32, device=self.device)
+        check_inputs(c, n, self.device, q, k, v, decay, beta, out)
+        check_state(c, self.sizes, pool, self.device)
         t = self._tensors(pool)
         inp = _lib.Inputs(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(beta))
         _lib.check(_lib.lib().qstate_decode_step_batch(self._h, ctypes.byref(t), ctypes.byref(inp), _ptr(out), n,

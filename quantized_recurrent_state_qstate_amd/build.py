@@ -1,9 +1,16 @@
 """Build libqstate.so (gfx950) in-tree with hipcc.
 
-Each kernel translation unit (one per qbits x rounding mode, plus the
-quantize/dequantize one) and the host C-ABI file compile in parallel to
-objects under build/, then link into quantized_recurrent_state_qstate_amd/
-libqstate.so.
+Translation units:
+  qstate_step_<family>.hip   one per step-kernel family (dense, mixed, keymap,
+                             lrb), compiled once per (qbits, rounding) pair with
+                             -DQS_QB=<8|4> -DQS_RND=<0|1|2>: 24 objects that
+                             compile in parallel
+  qstate_misc.hip            quantize / dequantize / fill kernels, dispatch
+  qstate_host.cpp            the C ABI: validation, planning, launches
+Objects go to build/qstate/ and link into
+quantized_recurrent_state_qstate_amd/libqstate.so.  build(force=False)
+recompiles only objects older than their source or any header it includes
+(followed through the local #include "..." lines).
 
 Flags:
   --offload-arch=gfx950            CDNA4 code object only
@@ -16,8 +23,8 @@ Flags:
 from __future__ import annotations
 
 import concurrent.futures
-import glob
 import os
+import re
 import subprocess
 import sys
 
@@ -36,43 +43,83 @@ FLAGS = [
     "-Wall", "-Wno-unused-result", "-Wno-unused-function",
 ]
 
+FAMILIES = ("dense", "mixed", "keymap", "lrb")
+QR = [(qb, rnd) for qb in (8, 4) for rnd in (0, 1, 2)]
+RND_NAME = {0: "rtn", 1: "sr16", 2: "sr8"}
 
-def sources():
-    return sorted(glob.glob(os.path.join(CSRC, "*.hip"))) + [os.path.join(CSRC, "qstate_host.cpp")]
+
+def units():
+    """(source, extra flags, object path) of every translation unit."""
+    out = []
+    for fam in FAMILIES:
+        src = os.path.join(CSRC, f"qstate_step_{fam}.hip")
+        for qb, rnd in QR:
+            obj = os.path.join(OBJ, f"qstate_step_{fam}_q{qb}_{RND_NAME[rnd]}.o")
+            out.append((src, [f"-DQS_QB={qb}", f"-DQS_RND={rnd}"], obj))
+    for name in ("qstate_misc.hip", "qstate_host.cpp"):
+        out.append((os.path.join(CSRC, name), [], os.path.join(OBJ, name + ".o")))
+    return out
 
 
-def headers():
-    return sorted(glob.glob(os.path.join(CSRC, "*.hpp"))) + [os.path.join(INCLUDE, "qstate.h")]
+_INC = re.compile(r'^\s*#\s*include\s+"([^"]+)"', re.M)
+
+
+def deps(src: str) -> set:
+    """The source and every local header it includes, transitively."""
+    seen, todo = set(), [src]
+    while todo:
+        p = todo.pop()
+        if p in seen or not os.path.exists(p):
+            continue
+        seen.add(p)
+        with open(p) as f:
+            for name in _INC.findall(f.read()):
+                for d in (os.path.dirname(p), CSRC, INCLUDE):
+                    q = os.path.join(d, name)
+                    if os.path.exists(q):
+                        todo.append(q)
+                        break
+    return seen
+
+
+def _stale(src: str, obj: str) -> bool:
+    if not os.path.exists(obj):
+        return True
+    t = os.path.getmtime(obj)
+    return any(os.path.getmtime(p) > t for p in deps(src))
 
 
 def stale() -> bool:
     if not os.path.exists(LIB):
         return True
     t = os.path.getmtime(LIB)
-    return any(os.path.getmtime(p) > t for p in sources() + headers())
+    return any(_stale(s, o) or os.path.getmtime(o) > t for s, _, o in units())
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(OBJ, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
+def _compile(unit, verbose: bool) -> str:
+    src, extra, obj = unit
+    cmd = [HIPCC, *FLAGS, *extra, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
+        raise RuntimeError(f"hipcc failed on {src} {' '.join(extra)}:\n{r.stderr}")
     return obj
 
 
 def build(force: bool = True, verbose: bool = False, jobs: int = 0) -> str:
-    """Compile libqstate.so; returns its path."""
+    """Compile libqstate.so (every unit when force, else the stale ones); returns its path."""
     if not force and not stale():
         return LIB
     os.makedirs(OBJ, exist_ok=True)
-    jobs = jobs or min(8, os.cpu_count() or 1)
+    todo = [u for u in units() if force or _stale(u[0], u[2])]
+    jobs = jobs or min(16, os.cpu_count() or 1)
+    # the step units take longest: start them first
+    todo.sort(key=lambda u: 0 if "qstate_step_" in u[0] else 1)
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), sources()))
+        list(ex.map(lambda u: _compile(u, verbose), todo))
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *[o for _, _, o in units()], "-o", tmp]
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
     subprocess.run(cmd, check=True)
@@ -81,4 +128,4 @@ def build(force: bool = True, verbose: bool = False, jobs: int = 0) -> str:
 
 
 if __name__ == "__main__":
-    print(build(force=True, verbose="-v" in sys.argv))
+    print(build(force="--force" in sys.argv or "-f" in sys.argv, verbose="-v" in sys.argv))

@@ -86,10 +86,18 @@ struct HeadIx {
 // Kernel families chosen at init.
 enum StepFamily : int { kFamDense = 0, kFamMixed = 1, kFamLrb = 2, kFamKeymap = 3 };
 
-// Launchers (qstate_misc.hip; launch_step_qr<QB, RND> in qstate_step_q*_*.hip).  Return hipSuccess or the
-// launch error.  `rnd`: 0 nearest, 1 stochastic 16-bit, 2 stochastic 8-bit.
+// Launchers.  Step kernels, one launcher per family, instantiated per
+// (qbits, rounding) in qstate_step_<family>.hip; launch_step (qstate_misc.hip)
+// dispatches to them.  Return hipSuccess or the launch error.  `rnd`: 0
+// nearest, 1 stochastic 16-bit, 2 stochastic 8-bit.
 template <int QB, int RND>
-hipError_t launch_step_qr(int family, int delta, const Args& a, hipStream_t s);
+hipError_t launch_dense(int delta, const Args& a, hipStream_t s);
+template <int QB, int RND>
+hipError_t launch_mixed(int delta, const Args& a, hipStream_t s);
+template <int QB, int RND>
+hipError_t launch_keymap(int delta, const Args& a, hipStream_t s);
+template <int QB, int RND>
+hipError_t launch_lrb(int delta, const Args& a, hipStream_t s);
 hipError_t launch_step(int family, int qbits, int rnd, int delta, const Args& a,
                        hipStream_t s);
 hipError_t launch_quantize(const Args& a, hipStream_t s);

@@ -222,10 +222,31 @@ __global__ __launch_bounds__(256) void k_step_keymap(const Args a) {
     }
   }
   __syncthreads();
+  // valid bits of each loaded word: a row's padding (to 4 bytes) is not a
+  // slot, so whatever it holds must not reach the row maximum or the sums
+  uint32_t cmask[CW], hmask[HW];
+  {
+    const int cbits = min(max(nq - lane * EPL, 0), EPL) * QB;
+    const int hbits = min(max(nhp - lane * EH, 0), EH) * 16;
+#pragma unroll
+    for (int i = 0; i < CW; ++i) {
+      const int b = cbits - 32 * i;
+      cmask[i] = b >= 32 ? ~0u : (b <= 0 ? 0u : (1u << b) - 1u);
+    }
+#pragma unroll
+    for (int i = 0; i < HW; ++i) {
+      const int b = hbits - 32 * i;
+      hmask[i] = b >= 32 ? ~0u : (b <= 0 ? 0u : (1u << b) - 1u);
+    }
+  }
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
     slice_fix<CW>(cw[r], csh[r], cnb[r]);
     slice_fix<HW>(hw[r], hsh[r], hnb[r]);
+#pragma unroll
+    for (int i = 0; i < CW; ++i) cw[r][i] &= cmask[i];
+#pragma unroll
+    for (int i = 0; i < HW; ++i) hw[r][i] &= hmask[i];
   }
 
   const float* kc = lc[0] + lane * EPL;
@@ -243,7 +264,7 @@ __global__ __launch_bounds__(256) void k_step_keymap(const Args a) {
   const int v = v0 + GPW * r;
   if (v < a.dv) {   // whole row groups
   const uint64_t row = ix.st * (uint64_t)a.dv + (uint64_t)v;   // state row (Philox counter)
-  // old values: codes (0 past nq: padding and unloaded dwords are zero)
+  // old values: codes (0 past nq: padding is masked, unloaded dwords are zero)
   auto code_at = [&](int i) -> float {
     if constexpr (QB == 8) return (float)(int32_t)(int8_t)(cw[r][i >> 2] >> (8 * (i & 3)));
     else return (float)((int32_t)(cw[r][i >> 3] << (28 - 4 * (i & 7))) >> 28);
@@ -369,6 +390,60 @@ __global__ __launch_bounds__(256) void k_step_keymap(const Args a) {
     st_nt(a.out + bh * (uint64_t)a.dv + vt, ol[t]);
     st_nt(a.scales + ix.st * (uint64_t)a.dv + vt, sl_[t]);
   }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers (qstate_step_keymap.hip instantiates launch_keymap once per
+// qbits x rounding pair).
+// ---------------------------------------------------------------------------
+namespace {
+
+template <int QB, int RND, int DELTA, int LPR, int EH, int RPL, int INBF>
+hipError_t launch_keymap_eh(const Args& a, hipStream_t s) {
+  constexpr int EPL = 128 / LPR;
+  const dim3 grid((uint32_t)((uint64_t)a.B * (uint64_t)a.H * (uint64_t)a.row_chunks));
+  if (a.bdr) {
+    if (a.decay_key) hipLaunchKernelGGL((k_step_keymap<QB, RND, DELTA, EPL, LPR, EH, 1, 1, RPL, INBF>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_step_keymap<QB, RND, DELTA, EPL, LPR, EH, 1, 0, RPL, INBF>), grid, dim3(256), 0, s, a);
+  } else {
+    if (a.decay_key) hipLaunchKernelGGL((k_step_keymap<QB, RND, DELTA, EPL, LPR, EH, 0, 1, RPL, INBF>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_step_keymap<QB, RND, DELTA, EPL, LPR, EH, 0, 0, RPL, INBF>), grid, dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+template <int QB, int RND, int DELTA, int EH>
+hipError_t launch_keymap_rpl(const Args& a, hipStream_t s) {
+  switch (a.keymap_rpl) {
+    case 1: return a.in_bf16 ? launch_keymap_eh<QB, RND, DELTA, 8, EH, 1, 1>(a, s)
+                             : launch_keymap_eh<QB, RND, DELTA, 8, EH, 1, 0>(a, s);
+    case 2: return a.in_bf16 ? launch_keymap_eh<QB, RND, DELTA, 8, EH, 2, 1>(a, s)
+                             : launch_keymap_eh<QB, RND, DELTA, 8, EH, 2, 0>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+// dk 128: 8 lanes per row (16 code slots each); keymap_eh protected slots
+// per lane, keymap_rpl (1 or 2) rows per lane group
+template <int QB, int RND, int DELTA>
+hipError_t launch_keymap_t(const Args& a, hipStream_t s) {
+  switch (a.keymap_eh) {
+    case 2: return launch_keymap_rpl<QB, RND, DELTA, 2>(a, s);
+    case 4: return launch_keymap_rpl<QB, RND, DELTA, 4>(a, s);
+    case 8: return launch_keymap_rpl<QB, RND, DELTA, 8>(a, s);
+    case 16: return launch_keymap_rpl<QB, RND, DELTA, 16>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+// dk 128: 8 lanes per row (16 code slots each); keymap_eh protected slots
+// per lane, keymap_rpl (1 or 2) rows per lane group
+template <int QB, int RND>
+hipError_t launch_keymap(int delta, const Args& a, hipStream_t s) {
+  if (a.dk != 128) return hipErrorInvalidValue;
+  return delta ? launch_keymap_t<QB, RND, 1>(a, s) : launch_keymap_t<QB, RND, 0>(a, s);
 }
 
 }  // namespace qs

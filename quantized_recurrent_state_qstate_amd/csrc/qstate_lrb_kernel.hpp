@@ -421,4 +421,49 @@ __attribute__((amdgpu_waves_per_eu(lrb_min_waves<QB, RND, RANK, DELTA, DKEY>(), 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Launchers (qstate_step_lrb.hip instantiates launch_lrb once per qbits x
+// rounding pair).
+// ---------------------------------------------------------------------------
+namespace {
+
+template <int QB, int RND, int DELTA, int EPL, int RANK>
+hipError_t launch_lrb_r(const Args& a, hipStream_t s) {
+  const dim3 grid((uint32_t)((uint64_t)a.B * (uint64_t)a.H));
+  if (a.bdr && a.bdr_bound == 0.0f) {   // the rule's zero-bound form
+    if (a.decay_key) hipLaunchKernelGGL((k_step_lrb<QB, RND, DELTA, EPL, RANK, 2, 1>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_step_lrb<QB, RND, DELTA, EPL, RANK, 2, 0>), grid, dim3(256), 0, s, a);
+  } else if (a.bdr) {
+    if (a.decay_key) hipLaunchKernelGGL((k_step_lrb<QB, RND, DELTA, EPL, RANK, 1, 1>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_step_lrb<QB, RND, DELTA, EPL, RANK, 1, 0>), grid, dim3(256), 0, s, a);
+  } else {
+    if (a.decay_key) hipLaunchKernelGGL((k_step_lrb<QB, RND, DELTA, EPL, RANK, 0, 1>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_step_lrb<QB, RND, DELTA, EPL, RANK, 0, 0>), grid, dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+template <int QB, int RND, int DELTA, int EPL>
+hipError_t launch_lrb_t(const Args& a, hipStream_t s) {
+  return a.lrb_rank <= 8 ? launch_lrb_r<QB, RND, DELTA, EPL, 8>(a, s)
+                         : launch_lrb_r<QB, RND, DELTA, EPL, 16>(a, s);
+}
+
+template <int QB, int RND, int DELTA>
+hipError_t launch_lrb_dk(const Args& a, hipStream_t s) {
+  switch (a.dk) {
+    case 64: return launch_lrb_t<QB, RND, DELTA, 8>(a, s);
+    case 128: return launch_lrb_t<QB, RND, DELTA, 16>(a, s);
+    case 256: return launch_lrb_t<QB, RND, DELTA, 32>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+template <int QB, int RND>
+hipError_t launch_lrb(int delta, const Args& a, hipStream_t s) {
+  return delta ? launch_lrb_dk<QB, RND, 1>(a, s) : launch_lrb_dk<QB, RND, 0>(a, s);
+}
+
 }  // namespace qs

@@ -97,6 +97,24 @@ __global__ __launch_bounds__(256) void k_quantize(const Args a) {
       }
     }
   }
+  // Padding is part of the format (rows to 4 bytes, blocks to 16): written
+  // as zeros, so a state quantized into memory of any prior content is the
+  // same state (the key-map step reads whole dwords of a row).
+  if (crow) {
+    for (uint32_t i = ((uint32_t)nq * (uint32_t)a.qbits + 7u) / 8u; i < rq; ++i) crow[i] = 0u;
+    if (v == (uint32_t)a.dv - 1u) {
+      const uint32_t used = (uint32_t)a.dv * rq;
+      for (uint32_t i = used; i < ((used + 15u) & ~15u); ++i) crow[i - v * rq] = 0u;
+    }
+  }
+  if (hrow) {
+    const uint32_t rh = hp_row_bytes(nhp, hpb);
+    for (uint32_t i = (uint32_t)(nhp * hpb); i < rh; ++i) hrow[i] = 0u;
+    if (v == (uint32_t)a.dv - 1u) {
+      const uint32_t used = (uint32_t)a.dv * rh;
+      for (uint32_t i = used; i < ((used + 15u) & ~15u); ++i) hrow[i - v * rh] = 0u;
+    }
+  }
   a.scales[row] = scale;
 }
 
@@ -154,6 +172,19 @@ __global__ __launch_bounds__(256) void k_zero(uint32_t* p, uint64_t nwords) {
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
+namespace {
+template <int QB, int RND>
+hipError_t launch_step_qr(int family, int delta, const Args& a, hipStream_t s) {
+  switch (family) {
+    case kFamDense: return launch_dense<QB, RND>(delta, a, s);
+    case kFamMixed: return launch_mixed<QB, RND>(delta, a, s);
+    case kFamKeymap: return launch_keymap<QB, RND>(delta, a, s);
+    case kFamLrb: return launch_lrb<QB, RND>(delta, a, s);
+  }
+  return hipErrorInvalidValue;
+}
+}  // namespace
+
 hipError_t launch_step(int family, int qbits, int rnd, int delta, const Args& a, hipStream_t s) {
   if (qbits == 8) {
     switch (rnd) {

@@ -1,0 +1,9 @@
+// Dense step kernels (precision map none or per head) for one qbits x rounding pair: the
+// build compiles this unit once per pair, with QS_QB (8 or 4) and QS_RND (0
+// nearest, 1 stochastic 16-bit, 2 stochastic 8-bit) defined, so the
+// instantiations compile in parallel.
+#include "qstate_step_launch.hpp"
+
+namespace qs {
+template hipError_t launch_dense<QS_QB, QS_RND>(int delta, const Args& a, hipStream_t s);
+}  // namespace qs

@@ -144,3 +144,42 @@ def test_build_map_matches_oracle():
     assert workload_map(WORKLOADS["gdn_large"]).reshape(32, 128)[:, :13].all()
     with pytest.raises(_lib.QStateError):
         build_map(np.array([np.nan, 1.0], np.float32), 1, 2, 0.5)
+
+
+def test_binding_argument_checks_raise_before_the_abi():
+    """The binding's host-side checks (dtype, element count, contiguity, then
+    device) reject mismatched tensors before any pointer reaches the library;
+    exercised on CPU tensors against a CPU 'device' so no GPU is needed."""
+    import torch
+    from quantized_recurrent_state_qstate_amd.api import check_inputs, check_state, check_tensor
+
+    cpu = torch.device("cpu")
+    cfg = StateConfig(B=2, H=3, dk=64, dv=8, in_dtype="bf16", decay_mode="key")
+    n, H, dk, dv = 2, 3, 64, 8
+    good = dict(q=torch.zeros(n, H, dk, dtype=torch.bfloat16), k=torch.zeros(n, H, dk, dtype=torch.bfloat16),
+                v=torch.zeros(n, H, dv, dtype=torch.bfloat16), decay=torch.zeros(n, H, dk),
+                beta=torch.zeros(n, H), out=torch.zeros(n, H, dv))
+    check_inputs(cfg, n, cpu, **good)
+    cases = [
+        (dict(q=good["q"].float()), "q: dtype"),
+        (dict(v=good["v"][:1]), "v: 24 elements, expected 48"),
+        (dict(decay=torch.zeros(n, H)), "decay: 6 elements, expected 384"),
+        (dict(k=good["k"].transpose(1, 2).contiguous().transpose(1, 2)), "k: not contiguous"),
+        (dict(beta=torch.zeros(n, H, dtype=torch.float64)), "beta: dtype"),
+        (dict(out=torch.zeros(3)), "out: 3 elements"),
+    ]
+    for bad, msg in cases:
+        with pytest.raises(ValueError, match=msg):
+            check_inputs(cfg, n, cpu, **dict(good, **bad))
+    with pytest.raises(ValueError, match="on cpu, expected meta"):
+        check_tensor("q", good["q"], torch.bfloat16, n * H * dk, torch.device("meta"))
+    with pytest.raises(ValueError, match="expected a torch.Tensor"):
+        check_tensor("q", np.zeros(4), torch.float32, 4, cpu)
+    sizes = plan(cfg)
+    st = {"codes": torch.zeros(sizes["codes"], dtype=torch.uint8),
+          "scales": torch.zeros(sizes["scales"] // 4), "hp": torch.zeros(0, dtype=torch.uint8)}
+    check_state(cfg, sizes, st, cpu)
+    with pytest.raises(ValueError, match="codes"):
+        check_state(cfg, sizes, dict(st, codes=st["codes"][:10]), cpu)
+    with pytest.raises(ValueError, match="scales.*dtype"):
+        check_state(cfg, sizes, dict(st, scales=st["scales"].half()), cpu)
