@@ -226,9 +226,14 @@ qs_status qstate_decode_step_batch(qstate_handle* h, const qstate_tensors* pool,
                                    const qstate_inputs* in, float* out, int32_t n,
                                    const int32_t* slot, const uint64_t* step, void* stream);
 
-/* Stored state -> fp32 effective state S [B][H][dv][dk] (device):
- * scale * code for quantized channels, the widened value for protected
- * ones, plus W U^T when LRB is on. */
+/* Stored state -> fp32 effective state S [B][H][dv][dk] (device), the
+ * state the method's readout sees: scale * code for quantized channels (one
+ * scale per row, the value-axis grouping of [LoReS]), the widened 16-bit or
+ * fp32 value for protected ones (decay-based mixed precision, [LoReS]), plus
+ * the low-rank buffer W U^T when LRB is on ([PU]: small updates held in the
+ * buffer are part of the state until merged).  Not on the decode path: for
+ * checks, checkpoints and hand-back.  Errors: QS_EINVAL (null handle or
+ * pointers, misaligned pointer). */
 qs_status qstate_dequantize(qstate_handle* h, const qstate_tensors* src, float* S,
                             void* stream);
 

@@ -11,6 +11,7 @@ allocation of the stored-state buffers in the documented layout.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import dataclasses
 import os
@@ -26,45 +27,64 @@ _LIB = None
 def lib():
     global _LIB
     if _LIB is None:
-        path = _build.build()
-        L = ctypes.CDLL(path)
-        P = ctypes.POINTER
-        c_cfg = P(_Cfg)
-        L.orc_layout.argtypes = [c_cfg, P(_Sizes), P(ctypes.c_uint64), P(ctypes.c_uint64),
-                                 P(ctypes.c_int32)]
-        L.orc_layout.restype = ctypes.c_int
-        L.orc_philox4x32_10.argtypes = [P(ctypes.c_uint32), P(ctypes.c_uint32), P(ctypes.c_uint32)]
-        L.orc_philox4x32_10.restype = None
-        L.orc_random_bits.argtypes = [c_cfg, ctypes.c_uint64, ctypes.c_uint64]
-        L.orc_random_bits.restype = ctypes.c_uint32
-        L.orc_sr_round.argtypes = [ctypes.c_float, ctypes.c_uint32, ctypes.c_int32]
-        L.orc_sr_round.restype = ctypes.c_float
-        L.orc_inv_rtz.argtypes = [ctypes.c_float, ctypes.c_float]
-        L.orc_inv_rtz.restype = ctypes.c_float
-        L.orc_to_bf16.argtypes = [ctypes.c_float]
-        L.orc_to_bf16.restype = ctypes.c_uint16
-        L.orc_to_fp16.argtypes = [ctypes.c_float]
-        L.orc_to_fp16.restype = ctypes.c_uint16
-        L.orc_from_bf16.argtypes = [ctypes.c_uint16]
-        L.orc_from_bf16.restype = ctypes.c_float
-        L.orc_from_fp16.argtypes = [ctypes.c_uint16]
-        L.orc_from_fp16.restype = ctypes.c_float
-        L.orc_build_map.argtypes = [P(ctypes.c_double), ctypes.c_int32, ctypes.c_int32,
-                                    ctypes.c_double, P(ctypes.c_uint8)]
-        L.orc_build_map.restype = ctypes.c_int
-        L.orc_quantize.argtypes = [c_cfg, P(ctypes.c_float), P(_State), ctypes.c_uint64]
-        L.orc_quantize.restype = ctypes.c_int
-        L.orc_dequantize.argtypes = [c_cfg, P(_State), P(ctypes.c_float)]
-        L.orc_dequantize.restype = ctypes.c_int
-        fp = P(ctypes.c_float)
-        L.orc_step.argtypes = [c_cfg, P(_State), fp, fp, fp, fp, fp, fp, ctypes.c_uint64, fp,
-                               P(ctypes.c_int64), ctypes.c_int64]
-        L.orc_step.restype = ctypes.c_int
-        L.orc_step_batch.argtypes = [c_cfg, P(_State), fp, fp, fp, fp, fp, fp, ctypes.c_int32,
-                                     P(ctypes.c_int32), P(ctypes.c_uint64)]
-        L.orc_step_batch.restype = ctypes.c_int
-        _LIB = L
+        _LIB = configure(ctypes.CDLL(_build.build()))
     return _LIB
+
+
+@contextlib.contextmanager
+def using(path: str):
+    """Run the wrappers below against another build of the oracle's source
+    (tests that plant a mistake in a copy of it, on the CPU)."""
+    global _LIB
+    saved = _LIB
+    _LIB = configure(ctypes.CDLL(path))
+    try:
+        yield _LIB
+    finally:
+        _LIB = saved
+
+
+def configure(L):
+    """Declare the C signatures on a loaded oracle library."""
+    P = ctypes.POINTER
+    c_cfg = P(_Cfg)
+    L.orc_layout.argtypes = [c_cfg, P(_Sizes), P(ctypes.c_uint64), P(ctypes.c_uint64),
+                             P(ctypes.c_int32)]
+    L.orc_layout.restype = ctypes.c_int
+    L.orc_philox4x32_10.argtypes = [P(ctypes.c_uint32), P(ctypes.c_uint32), P(ctypes.c_uint32)]
+    L.orc_philox4x32_10.restype = None
+    L.orc_random_bits.argtypes = [c_cfg, ctypes.c_uint64, ctypes.c_uint64]
+    L.orc_random_bits.restype = ctypes.c_uint32
+    L.orc_sr_round.argtypes = [ctypes.c_float, ctypes.c_uint32, ctypes.c_int32]
+    L.orc_sr_round.restype = ctypes.c_float
+    L.orc_inv_rtz.argtypes = [ctypes.c_float, ctypes.c_float]
+    L.orc_inv_rtz.restype = ctypes.c_float
+    L.orc_to_bf16.argtypes = [ctypes.c_float]
+    L.orc_to_bf16.restype = ctypes.c_uint16
+    L.orc_to_fp16.argtypes = [ctypes.c_float]
+    L.orc_to_fp16.restype = ctypes.c_uint16
+    L.orc_from_bf16.argtypes = [ctypes.c_uint16]
+    L.orc_from_bf16.restype = ctypes.c_float
+    L.orc_from_fp16.argtypes = [ctypes.c_uint16]
+    L.orc_from_fp16.restype = ctypes.c_float
+    L.orc_build_map.argtypes = [P(ctypes.c_double), ctypes.c_int32, ctypes.c_int32,
+                                ctypes.c_double, P(ctypes.c_uint8)]
+    L.orc_build_map.restype = ctypes.c_int
+    L.orc_quantize.argtypes = [c_cfg, P(ctypes.c_float), P(_State), ctypes.c_uint64]
+    L.orc_quantize.restype = ctypes.c_int
+    L.orc_dequantize.argtypes = [c_cfg, P(_State), P(ctypes.c_float)]
+    L.orc_dequantize.restype = ctypes.c_int
+    fp = P(ctypes.c_float)
+    L.orc_step.argtypes = [c_cfg, P(_State), fp, fp, fp, fp, fp, fp, ctypes.c_uint64, fp,
+                           P(ctypes.c_int64), ctypes.c_int64]
+    L.orc_step.restype = ctypes.c_int
+    L.orc_step_batch.argtypes = [c_cfg, P(_State), fp, fp, fp, fp, fp, fp, ctypes.c_int32,
+                                 P(ctypes.c_int32), P(ctypes.c_uint64)]
+    L.orc_step_batch.restype = ctypes.c_int
+    L.orc_step_lrb_trace.argtypes = [c_cfg, P(_State), fp, fp, fp, fp, fp, fp, ctypes.c_uint64, fp,
+                                     P(_Trace)]
+    L.orc_step_lrb_trace.restype = ctypes.c_int
+    return L
 
 
 class _Cfg(ctypes.Structure):
@@ -88,6 +108,11 @@ class _State(ctypes.Structure):
     _fields_ = [("codes", ctypes.POINTER(ctypes.c_uint8)), ("scales", ctypes.POINTER(ctypes.c_float)),
                 ("hp", ctypes.c_void_p), ("W", ctypes.POINTER(ctypes.c_float)),
                 ("U", ctypes.POINTER(ctypes.c_float)), ("n", ctypes.POINTER(ctypes.c_int32))]
+
+
+class _Trace(ctypes.Structure):
+    _fields_ = [("small", ctypes.POINTER(ctypes.c_int32)), ("merged", ctypes.POINTER(ctypes.c_int32)),
+                ("n_before", ctypes.POINTER(ctypes.c_int32)), ("n_after", ctypes.POINTER(ctypes.c_int32))]
 
 
 KIND = {"additive": 0, "delta": 1}
@@ -236,6 +261,36 @@ def step(cfg: Cfg, st: dict, q, k, v, decay, beta=None, step: int = 0, heads=Non
     if rc:
         raise ValueError("oracle step failed")
     return (out, sp) if want_sp else out
+
+
+def step_lrb_trace(cfg: Cfg, st: dict, q, k, v, decay, beta=None, step: int = 0):
+    """One step of every head (low-rank bypass on), in place on ``st``.
+    Returns o [B,H,dv], S_pre [B,H,dv,dk] and the buffer decisions: small and
+    merged [B,H,dk] (bool), basis size before and after [B,H]."""
+    B, H, dk, dv = cfg.B, cfg.H, cfg.dk, cfg.dv
+    q = _f32(q, (B, H, dk))
+    k = _f32(k, (B, H, dk))
+    v = _f32(v, (B, H, dv))
+    decay = _f32(decay, (B, H) if cfg.decay_mode == "head" else (B, H, dk))
+    beta_p = None
+    if beta is not None:
+        beta = _f32(beta, (B, H))
+        beta_p = _fp(beta)
+    out = np.zeros((B, H, dv), np.float32)
+    sp = np.zeros((B, H, dv, dk), np.float32)
+    small = np.zeros((B, H, dk), np.int32)
+    merged = np.zeros((B, H, dk), np.int32)
+    nb = np.zeros((B, H), np.int32)
+    na = np.zeros((B, H), np.int32)
+    ip = ctypes.POINTER(ctypes.c_int32)
+    tr = _Trace(small.ctypes.data_as(ip), merged.ctypes.data_as(ip), nb.ctypes.data_as(ip), na.ctypes.data_as(ip))
+    c = cfg.c()
+    s = _state_struct(st)
+    rc = lib().orc_step_lrb_trace(ctypes.byref(c), ctypes.byref(s), _fp(q), _fp(k), _fp(v), _fp(decay), beta_p,
+                                  _fp(out), step, _fp(sp), ctypes.byref(tr))
+    if rc:
+        raise ValueError("oracle traced step failed")
+    return out, sp, small.astype(bool), merged.astype(bool), nb, na
 
 
 def step_batch(cfg: Cfg, st: dict, q, k, v, decay, beta, slot, steps, out=None):

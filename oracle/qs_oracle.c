@@ -596,7 +596,8 @@ static void lrb_phase(const orc_cfg* c, float* W, float* U, int32_t* np_, const 
 /* ------------------------------------------------------------------------ */
 static void head_step(const orc_cfg* c, const layout_t* L, orc_state* st, int64_t bh, int64_t bi,
                       const float* q, const float* kin, const float* vin, const float* decay,
-                      const float* beta, float* out, uint64_t step, float* sp_dbg) {
+                      const float* beta, float* out, uint64_t step, float* sp_dbg,
+                      const orc_lrb_trace* tr) {
   const int dk = c->dk, dv = c->dv, r = c->lrb_rank;
   int* slot = (int*)malloc(sizeof(int) * (size_t)dk);
   head_addr a;
@@ -669,7 +670,16 @@ static void head_step(const orc_cfg* c, const layout_t* L, orc_state* st, int64_
   float* merged = NULL;
   if (r > 0) {
     merged = (float*)malloc(sizeof(float) * (size_t)dv * (size_t)dk);
+    const int32_t n_before = st->n[bh];
     lrb_phase(c, W, U, &st->n[bh], u, kh, s_old, step, small, u_perp, merged, mflag);
+    if (tr) {
+      for (int k = 0; k < dk; ++k) {
+        tr->small[(uint64_t)bh * dk + k] = small[k];
+        tr->merged[(uint64_t)bh * dk + k] = mflag[k];
+      }
+      tr->n_before[bh] = n_before;
+      tr->n_after[bh] = st->n[bh];
+    }
   }
   /* decay + update (+ merged buffer columns).  The decay multiplies the
    * row scale before the code: (d_k * s_v) * code for a quantized channel,
@@ -732,11 +742,11 @@ int orc_step(const orc_cfg* c, orc_state* st, const float* q, const float* k, co
         layout_free(&L);
         return -1;
       }
-      head_step(c, &L, st, heads[i], heads[i], q, k, v, decay, beta, out, step, sp_dbg);
+      head_step(c, &L, st, heads[i], heads[i], q, k, v, decay, beta, out, step, sp_dbg, NULL);
     }
   } else {
     for (int64_t bh = 0; bh < BH; ++bh)
-      head_step(c, &L, st, bh, bh, q, k, v, decay, beta, out, step, sp_dbg);
+      head_step(c, &L, st, bh, bh, q, k, v, decay, beta, out, step, sp_dbg, NULL);
   }
   layout_free(&L);
   return 0;
@@ -758,8 +768,25 @@ int orc_step_batch(const orc_cfg* c, orc_state* st, const float* q, const float*
     if (slot[b] < 0 || slot[b] >= c->B) continue;
     for (int32_t h = 0; h < c->H; ++h)
       head_step(c, &L, st, (int64_t)slot[b] * c->H + h, (int64_t)b * c->H + h, q, k, v, decay, beta, out,
-                step[b], NULL);
+                step[b], NULL, NULL);
   }
+  layout_free(&L);
+  return 0;
+}
+
+/* orc_step over every head, also reporting the low-rank bypass decisions the
+ * step took (for tests that check them against a separate simulation). */
+int orc_step_lrb_trace(const orc_cfg* c, orc_state* st, const float* q, const float* k,
+                       const float* v, const float* decay, const float* beta, float* out,
+                       uint64_t step, float* sp_dbg, const orc_lrb_trace* tr) {
+  layout_t L;
+  if (c->lrb_rank <= 0 || layout_make(c, &L)) {
+    if (c->lrb_rank > 0) layout_free(&L);
+    return -1;
+  }
+  int64_t BH = (int64_t)c->B * c->H;
+  for (int64_t bh = 0; bh < BH; ++bh)
+    head_step(c, &L, st, bh, bh, q, k, v, decay, beta, out, step, sp_dbg, tr);
   layout_free(&L);
   return 0;
 }

@@ -87,6 +87,20 @@ int  orc_step_batch(const orc_cfg* c, orc_state* st, const float* q, const float
                     const float* v, const float* decay, const float* beta, float* out,
                     int32_t n, const int32_t* slot, const uint64_t* step);
 
+/* Decisions of the low-rank bypass in one step, per (b,h) and key channel:
+ * small[bh*dk+k] = channel k was small (its in-span update went to the
+ * buffer), merged[bh*dk+k] = channel k was merged into the state; the basis
+ * size before and after the step. */
+typedef struct {
+  int32_t* small;
+  int32_t* merged;
+  int32_t* n_before;
+  int32_t* n_after;
+} orc_lrb_trace;
+int  orc_step_lrb_trace(const orc_cfg* c, orc_state* st, const float* q, const float* k,
+                        const float* v, const float* decay, const float* beta, float* out,
+                        uint64_t step, float* sp_dbg, const orc_lrb_trace* tr);
+
 #ifdef __cplusplus
 }
 #endif

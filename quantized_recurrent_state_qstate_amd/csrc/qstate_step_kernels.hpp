@@ -107,7 +107,8 @@ __device__ __forceinline__ float load_in_scalar(const void* base, uint64_t idx) 
 
 // max / Q, correctly rounded, as a multiply by fp32(1/Q) and one fused
 // correction step: equal to the IEEE quotient for every non-negative fp32
-// max (checked exhaustively for Q = 127 and Q = 7), in 3 instructions.
+// max, in 3 instructions (the test suite checks all 2^31 non-negative
+// floats for Q = 127 and Q = 7, and inv_toward_zero over the same range).
 template <int QB>
 __device__ __forceinline__ float div_by_q(float m) {
   constexpr float Q = (QB == 8) ? 127.0f : 7.0f;

@@ -1,12 +1,15 @@
 """Pins of the oracle's Philox4x32-10 and of its element -> random-bits mapping.
 
 Philox4x32-10 is defined by Salmon et al., "Parallel Random Numbers: As Easy
-as 1, 2, 3" (SC'11).  The oracle's implementation is checked against an
-independent one: rocRAND's philox4x32_10 engine, whose header-only engine is
-host-callable.  A tiny host program (built here with hipcc, host code only, no
-GPU call) prints the engine's outputs for chosen keys and counters; the
-engine's (seed, subsequence, offset) arguments map to key = seed and counter
-= (offset/4 as 64 bits, subsequence as 64 bits).
+as 1, 2, 3" (SC'11).  The oracle's implementation is checked against two
+independent ones:
+* the definition written out here with Python integers (and, for a million
+  counters, the same definition over numpy uint64 arrays);
+* rocRAND's philox4x32_10 engine, whose header-only engine is host-callable.
+  A tiny host program (built here with hipcc, host code only, no GPU call)
+  prints the engine's outputs for chosen keys and counters; the engine's
+  (seed, subsequence, offset) arguments map to key = seed and counter =
+  (offset/4 as 64 bits, subsequence as 64 bits).
 """
 import os
 import shutil
@@ -64,6 +67,82 @@ def test_philox_matches_rocrand_engine():
         key = (seed & 0xFFFFFFFF, seed >> 32)
         ctr = (grp & 0xFFFFFFFF, grp >> 32, sub & 0xFFFFFFFF, sub >> 32)
         assert oracle.philox(ctr, key) == words, (seed, sub, grp)
+
+
+# The definition (SC'11, the Philox family): a round multiplies counter words
+# 0 and 2 by the two multipliers; the new word 0 is the high half of the
+# second product xored with word 1 and key word 0, the new word 2 the high
+# half of the first product xored with word 3 and key word 1, and the low
+# halves become words 1 and 3 (second product, then first).  The key is
+# bumped by the two Weyl constants after each round; ten rounds.
+_M = (0xD2511F53, 0xCD9E8D57)
+_W = (0x9E3779B9, 0xBB67AE85)
+_MASK = (1 << 32) - 1
+
+
+def philox_int(ctr, key, rounds=10):
+    x0, x1, x2, x3 = (int(c) & _MASK for c in ctr)
+    k0, k1 = (int(k) & _MASK for k in key)
+    for _ in range(rounds):
+        p0, p1 = _M[0] * x0, _M[1] * x2
+        x0, x1, x2, x3 = (p1 >> 32) ^ x1 ^ k0, p1 & _MASK, (p0 >> 32) ^ x3 ^ k1, p0 & _MASK
+        k0, k1 = (k0 + _W[0]) & _MASK, (k1 + _W[1]) & _MASK
+    return [x0, x1, x2, x3]
+
+
+def philox_np(ctr, key, rounds=10):
+    """The same over uint64 arrays (a 32 x 32-bit product fits exactly)."""
+    x = [np.asarray(c, np.uint64) & np.uint64(_MASK) for c in ctr]
+    k0 = np.asarray(key[0], np.uint64) & np.uint64(_MASK)
+    k1 = np.asarray(key[1], np.uint64) & np.uint64(_MASK)
+    m, s32 = np.uint64(_MASK), np.uint64(32)
+    for _ in range(rounds):
+        p0, p1 = np.uint64(_M[0]) * x[0], np.uint64(_M[1]) * x[2]
+        x = [(p1 >> s32) ^ x[1] ^ k0, p1 & m, (p0 >> s32) ^ x[3] ^ k1, p0 & m]
+        k0, k1 = (k0 + np.uint64(_W[0])) & m, (k1 + np.uint64(_W[1])) & m
+    return x
+
+
+def _counters(n, seed):
+    """Counters and keys spanning every word: random, plus all-zero, all-one
+    and single-bit words."""
+    r = np.random.default_rng(seed)
+    ctr = r.integers(0, 1 << 32, (n, 4), dtype=np.uint64)
+    key = r.integers(0, 1 << 32, (n, 2), dtype=np.uint64)
+    special = np.array([0, 1, _MASK, 1 << 31, 0x80000001], np.uint64)
+    ctr[:200] = special[r.integers(0, special.size, (200, 4))]
+    key[:200] = special[r.integers(0, special.size, (200, 2))]
+    return ctr, key
+
+
+def _oracle_many(ctr, key):
+    import ctypes
+    f = oracle.lib().orc_philox4x32_10
+    c, k, o = (ctypes.c_uint32 * 4)(), (ctypes.c_uint32 * 2)(), (ctypes.c_uint32 * 4)()
+    out = np.zeros(ctr.shape, np.uint64)
+    for i in range(ctr.shape[0]):
+        c[0], c[1], c[2], c[3] = (int(x) for x in ctr[i])
+        k[0], k[1] = int(key[i, 0]), int(key[i, 1])
+        f(c, k, o)
+        out[i] = tuple(o)
+    return out
+
+
+def test_philox_matches_python_definition():
+    ctr, key = _counters(20000, 1)
+    got = _oracle_many(ctr, key)
+    for i in range(ctr.shape[0]):
+        assert list(got[i]) == philox_int(ctr[i], key[i]), (ctr[i], key[i])
+
+
+def test_philox_matches_definition_on_a_million_counters():
+    ctr, key = _counters(1_000_000, 2)
+    got = _oracle_many(ctr, key)
+    want = np.stack(philox_np(ctr.T, key.T), 1)
+    assert np.array_equal(got, want)
+    # and the two written-out forms agree with each other on a sample
+    for i in range(0, 1_000_000, 50_000):
+        assert list(want[i]) == philox_int(ctr[i], key[i])
 
 
 def test_random_bits_mapping_16():
