@@ -150,8 +150,13 @@ class Cfg:
         s.B, s.H, s.dk, s.dv = self.B, self.H, self.dk, self.dv
         s.qbits, s.hp_dtype, s.map_mode = self.qbits, HP[self.hp_dtype], MAP[self.map_mode]
         if self.map is not None:
-            self._map_keep = np.ascontiguousarray(self.map, dtype=np.uint8)
-            s.map = self._map_keep.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8))
+            # converted once per map object and kept: threads that share a Cfg
+            # must not free the array another thread's call is reading
+            keep = getattr(self, "_map_keep", None)
+            if keep is None or keep[0] is not self.map:
+                keep = (self.map, np.ascontiguousarray(self.map, dtype=np.uint8))
+                self._map_keep = keep
+            s.map = keep[1].ctypes.data_as(ctypes.POINTER(ctypes.c_uint8))
         s.rounding, s.sr_bits = ROUND[self.rounding], self.sr_bits
         s.bdr, s.bdr_bound = int(self.bdr), self.bdr_bound
         s.lrb_rank, s.lrb_period, s.lrb_theta = self.lrb_rank, self.lrb_period, self.lrb_theta

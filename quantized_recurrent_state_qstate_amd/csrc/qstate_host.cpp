@@ -200,11 +200,11 @@ qs_status make_plan(const qstate_config* c, Plan* p) {
     p->keymap_rpl = krpl;
     const int rows = 256 / p->dense_lpr * krpl;
     p->row_chunks = (dv + rows - 1) / rows;
-  } else if (c->map_mode == QS_MAP_KEY ||
-             (c->map_mode == QS_MAP_HEAD && (c->hp_dtype == QS_FP32 || H > 64))) {
-    // key-channel maps, fp32 protected heads and head maps over more than 64
-    // heads run the LDS-staged kernel; the dense kernel handles whole-head
-    // maps with 16-bit protected heads (addressed from a 64-bit head mask)
+  } else if (c->map_mode == QS_MAP_KEY || (c->map_mode == QS_MAP_HEAD && H > 64)) {
+    // key-channel maps (other than the 16-bit dk 128 ones above) and head
+    // maps over more than 64 heads run the LDS-staged kernel; the dense
+    // kernel handles whole-head maps with 16-bit or fp32 protected heads
+    // (addressed from a 64-bit head mask)
     p->family = qs::kFamMixed;
     uint64_t mx = 0;
     for (int h = 0; h < H; ++h) {

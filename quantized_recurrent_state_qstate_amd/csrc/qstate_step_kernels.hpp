@@ -132,16 +132,17 @@ __device__ __forceinline__ void row_scale_fast(float m, float& scale, float& inv
   invb = ok ? iz * (float)(1u << SRB) : 0.0f;
 }
 
-// A lane's k and q slices (EPL keys from k0, or the split slice of a 16-bit
-// row: keys 64 (i / 8) + 8 lane + i % 8).  REG: held in registers, for lanes
-// that compute several rows; otherwise read from the LDS copy where they are
-// used, which keeps 2*EPL registers free.
-template <int EPL, bool REG, bool SPLIT = false>
+// A lane's k and q slices (EPL keys from k0, or the split slice of a row
+// stored in 128-byte pieces of VPP values each (16 bytes per lane): keys
+// 8 VPP (i / VPP) + VPP lane + i % VPP; VPP = 8 for 16-bit rows, 4 for fp32).
+// REG: held in registers, for lanes that compute several rows; otherwise
+// read from the LDS copy where they are used, which keeps 2*EPL registers free.
+template <int EPL, bool REG, bool SPLIT = false, int VPP = 8>
 struct KQ {
   float kr[REG ? EPL : 1], qr[REG ? EPL : 1];
   const float* kl;   // the lane's first key in LDS
   const float* ql;
-  static __device__ __forceinline__ int off(int i) { return SPLIT ? 64 * (i >> 3) + (i & 7) : i; }
+  static __device__ __forceinline__ int off(int i) { return SPLIT ? 8 * VPP * (i / VPP) + (i % VPP) : i; }
   __device__ __forceinline__ float k(int i) const {
     if constexpr (REG) return kr[i];
     else return kl[off(i)];
@@ -152,11 +153,12 @@ struct KQ {
   }
 };
 
-// Key of element i of a lane's slice: contiguous (k0 + i), or, for 16-bit
-// rows split into 128-byte pieces (SPLIT), 64 (i / 8) + 8 lane + i % 8.
-template <int EPL, bool SPLIT>
+// Key of element i of a lane's slice: contiguous (k0 + i), or, for rows
+// split into 128-byte pieces of VPP values (SPLIT), 8 VPP (i / VPP) + VPP
+// lane + i % VPP.
+template <int EPL, bool SPLIT, int VPP = 8>
 __device__ __forceinline__ int slice_key(int lane8, int i) {
-  return SPLIT ? 64 * (i >> 3) + 8 * lane8 + (i & 7) : lane8 * EPL + i;
+  return SPLIT ? 8 * VPP * (i / VPP) + VPP * lane8 + (i % VPP) : lane8 * EPL + i;
 }
 
 // Staging of the head's k and q into LDS as fp32 (one conversion per value
@@ -180,9 +182,9 @@ __device__ __forceinline__ void qk_load(const Args& a, uint64_t bh, float (&f)[q
   }
 }
 
-template <int EPL, int LPR, int INBF, bool SPLIT, bool REG>
+template <int EPL, int LPR, int INBF, bool SPLIT, bool REG, int VPP = 8>
 __device__ __forceinline__ void stage_qk(const Args& a, uint64_t bh, int lane8, float* lds,
-                                         const float (&f)[qk_first<EPL * LPR>()], KQ<EPL, REG, SPLIT>& kq) {
+                                         const float (&f)[qk_first<EPL * LPR>()], KQ<EPL, REG, SPLIT, VPP>& kq) {
   constexpr int DK = EPL * LPR;
   constexpr int NF = qk_first<DK>();
 #pragma unroll
@@ -195,13 +197,13 @@ __device__ __forceinline__ void stage_qk(const Args& a, uint64_t bh, int lane8, 
     lds[t] = load_in_scalar<INBF>(src, bh * DK + (uint64_t)(t < DK ? t : t - DK));
   }
   __syncthreads();
-  const int k0 = slice_key<EPL, SPLIT>(lane8, 0);
+  const int k0 = slice_key<EPL, SPLIT, VPP>(lane8, 0);
   kq.kl = lds + k0;
   kq.ql = lds + DK + k0;
   if constexpr (REG) {
 #pragma unroll
     for (int i = 0; i < EPL; i += 4) {
-      const int kk = slice_key<EPL, SPLIT>(lane8, i);
+      const int kk = slice_key<EPL, SPLIT, VPP>(lane8, i);
       const float4 kv = *reinterpret_cast<const float4*>(lds + kk);
       const float4 qv = *reinterpret_cast<const float4*>(lds + DK + kk);
       kq.kr[i] = kv.x; kq.kr[i + 1] = kv.y; kq.kr[i + 2] = kv.z; kq.kr[i + 3] = kv.w;
@@ -405,27 +407,31 @@ __device__ __forceinline__ void dense_quant_rows(const Args& a, uint8_t* blk, co
   store_row_values<RPL, LPR>(a, ix, wrow0, lane8, o_row, s_row);
 }
 
-// Protected (16-bit) heads of a head map.  With 8 lanes per row a row is
-// split into 128-byte pieces, lane j holding bytes 16j + 128i of each (keys
-// 64i + 8j .. 64i + 8j + 7), so every load and store of the wave covers
-// whole cache lines; with 4 lanes per row a lane holds 32 consecutive keys.
-template <int DELTA, int EPL, int LPR, int RPL, int DKEY, int INBF>
-__device__ __forceinline__ void dense_prot_rows(const Args& a, uint8_t* blk, const HeadIx& ix, int v0, int wrow0,
-                                                int lane8, float* lds) {
+// Protected heads of a head map, stored as HP (0 fp32, 1 bf16, 2 fp16).  With
+// 8 lanes per row a row is split into 128-byte pieces, lane j holding bytes
+// 16j + 128i of each (VPP = 16 / value bytes consecutive keys per piece), so
+// every load and store of the wave covers whole cache lines; with 4 lanes per
+// row a lane holds 32 consecutive keys.
+template <int HP, int DELTA, int EPL, int LPR, int RPL, int DKEY, int INBF>
+__device__ __forceinline__ void dense_prot_rows_t(const Args& a, uint8_t* blk, const HeadIx& ix, int v0,
+                                                  int wrow0, int lane8, float* lds) {
   const uint64_t bh = ix.in;   // inputs and outputs
   constexpr int DK = EPL * LPR;
   constexpr int GPW = 64 / LPR;
   constexpr bool SPLIT = (LPR == 8);
-  constexpr int NPC = EPL / 8;               // 16-byte pieces per lane and row (SPLIT)
+  constexpr int VB = HP == 0 ? 4 : 2;        // bytes per stored value
+  constexpr int VPP = 16 / VB;               // values per 16-byte piece
+  constexpr int NW = EPL * VB / 4;           // words per lane and row
+  constexpr int NPC = NW / 4;                // 16-byte pieces per lane and row
   // byte offset of the lane's piece i within a row
   auto piece = [&](int i) -> uint32_t {
-    return SPLIT ? (uint32_t)(128 * i + 16 * lane8) : (uint32_t)(lane8 * EPL * 2 + 16 * i);
+    return SPLIT ? (uint32_t)(128 * i + 16 * lane8) : (uint32_t)(lane8 * EPL * VB + 16 * i);
   };
-  uint32_t hw[RPL][EPL / 2];
+  uint32_t hw[RPL][NW];
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
     const int v = v0 + GPW * r;
-    const uint8_t* rowp = blk + (uint64_t)(v < a.dv ? v : 0) * (DK * 2);   // rows past dv: unused
+    const uint8_t* rowp = blk + (uint64_t)(v < a.dv ? v : 0) * (DK * VB);   // rows past dv: unused
 #pragma unroll
     for (int i = 0; i < NPC; ++i) {
       const u32x4_t t = ld_nt(reinterpret_cast<const u32x4_t*>(rowp + piece(i)));
@@ -443,7 +449,8 @@ __device__ __forceinline__ void dense_prot_rows(const Args& a, uint8_t* blk, con
   if constexpr (DKEY) {
 #pragma unroll
     for (int i = 0; i < EPL; i += 4) {
-      const float4 t = *reinterpret_cast<const float4*>(a.decay + (uint64_t)bh * DK + slice_key<EPL, SPLIT>(lane8, i));
+      const float4 t =
+          *reinterpret_cast<const float4*>(a.decay + (uint64_t)bh * DK + slice_key<EPL, SPLIT, VPP>(lane8, i));
       df[i] = t.x; df[i + 1] = t.y; df[i + 2] = t.z; df[i + 3] = t.w;
     }
   } else {
@@ -453,12 +460,14 @@ __device__ __forceinline__ void dense_prot_rows(const Args& a, uint8_t* blk, con
   float qkf[qk_first<DK>()];
   qk_load<DK, INBF>(a, bh, qkf);
   if (a.load_prio) __builtin_amdgcn_s_setprio(0);
-  KQ<EPL, false, SPLIT> kq;   // one pass over the rows' k and q: read from LDS where used
-  stage_qk<EPL, LPR, INBF, SPLIT>(a, bh, lane8, lds, qkf, kq);
+  KQ<EPL, false, SPLIT, VPP> kq;   // one pass over the rows' k and q: read from LDS where used
+  stage_qk<EPL, LPR, INBF, SPLIT, false, VPP>(a, bh, lane8, lds, qkf, kq);
+  auto value = [&](int r, int i) -> float {
+    if constexpr (HP == 0) return __uint_as_float(hw[r][i]);
+    const uint32_t bits = (hw[r][i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+    return HP == 1 ? bf16_bits_to_f32(bits) : f16_bits_to_f32(bits);
+  };
   float o_row[RPL];
-  // one body per 16-bit format (a uniform branch around the rows)
-  auto rows = [&](auto fmt) {
-    constexpr bool is_bf16 = decltype(fmt)::value;
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
     const int v = v0 + GPW * r;
@@ -468,11 +477,7 @@ __device__ __forceinline__ void dense_prot_rows(const Args& a, uint8_t* blk, con
     if constexpr (DELTA) {
       float wk = 0.0f;   // key decay: sum_k (d_k value_k) k_k
 #pragma unroll
-      for (int i = 0; i < EPL; ++i) {
-        const uint32_t bits = (hw[r][i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
-        const float sh = is_bf16 ? bf16_bits_to_f32(bits) : f16_bits_to_f32(bits);
-        wk = fmaf(DKEY ? df[i] * sh : sh, kq.k(i), wk);
-      }
+      for (int i = 0; i < EPL; ++i) wk = fmaf(DKEY ? df[i] * value(r, i) : value(r, i), kq.k(i), wk);
       wk = red_sum<LPR>(wk);
       u = DKEY ? beta * (vin[r] - wk) : beta * (vin[r] - dh * wk);
     } else {
@@ -482,28 +487,34 @@ __device__ __forceinline__ void dense_prot_rows(const Args& a, uint8_t* blk, con
     float o = 0.0f;
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
-      const uint32_t bits = (hw[r][i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
-      const float sh = is_bf16 ? bf16_bits_to_f32(bits) : f16_bits_to_f32(bits);
-      sp[i] = fmaf(u, kq.k(i), (DKEY ? df[i] : dh) * sh);
+      sp[i] = fmaf(u, kq.k(i), (DKEY ? df[i] : dh) * value(r, i));
       o = fmaf(sp[i], kq.q(i), o);
     }
     o_row[r] = red_sum<LPR>(o);
-    uint32_t ow[EPL / 2];
+    uint32_t ow[NW];
 #pragma unroll
-    for (int i = 0; i < EPL / 2; ++i)
-      ow[i] = is_bf16 ? pack_bf16x2(sp[2 * i], sp[2 * i + 1])
-                      : pack_f16x2(sp[2 * i], sp[2 * i + 1]);
-    uint8_t* rowp = blk + (uint64_t)v * (DK * 2);
+    for (int i = 0; i < NW; ++i) {
+      if constexpr (HP == 0) ow[i] = __float_as_uint(sp[i]);
+      else if constexpr (HP == 1) ow[i] = pack_bf16x2(sp[2 * i], sp[2 * i + 1]);
+      else ow[i] = pack_f16x2(sp[2 * i], sp[2 * i + 1]);
+    }
+    uint8_t* rowp = blk + (uint64_t)v * (DK * VB);
 #pragma unroll
     for (int i = 0; i < NPC; ++i) {
       const u32x4_t t = {ow[4 * i], ow[4 * i + 1], ow[4 * i + 2], ow[4 * i + 3]};
       st_nt(reinterpret_cast<u32x4_t*>(rowp + piece(i)), t);
     }
   }
-  };
-  if (a.hp_dtype == 1) rows(std::true_type{});
-  else rows(std::false_type{});
   store_row_values<RPL, LPR>(a, ix, wrow0, lane8, o_row, nullptr);
+}
+
+// One body per storage format (a uniform branch).
+template <int DELTA, int EPL, int LPR, int RPL, int DKEY, int INBF>
+__device__ __forceinline__ void dense_prot_rows(const Args& a, uint8_t* blk, const HeadIx& ix, int v0, int wrow0,
+                                                int lane8, float* lds) {
+  if (a.hp_dtype == 1) dense_prot_rows_t<1, DELTA, EPL, LPR, RPL, DKEY, INBF>(a, blk, ix, v0, wrow0, lane8, lds);
+  else if (a.hp_dtype == 2) dense_prot_rows_t<2, DELTA, EPL, LPR, RPL, DKEY, INBF>(a, blk, ix, v0, wrow0, lane8, lds);
+  else dense_prot_rows_t<0, DELTA, EPL, LPR, RPL, DKEY, INBF>(a, blk, ix, v0, wrow0, lane8, lds);
 }
 
 // Register budget (minimum waves per SIMD the body is compiled for), chosen

@@ -448,6 +448,16 @@ EDGE = {
                             map_mode="key", hp_dtype="fp16"),
     "kda_keymap_fp32_dk64": dict(kind="delta", decay_mode="key", dk=64, dv=48, H=3, B=2, qbits=8,
                                  map_mode="key", hp_dtype="fp32"),
+    # fp32 protected heads in the dense kernel (split 128-byte pieces of four
+    # values with 8 lanes per row; 32 consecutive keys with 4)
+    "headmap_fp32_dk128": dict(kind="additive", decay_mode="head", dk=128, dv=64, H=4, B=2, qbits=8,
+                               map_mode="head", hp_dtype="fp32"),
+    "headmap_fp32_delta_4lanes": dict(kind="delta", decay_mode="key", dk=128, dv=40, H=4, B=2, qbits=8,
+                                      map_mode="head", hp_dtype="fp32"),
+    "headmap_fp32_dk64_int4_key": dict(kind="additive", decay_mode="key", dk=64, dv=24, H=4, B=2, qbits=4,
+                                       map_mode="head", hp_dtype="fp32", in_dtype="fp32"),
+    "headmap_fp32_dk256_delta_8lanes": dict(kind="delta", decay_mode="head", dk=256, dv=16, H=2, B=2, qbits=8,
+                                            map_mode="head", hp_dtype="fp32"),
 }
 
 
