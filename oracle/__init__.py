@@ -59,6 +59,8 @@ def configure(L):
     L.orc_sr_round.restype = ctypes.c_float
     L.orc_inv_rtz.argtypes = [ctypes.c_float, ctypes.c_float]
     L.orc_inv_rtz.restype = ctypes.c_float
+    L.orc_scale_bf16_up.argtypes = [ctypes.c_float, ctypes.c_float]
+    L.orc_scale_bf16_up.restype = ctypes.c_float
     L.orc_to_bf16.argtypes = [ctypes.c_float]
     L.orc_to_bf16.restype = ctypes.c_uint16
     L.orc_to_fp16.argtypes = [ctypes.c_float]
@@ -95,7 +97,7 @@ class _Cfg(ctypes.Structure):
         ("map", ctypes.POINTER(ctypes.c_uint8)), ("rounding", ctypes.c_int32),
         ("sr_bits", ctypes.c_int32), ("bdr", ctypes.c_int32), ("bdr_bound", ctypes.c_float),
         ("lrb_rank", ctypes.c_int32), ("lrb_period", ctypes.c_int32), ("lrb_theta", ctypes.c_float),
-        ("seed", ctypes.c_uint64),
+        ("seed", ctypes.c_uint64), ("scale_dtype", ctypes.c_int32), ("lrb_dtype", ctypes.c_int32),
     ]
 
 
@@ -105,9 +107,9 @@ class _Sizes(ctypes.Structure):
 
 
 class _State(ctypes.Structure):
-    _fields_ = [("codes", ctypes.POINTER(ctypes.c_uint8)), ("scales", ctypes.POINTER(ctypes.c_float)),
-                ("hp", ctypes.c_void_p), ("W", ctypes.POINTER(ctypes.c_float)),
-                ("U", ctypes.POINTER(ctypes.c_float)), ("n", ctypes.POINTER(ctypes.c_int32))]
+    _fields_ = [("codes", ctypes.POINTER(ctypes.c_uint8)), ("scales", ctypes.c_void_p),
+                ("hp", ctypes.c_void_p), ("W", ctypes.c_void_p),
+                ("U", ctypes.c_void_p), ("n", ctypes.POINTER(ctypes.c_int32))]
 
 
 class _Trace(ctypes.Structure):
@@ -120,6 +122,7 @@ DECAY = {"head": 0, "key": 1}
 HP = {"fp32": 0, "bf16": 1, "fp16": 2}
 MAP = {"none": 0, "head": 1, "key": 2}
 ROUND = {"rtn": 0, "sr": 1}
+SDT = {"fp32": 0, "bf16": 1}
 
 
 @dataclasses.dataclass
@@ -143,6 +146,8 @@ class Cfg:
     lrb_period: int = 64
     lrb_theta: float = 0.5
     seed: int = 0
+    scale_dtype: str = "fp32"   # fp32 | bf16
+    lrb_dtype: str = "fp32"     # fp32 | bf16
 
     def c(self) -> _Cfg:
         s = _Cfg()
@@ -161,6 +166,7 @@ class Cfg:
         s.bdr, s.bdr_bound = int(self.bdr), self.bdr_bound
         s.lrb_rank, s.lrb_period, s.lrb_theta = self.lrb_rank, self.lrb_period, self.lrb_theta
         s.seed = self.seed
+        s.scale_dtype, s.lrb_dtype = SDT[self.scale_dtype], SDT[self.lrb_dtype]
         return s
 
 
@@ -190,14 +196,23 @@ def new_state(cfg: Cfg) -> dict:
     L = layout(cfg)
     hp_dt = np.float32 if cfg.hp_dtype == "fp32" else np.uint16
     hp_item = 4 if cfg.hp_dtype == "fp32" else 2
+    s_dt = np.float32 if cfg.scale_dtype == "fp32" else np.uint16     # bf16: raw bits
+    l_dt = np.float32 if cfg.lrb_dtype == "fp32" else np.uint16
     return {
         "codes": np.zeros(L["codes"], np.uint8),
-        "scales": np.zeros(L["scales"] // 4, np.float32),
+        "scales": np.zeros(L["scales"] // np.dtype(s_dt).itemsize, s_dt),
         "hp": np.zeros(L["hp"] // hp_item, hp_dt),
-        "W": np.zeros(L["W"] // 4, np.float32),
-        "U": np.zeros(L["U"] // 4, np.float32),
+        "W": np.zeros(L["W"] // np.dtype(l_dt).itemsize, l_dt),
+        "U": np.zeros(L["U"] // np.dtype(l_dt).itemsize, l_dt),
         "n": np.zeros(L["n"] // 4, np.int32),
     }
+
+
+def widen(a: np.ndarray) -> np.ndarray:
+    """A stored scale or buffer array as float64 (bf16 bits widened exactly)."""
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
 
 
 def _state_struct(st: dict) -> _State:
@@ -206,10 +221,10 @@ def _state_struct(st: dict) -> _State:
         a = st[key]
         assert a.flags.c_contiguous
     s.codes = st["codes"].ctypes.data_as(ctypes.POINTER(ctypes.c_uint8))
-    s.scales = _fp(st["scales"])
+    s.scales = st["scales"].ctypes.data_as(ctypes.c_void_p)
     s.hp = st["hp"].ctypes.data_as(ctypes.c_void_p)
-    s.W = _fp(st["W"])
-    s.U = _fp(st["U"])
+    s.W = st["W"].ctypes.data_as(ctypes.c_void_p)
+    s.U = st["U"].ctypes.data_as(ctypes.c_void_p)
     s.n = st["n"].ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
     return s
 
@@ -346,6 +361,11 @@ def sr_round(x: float, u: int, sr_bits: int = 16) -> float:
 def inv_rtz(q: float, m: float) -> float:
     """q / m rounded toward zero to fp32 (q, m > 0, finite quotient)."""
     return float(lib().orc_inv_rtz(q, m))
+
+
+def scale_bf16_up(m: float, q: float) -> float:
+    """Smallest bf16 value s with q s >= m (the rounded-up bf16 row scale)."""
+    return float(lib().orc_scale_bf16_up(m, q))
 
 
 def to_bf16(x: float) -> int:

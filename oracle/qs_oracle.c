@@ -135,6 +135,22 @@ uint16_t orc_to_fp16(float f) { return (uint16_t)rne_encode(f, 5, 10); }
 float orc_from_bf16(uint16_t h) { return decode_bits(h, 8, 7); }
 float orc_from_fp16(uint16_t h) { return decode_bits(h, 5, 10); }
 
+/* The smallest bf16 value s with q * s >= m (m > 0, q > 0 small integer):
+ * start from the nearest bf16 of m / q and step by one bf16 unit either way
+ * while the exact comparison (a bf16 times a small integer is exact in
+ * double) asks for it.  Returns +inf when no finite bf16 qualifies. */
+float orc_scale_bf16_up(float m, float q) {
+  uint16_t b = orc_to_bf16(m / q);
+  /* down while the next smaller positive bf16 still qualifies */
+  while ((b & 0x7FFFu) > 0u && (double)orc_from_bf16((uint16_t)(b - 1u)) * (double)q >= (double)m) b -= 1u;
+  /* up while b does not qualify */
+  while ((double)orc_from_bf16(b) * (double)q < (double)m) {
+    if ((b & 0x7F80u) == 0x7F80u) return INFINITY;
+    b += 1u;
+  }
+  return orc_from_bf16(b);
+}
+
 /* ------------------------------------------------------------------------ */
 /* Decay-based mixed precision (LoReS abstract: protect slowly decaying      */
 /* heads or channels).  Within each group of `per_group` units, flag the     */
@@ -202,7 +218,23 @@ static int check_cfg(const orc_cfg* c) {
   if (c->rounding == 1 && c->sr_bits != 16 && c->sr_bits != 8) return -1;
   if (c->lrb_rank < 0) return -1;
   if (c->lrb_rank > 0 && (c->map_mode != 0 || c->lrb_period <= 0)) return -1;
+  if ((c->scale_dtype != 0 && c->scale_dtype != 1) || (c->lrb_dtype != 0 && c->lrb_dtype != 1)) return -1;
   return 0;
+}
+
+/* A stored fp32 or bf16 element, widened; a value stored, bf16 rounded to
+ * nearest even.  `bf` selects the format. */
+static float get_f(const void* p, uint64_t i, int bf) {
+  if (bf) return orc_from_bf16(((const uint16_t*)p)[i]);
+  return ((const float*)p)[i];
+}
+static void put_f(void* p, uint64_t i, float x, int bf) {
+  if (bf) ((uint16_t*)p)[i] = orc_to_bf16(x);
+  else ((float*)p)[i] = x;
+}
+/* x rounded to the storage format of the low-rank buffer (and widened back). */
+static float lrb_round(const orc_cfg* c, float x) {
+  return c->lrb_dtype ? orc_from_bf16(orc_to_bf16(x)) : x;
 }
 
 int orc_layout(const orc_cfg* c, orc_sizes* s, uint64_t* code_off, uint64_t* hp_off,
@@ -224,9 +256,9 @@ int orc_layout(const orc_cfg* c, orc_sizes* s, uint64_t* code_off, uint64_t* hp_
   s->hp_bstride = hoff;
   s->codes = (uint64_t)c->B * coff;
   s->hp = (uint64_t)c->B * hoff;
-  s->scales = BH * (uint64_t)c->dv * 4u;
-  s->W = BH * (uint64_t)c->dv * (uint64_t)c->lrb_rank * 4u;
-  s->U = BH * (uint64_t)c->dk * (uint64_t)c->lrb_rank * 4u;
+  s->scales = BH * (uint64_t)c->dv * (c->scale_dtype ? 2u : 4u);
+  s->W = BH * (uint64_t)c->dv * (uint64_t)c->lrb_rank * (c->lrb_dtype ? 2u : 4u);
+  s->U = BH * (uint64_t)c->dk * (uint64_t)c->lrb_rank * (c->lrb_dtype ? 2u : 4u);
   s->n = c->lrb_rank > 0 ? BH * 4u : 0u;
   return 0;
 }
@@ -358,7 +390,7 @@ static float requantize_row(const orc_cfg* c, const head_addr* a, int64_t bh, in
    * exactly, so |value * inv| <= Q for every element of the row and no code
    * ever reaches the clamp below. */
   float scale = 0.0f, inv = 0.0f, invb = 0.0f;
-  if (m > 0.0f) {
+  if (m > 0.0f && c->scale_dtype == 0) {
     scale = m / Q;
     inv = Q / m;
     invb = (c->rounding == 1) ? ldexpf(inv, c->sr_bits) : inv;
@@ -369,6 +401,22 @@ static float requantize_row(const orc_cfg* c, const head_addr* a, int64_t bh, in
     } else {
       inv = orc_inv_rtz(Q, m);
       invb = (c->rounding == 1) ? ldexpf(inv, c->sr_bits) : inv;
+    }
+  } else if (m > 0.0f) {
+    /* bf16 scales: the stored scale s is the smallest bf16 value with
+     * Q s >= m (Q s is exact in double), and codes are taken against s:
+     * inv is the largest float with inv s <= 1, so |value * inv| <= m / s
+     * <= Q.  A row whose s overflows, or whose inv (times 2^sr_bits) is not
+     * finite, is stored as zero. */
+    scale = orc_scale_bf16_up(m, Q);
+    if (isfinite(scale)) {
+      inv = orc_inv_rtz(1.0f, scale);
+      invb = (c->rounding == 1) ? ldexpf(inv, c->sr_bits) : inv;
+    }
+    if (!isfinite(scale) || !isfinite(inv) || !isfinite(invb)) {
+      scale = 0.0f;
+      inv = 0.0f;
+      invb = 0.0f;
     }
   }
   for (int k = 0; k < dk; ++k) {
@@ -416,11 +464,11 @@ int orc_quantize(const orc_cfg* c, const float* S, orc_state* st, uint64_t step)
     head_address(c, &L, st, bh, &a, slot);
     for (int v = 0; v < dv; ++v) {
       const float* row = S + ((uint64_t)bh * dv + (uint64_t)v) * (uint64_t)dk;
-      st->scales[(uint64_t)bh * dv + v] = requantize_row(c, &a, bh, v, row, NULL, step);
+      put_f(st->scales, (uint64_t)bh * dv + v, requantize_row(c, &a, bh, v, row, NULL, step), c->scale_dtype);
     }
     if (r > 0) {
-      memset(st->W + (uint64_t)bh * dv * r, 0, sizeof(float) * (size_t)dv * (size_t)r);
-      memset(st->U + (uint64_t)bh * dk * r, 0, sizeof(float) * (size_t)dk * (size_t)r);
+      for (uint64_t i = 0; i < (uint64_t)dv * r; ++i) put_f(st->W, (uint64_t)bh * dv * r + i, 0.0f, c->lrb_dtype);
+      for (uint64_t i = 0; i < (uint64_t)dk * r; ++i) put_f(st->U, (uint64_t)bh * dk * r + i, 0.0f, c->lrb_dtype);
       st->n[bh] = 0;
     }
   }
@@ -452,16 +500,21 @@ int orc_dequantize(const orc_cfg* c, const orc_state* st, float* S) {
   for (int64_t bh = 0; bh < BH; ++bh) {
     head_addr a;
     head_address(c, &L, st, bh, &a, slot);
+    float* W = (float*)malloc(sizeof(float) * (size_t)(dv * r + 1));
+    float* U = (float*)malloc(sizeof(float) * (size_t)(dk * r + 1));
+    for (int i = 0; i < dv * r; ++i) W[i] = get_f(st->W, (uint64_t)bh * dv * r + i, c->lrb_dtype);
+    for (int i = 0; i < dk * r; ++i) U[i] = get_f(st->U, (uint64_t)bh * dk * r + i, c->lrb_dtype);
     for (int v = 0; v < dv; ++v) {
-      float scale = st->scales[(uint64_t)bh * dv + v];
+      float scale = get_f(st->scales, (uint64_t)bh * dv + v, c->scale_dtype);
       float* row = S + ((uint64_t)bh * dv + (uint64_t)v) * (uint64_t)dk;
       for (int k = 0; k < dk; ++k) {
         float x = dequant_elem(c, &a, scale, v, k);
-        if (r > 0) x = x + lrb_entry(st->W + (uint64_t)bh * dv * r, st->U + (uint64_t)bh * dk * r,
-                                     r, st->n[bh], v, k);
+        if (r > 0) x = x + lrb_entry(W, U, r, st->n[bh], v, k);
         row[k] = x;
       }
     }
+    free(W);
+    free(U);
   }
   free(slot);
   layout_free(&L);
@@ -522,7 +575,8 @@ static void lrb_phase(const orc_cfg* c, float* W, float* U, int32_t* np_, const 
     float ny = sqrtf((float)dot_d(y, y, dv));
     float nu = sqrtf((float)dot_d(u, u, dv));
     if (ny > ldexpf(nu, -10)) {
-      for (int v = 0; v < dv; ++v) W[v * r + n] = y[v] / ny;
+      /* stored (and used from this step on) in the buffer's format */
+      for (int v = 0; v < dv; ++v) W[v * r + n] = lrb_round(c, y[v] / ny);
       n += 1;
     }
     free(y);
@@ -552,6 +606,9 @@ static void lrb_phase(const orc_cfg* c, float* W, float* U, int32_t* np_, const 
     if (small[k])
       for (int j = 0; j < n; ++j) U[k * r + j] = fmaf(kk[k], cj[j], U[k * r + j]);
   }
+  /* the updated buffer in its storage format, before the merge test (what is
+   * stored is what the state holds) */
+  for (int i = 0; i < dk * r; ++i) U[i] = lrb_round(c, U[i]);
   /* 5. merge */
   for (int k = 0; k < dk; ++k) merge_flag[k] = 0;
   memset(merged, 0, sizeof(float) * (size_t)dv * (size_t)dk);
@@ -609,7 +666,6 @@ static void head_step(const orc_cfg* c, const layout_t* L, orc_state* st, int64_
   for (int k = 0; k < dk; ++k)
     d[k] = (c->decay_mode == 0) ? decay[bi] : decay[(uint64_t)bi * dk + k];
   const float bt = beta ? beta[bi] : 1.0f;
-  float* scales = st->scales + (uint64_t)bh * dv;
 
   float* sh = (float*)malloc(sizeof(float) * (size_t)dv * (size_t)dk);
   float* sp = (float*)malloc(sizeof(float) * (size_t)dv * (size_t)dk);
@@ -618,7 +674,7 @@ static void head_step(const orc_cfg* c, const layout_t* L, orc_state* st, int64_
 
   /* dequantize */
   for (int v = 0; v < dv; ++v) {
-    s_old[v] = scales[v];
+    s_old[v] = get_f(st->scales, (uint64_t)bh * dv + v, c->scale_dtype);
     for (int k = 0; k < dk; ++k) sh[v * dk + k] = dequant_elem(c, &a, s_old[v], v, k);
   }
   /* the low-rank buffer decays first: the delta rule reads it decayed */
@@ -626,8 +682,11 @@ static void head_step(const orc_cfg* c, const layout_t* L, orc_state* st, int64_
   float* U = NULL;
   float* wb = (float*)calloc((size_t)dv, sizeof(float));
   if (r > 0) {
-    W = st->W + (uint64_t)bh * dv * r;
-    U = st->U + (uint64_t)bh * dk * r;
+    /* the buffer's factors, widened to fp32 for the step (stored back below) */
+    W = (float*)malloc(sizeof(float) * (size_t)dv * (size_t)r);
+    U = (float*)malloc(sizeof(float) * (size_t)dk * (size_t)r);
+    for (int i = 0; i < dv * r; ++i) W[i] = get_f(st->W, (uint64_t)bh * dv * r + i, c->lrb_dtype);
+    for (int i = 0; i < dk * r; ++i) U[i] = get_f(st->U, (uint64_t)bh * dk * r + i, c->lrb_dtype);
     lrb_decay(c, U, d);
     /* buffer part of the decayed effective state times k:
      * wb_v = sum_j W[v][j] zk_j, zk = U^T k (fp64 sums, rounded once) */
@@ -711,7 +770,14 @@ static void head_step(const orc_cfg* c, const layout_t* L, orc_state* st, int64_
   if (sp_dbg) memcpy(sp_dbg + (uint64_t)bi * dv * dk, sp, sizeof(float) * (size_t)dv * (size_t)dk);
   /* requantize */
   for (int v = 0; v < dv; ++v)
-    scales[v] = requantize_row(c, &a, bh, v, sp + (uint64_t)v * dk, sh + (uint64_t)v * dk, step);
+    put_f(st->scales, (uint64_t)bh * dv + v,
+          requantize_row(c, &a, bh, v, sp + (uint64_t)v * dk, sh + (uint64_t)v * dk, step), c->scale_dtype);
+  if (r > 0) {   /* values already in the buffer's format: stored exactly */
+    for (int i = 0; i < dv * r; ++i) put_f(st->W, (uint64_t)bh * dv * r + i, W[i], c->lrb_dtype);
+    for (int i = 0; i < dk * r; ++i) put_f(st->U, (uint64_t)bh * dk * r + i, U[i], c->lrb_dtype);
+    free(W);
+    free(U);
+  }
 
   free(z);
   free(wb);

@@ -47,14 +47,16 @@ typedef struct {
   int32_t lrb_period;  /* merge when (step+1) % period == 0 */
   float   lrb_theta;   /* merge / smallness threshold, in LSB */
   uint64_t seed;       /* Philox key */
+  int32_t scale_dtype; /* storage of row scales: 0 fp32, 1 bf16 (rounded up, see requantize_row) */
+  int32_t lrb_dtype;   /* storage of the low-rank buffer factors W and U: 0 fp32, 1 bf16 */
 } orc_cfg;
 
 typedef struct {
   uint8_t* codes;   /* packed codes, per-head blocks */
-  float*   scales;  /* [B,H,dv] */
+  void*    scales;  /* [B,H,dv], fp32 or bf16 bits per scale_dtype */
   void*    hp;      /* protected values, per-head blocks (uint16 bits or fp32) */
-  float*   W;       /* [B,H,dv,r] */
-  float*   U;       /* [B,H,dk,r] */
+  void*    W;       /* [B,H,dv,r], fp32 or bf16 bits per lrb_dtype */
+  void*    U;       /* [B,H,dk,r], fp32 or bf16 bits per lrb_dtype */
   int32_t* n;       /* [B,H] */
 } orc_state;
 
@@ -69,6 +71,7 @@ void orc_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t ou
 uint32_t orc_random_bits(const orc_cfg* c, uint64_t e, uint64_t step);
 float orc_sr_round(float xb, uint32_t rbits, int32_t sr_bits);  /* xb = x * 2^sr_bits */
 float orc_inv_rtz(float q, float m);   /* q / m rounded toward zero */
+float orc_scale_bf16_up(float m, float q);   /* smallest bf16 s with q s >= m (+inf if none) */
 uint16_t orc_to_bf16(float f);
 uint16_t orc_to_fp16(float f);
 float orc_from_bf16(uint16_t h);
