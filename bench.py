@@ -68,18 +68,21 @@ def algorithmic_bytes(w, m) -> dict:
     nq = dk - nhp
     hpb = 4 if w.hp_dtype == "fp32" else 2
     codes = B * int(sum(dv * (((int(n) * w.qbits + 7) // 8 + 3) // 4 * 4) for n in nq))   # rows padded to 4 B
-    scales = B * int(sum(dv * 4 for n in nq if n > 0))
+    ab = 2 if w.aux_dtype == "bf16" else 4                       # scale and buffer-factor bytes
+    scales = B * int(sum(dv * ab for n in nq if n > 0))
     hp = B * int(sum(dv * ((int(n) * hpb + 3) // 4 * 4) for n in nhp))
     state_rw = 2 * (codes + scales + hp)
+    resident = codes + scales + hp
     if w.lrb_rank:
         r = w.lrb_rank
-        state_rw += B * H * (dv * r * 4 + 2 * dk * r * 4 + 2 * 4)   # W read, U and n read+write
+        state_rw += B * H * (dv * r * ab + 2 * dk * r * ab + 2 * 4)   # W read, U and n read+write
+        resident += B * H * ((dv + dk) * r * ab + 4)
     inb = 2 if w.in_dtype == "bf16" else 4
     decay = B * H * (dk if w.decay_mode == "key" else 1) * 4
     beta = B * H * 4 if w.has_beta else 0
     inputs = B * H * (2 * dk + dv) * inb + decay + beta
     outputs = B * H * dv * 4
-    return {"state_rw": state_rw, "state": state_rw // 2, "inputs": inputs, "outputs": outputs,
+    return {"state_rw": state_rw, "state": resident, "inputs": inputs, "outputs": outputs,
             "total": state_rw + inputs + outputs}
 
 
@@ -88,7 +91,8 @@ def lib_config(w, m):
     return StateConfig(kind=w.kind, decay_mode=w.decay_mode, B=w.B, H=w.H, dk=w.dk, dv=w.dv, qbits=w.qbits,
                        hp_dtype=w.hp_dtype, map_mode=w.map_mode, map=m, in_dtype=w.in_dtype,
                        rounding=w.rounding, sr_bits=w.sr_bits, bdr=w.bdr, lrb_rank=w.lrb_rank,
-                       lrb_period=w.lrb_period, lrb_theta=w.lrb_theta, seed=w.philox_seed)
+                       lrb_period=w.lrb_period, lrb_theta=w.lrb_theta, seed=w.philox_seed,
+                       scale_dtype=w.aux_dtype, lrb_dtype=w.aux_dtype)
 
 
 def oracle_config(w, m, B):
@@ -96,7 +100,8 @@ def oracle_config(w, m, B):
     return oracle.Cfg(kind=w.kind, decay_mode=w.decay_mode, B=B, H=w.H, dk=w.dk, dv=w.dv, qbits=w.qbits,
                       hp_dtype=w.hp_dtype, map_mode=w.map_mode, map=m,
                       rounding="rtn" if w.rounding == "nearest" else "sr", sr_bits=w.sr_bits, bdr=w.bdr,
-                      lrb_rank=w.lrb_rank, lrb_period=w.lrb_period, lrb_theta=w.lrb_theta, seed=w.philox_seed)
+                      lrb_rank=w.lrb_rank, lrb_period=w.lrb_period, lrb_theta=w.lrb_theta, seed=w.philox_seed,
+                      scale_dtype=w.aux_dtype, lrb_dtype=w.aux_dtype)
 
 
 def cpu_baseline(w, m, budget_s: float, threads: int) -> dict:
@@ -236,7 +241,7 @@ def fp32_state_context(w, args, dev, pool, out, ms_ours, ours_state_bytes):
     compare against, run by the same streaming kernel family."""
     import numpy as np
     from quantized_recurrent_state_qstate_amd import QState
-    wf = w.scaled(map_mode="head", map_frac=1.0, hp_dtype="fp32", lrb_rank=0, bdr=False)
+    wf = w.scaled(map_mode="head", map_frac=1.0, hp_dtype="fp32", lrb_rank=0, bdr=False, aux_dtype="fp32")
     mf = np.ones(w.H, np.uint8)
     qf = QState(lib_config(wf, mf))
     resident = sum(qf.sizes.values())

@@ -55,6 +55,16 @@
  *   lrb_W fp32 [B][H][dv][r], lrb_U fp32 [B][H][dk][r], lrb_n int32 [B][H]
  *     (LRB only): effective state = dequantized state + W U^T using the
  *     first lrb_n columns.
+ *   bf16 layout (scale_dtype = lrb_dtype = QS_BF16, LRB on): scales, W and
+ *     U are bf16 [same shapes]; at a 128 x 128 head with int4 codes and
+ *     rank 8 the state is 5.22x smaller than fp32 (the "up to 5.3x" of
+ *     [PU] counts codes and factors: 5.33x).  A row's scale is the smallest
+ *     bf16 s with Q s >= max, and codes are taken against it: inv = the
+ *     largest fp32 with inv s <= 1 (a row whose s overflows, or whose inverse
+ *     times 2^sr_bits is not finite, is stored as zero).  A new basis column
+ *     is rounded to bf16 (nearest even) when made and used rounded; U is
+ *     updated in fp32 from its stored values and rounded to bf16 before the
+ *     merge test, so merge, readout and stored state see the same buffer.
  *   All-zero buffers are the state S = 0.
  *
  * Rounding of a quantized element x = S_pre * inv, inv = Q / max rounded
@@ -108,7 +118,7 @@
 extern "C" {
 #endif
 
-#define QSTATE_ABI_VERSION 1u
+#define QSTATE_ABI_VERSION 2u
 
 typedef enum {
   QS_OK = 0,
@@ -146,6 +156,10 @@ typedef struct {
   int32_t lrb_period;     /* merge when (step+1) % period == 0 */
   float lrb_theta;        /* merge / smallness threshold in LSB (> 0) */
   uint64_t seed;          /* Philox key for stochastic rounding */
+  int32_t scale_dtype;    /* row scales: QS_FP32, or QS_BF16 (low-rank bypass on, with
+                             lrb_dtype QS_BF16) */
+  int32_t lrb_dtype;      /* low-rank buffer factors W, U: QS_FP32, or QS_BF16 (with
+                             scale_dtype QS_BF16, lrb_rank <= 8) */
 } qstate_config;
 
 /* Byte sizes of the caller-owned device buffers (0 = buffer unused). */
@@ -153,13 +167,14 @@ typedef struct {
   uint64_t codes, scales, hp, lrb_W, lrb_U, lrb_n;
 } qstate_sizes;
 
-/* Device pointers of one stored state (16-byte aligned; unused ones may be NULL). */
+/* Device pointers of one stored state (16-byte aligned; unused ones may be NULL).
+ * scales, lrb_W and lrb_U hold fp32 or bf16 elements per scale_dtype / lrb_dtype. */
 typedef struct {
   void* codes;
-  float* scales;
+  void* scales;
   void* hp;
-  float* lrb_W;
-  float* lrb_U;
+  void* lrb_W;
+  void* lrb_U;
   int32_t* lrb_n;
 } qstate_tensors;
 

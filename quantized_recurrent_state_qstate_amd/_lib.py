@@ -12,7 +12,7 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libqstate.so")
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 QS_OK, QS_EINVAL, QS_EUNSUPPORTED, QS_ENOMEM, QS_EHIP = 0, -1, -2, -3, -4
 KIND = {"additive": 0, "delta": 1}
@@ -38,7 +38,7 @@ class Config(ctypes.Structure):
         ("rounding", ctypes.c_int32), ("sr_bits", ctypes.c_int32),
         ("bdr", ctypes.c_int32), ("bdr_bound", ctypes.c_float),
         ("lrb_rank", ctypes.c_int32), ("lrb_period", ctypes.c_int32), ("lrb_theta", ctypes.c_float),
-        ("seed", ctypes.c_uint64),
+        ("seed", ctypes.c_uint64), ("scale_dtype", ctypes.c_int32), ("lrb_dtype", ctypes.c_int32),
     ]
 
 

@@ -37,6 +37,8 @@ class StateConfig:
     lrb_period: int = 64
     lrb_theta: float = 0.5
     seed: int = 0
+    scale_dtype: str = "fp32"       # fp32 | bf16 (bf16: with lrb_dtype bf16 and the low-rank bypass)
+    lrb_dtype: str = "fp32"         # fp32 | bf16
 
     def to_c(self) -> _lib.Config:
         c = _lib.Config()
@@ -57,6 +59,8 @@ class StateConfig:
         c.bdr_bound = self.bdr_bound
         c.lrb_rank, c.lrb_period, c.lrb_theta = self.lrb_rank, self.lrb_period, self.lrb_theta
         c.seed = self.seed
+        c.scale_dtype = _lib.DTYPE[self.scale_dtype]
+        c.lrb_dtype = _lib.DTYPE[self.lrb_dtype]
         return c
 
 
@@ -82,8 +86,11 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
-_STATE_DTYPE = {"codes": "uint8", "scales": "float32", "hp": "uint8", "lrb_W": "float32",
-                "lrb_U": "float32", "lrb_n": "int32"}
+def _state_dtypes(cfg: "StateConfig") -> dict:
+    """torch dtype name of each state buffer (bf16 scales and factors in the bf16 layout)."""
+    sd = "bfloat16" if cfg.scale_dtype == "bf16" else "float32"
+    ld = "bfloat16" if cfg.lrb_dtype == "bf16" else "float32"
+    return {"codes": "uint8", "scales": sd, "hp": "uint8", "lrb_W": ld, "lrb_U": ld, "lrb_n": "int32"}
 
 
 def check_tensor(name: str, t, dtype, numel: int, device, at_least: bool = False) -> None:
@@ -107,7 +114,7 @@ def check_tensor(name: str, t, dtype, numel: int, device, at_least: bool = False
 def check_state(cfg: "StateConfig", sizes: dict, st: dict, device) -> None:
     """Every buffer the plan sizes > 0 must be present, typed and large enough."""
     import torch
-    for n, dt in _STATE_DTYPE.items():
+    for n, dt in _state_dtypes(cfg).items():
         nbytes = sizes[n]
         if nbytes == 0:
             continue
@@ -170,14 +177,8 @@ class QState:
         def buf(nbytes, dtype, item):
             return torch.zeros(max(nbytes // item, 1 if nbytes else 0), dtype=dtype, device=dev)
 
-        return {
-            "codes": buf(z["codes"], torch.uint8, 1),
-            "scales": buf(z["scales"], torch.float32, 4),
-            "hp": buf(z["hp"], torch.uint8, 1),
-            "lrb_W": buf(z["lrb_W"], torch.float32, 4),
-            "lrb_U": buf(z["lrb_U"], torch.float32, 4),
-            "lrb_n": buf(z["lrb_n"], torch.int32, 4),
-        }
+        dts = {n: getattr(torch, d) for n, d in _state_dtypes(self.cfg).items()}
+        return {n: buf(z[n], dts[n], torch.empty((), dtype=dts[n]).element_size()) for n in dts}
 
     @staticmethod
     def _tensors(st: dict) -> _lib.Tensors:

@@ -3,8 +3,9 @@
 Translation units:
   qstate_step_<family>.hip   one per step-kernel family (dense, mixed, keymap,
                              lrb), compiled once per (qbits, rounding) pair with
-                             -DQS_QB=<8|4> -DQS_RND=<0|1|2>: 24 objects that
-                             compile in parallel
+                             -DQS_QB=<8|4> -DQS_RND=<0|1|2> (lrb once per kind
+                             too, -DQS_DELTA=<0|1>): 30 objects that compile
+                             in parallel
   qstate_misc.hip            quantize / dequantize / fill kernels, dispatch
   qstate_host.cpp            the C ABI: validation, planning, launches
 Objects go to build/qstate/ and link into
@@ -54,6 +55,11 @@ def units():
     for fam in FAMILIES:
         src = os.path.join(CSRC, f"qstate_step_{fam}.hip")
         for qb, rnd in QR:
+            if fam == "lrb":   # the longest units: one per kind as well
+                for delta in (0, 1):
+                    obj = os.path.join(OBJ, f"qstate_step_{fam}_q{qb}_{RND_NAME[rnd]}_d{delta}.o")
+                    out.append((src, [f"-DQS_QB={qb}", f"-DQS_RND={rnd}", f"-DQS_DELTA={delta}"], obj))
+                continue
             obj = os.path.join(OBJ, f"qstate_step_{fam}_q{qb}_{RND_NAME[rnd]}.o")
             out.append((src, [f"-DQS_QB={qb}", f"-DQS_RND={rnd}"], obj))
     for name in ("qstate_misc.hip", "qstate_host.cpp"):
@@ -114,8 +120,8 @@ def build(force: bool = True, verbose: bool = False, jobs: int = 0) -> str:
     os.makedirs(OBJ, exist_ok=True)
     todo = [u for u in units() if force or _stale(u[0], u[2])]
     jobs = jobs or min(16, os.cpu_count() or 1)
-    # the step units take longest: start them first
-    todo.sort(key=lambda u: 0 if "qstate_step_" in u[0] else 1)
+    # the longest units first: low-rank bypass, then the other step kernels
+    todo.sort(key=lambda u: 0 if "qstate_step_lrb" in u[0] else (1 if "qstate_step_" in u[0] else 2))
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
         list(ex.map(lambda u: _compile(u, verbose), todo))
     tmp = LIB + ".tmp"

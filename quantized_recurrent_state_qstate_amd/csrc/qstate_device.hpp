@@ -395,6 +395,31 @@ __device__ __forceinline__ void row_scale(float m, float& scale, float& inv, flo
   }
 }
 
+// Row scale stored as bf16 (the bf16 layout of the low-rank bypass): the
+// smallest bf16 value s with Q s >= m, and codes are taken against it: inv =
+// the largest fp32 with inv s <= 1, so |value * inv| <= m / s <= Q.  q =
+// m / Q (nearest) rounded up to bf16 on its bit pattern is that s unless q
+// fell below m / Q while being a bf16 value itself; then the next bf16 up
+// is (a bf16 value times Q is exact in fp32, so the test is exact).  A row
+// with m = 0, or whose s overflows, or whose 2^SRB / s is not finite, is
+// stored as zero.  `mq` is m / Q, correctly rounded.
+template <int QB, int SRB>
+__device__ __forceinline__ void row_scale_bf16(float m, float mq, float& scale, float& inv, float& invb) {
+  constexpr float Q = (QB == 8) ? 127.0f : 7.0f;
+  uint32_t b = (__float_as_uint(mq) + 0xFFFFu) & 0xFFFF0000u;
+  if (__uint_as_float(b) * Q < m) b += 0x10000u;
+  const float sb = __uint_as_float(b);
+  const float i = 1.0f / sb;
+  const bool ok = __builtin_isfinite(sb) && __builtin_isfinite(i * (float)(1u << SRB));
+  const float iz = inv_toward_zero(1.0f, sb, i);
+  scale = ok ? sb : 0.0f;
+  inv = ok ? iz : 0.0f;
+  invb = ok ? iz * (float)(1u << SRB) : 0.0f;
+}
+
+// x rounded to bf16 (nearest even) and widened back.
+__device__ __forceinline__ float round_bf16(float x) { return bf16_bits_to_f32(f32_to_bf16_bits(x)); }
+
 // floor(x + 1/2) as an integer, one v_cvt_rpi_i32_f32 (exact for |x| < 2^23,
 // where x + 1/2 is representable).
 __device__ __forceinline__ int32_t cvt_rpi(float x) {

@@ -139,6 +139,16 @@ qs_status validate(const qstate_config* c) {
     if (c->lrb_period < 1) return fail(QS_EINVAL, "lrb_period %d", c->lrb_period);
     if (!std::isfinite(c->lrb_theta) || c->lrb_theta <= 0.0f) return fail(QS_EINVAL, "lrb_theta %g", c->lrb_theta);
   }
+  if ((c->scale_dtype != QS_FP32 && c->scale_dtype != QS_BF16) || (c->lrb_dtype != QS_FP32 && c->lrb_dtype != QS_BF16))
+    return fail(c->scale_dtype == QS_FP16 || c->lrb_dtype == QS_FP16 ? QS_EUNSUPPORTED : QS_EINVAL,
+                "scale_dtype %d, lrb_dtype %d (supported: fp32, bf16)", c->scale_dtype, c->lrb_dtype);
+  if (c->scale_dtype == QS_BF16 || c->lrb_dtype == QS_BF16) {
+    // the bf16 layout is the one of int4 states with the low-rank bypass:
+    // bf16 scales and bf16 buffer factors together, rank bound 8
+    if (c->lrb_rank == 0 || c->scale_dtype != c->lrb_dtype)
+      return fail(QS_EUNSUPPORTED, "bf16 scales and bf16 buffer factors come together, with the low-rank bypass");
+    if (c->lrb_rank > 8) return fail(QS_EUNSUPPORTED, "bf16 buffer factors: lrb_rank %d (max 8)", c->lrb_rank);
+  }
   return QS_OK;
 }
 
@@ -173,9 +183,10 @@ qs_status make_plan(const qstate_config* c, Plan* p) {
   const uint64_t B = (uint64_t)c->B, BH = B * (uint64_t)H, r = (uint64_t)c->lrb_rank;
   p->sizes.codes = B * coff;
   p->sizes.hp = B * hoff;
-  p->sizes.scales = BH * (uint64_t)dv * 4u;
-  p->sizes.lrb_W = BH * (uint64_t)dv * r * 4u;
-  p->sizes.lrb_U = BH * (uint64_t)dk * r * 4u;
+  const uint64_t sb = c->scale_dtype == QS_BF16 ? 2u : 4u, lb = c->lrb_dtype == QS_BF16 ? 2u : 4u;
+  p->sizes.scales = BH * (uint64_t)dv * sb;
+  p->sizes.lrb_W = BH * (uint64_t)dv * r * lb;
+  p->sizes.lrb_U = BH * (uint64_t)dk * r * lb;
   p->sizes.lrb_n = r > 0 ? BH * 4u : 0u;
 
   dense_shape(c->kind, dk, dv, &p->dense_lpr, &p->dense_rpl, &p->dense_threads, &p->row_chunks);
@@ -280,10 +291,10 @@ qs::Args base_args(const qstate_handle* h, const qstate_tensors* st) {
   qs::Args a{};
   const qstate_config& c = h->cfg;
   a.codes = reinterpret_cast<uint8_t*>(st->codes);
-  a.scales = st->scales;
+  a.scales = reinterpret_cast<float*>(st->scales);   // bf16 elements when scale_bf16
   a.hp = reinterpret_cast<uint8_t*>(st->hp);
-  a.W = st->lrb_W;
-  a.U = st->lrb_U;
+  a.W = reinterpret_cast<float*>(st->lrb_W);          // bf16 elements when lrb_bf16
+  a.U = reinterpret_cast<float*>(st->lrb_U);
   a.n = st->lrb_n;
   a.B = c.B;
   a.H = c.H;
@@ -316,6 +327,7 @@ qs::Args base_args(const qstate_handle* h, const qstate_tensors* st) {
   a.seed_lo = (uint32_t)c.seed;
   a.seed_hi = (uint32_t)(c.seed >> 32);
   a.mixed_lds = h->plan.lds;
+  a.bf16_layout = c.lrb_dtype == QS_BF16 ? 1 : 0;
   a.nslots = c.B;
   return a;
 }

@@ -67,6 +67,7 @@ struct Args {
   uint32_t seed_lo, seed_hi;
   uint32_t step_lo, step_hi;
   uint32_t mixed_lds;  // mixed kernel: dynamic LDS bytes
+  int32_t bf16_layout; // scales and low-rank buffer factors stored as bf16 (LRB only)
   // batched entry point: batch element b reads its inputs and writes its
   // outputs at b, and its state at slot[b] of a pool of nslots states, with
   // its own step; null = the plain step (slot b, step above)
@@ -87,8 +88,8 @@ struct HeadIx {
 enum StepFamily : int { kFamDense = 0, kFamMixed = 1, kFamLrb = 2, kFamKeymap = 3 };
 
 // Launchers.  Step kernels, one launcher per family, instantiated per
-// (qbits, rounding) in qstate_step_<family>.hip; launch_step (qstate_misc.hip)
-// dispatches to them.  Return hipSuccess or the launch error.  `rnd`: 0
+// (qbits, rounding) in qstate_step_<family>.hip (the low-rank-bypass one per
+// kind too); launch_step (qstate_misc.hip) dispatches to them.  Return hipSuccess or the launch error.  `rnd`: 0
 // nearest, 1 stochastic 16-bit, 2 stochastic 8-bit.
 template <int QB, int RND>
 hipError_t launch_dense(int delta, const Args& a, hipStream_t s);
@@ -96,8 +97,8 @@ template <int QB, int RND>
 hipError_t launch_mixed(int delta, const Args& a, hipStream_t s);
 template <int QB, int RND>
 hipError_t launch_keymap(int delta, const Args& a, hipStream_t s);
-template <int QB, int RND>
-hipError_t launch_lrb(int delta, const Args& a, hipStream_t s);
+template <int QB, int RND, int DELTA>
+hipError_t launch_lrb(const Args& a, hipStream_t s);
 hipError_t launch_step(int family, int qbits, int rnd, int delta, const Args& a,
                        hipStream_t s);
 hipError_t launch_quantize(const Args& a, hipStream_t s);

@@ -69,12 +69,17 @@ __device__ __forceinline__ float pick(const float (&p)[R], int j) {
 // Register budget: 5 waves per SIMD for int4 codes with nearest rounding at
 // rank bound 8, where it needs no spills (except with the delta rule and a
 // per-key decay together); otherwise the compiler's choice.
+//
+// BF = 1: the bf16 layout (row scales and the buffer factors W, U stored as
+// bf16; instantiated at rank bound 8).  A new basis column is rounded to
+// bf16 when made and used rounded; U is updated in fp32 and rounded before
+// the merge test; the row scale is the smallest bf16 s with Q s >= max.
 template <int QB, int RND, int RANK, int DELTA, int DKEY>
 constexpr int lrb_min_waves() {
   return (QB == 4 && RND == 0 && RANK == 8 && !(DELTA && DKEY)) ? 5 : 1;
 }
 
-template <int QB, int RND, int DELTA, int EPL, int RANK, int BDR, int DKEY>
+template <int QB, int RND, int DELTA, int EPL, int RANK, int BDR, int DKEY, int BF>
 __global__ __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(lrb_min_waves<QB, RND, RANK, DELTA, DKEY>(), 8))) void k_step_lrb(const Args a) {
   constexpr int DK = EPL * 8;
@@ -107,8 +112,16 @@ __attribute__((amdgpu_waves_per_eu(lrb_min_waves<QB, RND, RANK, DELTA, DKEY>(), 
   __shared__ float red[RANK + 4];
   __shared__ uint8_t smalll[DK], mflagl[DK];
 
-  float* Wg = a.W + bhs * (uint64_t)dv * (uint64_t)r;
-  float* Ug = a.U + bhs * (uint64_t)DK * (uint64_t)r;
+  // the buffer factors and the row scales, fp32 or bf16 (BF)
+  const uint64_t woff = bhs * (uint64_t)dv * (uint64_t)r, uoff = bhs * (uint64_t)DK * (uint64_t)r;
+  auto ld_buf = [&](const float* base, uint64_t i) -> float {
+    if constexpr (BF) return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(base)[i]);
+    else return base[i];
+  };
+  auto st_buf = [&](float* base, uint64_t i, float x) {
+    if constexpr (BF) reinterpret_cast<uint16_t*>(base)[i] = (uint16_t)(__float_as_uint(x) >> 16);   // exact
+    else base[i] = x;
+  };
   const float beta = a.beta ? a.beta[bh] : 1.0f;
   int n = a.n[bhs];
 
@@ -133,13 +146,15 @@ __attribute__((amdgpu_waves_per_eu(lrb_min_waves<QB, RND, RANK, DELTA, DKEY>(), 
   float Wr[RANK], Ur[RANK];
 #pragma unroll
   for (int j = 0; j < RANK; ++j) {
-    Wr[j] = j < r ? Wg[tv * r + j] : 0.0f;   // j < r: uniform
-    Ur[j] = j < r ? Ug[tk * r + j] : 0.0f;
+    Wr[j] = j < r ? ld_buf(a.W, woff + (uint64_t)(tv * r + j)) : 0.0f;   // j < r: uniform
+    Ur[j] = j < r ? ld_buf(a.U, uoff + (uint64_t)(tk * r + j)) : 0.0f;
   }
   const uint64_t trow = bh * (uint64_t)dv + (uint64_t)tv;
   const uint64_t tkey = bh * DK + (uint64_t)tk;
   const InRaw vraw = in_raw_load(a.v, a.in_bf16, trow);
-  const float so_raw = ld_nt(a.scales + bhs * (uint64_t)dv + (uint64_t)tv);
+  float so_raw;
+  if constexpr (BF) so_raw = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(a.scales)[bhs * (uint64_t)dv + tv]);
+  else so_raw = ld_nt(a.scales + bhs * (uint64_t)dv + (uint64_t)tv);
   const InRaw kraw = in_raw_load(a.k, a.in_bf16, tkey);
   const InRaw qraw = in_raw_load(a.q, a.in_bf16, tkey);
   const float dd_raw = DKEY ? a.decay[tkey] : a.decay[bh];
@@ -241,6 +256,7 @@ __attribute__((amdgpu_waves_per_eu(lrb_min_waves<QB, RND, RANK, DELTA, DKEY>(), 
     const float nu = sqrtf(block_sum(uv * uv, red));
     if (ny > ldexpf(nu, -10)) {
       wnew = tid < dv ? y / ny : 0.0f;
+      if constexpr (BF) wnew = round_bf16(wnew);   // stored and used in the buffer's format
 #pragma unroll
       for (int j = 0; j < RANK; ++j) Wr[j] = (j == n) ? wnew : Wr[j];
       n += 1;
@@ -278,6 +294,10 @@ __attribute__((amdgpu_waves_per_eu(lrb_min_waves<QB, RND, RANK, DELTA, DKEY>(), 
 #pragma unroll
       for (int j = 0; j < RANK; ++j) Ur[j] = fmaf(kk, c[j], Ur[j]);
     }
+  }
+  if constexpr (BF) {   // the updated buffer in its storage format, before the merge test
+#pragma unroll
+    for (int j = 0; j < RANK; ++j) Ur[j] = round_bf16(Ur[j]);
   }
   // W transposed into LDS for the merge test and the rows
 #pragma unroll
@@ -335,14 +355,14 @@ __attribute__((amdgpu_waves_per_eu(lrb_min_waves<QB, RND, RANK, DELTA, DKEY>(), 
   if (tid < DK) {
 #pragma unroll
     for (int j = 0; j < RANK; ++j)
-      if (j < r) Ug[tid * r + j] = Ur[j];
+      if (j < r) st_buf(a.U, uoff + (uint64_t)(tid * r + j), Ur[j]);
     kl[tid] = kk;
     ql[tid] = qq;
     dl[tid] = dd;
     smalll[tid] = sm ? 1 : 0;
     mflagl[tid] = merged ? 1 : 0;
   }
-  if (grown && tid < dv) Wg[tid * r + (n - 1)] = wnew;   // only the new column changed
+  if (grown && tid < dv) st_buf(a.W, woff + (uint64_t)(tid * r + (n - 1)), wnew);   // only the new column changed
   if (tid == 0) a.n[bhs] = n_new;
   __syncthreads();
 
@@ -391,7 +411,8 @@ __attribute__((amdgpu_waves_per_eu(lrb_min_waves<QB, RND, RANK, DELTA, DKEY>(), 
     o = red_sum<8>(o);
     const float m = red_absmax<8>(mx);
     float scale, inv, invb;
-    row_scale_fast<QB, SRB>(m, scale, inv, invb);
+    if constexpr (BF) row_scale_bf16<QB, SRB>(m, div_by_q<QB>(m), scale, inv, invb);
+    else row_scale_fast<QB, SRB>(m, scale, inv, invb);
     uint32_t rb[EPL];
     if constexpr (RND != 0) rand_bits<RND, EPL>(row * DK + (uint64_t)k0, a.seed_lo, a.seed_hi, ix.step_lo, ix.step_hi, rb);
     int32_t code[EPL];
@@ -417,36 +438,41 @@ __attribute__((amdgpu_waves_per_eu(lrb_min_waves<QB, RND, RANK, DELTA, DKEY>(), 
   __syncthreads();
   if (tid < dv) {
     st_nt(a.out + bh * (uint64_t)dv + (uint64_t)tid, ol[tid]);
-    st_nt(a.scales + bhs * (uint64_t)dv + (uint64_t)tid, sl_[tid]);
+    if constexpr (BF)
+      reinterpret_cast<uint16_t*>(a.scales)[bhs * (uint64_t)dv + tid] = (uint16_t)(__float_as_uint(sl_[tid]) >> 16);
+    else
+      st_nt(a.scales + bhs * (uint64_t)dv + (uint64_t)tid, sl_[tid]);
   }
 }
 
 // ---------------------------------------------------------------------------
 // Launchers (qstate_step_lrb.hip instantiates launch_lrb once per qbits x
-// rounding pair).
+// rounding x kind).
 // ---------------------------------------------------------------------------
 namespace {
 
-template <int QB, int RND, int DELTA, int EPL, int RANK>
+template <int QB, int RND, int DELTA, int EPL, int RANK, int BF>
 hipError_t launch_lrb_r(const Args& a, hipStream_t s) {
   const dim3 grid((uint32_t)((uint64_t)a.B * (uint64_t)a.H));
   if (a.bdr && a.bdr_bound == 0.0f) {   // the rule's zero-bound form
-    if (a.decay_key) hipLaunchKernelGGL((k_step_lrb<QB, RND, DELTA, EPL, RANK, 2, 1>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((k_step_lrb<QB, RND, DELTA, EPL, RANK, 2, 0>), grid, dim3(256), 0, s, a);
+    if (a.decay_key) hipLaunchKernelGGL((k_step_lrb<QB, RND, DELTA, EPL, RANK, 2, 1, BF>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_step_lrb<QB, RND, DELTA, EPL, RANK, 2, 0, BF>), grid, dim3(256), 0, s, a);
   } else if (a.bdr) {
-    if (a.decay_key) hipLaunchKernelGGL((k_step_lrb<QB, RND, DELTA, EPL, RANK, 1, 1>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((k_step_lrb<QB, RND, DELTA, EPL, RANK, 1, 0>), grid, dim3(256), 0, s, a);
+    if (a.decay_key) hipLaunchKernelGGL((k_step_lrb<QB, RND, DELTA, EPL, RANK, 1, 1, BF>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_step_lrb<QB, RND, DELTA, EPL, RANK, 1, 0, BF>), grid, dim3(256), 0, s, a);
   } else {
-    if (a.decay_key) hipLaunchKernelGGL((k_step_lrb<QB, RND, DELTA, EPL, RANK, 0, 1>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((k_step_lrb<QB, RND, DELTA, EPL, RANK, 0, 0>), grid, dim3(256), 0, s, a);
+    if (a.decay_key) hipLaunchKernelGGL((k_step_lrb<QB, RND, DELTA, EPL, RANK, 0, 1, BF>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_step_lrb<QB, RND, DELTA, EPL, RANK, 0, 0, BF>), grid, dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }
 
+// rank bound 8 or 16; the bf16 layout at rank bound 8 only
 template <int QB, int RND, int DELTA, int EPL>
 hipError_t launch_lrb_t(const Args& a, hipStream_t s) {
-  return a.lrb_rank <= 8 ? launch_lrb_r<QB, RND, DELTA, EPL, 8>(a, s)
-                         : launch_lrb_r<QB, RND, DELTA, EPL, 16>(a, s);
+  if (a.bf16_layout) return a.lrb_rank <= 8 ? launch_lrb_r<QB, RND, DELTA, EPL, 8, 1>(a, s) : hipErrorInvalidValue;
+  return a.lrb_rank <= 8 ? launch_lrb_r<QB, RND, DELTA, EPL, 8, 0>(a, s)
+                         : launch_lrb_r<QB, RND, DELTA, EPL, 16, 0>(a, s);
 }
 
 template <int QB, int RND, int DELTA>
@@ -461,9 +487,9 @@ hipError_t launch_lrb_dk(const Args& a, hipStream_t s) {
 
 }  // namespace
 
-template <int QB, int RND>
-hipError_t launch_lrb(int delta, const Args& a, hipStream_t s) {
-  return delta ? launch_lrb_dk<QB, RND, 1>(a, s) : launch_lrb_dk<QB, RND, 0>(a, s);
+template <int QB, int RND, int DELTA>
+hipError_t launch_lrb(const Args& a, hipStream_t s) {
+  return launch_lrb_dk<QB, RND, DELTA>(a, s);
 }
 
 }  // namespace qs

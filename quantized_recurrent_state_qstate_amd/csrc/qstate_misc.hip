@@ -43,7 +43,18 @@ __global__ __launch_bounds__(256) void k_quantize(const Args a) {
     if (!(sl[k] & kSlotProt)) m = fmaxf(m, fabsf(srow[k]));
   float scale, inv, invb;
   const int srb = a.rounding ? a.sr_bits : 0;
-  if (a.qbits == 8) {
+  if (a.bf16_layout) {   // bf16 scale rounded up, codes against it
+    const float mq = m / (a.qbits == 8 ? 127.0f : 7.0f);
+    if (a.qbits == 8) {
+      if (srb == 16) row_scale_bf16<8, 16>(m, mq, scale, inv, invb);
+      else if (srb == 8) row_scale_bf16<8, 8>(m, mq, scale, inv, invb);
+      else row_scale_bf16<8, 0>(m, mq, scale, inv, invb);
+    } else {
+      if (srb == 16) row_scale_bf16<4, 16>(m, mq, scale, inv, invb);
+      else if (srb == 8) row_scale_bf16<4, 8>(m, mq, scale, inv, invb);
+      else row_scale_bf16<4, 0>(m, mq, scale, inv, invb);
+    }
+  } else if (a.qbits == 8) {
     if (srb == 16) row_scale<8, 16>(m, scale, inv, invb);
     else if (srb == 8) row_scale<8, 8>(m, scale, inv, invb);
     else row_scale<8, 0>(m, scale, inv, invb);
@@ -115,7 +126,8 @@ __global__ __launch_bounds__(256) void k_quantize(const Args a) {
       for (uint32_t i = used; i < ((used + 15u) & ~15u); ++i) hrow[i - v * rh] = 0u;
     }
   }
-  a.scales[row] = scale;
+  if (a.bf16_layout) reinterpret_cast<uint16_t*>(a.scales)[row] = (uint16_t)(__float_as_uint(scale) >> 16);
+  else a.scales[row] = scale;
 }
 
 __global__ __launch_bounds__(256) void k_dequantize(const Args a) {
@@ -134,11 +146,15 @@ __global__ __launch_bounds__(256) void k_dequantize(const Args a) {
   const uint8_t* crow = a.codes ? code_block_m(a, b, h) + (uint64_t)v * rq : nullptr;
   const uint8_t* hrow = a.hp ? hp_block_m(a, b, h) + (uint64_t)v * hp_row_bytes(nhp, hpb) : nullptr;
   const uint16_t* sl = a.t.slots + (uint64_t)h * dk;
-  const float scale = a.scales ? a.scales[row] : 0.0f;
+  const int bf = a.bf16_layout;
+  // a scale or buffer element, fp32 or bf16
+  auto ld = [bf](const float* base, uint64_t i) -> float {
+    return bf ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(base)[i]) : base[i];
+  };
+  const float scale = a.scales ? ld(a.scales, row) : 0.0f;
   const int r = a.lrb_rank;
   const int n = r > 0 ? a.n[bh] : 0;
-  const float* W = r > 0 ? a.W + (bh * (uint64_t)a.dv + v) * (uint64_t)r : nullptr;
-  const float* U = r > 0 ? a.U + bh * (uint64_t)dk * (uint64_t)r : nullptr;
+  const uint64_t w0 = (bh * (uint64_t)a.dv + v) * (uint64_t)r, u0 = bh * (uint64_t)dk * (uint64_t)r;
   float* orow = a.S_out + row * (uint64_t)dk;
   for (int k = 0; k < dk; ++k) {
     const uint32_t s = sl[k] & 0x7FFFu;
@@ -157,7 +173,7 @@ __global__ __launch_bounds__(256) void k_dequantize(const Args a) {
     }
     if (n > 0) {
       float col = 0.0f;
-      for (int j = 0; j < n; ++j) col = fmaf(W[j], U[(uint64_t)k * r + j], col);
+      for (int j = 0; j < n; ++j) col = fmaf(ld(a.W, w0 + j), ld(a.U, u0 + (uint64_t)k * r + j), col);
       val = val + col;
     }
     orow[k] = val;
@@ -166,6 +182,10 @@ __global__ __launch_bounds__(256) void k_dequantize(const Args a) {
 
 __global__ __launch_bounds__(256) void k_zero(uint32_t* p, uint64_t nwords) {
   for (uint64_t i = (uint64_t)blockIdx.x * 256u + threadIdx.x; i < nwords; i += (uint64_t)gridDim.x * 256u)
+    p[i] = 0u;
+}
+__global__ __launch_bounds__(256) void k_zero16(uint16_t* p, uint64_t n) {
+  for (uint64_t i = (uint64_t)blockIdx.x * 256u + threadIdx.x; i < n; i += (uint64_t)gridDim.x * 256u)
     p[i] = 0u;
 }
 
@@ -179,7 +199,7 @@ hipError_t launch_step_qr(int family, int delta, const Args& a, hipStream_t s) {
     case kFamDense: return launch_dense<QB, RND>(delta, a, s);
     case kFamMixed: return launch_mixed<QB, RND>(delta, a, s);
     case kFamKeymap: return launch_keymap<QB, RND>(delta, a, s);
-    case kFamLrb: return launch_lrb<QB, RND>(delta, a, s);
+    case kFamLrb: return delta ? launch_lrb<QB, RND, 1>(a, s) : launch_lrb<QB, RND, 0>(a, s);
   }
   return hipErrorInvalidValue;
 }
@@ -211,8 +231,13 @@ hipError_t launch_quantize(const Args& a, hipStream_t s) {
   const uint64_t bh = (uint64_t)a.B * (uint64_t)a.H;
   const uint64_t nW = bh * (uint64_t)a.dv * (uint64_t)a.lrb_rank;
   const uint64_t nU = bh * (uint64_t)a.dk * (uint64_t)a.lrb_rank;
-  hipLaunchKernelGGL(k_zero, dim3(1024), dim3(256), 0, s, reinterpret_cast<uint32_t*>(a.W), nW);
-  hipLaunchKernelGGL(k_zero, dim3(1024), dim3(256), 0, s, reinterpret_cast<uint32_t*>(a.U), nU);
+  if (a.bf16_layout) {
+    hipLaunchKernelGGL(k_zero16, dim3(1024), dim3(256), 0, s, reinterpret_cast<uint16_t*>(a.W), nW);
+    hipLaunchKernelGGL(k_zero16, dim3(1024), dim3(256), 0, s, reinterpret_cast<uint16_t*>(a.U), nU);
+  } else {
+    hipLaunchKernelGGL(k_zero, dim3(1024), dim3(256), 0, s, reinterpret_cast<uint32_t*>(a.W), nW);
+    hipLaunchKernelGGL(k_zero, dim3(1024), dim3(256), 0, s, reinterpret_cast<uint32_t*>(a.U), nU);
+  }
   hipLaunchKernelGGL(k_zero, dim3(64), dim3(256), 0, s, reinterpret_cast<uint32_t*>(a.n), bh);
   return hipGetLastError();
 }

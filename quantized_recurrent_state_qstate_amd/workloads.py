@@ -30,6 +30,8 @@ Workloads (S[v][k] orientation; v = value / output channel, k = key):
   gdn_int4    Gated DeltaNet B=64 H=32 dk=dv=128 T=1024, inputs as gdn;
               int4 + low-rank bypass (rank 8, merge every 64 steps, 0.5 LSB)
               + BDR over nearest rounding, as gla_int4.
+  gla_int4_bf16  gla_int4 with bf16 row scales and bf16 buffer factors (the
+              layout behind the pages' "up to 5.3x" state-memory figure).
 """
 from __future__ import annotations
 
@@ -64,6 +66,7 @@ class Workload:
     philox_seed: int = 0
     qk_scale: float = 1.0    # GLA: q, k ~ N(0,1) * qk_scale
     decay_mu: float = 3.0    # GLA: a = sigmoid(N(decay_mu, 1))
+    aux_dtype: str = "fp32"  # row scales and low-rank buffer factors: fp32 | bf16
 
     @property
     def kind(self) -> str:
@@ -150,4 +153,7 @@ WORKLOADS = {
     "gdn_int4": Workload("gdn_int4", "gdn", B=64, H=32, dk=128, dv=128, T=1024, in_dtype="bf16",
                          qbits=4, rounding="nearest", bdr=True, lrb_rank=8, lrb_period=64,
                          lrb_theta=0.5, seed_base=1006),
+    "gla_int4_bf16": Workload("gla_int4_bf16", "gla", B=128, H=32, dk=128, dv=128, T=4096, in_dtype="bf16",
+                              qbits=4, rounding="nearest", bdr=True, lrb_rank=8, lrb_period=64,
+                              lrb_theta=0.5, decay_mu=5.0, seed_base=1004, aux_dtype="bf16"),
 }

@@ -28,7 +28,7 @@ def oracle_cfg(w: Workload, B=None, m=None) -> oracle.Cfg:
                       dk=w.dk, dv=w.dv, qbits=w.qbits, hp_dtype=w.hp_dtype, map_mode=w.map_mode,
                       map=m, rounding=ROUND_ORC[w.rounding], sr_bits=w.sr_bits, bdr=w.bdr,
                       bdr_bound=0.0, lrb_rank=w.lrb_rank, lrb_period=w.lrb_period,
-                      lrb_theta=w.lrb_theta, seed=w.philox_seed)
+                      lrb_theta=w.lrb_theta, seed=w.philox_seed, scale_dtype=w.aux_dtype, lrb_dtype=w.aux_dtype)
 
 
 def lib_cfg(w: Workload, B=None, m=None):
@@ -39,7 +39,8 @@ def lib_cfg(w: Workload, B=None, m=None):
                        dk=w.dk, dv=w.dv, qbits=w.qbits, hp_dtype=w.hp_dtype, map_mode=w.map_mode,
                        map=m, in_dtype=w.in_dtype, rounding=ROUND_LIB[w.rounding], sr_bits=w.sr_bits,
                        bdr=w.bdr, bdr_bound=0.0, lrb_rank=w.lrb_rank, lrb_period=w.lrb_period,
-                       lrb_theta=w.lrb_theta, seed=w.philox_seed)
+                       lrb_theta=w.lrb_theta, seed=w.philox_seed, scale_dtype=w.aux_dtype,
+                       lrb_dtype=w.aux_dtype)
 
 
 def inputs_f32(inp: dict) -> dict:
@@ -50,6 +51,14 @@ def inputs_f32(inp: dict) -> dict:
     return out
 
 
+def _np(t):
+    """A device tensor's bytes as numpy (bf16 as its uint16 bit patterns)."""
+    import torch
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16).copy()
+    return t.cpu().numpy().copy()
+
+
 def gpu_state_to_oracle(st: dict, hp_dtype: str) -> dict:
     """Copy the library's device buffers into the oracle's numpy layout (same bytes)."""
     codes = st["codes"].cpu().numpy().copy()
@@ -57,24 +66,29 @@ def gpu_state_to_oracle(st: dict, hp_dtype: str) -> dict:
     hp = hp_bytes.view(np.float32) if hp_dtype == "fp32" else hp_bytes.view(np.uint16)
     return {
         "codes": codes,
-        "scales": st["scales"].cpu().numpy().copy(),
+        "scales": _np(st["scales"]),
         "hp": hp.copy(),
-        "W": st["lrb_W"].cpu().numpy().copy(),
-        "U": st["lrb_U"].cpu().numpy().copy(),
+        "W": _np(st["lrb_W"]),
+        "U": _np(st["lrb_U"]),
         "n": st["lrb_n"].cpu().numpy().copy(),
     }
 
 
 def oracle_state_to_gpu(ost: dict, device) -> dict:
     import torch
+
+    def dev(a):
+        if a.dtype == np.uint16:   # bf16 bit patterns
+            return torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16).to(device)
+        return torch.from_numpy(a.copy()).to(device)
     hp = ost["hp"]
     return {
-        "codes": torch.from_numpy(ost["codes"].copy()).to(device),
-        "scales": torch.from_numpy(ost["scales"].copy()).to(device),
+        "codes": dev(ost["codes"]),
+        "scales": dev(ost["scales"]),
         "hp": torch.from_numpy(hp.view(np.uint8).copy()).to(device),
-        "lrb_W": torch.from_numpy(ost["W"].copy()).to(device),
-        "lrb_U": torch.from_numpy(ost["U"].copy()).to(device),
-        "lrb_n": torch.from_numpy(ost["n"].copy()).to(device),
+        "lrb_W": dev(ost["W"]),
+        "lrb_U": dev(ost["U"]),
+        "lrb_n": dev(ost["n"]),
     }
 
 

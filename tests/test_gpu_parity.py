@@ -64,7 +64,7 @@ def compare(ocfg, exact, ref, got, o_ref, o_got, heads=None, what=""):
     """Compare oracle state `ref` with GPU state `got` (numpy dicts) on `heads`."""
     sl = _head_slices(ocfg)
     heads = range(ocfg.B * ocfg.H) if heads is None else heads
-    ndiff = ntot = hdiff = htot = 0
+    ndiff = ntot = hdiff = htot = sdiff = bdiff = btot = 0
     o_ref = o_ref.reshape(-1, ocfg.dv).astype(np.float64)
     o_got = o_got.reshape(-1, ocfg.dv).astype(np.float64)
     for bh in heads:
@@ -82,8 +82,16 @@ def compare(ocfg, exact, ref, got, o_ref, o_got, heads=None, what=""):
             ndiff += int((d > 0).sum())
             ntot += d.size
             if s["quant"]:
-                np.testing.assert_allclose(got["scales"][s["scales"]], ref["scales"][s["scales"]], rtol=1e-5,
-                                           atol=0, err_msg=f"{what} head {bh} scales")
+                sr, sg = ref["scales"][s["scales"]], got["scales"][s["scales"]]
+                if sr.dtype == np.uint16:
+                    # bf16 scales: equal, but for a row maximum whose fp32
+                    # noise crossed a bf16 rounding boundary (one unit apart)
+                    differ = sr != sg
+                    sdiff += int(differ.sum())
+                    a_, b_ = oracle.widen(sr[differ]), oracle.widen(sg[differ])
+                    assert (np.abs(a_ - b_) <= np.ldexp(np.maximum(a_, b_), -7)).all(), f"{what} {bh} scales"
+                else:
+                    np.testing.assert_allclose(sg, sr, rtol=1e-5, atol=0, err_msg=f"{what} head {bh} scales")
             hr, hg = ref["hp"][s["hp"]], got["hp"][s["hp"]]
             if hr.size:
                 if ocfg.hp_dtype == "fp32":
@@ -121,15 +129,29 @@ def compare(ocfg, exact, ref, got, o_ref, o_got, heads=None, what=""):
                                                f"{fr[bad][:4]} vs {fg[bad][:4]}")
         if ocfg.lrb_rank:
             assert got["n"][bh] == ref["n"][bh], f"{what} head {bh}: buffer rank"
-            np.testing.assert_allclose(got["W"][s["W"]], ref["W"][s["W"]], rtol=0, atol=2e-5)
-            np.testing.assert_allclose(got["U"][s["U"]], ref["U"][s["U"]], rtol=2e-4,
-                                       atol=2e-5 * (np.abs(ref["U"][s["U"]]).max(initial=0) + 1e-3))
+            Wr, Wg = oracle.widen(ref["W"][s["W"]]), oracle.widen(got["W"][s["W"]])
+            Ur, Ug = oracle.widen(ref["U"][s["U"]]), oracle.widen(got["U"][s["U"]])
+            if ref["W"].dtype == np.uint16:
+                # bf16 factors: fp32 noise of the sums before rounding can move
+                # an entry by one bf16 unit; counted over the step
+                for name, a_, b_ in (("W", Wr, Wg), ("U", Ur, Ug)):
+                    differ = a_ != b_
+                    bdiff += int(differ.sum())
+                    btot += a_.size
+                    lim = np.ldexp(np.maximum(np.abs(a_), np.abs(b_)), -7) + 2e-5 * (np.abs(a_).max(initial=0) + 1e-3)
+                    assert (np.abs(a_ - b_) <= lim).all(), f"{what} head {bh}: buffer {name}"
+            else:
+                np.testing.assert_allclose(Wg, Wr, rtol=0, atol=2e-5)
+                np.testing.assert_allclose(Ug, Ur, rtol=2e-4, atol=2e-5 * (np.abs(Ur).max(initial=0) + 1e-3))
         nr = np.linalg.norm(o_ref[bh])
         assert np.linalg.norm(o_got[bh] - o_ref[bh]) <= 1e-3 * nr + 1e-30, f"{what} head {bh}: output"
     if not exact and ntot:
         assert ndiff <= max(1e-4 * ntot, 2), f"{what}: {ndiff} of {ntot} codes differ by 1 LSB"
     if not exact and htot:
         assert hdiff <= max(1e-4 * htot, 2), f"{what}: {hdiff} of {htot} 16-bit protected values differ"
+    assert sdiff <= 1, f"{what}: {sdiff} bf16 scales differ"
+    if btot:
+        assert bdiff <= max(1e-3 * btot, 2), f"{what}: {bdiff} of {btot} bf16 buffer entries differ"
     return ndiff, ntot
 
 
@@ -165,6 +187,7 @@ SMALL = {
     "gla_int4": dict(B=2, T=6),
     "gdn_large": dict(B=2, T=6),
     "gdn_int4": dict(B=2, T=6),
+    "gla_int4_bf16": dict(B=2, T=6),
 }
 
 
@@ -176,7 +199,7 @@ def test_step_teacher_forced_small(name):
     run_teacher_forced(w, p["B"], p["T"], warm=4 if name != "gla_small" else 0)
 
 
-@pytest.mark.parametrize("name", ["gla_int4", "gdn_int4"])
+@pytest.mark.parametrize("name", ["gla_int4", "gdn_int4", "gla_int4_bf16"])
 def test_lrb_merge_steps(name):
     """Low-rank bypass across a merge (period 64: step 63)."""
     w = WORKLOADS[name]
@@ -368,10 +391,10 @@ def test_dequantize_with_buffer():
 
 
 # Full size, in the benchmark's launch configuration, sampled heads.
-FULL_STEPS = {"gdn": 2, "mamba2": 2, "gla_int4": 2, "gdn_large": 1, "gdn_int4": 2}
+FULL_STEPS = {"gdn": 2, "mamba2": 2, "gla_int4": 2, "gdn_large": 1, "gdn_int4": 2, "gla_int4_bf16": 2}
 
 
-@pytest.mark.parametrize("name", ["gdn", "mamba2", "gla_int4", "gdn_large", "gdn_int4"])
+@pytest.mark.parametrize("name", ["gdn", "mamba2", "gla_int4", "gdn_large", "gdn_int4", "gla_int4_bf16"])
 def test_full_size_sampled_heads(name):
     w = WORKLOADS[name]
     r = np.random.default_rng(5)
@@ -458,6 +481,18 @@ EDGE = {
                                        map_mode="head", hp_dtype="fp32", in_dtype="fp32"),
     "headmap_fp32_dk256_delta_8lanes": dict(kind="delta", decay_mode="head", dk=256, dv=16, H=2, B=2, qbits=8,
                                             map_mode="head", hp_dtype="fp32"),
+    # the bf16 layout: bf16 row scales (rounded up) and bf16 buffer factors
+    "lrb_bf16_gla_int4": dict(kind="additive", decay_mode="key", dk=128, dv=96, H=2, B=2, qbits=4,
+                              rounding="nearest", bdr=True, lrb_rank=8, lrb_period=4,
+                              scale_dtype="bf16", lrb_dtype="bf16"),
+    "lrb_bf16_delta_int4_dk64": dict(kind="delta", decay_mode="head", dk=64, dv=40, H=2, B=2, qbits=4,
+                                     rounding="nearest", bdr=True, lrb_rank=6, lrb_period=3,
+                                     scale_dtype="bf16", lrb_dtype="bf16"),
+    "lrb_bf16_int8_sr_dk256": dict(kind="additive", decay_mode="key", dk=256, dv=24, H=2, B=2, qbits=8,
+                                   lrb_rank=8, lrb_period=5, scale_dtype="bf16", lrb_dtype="bf16"),
+    "lrb_bf16_kda_int4_sr8_bdr": dict(kind="delta", decay_mode="key", dk=128, dv=64, H=2, B=2, qbits=4,
+                                      sr_bits=8, bdr=True, lrb_rank=4, lrb_period=2,
+                                      scale_dtype="bf16", lrb_dtype="bf16"),
 }
 
 

@@ -183,3 +183,21 @@ def test_binding_argument_checks_raise_before_the_abi():
         check_state(cfg, sizes, dict(st, codes=st["codes"][:10]), cpu)
     with pytest.raises(ValueError, match="scales.*dtype"):
         check_state(cfg, sizes, dict(st, scales=st["scales"].half()), cpu)
+
+
+def test_bf16_layout_supported_set():
+    """bf16 row scales and bf16 buffer factors come together, with the
+    low-rank bypass at rank <= 8; sizes halve for those buffers."""
+    base = dict(B=2, H=3, dk=128, dv=128, qbits=4, rounding="nearest", bdr=True, lrb_rank=8)
+    z = plan(StateConfig(**base, scale_dtype="bf16", lrb_dtype="bf16"))
+    z32 = plan(StateConfig(**base))
+    assert (z["scales"], z["lrb_W"], z["lrb_U"]) == (z32["scales"] // 2, z32["lrb_W"] // 2, z32["lrb_U"] // 2)
+    assert z["codes"] == z32["codes"]
+    bad = [dict(base, scale_dtype="bf16"), dict(base, lrb_dtype="bf16"),
+           dict(base, lrb_rank=0, scale_dtype="bf16", lrb_dtype="bf16"),
+           dict(base, lrb_rank=12, scale_dtype="bf16", lrb_dtype="bf16"),
+           dict(base, scale_dtype="fp16", lrb_dtype="fp16")]
+    for kw in bad:
+        with pytest.raises(_lib.QStateError) as e:
+            plan(StateConfig(**kw))
+        assert e.value.status == _lib.QS_EUNSUPPORTED, kw
