@@ -32,6 +32,7 @@ compared in a float64 simulation of nearest and stochastic rounding, since
 the library stores value-axis scales only.
 
     python -m quantized_recurrent_state_qstate_amd.error_study [--T 256] [--json out.json]
+    python -m quantized_recurrent_state_qstate_amd.error_study --horizons   # error after 64/256/1024 steps
 """
 from __future__ import annotations
 
@@ -88,7 +89,7 @@ def _exact_step(S, q, k, v, a):
     return S, (S * q[..., None, :]).sum(-1)
 
 
-def run_library(cfgkw, B, H, dk, dv, T, rp, seed, warm):
+def run_library(cfgkw, B, H, dk, dv, T, rp, seed, warm, checkpoints=()):
     import torch
 
     from . import QState, StateConfig
@@ -108,6 +109,13 @@ def run_library(cfgkw, B, H, dk, dv, T, rp, seed, warm):
     ret, rev, coh = [], [], []
     E_prev = None
     o = o_ref = None
+    at = {}
+
+    def errors(S_q, o, S_ref, o_ref):
+        nr = S_ref.norm(dim=(-1, -2)).clamp_min(1e-300)
+        return dict(state_err=((S_q - S_ref).norm(dim=(-1, -2)) / nr).mean().item(),
+                    out_err=((o.to(f64) - o_ref).norm(dim=-1) / o_ref.norm(dim=-1).clamp_min(1e-300)).mean().item())
+
     for t in range(T):
         q, k, v, a = (x.to(dev) for x in _inputs(B, H, dk, dv, t, rp, seed))
         o = qs.step(st, q, k, v, a, step=t + 1)
@@ -129,12 +137,14 @@ def run_library(cfgkw, B, H, dk, dv, T, rp, seed, warm):
                 coh.append((num / den).mean().item())
             E_prev = E
         S_prev = S_q
-    nr = S_ref.norm(dim=(-1, -2)).clamp_min(1e-300)
-    state_err = ((S_prev - S_ref).norm(dim=(-1, -2)) / nr).mean().item()
-    out_err = ((o.to(f64) - o_ref).norm(dim=-1) / o_ref.norm(dim=-1).clamp_min(1e-300)).mean().item()
+        if t + 1 in checkpoints:
+            at[t + 1] = errors(S_q, o, S_ref, o_ref)
+    e = errors(S_prev, o, S_ref, o_ref)
     qs.close()
-    return dict(state_err=state_err, out_err=out_err, retention=float(np.mean(ret)),
-                reversal=float(np.mean(rev)), coherence=float(np.mean(coh)) if coh else float("nan"))
+    return dict(state_err=e["state_err"], out_err=e["out_err"],
+                retention=float(np.mean(ret)) if ret else float("nan"),
+                reversal=float(np.mean(rev)) if rev else float("nan"),
+                coherence=float(np.mean(coh)) if coh else float("nan"), at=at)
 
 
 def run_grouping(grouping, qbits, rounding, B, H, dk, dv, T, rp, seed):
@@ -221,6 +231,45 @@ def study(B=16, H=4, dk=128, dv=128, T=256, seed=2024, warm=16, regimes=None, gr
                            seed=seed, warm=warm), regimes=out)
 
 
+HORIZON_CONFIGS = [
+    ("int8 SR16", dict(qbits=8, rounding="stochastic", sr_bits=16)),
+    ("int4 SR16", dict(qbits=4, rounding="stochastic", sr_bits=16)),
+    ("int4 nearest", dict(qbits=4, rounding="nearest")),
+    ("int4 nearest+BDR+LRB r8", dict(qbits=4, rounding="nearest", bdr=True, lrb_rank=8, lrb_period=64,
+                                      lrb_theta=0.5)),
+]
+
+
+def horizon_study(B=16, H=4, dk=128, dv=128, horizons=(64, 256, 1024), seed=2024, regime=None):
+    """Error after 64, 256 and 1024 decode steps from the same start (one run
+    per configuration, read at each horizon): how a low-precision state fares
+    on short decode horizons ("lower effective precision on shorter decode
+    horizons", abstract of "Quantizing Recurrent Language Models Is Easier
+    Than You Think").  Default regime: i.i.d. updates under very slow decay
+    from an empty state, where the state keeps growing and each step's
+    rounding error adds to the last (under the structured regime the error
+    of a large stored context saturates within the first steps instead)."""
+    rname, rp = regime or REGIMES[2]
+    T = max(horizons)
+    rows = []
+    for name, kw in HORIZON_CONFIGS:
+        r = run_library(kw, B, H, dk, dv, T, rp, seed, warm=T, checkpoints=set(horizons))
+        rows.append(dict(config=name, at={h: r["at"][h] for h in horizons}))
+    return dict(regime=rname, params=rp, horizons=list(horizons), rows=rows,
+                setup=dict(B=B, H=H, dk=dk, dv=dv, seed=seed))
+
+
+def horizon_markdown(res) -> str:
+    hs = res["horizons"]
+    out = [f"**{res['regime']}**: state error / output error after T decode steps", "",
+           "| configuration | " + " | ".join(f"T = {h}" for h in hs) + " |",
+           "|---|" + "---:|" * len(hs)]
+    for r in res["rows"]:
+        out.append(f"| {r['config']} | " + " | ".join(
+            f"{r['at'][h]['state_err']:.3f} / {r['at'][h]['out_err']:.3f}" for h in hs) + " |")
+    return "\n".join(out)
+
+
 def to_markdown(res) -> str:
     out = []
     for reg in res["regimes"]:
@@ -244,9 +293,14 @@ def main(argv=None):
     ap.add_argument("--B", type=int, default=16)
     ap.add_argument("--T", type=int, default=256)
     ap.add_argument("--json", default=None)
+    ap.add_argument("--horizons", action="store_true", help="the decode-horizon table instead")
     args = ap.parse_args(argv)
-    res = study(B=args.B, T=args.T)
-    print(to_markdown(res))
+    if args.horizons:
+        res = [horizon_study(B=args.B, regime=reg) for reg in (REGIMES[2], REGIMES[-1])]
+        print("\n\n".join(horizon_markdown(r) for r in res))
+    else:
+        res = study(B=args.B, T=args.T)
+        print(to_markdown(res))
     if args.json:
         with open(args.json, "w") as f:
             json.dump(res, f, indent=1)

@@ -30,6 +30,9 @@ Workloads (S[v][k] orientation; v = value / output channel, k = key):
   gdn_int4    Gated DeltaNet B=64 H=32 dk=dv=128 T=1024, inputs as gdn;
               int4 + low-rank bypass (rank 8, merge every 64 steps, 0.5 LSB)
               + BDR over nearest rounding, as gla_int4.
+  gla_int4_sr GLA per-key decay, B=128 H=32 dk=dv=128 T=256, inputs as
+              gla_int4; int4 with stochastic rounding and no buffer: low
+              precision for short decode horizons.
   gla_int4_bf16  gla_int4 with bf16 row scales and bf16 buffer factors (the
               layout behind the pages' "up to 5.3x" state-memory figure).
 """
@@ -153,6 +156,8 @@ WORKLOADS = {
     "gdn_int4": Workload("gdn_int4", "gdn", B=64, H=32, dk=128, dv=128, T=1024, in_dtype="bf16",
                          qbits=4, rounding="nearest", bdr=True, lrb_rank=8, lrb_period=64,
                          lrb_theta=0.5, seed_base=1006),
+    "gla_int4_sr": Workload("gla_int4_sr", "gla", B=128, H=32, dk=128, dv=128, T=256, in_dtype="bf16",
+                            qbits=4, rounding="stochastic", sr_bits=16, decay_mu=5.0, seed_base=1007),
     "gla_int4_bf16": Workload("gla_int4_bf16", "gla", B=128, H=32, dk=128, dv=128, T=4096, in_dtype="bf16",
                               qbits=4, rounding="nearest", bdr=True, lrb_rank=8, lrb_period=64,
                               lrb_theta=0.5, decay_mu=5.0, seed_base=1004, aux_dtype="bf16"),

@@ -48,3 +48,20 @@ def test_claims_reproduce_on_structured_inputs():
     assert g8["value"] < g8["key"] < g8["head"]
     # the library against the float64 simulation of the same quantizer
     assert abs(rtn8["state_err"] - g8["value"]) <= 0.05 * g8["value"]
+
+
+def test_low_precision_fares_best_on_short_horizons():
+    """Errors accumulate with the decode horizon (i.i.d. updates, very slow
+    decay, from an empty state): int4 with stochastic rounding (no buffer)
+    after 64 steps is well below its own error after 1024, and int8's error
+    stays below int4's at every horizon."""
+    from quantized_recurrent_state_qstate_amd import error_study as es
+    print("[study] horizons", file=sys.stderr, flush=True)
+    res = es.horizon_study(B=4, H=2, horizons=(64, 256, 1024), regime=es.REGIMES[2])
+    print(es.horizon_markdown(res), file=sys.stderr, flush=True)
+    rows = {r["config"]: r["at"] for r in res["rows"]}
+    sr4, sr8 = rows["int4 SR16"], rows["int8 SR16"]
+    assert sr4[64]["state_err"] < 0.5 * sr4[1024]["state_err"]
+    assert sr4[64]["state_err"] < sr4[256]["state_err"] < sr4[1024]["state_err"]
+    for h in (64, 256, 1024):
+        assert sr8[h]["state_err"] < sr4[h]["state_err"]

@@ -188,6 +188,7 @@ SMALL = {
     "gdn_large": dict(B=2, T=6),
     "gdn_int4": dict(B=2, T=6),
     "gla_int4_bf16": dict(B=2, T=6),
+    "gla_int4_sr": dict(B=2, T=6),
 }
 
 
