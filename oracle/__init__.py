@@ -98,6 +98,7 @@ class _Cfg(ctypes.Structure):
         ("sr_bits", ctypes.c_int32), ("bdr", ctypes.c_int32), ("bdr_bound", ctypes.c_float),
         ("lrb_rank", ctypes.c_int32), ("lrb_period", ctypes.c_int32), ("lrb_theta", ctypes.c_float),
         ("seed", ctypes.c_uint64), ("scale_dtype", ctypes.c_int32), ("lrb_dtype", ctypes.c_int32),
+        ("scale_axis", ctypes.c_int32),
     ]
 
 
@@ -123,6 +124,7 @@ HP = {"fp32": 0, "bf16": 1, "fp16": 2}
 MAP = {"none": 0, "head": 1, "key": 2}
 ROUND = {"rtn": 0, "sr": 1}
 SDT = {"fp32": 0, "bf16": 1}
+AXIS = {"value": 0, "key": 1, "head": 2}
 
 
 @dataclasses.dataclass
@@ -148,6 +150,7 @@ class Cfg:
     seed: int = 0
     scale_dtype: str = "fp32"   # fp32 | bf16
     lrb_dtype: str = "fp32"     # fp32 | bf16
+    scale_axis: str = "value"   # value | key | head
 
     def c(self) -> _Cfg:
         s = _Cfg()
@@ -167,6 +170,7 @@ class Cfg:
         s.lrb_rank, s.lrb_period, s.lrb_theta = self.lrb_rank, self.lrb_period, self.lrb_theta
         s.seed = self.seed
         s.scale_dtype, s.lrb_dtype = SDT[self.scale_dtype], SDT[self.lrb_dtype]
+        s.scale_axis = AXIS[self.scale_axis]
         return s
 
 

@@ -206,6 +206,13 @@ static uint64_t hp_row_bytes(const orc_cfg* c, int nhp) {
   return round4((uint64_t)nhp * (uint64_t)hp_bytes(c));
 }
 
+/* Scale groups of a head: value axis (a row, scale_axis 0), key axis (a
+ * column, 1), the whole head (2). */
+static int n_groups(const orc_cfg* c) { return c->scale_axis == 0 ? c->dv : (c->scale_axis == 1 ? c->dk : 1); }
+static int group_of(const orc_cfg* c, int v, int k) {
+  return c->scale_axis == 0 ? v : (c->scale_axis == 1 ? k : 0);
+}
+
 static int check_cfg(const orc_cfg* c) {
   if (c->kind != 0 && c->kind != 1) return -1;
   if (c->decay_mode != 0 && c->decay_mode != 1) return -1;
@@ -219,6 +226,9 @@ static int check_cfg(const orc_cfg* c) {
   if (c->lrb_rank < 0) return -1;
   if (c->lrb_rank > 0 && (c->map_mode != 0 || c->lrb_period <= 0)) return -1;
   if ((c->scale_dtype != 0 && c->scale_dtype != 1) || (c->lrb_dtype != 0 && c->lrb_dtype != 1)) return -1;
+  /* key-axis and per-head groups: every channel quantized, no buffer */
+  if (c->scale_axis < 0 || c->scale_axis > 2) return -1;
+  if (c->scale_axis != 0 && (c->map_mode != 0 || c->lrb_rank != 0)) return -1;
   return 0;
 }
 
@@ -256,7 +266,7 @@ int orc_layout(const orc_cfg* c, orc_sizes* s, uint64_t* code_off, uint64_t* hp_
   s->hp_bstride = hoff;
   s->codes = (uint64_t)c->B * coff;
   s->hp = (uint64_t)c->B * hoff;
-  s->scales = BH * (uint64_t)c->dv * (c->scale_dtype ? 2u : 4u);
+  s->scales = BH * (uint64_t)n_groups(c) * (c->scale_dtype ? 2u : 4u);
   s->W = BH * (uint64_t)c->dv * (uint64_t)c->lrb_rank * (c->lrb_dtype ? 2u : 4u);
   s->U = BH * (uint64_t)c->dk * (uint64_t)c->lrb_rank * (c->lrb_dtype ? 2u : 4u);
   s->n = c->lrb_rank > 0 ? BH * 4u : 0u;
@@ -361,91 +371,128 @@ static float dequant_elem(const orc_cfg* c, const head_addr* a, float scale, int
 }
 
 /* ------------------------------------------------------------------------ */
-/* Requantization of one row (value-axis scale grouping, LoReS abstract):    */
-/* the row's scale is its largest magnitude over quantized channels divided  */
-/* by Q (127 for 8 bits, 7 for 4 bits; symmetric grid, no zero point).       */
-/* Each element is x = value * (Q / max), rounded to nearest even or         */
+/* Requantization (LoReS abstract: value-axis scale grouping; the groups of  */
+/* the other axes are the ablations the abstract contrasts it with).  A      */
+/* group's scale is its largest magnitude over quantized channels divided by */
+/* Q (127 for 8 bits, 7 for 4 bits; symmetric grid, no zero point).  Each    */
+/* element is x = value * (Q / max), rounded to nearest even or              */
 /* stochastically (LoReS abstract); with BDR (abstract of the page on        */
 /* preserving updates: reversed elements are rounded toward their update) an */
 /* element whose new level lies on the wrong side of its previous value by   */
 /* more than the bound takes the other neighbour of x instead.  Codes are    */
 /* clamped to [-Q, Q].  Protected channels store the nearest 16-bit (or the  */
 /* fp32) value.  `old` is the value before the step (BDR only; may be NULL). */
-/* Returns the row's new scale.                                             */
 /* ------------------------------------------------------------------------ */
+typedef struct {
+  float scale, inv, invb;
+} group_scale;
+
+/* Scale and rounding inverse of a group whose largest magnitude is m. */
+static group_scale scale_of(const orc_cfg* c, float m) {
+  const float Q = (c->qbits == 8) ? 127.0f : 7.0f;
+  /* A group whose nearest inverse Q / max (times 2^sr_bits under stochastic
+   * rounding) overflows, i.e. max below about Q*2^16/FLT_MAX, is stored as
+   * zero.  The inverse used for rounding is Q / max rounded toward zero: the
+   * largest float inv with inv * max <= Q exactly, so |value * inv| <= Q for
+   * every element of the group and no code ever reaches the clamp. */
+  group_scale g = {0.0f, 0.0f, 0.0f};
+  if (m > 0.0f && c->scale_dtype == 0) {
+    g.scale = m / Q;
+    g.inv = Q / m;
+    g.invb = (c->rounding == 1) ? ldexpf(g.inv, c->sr_bits) : g.inv;
+    if (!isfinite(g.inv) || !isfinite(g.invb)) {
+      g.scale = g.inv = g.invb = 0.0f;
+    } else {
+      g.inv = orc_inv_rtz(Q, m);
+      g.invb = (c->rounding == 1) ? ldexpf(g.inv, c->sr_bits) : g.inv;
+    }
+  } else if (m > 0.0f) {
+    /* bf16 scales: the stored scale s is the smallest bf16 value with
+     * Q s >= m (Q s is exact in double), and codes are taken against s:
+     * inv is the largest float with inv s <= 1, so |value * inv| <= m / s
+     * <= Q.  A group whose s overflows, or whose inv (times 2^sr_bits) is
+     * not finite, is stored as zero. */
+    g.scale = orc_scale_bf16_up(m, Q);
+    if (isfinite(g.scale)) {
+      g.inv = orc_inv_rtz(1.0f, g.scale);
+      g.invb = (c->rounding == 1) ? ldexpf(g.inv, c->sr_bits) : g.inv;
+    }
+    if (!isfinite(g.scale) || !isfinite(g.inv) || !isfinite(g.invb)) g.scale = g.inv = g.invb = 0.0f;
+  }
+  return g;
+}
+
+/* The code of one quantized element (stored slot `slot` of row v). */
+static int32_t round_code(const orc_cfg* c, int64_t bh, int v, int slot, float sp, const float* old,
+                          group_scale g, uint64_t step) {
+  const float Q = (c->qbits == 8) ? 127.0f : 7.0f;
+  float x = sp * g.inv;
+  float code;
+  if (c->rounding == 0) {
+    code = rintf(x);
+  } else {
+    /* the element's index in the stored code rows: its slot, which is the
+     * key channel itself when the whole head is quantized */
+    uint64_t e = ((uint64_t)bh * (uint64_t)c->dv + (uint64_t)v) * (uint64_t)c->dk + (uint64_t)slot;
+    code = orc_sr_round(sp * g.invb, orc_random_bits(c, e, step), c->sr_bits);
+  }
+  if (c->bdr && old) {
+    float xo = *old * g.inv;
+    float d = sp - *old;
+    if (d > 0.0f && code < xo - c->bdr_bound) code = ceilf(x);
+    else if (d < 0.0f && code > xo + c->bdr_bound) code = floorf(x);
+  }
+  if (code > Q) code = Q;
+  if (code < -Q) code = -Q;
+  return (int32_t)code;
+}
+
+/* Value-axis groups: one row.  Returns the row's new scale. */
 static float requantize_row(const orc_cfg* c, const head_addr* a, int64_t bh, int v,
                             const float* sp, const float* old, uint64_t step) {
   const int dk = c->dk;
-  const float Q = (c->qbits == 8) ? 127.0f : 7.0f;
   float m = 0.0f;
   for (int k = 0; k < dk; ++k)
     if (a->slot[k] >= 0) {
       float mag = fabsf(sp[k]);
       if (mag > m) m = mag;
     }
-  /* Scale and its inverse.  A row whose nearest inverse Q / max (times
-   * 2^sr_bits under stochastic rounding) overflows, i.e. max below about
-   * Q*2^16/FLT_MAX, is stored as zero.  The inverse used for rounding is
-   * Q / max rounded toward zero: the largest float inv with inv * max <= Q
-   * exactly, so |value * inv| <= Q for every element of the row and no code
-   * ever reaches the clamp below. */
-  float scale = 0.0f, inv = 0.0f, invb = 0.0f;
-  if (m > 0.0f && c->scale_dtype == 0) {
-    scale = m / Q;
-    inv = Q / m;
-    invb = (c->rounding == 1) ? ldexpf(inv, c->sr_bits) : inv;
-    if (!isfinite(inv) || !isfinite(invb)) {
-      scale = 0.0f;
-      inv = 0.0f;
-      invb = 0.0f;
-    } else {
-      inv = orc_inv_rtz(Q, m);
-      invb = (c->rounding == 1) ? ldexpf(inv, c->sr_bits) : inv;
-    }
-  } else if (m > 0.0f) {
-    /* bf16 scales: the stored scale s is the smallest bf16 value with
-     * Q s >= m (Q s is exact in double), and codes are taken against s:
-     * inv is the largest float with inv s <= 1, so |value * inv| <= m / s
-     * <= Q.  A row whose s overflows, or whose inv (times 2^sr_bits) is not
-     * finite, is stored as zero. */
-    scale = orc_scale_bf16_up(m, Q);
-    if (isfinite(scale)) {
-      inv = orc_inv_rtz(1.0f, scale);
-      invb = (c->rounding == 1) ? ldexpf(inv, c->sr_bits) : inv;
-    }
-    if (!isfinite(scale) || !isfinite(inv) || !isfinite(invb)) {
-      scale = 0.0f;
-      inv = 0.0f;
-      invb = 0.0f;
-    }
-  }
+  group_scale g = scale_of(c, m);
   for (int k = 0; k < dk; ++k) {
     int slot = a->slot[k];
     if (slot < 0) {
       put_hp(c, a, v, ~slot, sp[k]);
       continue;
     }
-    float x = sp[k] * inv;
-    float code;
-    if (c->rounding == 0) {
-      code = rintf(x);
-    } else {
-      /* the element's index in the stored code rows: its slot, which is
-       * the key channel itself when the whole head is quantized */
-      uint64_t e = ((uint64_t)bh * (uint64_t)c->dv + (uint64_t)v) * (uint64_t)dk + (uint64_t)slot;
-      code = orc_sr_round(sp[k] * invb, orc_random_bits(c, e, step), c->sr_bits);
-    }
-    if (c->bdr && old) {
-      float xo = old[k] * inv;
-      float d = sp[k] - old[k];
-      if (d > 0.0f && code < xo - c->bdr_bound) code = ceilf(x);
-      else if (d < 0.0f && code > xo + c->bdr_bound) code = floorf(x);
-    }
-    if (code > Q) code = Q;
-    if (code < -Q) code = -Q;
-    put_code(c, a, v, slot, (int32_t)code);
+    put_code(c, a, v, slot, round_code(c, bh, v, slot, sp[k], old ? &old[k] : NULL, g, step));
   }
-  return scale;
+  return g.scale;
+}
+
+/* Requantization of a whole head with key-axis or per-head groups (map NONE,
+ * every channel quantized, slot = k): the groups' maxima over sp [dv][dk],
+ * then every element against its group's scale.  scales[G] receives them. */
+static void requantize_grouped(const orc_cfg* c, const head_addr* a, int64_t bh, const float* sp,
+                               const float* old, uint64_t step, float* scales) {
+  const int dk = c->dk, dv = c->dv, G = n_groups(c);
+  float* m = (float*)calloc((size_t)G, sizeof(float));
+  group_scale* g = (group_scale*)malloc(sizeof(group_scale) * (size_t)G);
+  for (int v = 0; v < dv; ++v)
+    for (int k = 0; k < dk; ++k) {
+      float mag = fabsf(sp[v * dk + k]);
+      int gi = group_of(c, v, k);
+      if (mag > m[gi]) m[gi] = mag;
+    }
+  for (int i = 0; i < G; ++i) {
+    g[i] = scale_of(c, m[i]);
+    scales[i] = g[i].scale;
+  }
+  for (int v = 0; v < dv; ++v)
+    for (int k = 0; k < dk; ++k)
+      put_code(c, a, v, k, round_code(c, bh, v, k, sp[v * dk + k], old ? &old[v * dk + k] : NULL,
+                                      g[group_of(c, v, k)], step));
+  free(m);
+  free(g);
 }
 
 /* fp32 logical state [B,H,dv,dk] -> stored state.  No previous value, so no
@@ -462,9 +509,17 @@ int orc_quantize(const orc_cfg* c, const float* S, orc_state* st, uint64_t step)
   for (int64_t bh = 0; bh < BH; ++bh) {
     head_addr a;
     head_address(c, &L, st, bh, &a, slot);
-    for (int v = 0; v < dv; ++v) {
-      const float* row = S + ((uint64_t)bh * dv + (uint64_t)v) * (uint64_t)dk;
-      put_f(st->scales, (uint64_t)bh * dv + v, requantize_row(c, &a, bh, v, row, NULL, step), c->scale_dtype);
+    if (c->scale_axis == 0) {
+      for (int v = 0; v < dv; ++v) {
+        const float* row = S + ((uint64_t)bh * dv + (uint64_t)v) * (uint64_t)dk;
+        put_f(st->scales, (uint64_t)bh * dv + v, requantize_row(c, &a, bh, v, row, NULL, step), c->scale_dtype);
+      }
+    } else {
+      const int G = n_groups(c);
+      float* sc = (float*)malloc(sizeof(float) * (size_t)G);
+      requantize_grouped(c, &a, bh, S + (uint64_t)bh * dv * dk, NULL, step, sc);
+      for (int i = 0; i < G; ++i) put_f(st->scales, (uint64_t)bh * G + i, sc[i], c->scale_dtype);
+      free(sc);
     }
     if (r > 0) {
       for (uint64_t i = 0; i < (uint64_t)dv * r; ++i) put_f(st->W, (uint64_t)bh * dv * r + i, 0.0f, c->lrb_dtype);
@@ -504,10 +559,11 @@ int orc_dequantize(const orc_cfg* c, const orc_state* st, float* S) {
     float* U = (float*)malloc(sizeof(float) * (size_t)(dk * r + 1));
     for (int i = 0; i < dv * r; ++i) W[i] = get_f(st->W, (uint64_t)bh * dv * r + i, c->lrb_dtype);
     for (int i = 0; i < dk * r; ++i) U[i] = get_f(st->U, (uint64_t)bh * dk * r + i, c->lrb_dtype);
+    const int G = n_groups(c);
     for (int v = 0; v < dv; ++v) {
-      float scale = get_f(st->scales, (uint64_t)bh * dv + v, c->scale_dtype);
       float* row = S + ((uint64_t)bh * dv + (uint64_t)v) * (uint64_t)dk;
       for (int k = 0; k < dk; ++k) {
+        float scale = get_f(st->scales, (uint64_t)bh * G + group_of(c, v, k), c->scale_dtype);
         float x = dequant_elem(c, &a, scale, v, k);
         if (r > 0) x = x + lrb_entry(W, U, r, st->n[bh], v, k);
         row[k] = x;
@@ -670,13 +726,13 @@ static void head_step(const orc_cfg* c, const layout_t* L, orc_state* st, int64_
   float* sh = (float*)malloc(sizeof(float) * (size_t)dv * (size_t)dk);
   float* sp = (float*)malloc(sizeof(float) * (size_t)dv * (size_t)dk);
   float* u = (float*)malloc(sizeof(float) * (size_t)dv);
-  float* s_old = (float*)malloc(sizeof(float) * (size_t)dv);
+  const int G = n_groups(c);
+  float* s_old = (float*)malloc(sizeof(float) * (size_t)G);   /* group scales on entry */
 
   /* dequantize */
-  for (int v = 0; v < dv; ++v) {
-    s_old[v] = get_f(st->scales, (uint64_t)bh * dv + v, c->scale_dtype);
-    for (int k = 0; k < dk; ++k) sh[v * dk + k] = dequant_elem(c, &a, s_old[v], v, k);
-  }
+  for (int i = 0; i < G; ++i) s_old[i] = get_f(st->scales, (uint64_t)bh * G + i, c->scale_dtype);
+  for (int v = 0; v < dv; ++v)
+    for (int k = 0; k < dk; ++k) sh[v * dk + k] = dequant_elem(c, &a, s_old[group_of(c, v, k)], v, k);
   /* the low-rank buffer decays first: the delta rule reads it decayed */
   float* W = NULL;
   float* U = NULL;
@@ -715,7 +771,7 @@ static void head_step(const orc_cfg* c, const layout_t* L, orc_state* st, int64_
     } else {
       double w = 0.0;
       for (int k = 0; k < dk; ++k) {
-        float dec = (a.slot[k] >= 0) ? (d[k] * s_old[v]) * (float)get_code(c, &a, v, a.slot[k])
+        float dec = (a.slot[k] >= 0) ? (d[k] * s_old[group_of(c, v, k)]) * (float)get_code(c, &a, v, a.slot[k])
                                      : d[k] * sh[v * dk + k];
         w += (double)dec * (double)kh[k];
       }
@@ -747,7 +803,7 @@ static void head_step(const orc_cfg* c, const layout_t* L, orc_state* st, int64_
     for (int k = 0; k < dk; ++k) {
       float uu = small[k] ? u_perp[v] : u[v];
       float decayed;
-      if (a.slot[k] >= 0) decayed = (d[k] * s_old[v]) * (float)get_code(c, &a, v, a.slot[k]);
+      if (a.slot[k] >= 0) decayed = (d[k] * s_old[group_of(c, v, k)]) * (float)get_code(c, &a, v, a.slot[k]);
       else decayed = d[k] * sh[v * dk + k];
       float x = fmaf(uu, kh[k], decayed);
       if (mflag[k]) x = x + merged[v * dk + k];
@@ -769,9 +825,16 @@ static void head_step(const orc_cfg* c, const layout_t* L, orc_state* st, int64_
   }
   if (sp_dbg) memcpy(sp_dbg + (uint64_t)bi * dv * dk, sp, sizeof(float) * (size_t)dv * (size_t)dk);
   /* requantize */
-  for (int v = 0; v < dv; ++v)
-    put_f(st->scales, (uint64_t)bh * dv + v,
-          requantize_row(c, &a, bh, v, sp + (uint64_t)v * dk, sh + (uint64_t)v * dk, step), c->scale_dtype);
+  if (c->scale_axis == 0) {
+    for (int v = 0; v < dv; ++v)
+      put_f(st->scales, (uint64_t)bh * dv + v,
+            requantize_row(c, &a, bh, v, sp + (uint64_t)v * dk, sh + (uint64_t)v * dk, step), c->scale_dtype);
+  } else {
+    float* sc = (float*)malloc(sizeof(float) * (size_t)G);
+    requantize_grouped(c, &a, bh, sp, sh, step, sc);
+    for (int i = 0; i < G; ++i) put_f(st->scales, (uint64_t)bh * G + i, sc[i], c->scale_dtype);
+    free(sc);
+  }
   if (r > 0) {   /* values already in the buffer's format: stored exactly */
     for (int i = 0; i < dv * r; ++i) put_f(st->W, (uint64_t)bh * dv * r + i, W[i], c->lrb_dtype);
     for (int i = 0; i < dk * r; ++i) put_f(st->U, (uint64_t)bh * dk * r + i, U[i], c->lrb_dtype);

@@ -49,11 +49,14 @@ typedef struct {
   uint64_t seed;       /* Philox key */
   int32_t scale_dtype; /* storage of row scales: 0 fp32, 1 bf16 (rounded up, see requantize_row) */
   int32_t lrb_dtype;   /* storage of the low-rank buffer factors W and U: 0 fp32, 1 bf16 */
+  int32_t scale_axis;  /* scale groups: 0 value axis (one scale per row v), 1 key axis (one
+                          per column k), 2 one per head; 1 and 2 need map 0 and no buffer.
+                          scales are [B,H,G], G = dv, dk or 1 */
 } orc_cfg;
 
 typedef struct {
   uint8_t* codes;   /* packed codes, per-head blocks */
-  void*    scales;  /* [B,H,dv], fp32 or bf16 bits per scale_dtype */
+  void*    scales;  /* [B,H,G] (G per scale_axis), fp32 or bf16 bits per scale_dtype */
   void*    hp;      /* protected values, per-head blocks (uint16 bits or fp32) */
   void*    W;       /* [B,H,dv,r], fp32 or bf16 bits per lrb_dtype */
   void*    U;       /* [B,H,dk,r], fp32 or bf16 bits per lrb_dtype */

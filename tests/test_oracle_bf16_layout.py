@@ -195,8 +195,8 @@ def test_bf16_layout_state_bytes_at_the_pages_shape():
 # fail the pins above.
 MUTANTS = {
     # the scale rounded to nearest instead of up (codes may then exceed Q)
-    "scale_nearest": ("    scale = orc_scale_bf16_up(m, Q);\n",
-                      "    scale = orc_from_bf16(orc_to_bf16(m / Q));\n"),
+    "scale_nearest": ("    g.scale = orc_scale_bf16_up(m, Q);\n",
+                      "    g.scale = orc_from_bf16(orc_to_bf16(m / Q));\n"),
     # a new basis column used unrounded in its first step (stored rounded)
     "basis_unrounded": ("W[v * r + n] = lrb_round(c, y[v] / ny);", "W[v * r + n] = y[v] / ny;"),
     # the buffer rounded only when stored, after the merge test and readout
