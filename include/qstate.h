@@ -48,7 +48,10 @@
  *     within a batch element, then batch order.  Padding bytes stay zero.
  *   scales: fp32 [B][H][dv], one per row (value-axis grouping [LoReS]):
  *     scale = max_k |S_pre[v][k]| / Q over quantized k, Q = 127 (int8) or
- *     7 (int4); a row with max 0 has scale 0 and codes 0.
+ *     7 (int4); a row with max 0 has scale 0 and codes 0.  With scale_axis
+ *     QS_AXIS_KEY: [B][H][dk], one per key channel (max over v); with
+ *     QS_AXIS_HEAD: [B][H], one per head (max over the head) -- the groupings
+ *     [LoReS] contrasts value-axis grouping with.
  *   hp: per (b,h) a block of dv rows of nhp(h) protected values in
  *     ascending k (bf16, fp16 or fp32 per hp_dtype), each row padded to a
  *     multiple of 4 bytes, the block to 16 bytes.
@@ -133,6 +136,7 @@ typedef enum { QS_DECAY_HEAD = 0, QS_DECAY_KEY = 1 } qs_decay_mode;
 typedef enum { QS_FP32 = 0, QS_BF16 = 1, QS_FP16 = 2 } qs_dtype;
 typedef enum { QS_MAP_NONE = 0, QS_MAP_HEAD = 1, QS_MAP_KEY = 2 } qs_map_mode;
 typedef enum { QS_ROUND_NEAREST = 0, QS_ROUND_STOCHASTIC = 1 } qs_rounding;
+typedef enum { QS_AXIS_VALUE = 0, QS_AXIS_KEY = 1, QS_AXIS_HEAD = 2 } qs_scale_axis;
 
 typedef struct {
   uint32_t abi_version;   /* QSTATE_ABI_VERSION */
@@ -160,6 +164,9 @@ typedef struct {
                              lrb_dtype QS_BF16) */
   int32_t lrb_dtype;      /* low-rank buffer factors W, U: QS_FP32, or QS_BF16 (with
                              scale_dtype QS_BF16, lrb_rank <= 8) */
+  int32_t scale_axis;     /* qs_scale_axis: scale groups are rows (QS_AXIS_VALUE, the
+                             method's grouping), key channels or whole heads (ablations;
+                             map NONE, no low-rank bypass, fp32 scales) */
 } qstate_config;
 
 /* Byte sizes of the caller-owned device buffers (0 = buffer unused). */

@@ -20,6 +20,7 @@ DECAY = {"head": 0, "key": 1}
 DTYPE = {"fp32": 0, "bf16": 1, "fp16": 2}
 MAP = {"none": 0, "head": 1, "key": 2}
 ROUNDING = {"nearest": 0, "stochastic": 1}
+AXIS = {"value": 0, "key": 1, "head": 2}
 
 EXPORTS = (
     "qstate_plan", "qstate_init", "qstate_quantize", "qstate_decode_step", "qstate_decode_step_batch",
@@ -39,6 +40,7 @@ class Config(ctypes.Structure):
         ("bdr", ctypes.c_int32), ("bdr_bound", ctypes.c_float),
         ("lrb_rank", ctypes.c_int32), ("lrb_period", ctypes.c_int32), ("lrb_theta", ctypes.c_float),
         ("seed", ctypes.c_uint64), ("scale_dtype", ctypes.c_int32), ("lrb_dtype", ctypes.c_int32),
+        ("scale_axis", ctypes.c_int32),
     ]
 
 

@@ -39,6 +39,7 @@ class StateConfig:
     seed: int = 0
     scale_dtype: str = "fp32"       # fp32 | bf16 (bf16: with lrb_dtype bf16 and the low-rank bypass)
     lrb_dtype: str = "fp32"         # fp32 | bf16
+    scale_axis: str = "value"       # value | key | head (key and head: ablations, map none, no buffer)
 
     def to_c(self) -> _lib.Config:
         c = _lib.Config()
@@ -61,6 +62,7 @@ class StateConfig:
         c.seed = self.seed
         c.scale_dtype = _lib.DTYPE[self.scale_dtype]
         c.lrb_dtype = _lib.DTYPE[self.lrb_dtype]
+        c.scale_axis = _lib.AXIS[self.scale_axis]
         return c
 
 

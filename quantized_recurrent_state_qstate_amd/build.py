@@ -2,10 +2,10 @@
 
 Translation units:
   qstate_step_<family>.hip   one per step-kernel family (dense, mixed, keymap,
-                             lrb), compiled once per (qbits, rounding) pair with
-                             -DQS_QB=<8|4> -DQS_RND=<0|1|2> (lrb once per kind
-                             too, -DQS_DELTA=<0|1>): 30 objects that compile
-                             in parallel
+                             lrb, grouped), compiled once per (qbits, rounding)
+                             pair with -DQS_QB=<8|4> -DQS_RND=<0|1|2> (lrb once
+                             per kind too, -DQS_DELTA=<0|1>): 36 objects that
+                             compile in parallel
   qstate_misc.hip            quantize / dequantize / fill kernels, dispatch
   qstate_host.cpp            the C ABI: validation, planning, launches
 Objects go to build/qstate/ and link into
@@ -44,7 +44,7 @@ FLAGS = [
     "-Wall", "-Wno-unused-result", "-Wno-unused-function",
 ]
 
-FAMILIES = ("dense", "mixed", "keymap", "lrb")
+FAMILIES = ("dense", "mixed", "keymap", "lrb", "grouped")
 QR = [(qb, rnd) for qb in (8, 4) for rnd in (0, 1, 2)]
 RND_NAME = {0: "rtn", 1: "sr16", 2: "sr8"}
 

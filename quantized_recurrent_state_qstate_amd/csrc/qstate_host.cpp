@@ -142,6 +142,11 @@ qs_status validate(const qstate_config* c) {
   if ((c->scale_dtype != QS_FP32 && c->scale_dtype != QS_BF16) || (c->lrb_dtype != QS_FP32 && c->lrb_dtype != QS_BF16))
     return fail(c->scale_dtype == QS_FP16 || c->lrb_dtype == QS_FP16 ? QS_EUNSUPPORTED : QS_EINVAL,
                 "scale_dtype %d, lrb_dtype %d (supported: fp32, bf16)", c->scale_dtype, c->lrb_dtype);
+  if (c->scale_axis != QS_AXIS_VALUE && c->scale_axis != QS_AXIS_KEY && c->scale_axis != QS_AXIS_HEAD)
+    return fail(QS_EINVAL, "scale_axis %d", c->scale_axis);
+  if (c->scale_axis != QS_AXIS_VALUE &&
+      (c->map_mode != QS_MAP_NONE || c->lrb_rank != 0 || c->scale_dtype != QS_FP32))
+    return fail(QS_EUNSUPPORTED, "key-axis and per-head scales: map NONE, no low-rank bypass, fp32 scales");
   if (c->scale_dtype == QS_BF16 || c->lrb_dtype == QS_BF16) {
     // the bf16 layout is the one of int4 states with the low-rank bypass:
     // bf16 scales and bf16 buffer factors together, rank bound 8
@@ -184,13 +189,17 @@ qs_status make_plan(const qstate_config* c, Plan* p) {
   p->sizes.codes = B * coff;
   p->sizes.hp = B * hoff;
   const uint64_t sb = c->scale_dtype == QS_BF16 ? 2u : 4u, lb = c->lrb_dtype == QS_BF16 ? 2u : 4u;
-  p->sizes.scales = BH * (uint64_t)dv * sb;
+  const uint64_t G = c->scale_axis == QS_AXIS_KEY ? (uint64_t)dk : (c->scale_axis == QS_AXIS_HEAD ? 1u : (uint64_t)dv);
+  p->sizes.scales = BH * G * sb;
   p->sizes.lrb_W = BH * (uint64_t)dv * r * lb;
   p->sizes.lrb_U = BH * (uint64_t)dk * r * lb;
   p->sizes.lrb_n = r > 0 ? BH * 4u : 0u;
 
   dense_shape(c->kind, dk, dv, &p->dense_lpr, &p->dense_rpl, &p->dense_threads, &p->row_chunks);
-  if (c->lrb_rank > 0) {
+  if (c->scale_axis != QS_AXIS_VALUE) {
+    // key-axis or per-head groups: one workgroup per head, two passes
+    p->family = qs::kFamGrouped;
+  } else if (c->lrb_rank > 0) {
     // one workgroup per head; the buffer and the head's vectors live in
     // static LDS
     p->family = qs::kFamLrb;
@@ -234,7 +243,7 @@ qs_status make_plan(const qstate_config* c, Plan* p) {
   }
   if (p->lds > kMaxLds)
     return fail(QS_EUNSUPPORTED, "a head needs %u bytes of LDS staging (max %u)", p->lds, kMaxLds);
-  const bool chunked = p->family == qs::kFamDense || p->family == qs::kFamKeymap;
+  const bool chunked = p->family == qs::kFamDense || p->family == qs::kFamKeymap;   // others: one group per head
   const uint64_t grid = BH * (chunked ? (uint64_t)p->row_chunks : 1u);
   if (grid > 0x7FFFFFFFu) return fail(QS_EUNSUPPORTED, "B*H too large for one launch");
   // the kernels form Philox block counters in 32 bits: element indices
@@ -328,6 +337,7 @@ qs::Args base_args(const qstate_handle* h, const qstate_tensors* st) {
   a.seed_hi = (uint32_t)(c.seed >> 32);
   a.mixed_lds = h->plan.lds;
   a.bf16_layout = c.lrb_dtype == QS_BF16 ? 1 : 0;
+  a.scale_axis = c.scale_axis;
   a.nslots = c.B;
   return a;
 }

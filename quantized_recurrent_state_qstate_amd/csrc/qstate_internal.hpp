@@ -68,6 +68,7 @@ struct Args {
   uint32_t step_lo, step_hi;
   uint32_t mixed_lds;  // mixed kernel: dynamic LDS bytes
   int32_t bf16_layout; // scales and low-rank buffer factors stored as bf16 (LRB only)
+  int32_t scale_axis;  // scale groups: 0 rows (value axis), 1 columns (key axis), 2 the head
   // batched entry point: batch element b reads its inputs and writes its
   // outputs at b, and its state at slot[b] of a pool of nslots states, with
   // its own step; null = the plain step (slot b, step above)
@@ -85,7 +86,7 @@ struct HeadIx {
 };
 
 // Kernel families chosen at init.
-enum StepFamily : int { kFamDense = 0, kFamMixed = 1, kFamLrb = 2, kFamKeymap = 3 };
+enum StepFamily : int { kFamDense = 0, kFamMixed = 1, kFamLrb = 2, kFamKeymap = 3, kFamGrouped = 4 };
 
 // Launchers.  Step kernels, one launcher per family, instantiated per
 // (qbits, rounding) in qstate_step_<family>.hip (the low-rank-bypass one per
@@ -99,6 +100,8 @@ template <int QB, int RND>
 hipError_t launch_keymap(int delta, const Args& a, hipStream_t s);
 template <int QB, int RND, int DELTA>
 hipError_t launch_lrb(const Args& a, hipStream_t s);
+template <int QB, int RND>
+hipError_t launch_grouped(int delta, const Args& a, hipStream_t s);
 hipError_t launch_step(int family, int qbits, int rnd, int delta, const Args& a,
                        hipStream_t s);
 hipError_t launch_quantize(const Args& a, hipStream_t s);

@@ -130,6 +130,83 @@ __global__ __launch_bounds__(256) void k_quantize(const Args a) {
   else a.scales[row] = scale;
 }
 
+// Quantize with key-axis or per-head groups (map NONE): one workgroup per
+// head; the groups' maxima through LDS, then one thread per row.
+__global__ __launch_bounds__(256) void k_quantize_grouped(const Args a) {
+  const int dk = a.dk, dv = a.dv;
+  const uint64_t bh = blockIdx.x;
+  const uint32_t h = (uint32_t)(bh % (uint64_t)a.H), b = (uint32_t)(bh / (uint64_t)a.H);
+  const int G = a.scale_axis == 1 ? dk : 1;
+  __shared__ uint32_t gmax[256];
+  __shared__ float ginv[256], ginvb[256];
+  const float* S = a.S + bh * (uint64_t)dv * (uint64_t)dk;
+  for (int t = threadIdx.x; t < G; t += 256) gmax[t] = 0u;
+  __syncthreads();
+  for (int e = threadIdx.x; e < dv * dk; e += 256)
+    atomicMax(&gmax[a.scale_axis == 1 ? e % dk : 0], __float_as_uint(fabsf(S[e])));
+  __syncthreads();
+  const int srb = a.rounding ? a.sr_bits : 0;
+  for (int t = threadIdx.x; t < G; t += 256) {
+    const float m = __uint_as_float(gmax[t]);
+    float scale, inv, invb;
+    if (a.qbits == 8) {
+      if (srb == 16) row_scale<8, 16>(m, scale, inv, invb);
+      else if (srb == 8) row_scale<8, 8>(m, scale, inv, invb);
+      else row_scale<8, 0>(m, scale, inv, invb);
+    } else {
+      if (srb == 16) row_scale<4, 16>(m, scale, inv, invb);
+      else if (srb == 8) row_scale<4, 8>(m, scale, inv, invb);
+      else row_scale<4, 0>(m, scale, inv, invb);
+    }
+    ginv[t] = inv;
+    ginvb[t] = invb;
+    a.scales[bh * (uint64_t)G + t] = scale;
+  }
+  __syncthreads();
+  uint8_t* cblk = const_cast<uint8_t*>(code_block_m(a, b, h));
+  const uint32_t rq = code_row_bytes(dk, a.qbits);
+  for (int v = threadIdx.x; v < dv; v += 256) {
+    uint8_t* crow = cblk + (uint64_t)v * rq;
+    const uint64_t row = bh * (uint64_t)dv + (uint64_t)v;
+    uint64_t cached = ~(uint64_t)0;
+    uint32_t x[4] = {0, 0, 0, 0};
+    uint32_t pend = 0;
+    for (int k = 0; k < dk; ++k) {
+      const int g = a.scale_axis == 1 ? k : 0;
+      const float val = S[(uint64_t)v * dk + k];
+      uint32_t rbits = 0;
+      if (a.rounding) {
+        const uint64_t e = row * (uint64_t)dk + (uint64_t)k;
+        const uint64_t gi = (a.sr_bits == 16) ? (e >> 3) : (e >> 4);
+        if (gi != cached) {
+          x[0] = (uint32_t)gi;
+          x[1] = (uint32_t)(gi >> 32);
+          x[2] = a.step_lo;
+          x[3] = a.step_hi;
+          philox10(x, a.seed_lo, a.seed_hi);
+          cached = gi;
+        }
+        rbits = (a.sr_bits == 16) ? ((e & 1u) ? (x[(e >> 1) & 3u] >> 16) : (x[(e >> 1) & 3u] & 0xFFFFu))
+                                  : ((x[(e >> 2) & 3u] >> (8u * (uint32_t)(e & 3u))) & 0xFFu);
+      }
+      const float inv = ginv[g], invb = ginvb[g];
+      int32_t c;
+      if (a.qbits == 8) {
+        c = !a.rounding ? round_elem<8, 0, 0>(val, 0.0f, inv, invb, 0u, 0.0f)
+                        : (a.sr_bits == 16 ? round_elem<8, 1, 0>(val, 0.0f, inv, invb, rbits, 0.0f)
+                                           : round_elem<8, 2, 0>(val, 0.0f, inv, invb, rbits, 0.0f));
+        crow[k] = (uint8_t)c;
+      } else {
+        c = !a.rounding ? round_elem<4, 0, 0>(val, 0.0f, inv, invb, 0u, 0.0f)
+                        : (a.sr_bits == 16 ? round_elem<4, 1, 0>(val, 0.0f, inv, invb, rbits, 0.0f)
+                                           : round_elem<4, 2, 0>(val, 0.0f, inv, invb, rbits, 0.0f));
+        if ((k & 1) == 0) pend = (uint32_t)c & 0xFu;
+        else crow[k >> 1] = (uint8_t)(pend | (((uint32_t)c & 0xFu) << 4));
+      }
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void k_dequantize(const Args a) {
   const uint64_t row = (uint64_t)blockIdx.x * 256u + threadIdx.x;
   const uint64_t nrows = (uint64_t)a.B * (uint64_t)a.H * (uint64_t)a.dv;
@@ -151,7 +228,9 @@ __global__ __launch_bounds__(256) void k_dequantize(const Args a) {
   auto ld = [bf](const float* base, uint64_t i) -> float {
     return bf ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(base)[i]) : base[i];
   };
-  const float scale = a.scales ? ld(a.scales, row) : 0.0f;
+  // scale groups: the row (value axis), the key channel, or the head
+  const int G = a.scale_axis == 0 ? a.dv : (a.scale_axis == 1 ? dk : 1);
+  const float row_scale_v = a.scales && a.scale_axis == 0 ? ld(a.scales, row) : 0.0f;
   const int r = a.lrb_rank;
   const int n = r > 0 ? a.n[bh] : 0;
   const uint64_t w0 = (bh * (uint64_t)a.dv + v) * (uint64_t)r, u0 = bh * (uint64_t)dk * (uint64_t)r;
@@ -169,6 +248,8 @@ __global__ __launch_bounds__(256) void k_dequantize(const Args a) {
       int32_t c;
       if (a.qbits == 8) c = (int32_t)(int8_t)crow[s];
       else c = (int32_t)((uint32_t)crow[s >> 1] << (28 - 4 * (s & 1))) >> 28;
+      const float scale = a.scale_axis == 0 ? row_scale_v
+                          : (a.scales ? ld(a.scales, bh * (uint64_t)G + (a.scale_axis == 1 ? (uint64_t)k : 0u)) : 0.0f);
       val = scale * (float)c;
     }
     if (n > 0) {
@@ -200,6 +281,7 @@ hipError_t launch_step_qr(int family, int delta, const Args& a, hipStream_t s) {
     case kFamMixed: return launch_mixed<QB, RND>(delta, a, s);
     case kFamKeymap: return launch_keymap<QB, RND>(delta, a, s);
     case kFamLrb: return delta ? launch_lrb<QB, RND, 1>(a, s) : launch_lrb<QB, RND, 0>(a, s);
+    case kFamGrouped: return launch_grouped<QB, RND>(delta, a, s);
   }
   return hipErrorInvalidValue;
 }
@@ -225,6 +307,10 @@ hipError_t launch_step(int family, int qbits, int rnd, int delta, const Args& a,
 hipError_t launch_quantize(const Args& a, hipStream_t s) {
   const uint64_t nrows = (uint64_t)a.B * (uint64_t)a.H * (uint64_t)a.dv;
   if (nrows == 0) return hipSuccess;
+  if (a.scale_axis != 0) {   // key-axis or per-head groups: one workgroup per head
+    hipLaunchKernelGGL(k_quantize_grouped, dim3((uint32_t)((uint64_t)a.B * (uint64_t)a.H)), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(k_quantize, dim3((uint32_t)((nrows + 255u) / 256u)), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.lrb_rank == 0) return e;
@@ -253,7 +339,8 @@ const char* step_kernel_name(int family, int qbits, int rnd, int delta, int dk) 
   static thread_local char buf[96];
   const char* fam = family == kFamDense ? "dense"
                     : family == kFamMixed ? "mixed"
-                    : family == kFamKeymap ? "keymap" : "lrb";
+                    : family == kFamKeymap ? "keymap"
+                    : family == kFamGrouped ? "grouped" : "lrb";
   const char* rn = rnd == 0 ? "rtn" : (rnd == 1 ? "sr16" : "sr8");
   snprintf(buf, sizeof(buf), "k_step_%s<int%d,%s,%s,dk%d>", fam, qbits, rn, delta ? "delta" : "additive", dk);
   return buf;

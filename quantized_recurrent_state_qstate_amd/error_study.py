@@ -27,9 +27,9 @@ Metrics of one configuration (means over heads; steps after a warm-up):
   coherence   cosine between consecutive steps' rounding errors
               E_t = S_q,t - (exact step of S_q,t-1)
 
-Scale grouping (value axis as stored here, key axis, one scale per head) is
-compared in a float64 simulation of nearest and stochastic rounding, since
-the library stores value-axis scales only.
+Scale grouping (value axis, key axis, one scale per head) runs through the
+library's scale_axis; run_grouping is a float64 simulation of the same
+quantizer, kept as an independent cross-check of the grouped path.
 
     python -m quantized_recurrent_state_qstate_amd.error_study [--T 256] [--json out.json]
     python -m quantized_recurrent_state_qstate_amd.error_study --horizons   # error after 64/256/1024 steps
@@ -220,10 +220,12 @@ def study(B=16, H=4, dk=128, dv=128, T=256, seed=2024, warm=16, regimes=None, gr
             rows.append(r)
         groups = []
         if groupings:
+            # through the library's scale_axis: rows (value axis), key
+            # channels, one per head
             for qbits in (8, 4):
                 for rounding in ("nearest", "stochastic"):
-                    e = {g: run_grouping(g, qbits, rounding, B, H, dk, dv, T, rp, seed)
-                         for g in ("value", "key", "head")}
+                    e = {g: run_library(dict(qbits=qbits, rounding=rounding, scale_axis=g), B, H, dk, dv, T, rp,
+                                        seed, warm)["state_err"] for g in ("value", "key", "head")}
                     groups.append(dict(qbits=qbits, rounding=rounding, **e))
         out.append(dict(regime=rname, decay=f"sigmoid(N({rp['mu']},1)) per key", params=rp,
                         library=rows, grouping=groups))

@@ -14,8 +14,8 @@ decay; see quantized_recurrent_state_qstate_amd.error_study):
 * scales grouped along the value axis beat key-axis and per-head scales (the
   first page's abstract).
 
-The library's value-axis nearest rounding also matches an independent
-float64 simulation of the same quantizer over the whole run."""
+The library's value-axis and key-axis nearest rounding also match an
+independent float64 simulation of the same quantizer over the whole run."""
 import sys
 
 import pytest
@@ -46,8 +46,11 @@ def test_claims_reproduce_on_structured_inputs():
     # scale grouping
     g8 = grp[(8, "nearest")]
     assert g8["value"] < g8["key"] < g8["head"]
-    # the library against the float64 simulation of the same quantizer
-    assert abs(rtn8["state_err"] - g8["value"]) <= 0.05 * g8["value"]
+    # the library against a float64 simulation of the same quantizer, over the
+    # whole run, for the row and the key-channel groups
+    for axis in ("value", "key"):
+        sim = es.run_grouping(axis, 8, "nearest", 4, 2, 128, 128, 128, rp, 2024)
+        assert abs(g8[axis] - sim) <= 0.05 * sim, (axis, g8[axis], sim)
 
 
 def test_low_precision_fares_best_on_short_horizons():

@@ -54,7 +54,8 @@ def _head_slices(ocfg):
         c0 = b * L["code_bstride"] + int(L["code_off"][h])
         hb = dv * (((dk - nq) * hp_item + 3) // 4 * 4) // hp_item
         h0 = (b * L["hp_bstride"] + int(L["hp_off"][h])) // hp_item
-        out.append(dict(codes=slice(c0, c0 + cb), hp=slice(h0, h0 + hb), scales=slice(bh * dv, bh * dv + dv),
+        G = {"value": dv, "key": dk, "head": 1}[ocfg.scale_axis]    # scale groups per head
+        out.append(dict(codes=slice(c0, c0 + cb), hp=slice(h0, h0 + hb), scales=slice(bh * G, bh * G + G),
                         quant=nq > 0, W=slice(bh * dv * r, (bh + 1) * dv * r),
                         U=slice(bh * dk * r, (bh + 1) * dk * r)))
     return out
@@ -246,6 +247,29 @@ def test_quantize_dequantize_bitexact(name):
     assert np.array_equal(got["hp"].view(np.uint8), ost["hp"].view(np.uint8))
     D = qs.dequantize(st).cpu().numpy()
     assert np.array_equal(D, oracle.dequantize(ocfg, ost))
+
+
+@pytest.mark.parametrize("axis", ["key", "head"])
+@pytest.mark.parametrize("qbits,rounding", [(8, "stochastic"), (4, "nearest"), (4, "stochastic")])
+def test_quantize_grouped_scales_bitexact(axis, qbits, rounding):
+    B, H, dk, dv = 2, 3, 128, 48
+    g = torch.Generator().manual_seed(3)
+    S = torch.randn(B, H, dv, dk, generator=g) * torch.exp(torch.rand(B, H, 1, dk, generator=g) * 4)
+    S[0, 0, :, 5] = 0.0
+    qs = QState(StateConfig(B=B, H=H, dk=dk, dv=dv, qbits=qbits, rounding=rounding, scale_axis=axis, seed=5))
+    ocfg = oracle.Cfg(B=B, H=H, dk=dk, dv=dv, qbits=qbits, rounding="rtn" if rounding == "nearest" else "sr",
+                      scale_axis=axis, seed=5)
+    st = qs.new_state()
+    _log(f"[parity] quantize {axis} axis int{qbits} {rounding}")
+    qs.quantize(S.to(DEV), st, step=3)
+    torch.cuda.synchronize()
+    ost = oracle.new_state(ocfg)
+    oracle.quantize(ocfg, S.numpy(), ost, step=3)
+    got = gpu_state_to_oracle(st, "bf16")
+    assert np.array_equal(got["codes"], ost["codes"])
+    assert np.array_equal(got["scales"], ost["scales"])
+    assert np.array_equal(qs.dequantize(st).cpu().numpy(), oracle.dequantize(ocfg, ost))
+    qs.close()
 
 
 def _pad_bytes(ocfg):
@@ -494,6 +518,15 @@ EDGE = {
     "lrb_bf16_kda_int4_sr8_bdr": dict(kind="delta", decay_mode="key", dk=128, dv=64, H=2, B=2, qbits=4,
                                       sr_bits=8, bdr=True, lrb_rank=4, lrb_period=2,
                                       scale_dtype="bf16", lrb_dtype="bf16"),
+    # scale groups other than rows: one per key channel, one per head
+    "axis_key_additive_sr": dict(kind="additive", decay_mode="key", dk=128, dv=64, H=2, B=2, qbits=8,
+                                 scale_axis="key"),
+    "axis_head_delta_int4_rtn_bdr": dict(kind="delta", decay_mode="head", dk=64, dv=40, H=2, B=2, qbits=4,
+                                         rounding="nearest", bdr=True, scale_axis="head"),
+    "axis_key_kda_int4_sr8_dk256": dict(kind="delta", decay_mode="key", dk=256, dv=24, H=2, B=2, qbits=4,
+                                        sr_bits=8, scale_axis="key"),
+    "axis_head_additive_dv200_rtn": dict(kind="additive", decay_mode="head", dk=128, dv=200, H=2, B=1, qbits=8,
+                                         rounding="nearest", scale_axis="head"),
 }
 
 

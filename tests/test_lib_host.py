@@ -201,3 +201,19 @@ def test_bf16_layout_supported_set():
         with pytest.raises(_lib.QStateError) as e:
             plan(StateConfig(**kw))
         assert e.value.status == _lib.QS_EUNSUPPORTED, kw
+
+
+def test_scale_axis_supported_set():
+    """Key-axis and per-head scale groups: scales [B,H,dk] or [B,H]; map NONE,
+    no low-rank bypass, fp32 scales only."""
+    base = dict(B=2, H=3, dk=128, dv=96, qbits=8)
+    for axis, G in (("value", 96), ("key", 128), ("head", 1)):
+        z = plan(StateConfig(**base, scale_axis=axis))
+        o = oracle.layout(oracle.Cfg(**base, scale_axis=axis))
+        assert z["scales"] == o["scales"] == 2 * 3 * G * 4
+    bad = [dict(base, scale_axis="key", lrb_rank=4), dict(base, scale_axis="head", map_mode="head",
+                                                        map=np.array([1, 0, 0], np.uint8))]
+    for kw in bad:
+        with pytest.raises(_lib.QStateError) as e:
+            plan(StateConfig(**kw))
+        assert e.value.status == _lib.QS_EUNSUPPORTED, kw
