@@ -43,13 +43,15 @@ METRIC = "quantized-state decode steps/sec and state GB/s (% HBM peak) at B=256,
 CSRC = os.path.join(ROOT, "quantized_recurrent_state_qstate_amd", "csrc")
 
 
-def kernel_hash() -> str:
-    """Hash of the device sources: counter-derived traffic is valid only for these."""
-    import glob
+def kernel_hash(family: str = "dense") -> str:
+    """Hash of the sources one step-kernel family is compiled from (its unit
+    and every header it includes): counter-derived traffic is valid only for
+    these."""
+    from quantized_recurrent_state_qstate_amd.build import deps
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.hpp"))):
+    for p in sorted(deps(os.path.join(CSRC, f"qstate_step_{family}.hip"))):
         with open(p, "rb") as f:
-            h.update(f.read())
+            h.update(os.path.basename(p).encode() + f.read())
     return h.hexdigest()[:16]
 
 
