@@ -24,35 +24,132 @@ namespace qs {
 
 namespace {
 
-// Block sums of the R-vector p and block max of mx; every thread gets them
-// in out[] and the return value.  Through LDS: each thread writes its R
-// partial values to P [R][256], 256/R threads sum one component (a fixed
-// order), and a shuffle tree finishes it.  red: R + 4 floats.
+// ---------------------------------------------------------------------------
+// Reductions across the workgroup (256 threads, 4 waves) with DPP steps: the
+// row steps of the 8-lane sums (swap neighbours, swap pairs, mirror the half
+// row), then the row mirror, which leaves every lane of a 16-lane row with
+// the row's total, and the GFX9 row broadcasts, which add lane 15 of each
+// row into the next row (row mask 1010b) and lane 31 into the upper half
+// (row mask 1100b).  A masked-off row reads the 0 that update_dpp supplies,
+// an exact no-op for sums (and for maxima of non-negative bit patterns).
+// ---------------------------------------------------------------------------
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dppf_rows(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROWS, 0xF, false));
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dppu_rows(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROWS, 0xF, false);
+}
+constexpr int kDppRowMirror = 0x140;
+constexpr int kDppBcast15 = 0x142;
+constexpr int kDppBcast31 = 0x143;
+
+// Sum over groups of L = 16, 32 or 64 consecutive lanes; the group's last
+// lane holds the total (every lane of the group for L = 16).
+template <int L>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(L == 16 || L == 32 || L == 64, "16, 32 or 64 lanes");
+  x = x + dppf_rows<0xB1, 0xF>(x);
+  x = x + dppf_rows<0x4E, 0xF>(x);
+  x = x + dppf_rows<0x141, 0xF>(x);
+  x = x + dppf_rows<kDppRowMirror, 0xF>(x);
+  if constexpr (L >= 32) x = x + dppf_rows<kDppBcast15, 0xA>(x);
+  if constexpr (L == 64) x = x + dppf_rows<kDppBcast31, 0xC>(x);
+  return x;
+}
+// Maximum of non-negative floats over the wave (on their bit patterns, whose
+// unsigned order is the numeric order); lane 63 holds it.
+__device__ __forceinline__ float wave_absmax(float x) {
+  uint32_t u = __float_as_uint(x);
+  u = max(u, dppu_rows<0xB1, 0xF>(u));
+  u = max(u, dppu_rows<0x4E, 0xF>(u));
+  u = max(u, dppu_rows<0x141, 0xF>(u));
+  u = max(u, dppu_rows<kDppRowMirror, 0xF>(u));
+  u = max(u, dppu_rows<kDppBcast15, 0xA>(u));
+  u = max(u, dppu_rows<kDppBcast31, 0xC>(u));
+  return __uint_as_float(u);
+}
+
+// Block sum; every thread gets the same value.  red: 4 floats.
+__device__ __forceinline__ float block_sum_dpp(float x, float* red) {
+  x = group_sum<64>(x);
+  __syncthreads();   // red may still be read by an earlier reduction
+  if ((threadIdx.x & 63) == 63) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+// Block sums of the R-vector p and block max of mx (mx >= 0); every thread
+// gets them in out[] and the return value.  Through LDS: each thread writes
+// its R partial values to P [R][256], 256/R consecutive threads sum one
+// component (a fixed order: EPT entries each, then the DPP steps).  red:
+// R + 4 floats.
 template <int R>
 __device__ __forceinline__ float block_sum_vec(const float (&p)[R], float mx, float (&out)[R], float* P,
                                                float* red) {
   static_assert(R == 8 || R == 16, "rank bound 8 or 16");
-  constexpr int TPC = 256 / R;   // threads per component
+  constexpr int TPC = 256 / R;   // threads per component: 32 or 16
   constexpr int EPT = 256 / TPC; // entries each of them sums
   const int t = threadIdx.x;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+  mx = wave_absmax(mx);
   __syncthreads();   // P and red may still be read by an earlier reduction
 #pragma unroll
   for (int j = 0; j < R; ++j) P[j * 256 + t] = p[j];
-  if ((t & 63) == 0) red[R + (t >> 6)] = mx;
+  if ((t & 63) == 63) red[R + (t >> 6)] = mx;
   __syncthreads();
   const int j = t / TPC, part = t % TPC;
   float sum = 0.0f;
 #pragma unroll
   for (int e = 0; e < EPT; ++e) sum += P[j * 256 + part * EPT + e];
-#pragma unroll
-  for (int off = TPC / 2; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
-  if (part == 0) red[j] = sum;
+  sum = group_sum<TPC>(sum);
+  if (part == TPC - 1) red[j] = sum;
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < R; ++i) out[i] = red[i];
   return fmaxf(fmaxf(red[R], red[R + 1]), fmaxf(red[R + 2], red[R + 3]));
+}
+
+// Nearest rounding of x = sp inv, with BDR, as the bit pattern of a float
+// whose low bits hold the code: BDR's limits are whole numbers (or
+// infinite), and at most one of them is finite, so clamping x before
+// rounding gives the code the rule gives after it (rint is monotone and
+// fixes whole numbers).  Adding 1.5 * 2^23 rounds |x| <= Q to the nearest
+// whole number, ties to even (the sum's last place is 1), and leaves it in
+// the low mantissa bits: bits = c + 0x4B400000, whose low byte is c mod 256.
+template <int BDR>
+__device__ __forceinline__ uint32_t round_nearest_bits(float sp, float sh, float inv, float bound) {
+  float x = sp * inv;
+  if constexpr (BDR) x = bdr_clamp<BDR>(x, sp, sh, inv, bound);
+  return __float_as_uint(x + 12582912.0f);
+}
+
+// Pack N codes given as such bit patterns (c + 0x4B400000).  int8: the low
+// byte of each.  int4: the digit sum of the offset codes as in pack_codes,
+// with the constant sum of 0x4B400000 16^i (mod 2^32) taken out of the base.
+constexpr uint32_t magic_digit_sum() {
+  uint32_t k = 0u;
+  for (int i = 0; i < 8; ++i) k += 0x4B400000u << (4 * i);
+  return k;
+}
+template <int QB, int N>
+__device__ __forceinline__ void pack_code_bits(const uint32_t (&b)[N], uint32_t (&w)[(N * QB + 31) / 32]) {
+  constexpr int NW = (N * QB + 31) / 32;
+  if constexpr (QB == 8) {
+#pragma unroll
+    for (int j = 0; j < NW; ++j) w[j] = 0u;
+#pragma unroll
+    for (int i = 0; i < N; ++i) w[i >> 2] |= (b[i] & 0xFFu) << (8 * (i & 3));
+  } else {
+    static_assert(N % 8 == 0, "whole words of int4 codes");
+    constexpr uint32_t base = 0x88888888u - magic_digit_sum();
+#pragma unroll
+    for (int j = 0; j < NW; ++j) w[j] = base;
+#pragma unroll
+    for (int i = 0; i < N; ++i) w[i >> 3] += b[i] << (4 * (i & 7));
+#pragma unroll
+    for (int j = 0; j < NW; ++j) w[j] ^= 0x88888888u;
+  }
 }
 
 // Element j (runtime) of a register array, by selects.
@@ -110,7 +207,7 @@ __attribute__((amdgpu_waves_per_eu(lrb_min_waves<QB, RND, RANK, DELTA, DKEY>(), 
   float* const ol = P;
   float* const sl_ = P + 256;
   __shared__ float red[RANK + 4];
-  __shared__ uint8_t smalll[DK], mflagl[DK];
+  __shared__ uint64_t smallw[4], mflagw[4];   // per-key flags, bit k of the DK-bit words
 
   // the buffer factors and the row scales, fp32 or bf16 (BF)
   const uint64_t woff = bhs * (uint64_t)dv * (uint64_t)r, uoff = bhs * (uint64_t)DK * (uint64_t)r;
@@ -249,11 +346,11 @@ __attribute__((amdgpu_waves_per_eu(lrb_min_waves<QB, RND, RANK, DELTA, DKEY>(), 
     for (int pass = 0; pass < 2; ++pass)
       for (int j = 0; j < n; ++j) {
         const float wv = pick<RANK>(Wr, j);
-        const float p = block_sum(wv * y, red);
+        const float p = block_sum_dpp(wv * y, red);
         y = fmaf(-p, wv, y);
       }
-    const float ny = sqrtf(block_sum(y * y, red));
-    const float nu = sqrtf(block_sum(uv * uv, red));
+    const float ny = sqrtf(block_sum_dpp(y * y, red));
+    const float nu = sqrtf(block_sum_dpp(uv * uv, red));
     if (ny > ldexpf(nu, -10)) {
       wnew = tid < dv ? y / ny : 0.0f;
       if constexpr (BF) wnew = round_bf16(wnew);   // stored and used in the buffer's format
@@ -359,8 +456,13 @@ __attribute__((amdgpu_waves_per_eu(lrb_min_waves<QB, RND, RANK, DELTA, DKEY>(), 
     kl[tid] = kk;
     ql[tid] = qq;
     dl[tid] = dd;
-    smalll[tid] = sm ? 1 : 0;
-    mflagl[tid] = merged ? 1 : 0;
+  }
+  {
+    const uint64_t bs_ = __ballot(sm), bm_ = __ballot(merged);   // wave w: keys 64w .. 64w + 63
+    if ((tid & 63) == 0 && tid < DK) {
+      smallw[tid >> 6] = bs_;
+      mflagw[tid >> 6] = bm_;
+    }
   }
   if (grown && tid < dv) st_buf(a.W, woff + (uint64_t)(tid * r + (n - 1)), wnew);   // only the new column changed
   if (tid == 0) a.n[bhs] = n_new;
@@ -372,12 +474,10 @@ __attribute__((amdgpu_waves_per_eu(lrb_min_waves<QB, RND, RANK, DELTA, DKEY>(), 
   const float* kf = kl + k0;
   const float* qf = ql + k0;
   const float* df = dl + k0;
-  uint32_t smask = 0u, mmask = 0u;
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    smask |= (smalll[k0 + i] ? 1u : 0u) << i;
-    mmask |= (mflagl[k0 + i] ? 1u : 0u) << i;
-  }
+  // the lane's keys k0 .. k0 + EPL - 1 lie in one 64-bit word (EPL <= 32 divides 64)
+  constexpr uint64_t kLaneBits = EPL == 32 ? 0xFFFFFFFFull : ((1ull << EPL) - 1ull);
+  const uint32_t smask = (uint32_t)((smallw[k0 >> 6] >> (k0 & 63)) & kLaneBits);
+  const uint32_t mmask = (uint32_t)((mflagw[k0 >> 6] >> (k0 & 63)) & kLaneBits);
   uint8_t* gcode = const_cast<uint8_t*>(gc);
   auto row_step = [&](const int v, const uint32_t (&cw)[CW]) {
     const uint64_t row = bhs * (uint64_t)dv + (uint64_t)v;   // state row (Philox counter)
@@ -415,12 +515,18 @@ __attribute__((amdgpu_waves_per_eu(lrb_min_waves<QB, RND, RANK, DELTA, DKEY>(), 
     else row_scale_fast<QB, SRB>(m, scale, inv, invb);
     uint32_t rb[EPL];
     if constexpr (RND != 0) rand_bits<RND, EPL>(row * DK + (uint64_t)k0, a.seed_lo, a.seed_hi, ix.step_lo, ix.step_hi, rb);
-    int32_t code[EPL];
-#pragma unroll
-    for (int i = 0; i < EPL; ++i)
-      code[i] = round_elem<QB, RND, BDR>(sp[i], sh[i], inv, invb, (RND != 0) ? rb[i] : 0u, a.bdr_bound);
     uint32_t out[CW];
-    pack_codes<QB, EPL>(code, out);
+    if constexpr (RND == 0) {
+      uint32_t cb[EPL];
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) cb[i] = round_nearest_bits<BDR>(sp[i], sh[i], inv, a.bdr_bound);
+      pack_code_bits<QB, EPL>(cb, out);
+    } else {
+      int32_t code[EPL];
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) code[i] = round_elem<QB, RND, BDR>(sp[i], sh[i], inv, invb, rb[i], a.bdr_bound);
+      pack_codes<QB, EPL>(code, out);
+    }
     store_bytes<EPL * QB / 8, true>(gcode + (uint64_t)v * (DK * QB / 8) + k0 * QB / 8, out);
     if (lane8 == 0) {   // collected in LDS, stored below as whole cache lines
       ol[v] = o + lrl[v];
