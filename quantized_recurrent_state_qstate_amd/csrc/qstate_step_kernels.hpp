@@ -133,16 +133,16 @@ __device__ __forceinline__ void row_scale_fast(float m, float& scale, float& inv
 }
 
 // A lane's k and q slices (EPL keys from k0, or the split slice of a row
-// stored in 128-byte pieces of VPP values each (16 bytes per lane): keys
-// 8 VPP (i / VPP) + VPP lane + i % VPP; VPP = 8 for 16-bit rows, 4 for fp32).
+// stored in pieces of GW lanes x 16 bytes of VPP values each: keys
+// GW VPP (i / VPP) + VPP lane + i % VPP; VPP = 8 for 16-bit rows, 4 for fp32).
 // REG: held in registers, for lanes that compute several rows; otherwise
 // read from the LDS copy where they are used, which keeps 2*EPL registers free.
-template <int EPL, bool REG, bool SPLIT = false, int VPP = 8>
+template <int EPL, bool REG, bool SPLIT = false, int VPP = 8, int GW = 8>
 struct KQ {
   float kr[REG ? EPL : 1], qr[REG ? EPL : 1];
   const float* kl;   // the lane's first key in LDS
   const float* ql;
-  static __device__ __forceinline__ int off(int i) { return SPLIT ? 8 * VPP * (i / VPP) + (i % VPP) : i; }
+  static __device__ __forceinline__ int off(int i) { return SPLIT ? GW * VPP * (i / VPP) + (i % VPP) : i; }
   __device__ __forceinline__ float k(int i) const {
     if constexpr (REG) return kr[i];
     else return kl[off(i)];
@@ -154,11 +154,11 @@ struct KQ {
 };
 
 // Key of element i of a lane's slice: contiguous (k0 + i), or, for rows
-// split into 128-byte pieces of VPP values (SPLIT), 8 VPP (i / VPP) + VPP
-// lane + i % VPP.
-template <int EPL, bool SPLIT, int VPP = 8>
+// split into pieces of GW x 16 bytes (SPLIT; GW lanes per row, VPP values
+// per 16 bytes), GW VPP (i / VPP) + VPP lane + i % VPP.
+template <int EPL, bool SPLIT, int VPP = 8, int GW = 8>
 __device__ __forceinline__ int slice_key(int lane8, int i) {
-  return SPLIT ? 8 * VPP * (i / VPP) + VPP * lane8 + (i % VPP) : lane8 * EPL + i;
+  return SPLIT ? GW * VPP * (i / VPP) + VPP * lane8 + (i % VPP) : lane8 * EPL + i;
 }
 
 // Staging of the head's k and q into LDS as fp32 (one conversion per value
@@ -184,7 +184,8 @@ __device__ __forceinline__ void qk_load(const Args& a, uint64_t bh, float (&f)[q
 
 template <int EPL, int LPR, int INBF, bool SPLIT, bool REG, int VPP = 8>
 __device__ __forceinline__ void stage_qk(const Args& a, uint64_t bh, int lane8, float* lds,
-                                         const float (&f)[qk_first<EPL * LPR>()], KQ<EPL, REG, SPLIT, VPP>& kq) {
+                                         const float (&f)[qk_first<EPL * LPR>()],
+                                         KQ<EPL, REG, SPLIT, VPP, LPR>& kq) {
   constexpr int DK = EPL * LPR;
   constexpr int NF = qk_first<DK>();
 #pragma unroll
@@ -197,13 +198,13 @@ __device__ __forceinline__ void stage_qk(const Args& a, uint64_t bh, int lane8, 
     lds[t] = load_in_scalar<INBF>(src, bh * DK + (uint64_t)(t < DK ? t : t - DK));
   }
   __syncthreads();
-  const int k0 = slice_key<EPL, SPLIT, VPP>(lane8, 0);
+  const int k0 = slice_key<EPL, SPLIT, VPP, LPR>(lane8, 0);
   kq.kl = lds + k0;
   kq.ql = lds + DK + k0;
   if constexpr (REG) {
 #pragma unroll
     for (int i = 0; i < EPL; i += 4) {
-      const int kk = slice_key<EPL, SPLIT, VPP>(lane8, i);
+      const int kk = slice_key<EPL, SPLIT, VPP, LPR>(lane8, i);
       const float4 kv = *reinterpret_cast<const float4*>(lds + kk);
       const float4 qv = *reinterpret_cast<const float4*>(lds + DK + kk);
       kq.kr[i] = kv.x; kq.kr[i + 1] = kv.y; kq.kr[i + 2] = kv.z; kq.kr[i + 3] = kv.w;
@@ -298,7 +299,7 @@ __device__ __forceinline__ void dense_quant_rows(const Args& a, uint8_t* blk, co
       }
     }
   }
-  KQ<EPL, KQREG> kq;
+  KQ<EPL, KQREG, false, 8, LPR> kq;
   stage_qk<EPL, LPR, INBF, false>(a, bh, lane8, lds, qkf, kq);
   float o_row[RPL], s_row[RPL];
 #pragma unroll
@@ -407,26 +408,28 @@ __device__ __forceinline__ void dense_quant_rows(const Args& a, uint8_t* blk, co
   store_row_values<RPL, LPR>(a, ix, wrow0, lane8, o_row, s_row);
 }
 
-// Protected heads of a head map, stored as HP (0 fp32, 1 bf16, 2 fp16).  With
-// 8 lanes per row a row is split into 128-byte pieces, lane j holding bytes
-// 16j + 128i of each (VPP = 16 / value bytes consecutive keys per piece), so
-// every load and store of the wave covers whole cache lines; with 4 lanes per
-// row a lane holds 32 consecutive keys.
+// Protected heads of a head map, stored as HP (0 fp32, 1 bf16, 2 fp16).  A
+// row is split into pieces of 16 LPR bytes, lane j holding bytes 16j + 16 LPR i
+// of each (VPP = 16 / value bytes consecutive keys per 16 bytes): with 8 lanes
+// per row every load and store of the wave covers whole cache lines, with 4
+// half lines.
 template <int HP, int DELTA, int EPL, int LPR, int RPL, int DKEY, int INBF>
 __device__ __forceinline__ void dense_prot_rows_t(const Args& a, uint8_t* blk, const HeadIx& ix, int v0,
                                                   int wrow0, int lane8, float* lds) {
   const uint64_t bh = ix.in;   // inputs and outputs
   constexpr int DK = EPL * LPR;
   constexpr int GPW = 64 / LPR;
-  constexpr bool SPLIT = (LPR == 8);
+  // Rows are split into pieces of LPR x 16 bytes: lane j of a row group holds
+  // bytes 16 j + 16 LPR i, so each load covers whole 16 LPR-byte runs of a
+  // row (whole cache lines with 8 lanes a row, half lines with 4) instead of
+  // one 16-byte piece per line.
+  constexpr bool SPLIT = true;
   constexpr int VB = HP == 0 ? 4 : 2;        // bytes per stored value
   constexpr int VPP = 16 / VB;               // values per 16-byte piece
   constexpr int NW = EPL * VB / 4;           // words per lane and row
   constexpr int NPC = NW / 4;                // 16-byte pieces per lane and row
   // byte offset of the lane's piece i within a row
-  auto piece = [&](int i) -> uint32_t {
-    return SPLIT ? (uint32_t)(128 * i + 16 * lane8) : (uint32_t)(lane8 * EPL * VB + 16 * i);
-  };
+  auto piece = [&](int i) -> uint32_t { return (uint32_t)(16 * LPR * i + 16 * lane8); };
   uint32_t hw[RPL][NW];
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
@@ -450,7 +453,7 @@ __device__ __forceinline__ void dense_prot_rows_t(const Args& a, uint8_t* blk, c
 #pragma unroll
     for (int i = 0; i < EPL; i += 4) {
       const float4 t =
-          *reinterpret_cast<const float4*>(a.decay + (uint64_t)bh * DK + slice_key<EPL, SPLIT, VPP>(lane8, i));
+          *reinterpret_cast<const float4*>(a.decay + (uint64_t)bh * DK + slice_key<EPL, SPLIT, VPP, LPR>(lane8, i));
       df[i] = t.x; df[i + 1] = t.y; df[i + 2] = t.z; df[i + 3] = t.w;
     }
   } else {
@@ -460,7 +463,7 @@ __device__ __forceinline__ void dense_prot_rows_t(const Args& a, uint8_t* blk, c
   float qkf[qk_first<DK>()];
   qk_load<DK, INBF>(a, bh, qkf);
   if (a.load_prio) __builtin_amdgcn_s_setprio(0);
-  KQ<EPL, false, SPLIT, VPP> kq;   // one pass over the rows' k and q: read from LDS where used
+  KQ<EPL, false, SPLIT, VPP, LPR> kq;   // one pass over the rows' k and q: read from LDS where used
   stage_qk<EPL, LPR, INBF, SPLIT, false, VPP>(a, bh, lane8, lds, qkf, kq);
   auto value = [&](int r, int i) -> float {
     if constexpr (HP == 0) return __uint_as_float(hw[r][i]);
