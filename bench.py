@@ -186,13 +186,32 @@ class Timer:
             bad |= f(h, self.tref[i % self.R], self.iref[i % self.P], self.optr, i, stream_ptr)
         return bad
 
-    def run(self, warmup, steps, graph=False):
-        """Returns (ms per step from events, host enqueue ms per step, steps timed)."""
+    def prewarm(self, ms):
+        """Steps back to back for at least `ms` of wall time before the warmup:
+        an idle MI355X takes tens of milliseconds of sustained load to reach its
+        working clocks (a step's duration falls by about a quarter over the first
+        ~50 ms), and a decode server runs steps back to back.  Returns the
+        number of launches (step indices 0 .. n - 1; warmup and timed steps
+        follow them)."""
+        import torch
+        from quantized_recurrent_state_qstate_amd import _lib
+        sp = torch.cuda.current_stream().cuda_stream
+        n, t0 = 0, time.perf_counter()
+        while (time.perf_counter() - t0) * 1e3 < ms:
+            if self.enqueue(n, 64, sp):
+                _lib.check(-4, "prewarm")
+            n += 64
+            torch.cuda.synchronize()
+        return n
+
+    def run(self, warmup, steps, graph=False, first=0):
+        """Returns (ms per step from events, host enqueue ms per step, steps
+        timed); step indices start at `first`."""
         import torch
         from quantized_recurrent_state_qstate_amd import _lib
         stream = torch.cuda.current_stream()
         sp = stream.cuda_stream
-        if self.enqueue(0, warmup, sp):
+        if self.enqueue(first, warmup, sp):
             _lib.check(-4, "warmup")
         torch.cuda.synchronize()
         g = None
@@ -203,7 +222,7 @@ class Timer:
             cap = torch.cuda.Stream()
             with torch.cuda.stream(cap):
                 with torch.cuda.graph(g, stream=cap):
-                    if self.enqueue(warmup, G, torch.cuda.current_stream().cuda_stream):
+                    if self.enqueue(first + warmup, G, torch.cuda.current_stream().cuda_stream):
                         _lib.check(-4, "capture")
             torch.cuda.synchronize()
             reps = max(1, steps // G)
@@ -220,7 +239,7 @@ class Timer:
             for _ in range(reps):
                 g.replay()
         else:
-            bad = self.enqueue(warmup, steps, sp)
+            bad = self.enqueue(first + warmup, steps, sp)
         e1.record(stream)
         c1 = time.perf_counter()
         torch.cuda.synchronize()
@@ -261,14 +280,15 @@ def fp32_state_context(w, args, dev, pool, out, ms_ours, ours_state_bytes):
     return res
 
 
-TRACE_NOTE = ("launch order of the step kernel: the headline's warmup then timed launches, then (with the "
-              "context runs) the hot-mode and the FP32-state runs, each warmup then timed")
+TRACE_NOTE = ("launch order of the step kernel: the headline's prewarm, warmup and timed launches, then (with "
+              "the context runs) the hot-mode and the FP32-state runs, each warmup then timed")
 
 
-def trace_summary(path, warmup, steps, kernel_hint="k_step_"):
+def trace_summary(path, skip, steps, kernel_hint="k_step_"):
     """Markdown summary of a rocprofv3 kernel trace (csv) of a bench command:
     per kernel calls and durations, and for the step kernel the headline run's
-    timed launches alone (launches warmup .. warmup + steps - 1 of it)."""
+    timed launches alone (launches skip .. skip + steps - 1 of it, skip = the
+    bench line's prewarm launches plus its warmup)."""
     import csv
     import glob
     files = glob.glob(os.path.join(path, "**", "*kernel_trace.csv"), recursive=True)
@@ -291,8 +311,8 @@ def trace_summary(path, warmup, steps, kernel_hint="k_step_"):
     step = [n for n in per if kernel_hint in n]
     if step:
         name = max(step, key=lambda n: len(per[n]))
-        d = per[name][warmup:warmup + steps]
-        lines += ["", f"Headline run of `{name[:90]}` (launches {warmup} .. {warmup + steps - 1} in launch order, "
+        d = per[name][skip:skip + steps]
+        lines += ["", f"Headline run of `{name[:90]}` (launches {skip} .. {skip + steps - 1} in launch order, "
                       f"the timed ones): {len(d)} launches, average {sum(d) / max(len(d), 1):.0f} ns, "
                       f"min {min(d)} ns, max {max(d)} ns."]
     return "\n".join(lines)
@@ -315,14 +335,19 @@ def main():
                     help="override the workload's rounding mode")
     ap.add_argument("--map-frac", type=float, default=None,
                     help="override the fraction of protected heads or channels")
+    ap.add_argument("--prewarm-ms", type=float, default=200.0,
+                    help="untimed steps back to back for this long before the warmup (working clocks)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run one device copy of this size (for counter calibration)")
+    ap.add_argument("--trace-skip", type=int, default=None, metavar="N",
+                    help="with --trace-summary: step-kernel launches before the timed ones (prewarm + warmup)")
     ap.add_argument("--trace-summary", default=None, metavar="DIR",
                     help="print the summary of a rocprofv3 kernel trace of a bench command (no GPU) and exit")
     args = ap.parse_args()
 
     if args.trace_summary:
-        print(trace_summary(args.trace_summary, args.warmup, args.steps))
+        skip = args.warmup if args.trace_skip is None else args.trace_skip
+        print(trace_summary(args.trace_summary, skip, args.steps))
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -357,9 +382,12 @@ def main():
     pool = input_pool(w, dev)
     out = torch.empty(w.B, w.H, w.dv, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
-    print(f"[bench] {TRACE_NOTE}; warmup {args.warmup}, timed {args.steps}", file=sys.stderr, flush=True)
-
-    ms, host_ms, args.steps = Timer(qs, states, pool, out).run(args.warmup, args.steps, args.graph)
+    timer = Timer(qs, states, pool, out)
+    n_pre = timer.prewarm(args.prewarm_ms) if args.prewarm_ms > 0 else 0
+    print(f"[bench] {TRACE_NOTE}; prewarm {n_pre}, warmup {args.warmup}, timed {args.steps}",
+          file=sys.stderr, flush=True)
+    ms, host_ms, args.steps = timer.run(args.warmup, args.steps, args.graph, first=n_pre)
+    del timer
     steps_per_s = 1e3 / ms
     state_gbps = alg["state_rw"] / (ms * 1e-3) / 1e9
     achieved = alg["total"] / (ms * 1e-3) / 1e9
@@ -426,6 +454,9 @@ def main():
                                     f"(one launch per step, after {args.warmup} untimed)",
                      "kernel": qs.kernel_name},
         "host_enqueue_ms_per_step": round(host_ms, 4),
+        "prewarm": {"ms": args.prewarm_ms, "launches": n_pre,
+                    "note": "untimed steps back to back before the warmup, so the timed steps run at the "
+                            "GPU's working clocks"},
     }
     if context is not None:
         res["context"] = context
