@@ -161,6 +161,52 @@ __device__ __forceinline__ float pick(const float (&p)[R], int j) {
   return x;
 }
 
+// A buffer row of R entries from element index i (R * entry bytes a multiple
+// of 16 and the row 16-byte aligned): fp32, or bf16 (BF) widened exactly.
+template <int R, int BF>
+__device__ __forceinline__ void load_buf_row(const float* base, uint64_t i, float (&x)[R]) {
+  if constexpr (BF) {
+    const u32x4_t* p = reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(base) + i);
+#pragma unroll
+    for (int c = 0; c < R / 8; ++c) {
+      const u32x4_t t = p[c];
+      const uint32_t w[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[8 * c + 2 * e] = __uint_as_float(w[e] << 16);
+        x[8 * c + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+      }
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(base + i);
+#pragma unroll
+    for (int c = 0; c < R / 4; ++c) {
+      const float4 t = p[c];
+      x[4 * c] = t.x; x[4 * c + 1] = t.y; x[4 * c + 2] = t.z; x[4 * c + 3] = t.w;
+    }
+  }
+}
+// The same row stored; bf16 entries are already bf16 values (the low half of
+// each pattern is zero), so keeping the high half is exact.
+template <int R, int BF>
+__device__ __forceinline__ void store_buf_row(float* base, uint64_t i, const float (&x)[R]) {
+  if constexpr (BF) {
+    u32x4_t* p = reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(base) + i);
+#pragma unroll
+    for (int c = 0; c < R / 8; ++c) {
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        w[e] = (__float_as_uint(x[8 * c + 2 * e]) >> 16) | (__float_as_uint(x[8 * c + 2 * e + 1]) & 0xFFFF0000u);
+      p[c] = u32x4_t{w[0], w[1], w[2], w[3]};
+    }
+  } else {
+    float4* p = reinterpret_cast<float4*>(base + i);
+#pragma unroll
+    for (int c = 0; c < R / 4; ++c) p[c] = make_float4(x[4 * c], x[4 * c + 1], x[4 * c + 2], x[4 * c + 3]);
+  }
+}
+
 }  // namespace
 
 // Register budget: 5 waves per SIMD for int4 codes with nearest rounding at
@@ -241,10 +287,15 @@ __attribute__((amdgpu_waves_per_eu(lrb_min_waves<QB, RND, RANK, DELTA, DKEY>(), 
   }
   const int tv = tid < dv ? tid : 0, tk = tid < DK ? tid : 0;
   float Wr[RANK], Ur[RANK];
+  if (r == RANK) {   // uniform: whole 16-byte-aligned rows of RANK entries, vector loads
+    load_buf_row<RANK, BF>(a.W, woff + (uint64_t)tv * RANK, Wr);
+    load_buf_row<RANK, BF>(a.U, uoff + (uint64_t)tk * RANK, Ur);
+  } else {
 #pragma unroll
-  for (int j = 0; j < RANK; ++j) {
-    Wr[j] = j < r ? ld_buf(a.W, woff + (uint64_t)(tv * r + j)) : 0.0f;   // j < r: uniform
-    Ur[j] = j < r ? ld_buf(a.U, uoff + (uint64_t)(tk * r + j)) : 0.0f;
+    for (int j = 0; j < RANK; ++j) {
+      Wr[j] = j < r ? ld_buf(a.W, woff + (uint64_t)(tv * r + j)) : 0.0f;   // j < r: uniform
+      Ur[j] = j < r ? ld_buf(a.U, uoff + (uint64_t)(tk * r + j)) : 0.0f;
+    }
   }
   const uint64_t trow = bh * (uint64_t)dv + (uint64_t)tv;
   const uint64_t tkey = bh * DK + (uint64_t)tk;
@@ -450,9 +501,13 @@ __attribute__((amdgpu_waves_per_eu(lrb_min_waves<QB, RND, RANK, DELTA, DKEY>(), 
   }
   // write the buffer back
   if (tid < DK) {
+    if (r == RANK) {
+      store_buf_row<RANK, BF>(a.U, uoff + (uint64_t)tid * RANK, Ur);
+    } else {
 #pragma unroll
-    for (int j = 0; j < RANK; ++j)
-      if (j < r) st_buf(a.U, uoff + (uint64_t)(tid * r + j), Ur[j]);
+      for (int j = 0; j < RANK; ++j)
+        if (j < r) st_buf(a.U, uoff + (uint64_t)(tid * r + j), Ur[j]);
+    }
     kl[tid] = kk;
     ql[tid] = qq;
     dl[tid] = dd;
