@@ -518,6 +518,16 @@ EDGE = {
     "lrb_bf16_kda_int4_sr8_bdr": dict(kind="delta", decay_mode="key", dk=128, dv=64, H=2, B=2, qbits=4,
                                       sr_bits=8, bdr=True, lrb_rank=4, lrb_period=2,
                                       scale_dtype="bf16", lrb_dtype="bf16"),
+    # nearest rounding in the buffer kernel without stochastic bits: int8 codes
+    # (low byte of the rounding add), int4 without BDR, rank bound 16, and the
+    # bf16 layout at int8
+    "lrb_int8_rtn_bdr": dict(kind="additive", decay_mode="key", dk=128, dv=72, H=2, B=2, qbits=8,
+                             rounding="nearest", bdr=True, lrb_rank=8, lrb_period=3),
+    "lrb_delta_int4_rtn_plain_r16": dict(kind="delta", decay_mode="head", dk=128, dv=64, H=2, B=2, qbits=4,
+                                         rounding="nearest", lrb_rank=16, lrb_period=3),
+    "lrb_bf16_int8_rtn_dk64": dict(kind="additive", decay_mode="head", dk=64, dv=40, H=2, B=2, qbits=8,
+                                   rounding="nearest", bdr=True, lrb_rank=8, lrb_period=2,
+                                   scale_dtype="bf16", lrb_dtype="bf16"),
     # scale groups other than rows: one per key channel, one per head
     "axis_key_additive_sr": dict(kind="additive", decay_mode="key", dk=128, dv=64, H=2, B=2, qbits=8,
                                  scale_axis="key"),
