@@ -463,6 +463,7 @@ def main():
     if not args.no_cpu_baseline:
         threads = args.cpu_threads or min(16, os.cpu_count() or 1)
         res["cpu_baseline"] = cpu_baseline(w, m, args.cpu_budget, threads)
+        res["cpu_baseline"]["state_GBps"] = round(res["cpu_baseline"]["value"] * alg["state_rw"] / 1e9, 3)
     print(json.dumps(res), flush=True)
 
 
