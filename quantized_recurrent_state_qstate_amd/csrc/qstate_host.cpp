@@ -62,7 +62,7 @@ struct Plan {
   int keymap_rpl = 1;
   int dense_threads = 256;
   uint32_t lds = 0;
-  uint64_t prot_mask = 0;       // dense family: protected heads
+  uint64_t prot_mask[4] = {0, 0, 0, 0};   // dense family: protected heads (H <= 256)
   uint64_t code_hblk = 0, hp_hblk = 0;
 };
 
@@ -220,11 +220,11 @@ qs_status make_plan(const qstate_config* c, Plan* p) {
     p->keymap_rpl = krpl;
     const int rows = 256 / p->dense_lpr * krpl;
     p->row_chunks = (dv + rows - 1) / rows;
-  } else if (c->map_mode == QS_MAP_KEY || (c->map_mode == QS_MAP_HEAD && H > 64)) {
+  } else if (c->map_mode == QS_MAP_KEY || (c->map_mode == QS_MAP_HEAD && H > 256)) {
     // key-channel maps (other than the 16-bit dk 128 ones above) and head
-    // maps over more than 64 heads run the LDS-staged kernel; the dense
+    // maps over more than 256 heads run the LDS-staged kernel; the dense
     // kernel handles whole-head maps with 16-bit or fp32 protected heads
-    // (addressed from a 64-bit head mask)
+    // (addressed from a 256-bit head mask in the kernel arguments)
     p->family = qs::kFamMixed;
     uint64_t mx = 0;
     for (int h = 0; h < H; ++h) {
@@ -236,8 +236,8 @@ qs_status make_plan(const qstate_config* c, Plan* p) {
     (void)any_mixed;
   } else {
     p->family = qs::kFamDense;
-    for (int h = 0; h < H && h < 64; ++h)
-      if (p->head_type[h] == qs::kHeadProt) p->prot_mask |= 1ull << h;
+    for (int h = 0; h < H && h < 256; ++h)
+      if (p->head_type[h] == qs::kHeadProt) p->prot_mask[h >> 6] |= 1ull << (h & 63);
     p->code_hblk = round16((uint64_t)dv * code_row((uint64_t)dk, (uint64_t)c->qbits));
     p->hp_hblk = round16((uint64_t)dv * hp_row((uint64_t)dk, hpb));
   }
@@ -319,7 +319,7 @@ qs::Args base_args(const qstate_handle* h, const qstate_tensors* st) {
   a.keymap_rpl = h->plan.keymap_rpl;
   a.load_prio = env_int("QSTATE_LOAD_PRIO", 1) ? 1 : 0;
   a.dense_threads = h->plan.dense_threads;
-  a.prot_mask = h->plan.prot_mask;
+  for (int w = 0; w < 4; ++w) a.prot_mask[w] = h->plan.prot_mask[w];
   a.code_hblk = h->plan.code_hblk;
   a.hp_hblk = h->plan.hp_hblk;
   a.hp_dtype = c.hp_dtype == QS_FP32 ? 0 : (c.hp_dtype == QS_BF16 ? 1 : 2);

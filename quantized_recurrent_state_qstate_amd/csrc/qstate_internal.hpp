@@ -51,7 +51,7 @@ struct Args {
   int32_t keymap_eh;   // key-map kernel: protected slots per lane (2, 4, 8, 16)
   int32_t keymap_rpl;  // key-map kernel: rows per lane group (1, 2)
   int32_t load_prio;   // dense kernel: raised wave priority until the loads are issued
-  uint64_t prot_mask;  // dense kernel: bit h set = head h protected (H <= 64 with a head map)
+  uint64_t prot_mask[4];  // dense kernel: bit h % 64 of word h / 64 set = head h protected (H <= 256)
   uint64_t code_hblk;  // dense kernel: bytes of one quantized head's code block
   uint64_t hp_hblk;    // dense kernel: bytes of one protected head's block
   int32_t hp_dtype;    // 0 fp32, 1 bf16, 2 fp16

@@ -568,11 +568,24 @@ void k_step_dense(const Args a) {
   const int wrow0 = ((int)chunk * ng + (g / GPW) * GPW) * RPL;
   const int v0 = wrow0 + g % GPW;
   __shared__ __align__(16) float lds[2 * EPL * LPR];
-  // head storage from the protected-head mask: no table lookup stands
-  // between the launch and the state loads
-  const uint64_t below = (h >= 64u) ? 0ull : (a.prot_mask & ((1ull << h) - 1ull));
-  const uint32_t np = (uint32_t)__builtin_popcountll(below);
-  const bool prot = (h < 64u) && ((a.prot_mask >> h) & 1ull);
+  // head storage from the protected-head mask (bit h % 64 of word h / 64;
+  // a head map here has at most 256 heads, and heads past 256 are
+  // quantized): no table lookup stands between the launch and the state
+  // loads, only scalar bit counts over the kernel arguments
+  uint32_t np = 0;   // protected heads below h
+  bool prot = false;
+#pragma unroll
+  for (uint32_t w = 0; w < 4u; ++w) {
+    const uint64_t m = a.prot_mask[w];
+    const uint32_t lo = 64u * w;
+    if (h >= lo + 64u) {
+      np += (uint32_t)__builtin_popcountll(m);
+    } else if (h >= lo) {
+      const uint32_t bit = h - lo;
+      np += (uint32_t)__builtin_popcountll(m & ((1ull << bit) - 1ull));
+      prot = ((m >> bit) & 1ull) != 0ull;
+    }
+  }
   if (!prot) {
     uint8_t* blk = a.codes + (uint64_t)bs * a.code_bstride + (uint64_t)(h - np) * a.code_hblk;
     dense_quant_rows<QB, RND, DELTA, EPL, LPR, RPL, BDR, DKEY, INBF>(a, blk, ix, v0, wrow0, lane8, lds);

@@ -528,6 +528,15 @@ EDGE = {
     "lrb_bf16_int8_rtn_dk64": dict(kind="additive", decay_mode="head", dk=64, dv=40, H=2, B=2, qbits=8,
                                    rounding="nearest", bdr=True, lrb_rank=8, lrb_period=2,
                                    scale_dtype="bf16", lrb_dtype="bf16"),
+    # head maps over more than 64 heads: the dense kernel's 256-bit head mask
+    # (words 0-1, and 0-3), and past 256 heads the LDS-staged kernel
+    "headmap_h96_bf16_sr": dict(kind="additive", decay_mode="head", dk=128, dv=40, H=96, B=2, qbits=8,
+                                map_mode="head", hp_dtype="bf16", kernel="k_step_dense"),
+    "headmap_h200_fp32_delta_int4": dict(kind="delta", decay_mode="key", dk=64, dv=24, H=200, B=1, qbits=4,
+                                         rounding="nearest", bdr=True, map_mode="head", hp_dtype="fp32",
+                                         kernel="k_step_dense"),
+    "headmap_h260_fp16_mixed": dict(kind="additive", decay_mode="head", dk=64, dv=8, H=260, B=1, qbits=8,
+                                    map_mode="head", hp_dtype="fp16", kernel="k_step_mixed"),
     # scale groups other than rows: one per key channel, one per head
     "axis_key_additive_sr": dict(kind="additive", decay_mode="key", dk=128, dv=64, H=2, B=2, qbits=8,
                                  scale_axis="key"),
@@ -565,6 +574,7 @@ def test_edge_cases(case, monkeypatch):
     lanes = kw.pop("lanes", None)         # lanes per row of the dense kernel, when not the default
     if lanes is not None:
         monkeypatch.setenv("QSTATE_DENSE_LPR", str(lanes))
+    kernel = kw.pop("kernel", None)       # the kernel family the plan must choose, when stated
     krows = kw.pop("keymap_rows", None)   # rows per lane group of the key-map kernel
     if krows is not None:
         monkeypatch.setenv("QSTATE_KEYMAP_RPL", str(krows))
@@ -584,6 +594,8 @@ def test_edge_cases(case, monkeypatch):
     okw["rounding"] = "rtn" if lkw["rounding"] == "nearest" else "sr"
     ocfg = oracle.Cfg(map=m, seed=0x1234_5678_9ABC, **okw)
     qs = QState(lcfg)
+    if kernel is not None:
+        assert qs.kernel_name.startswith(kernel), qs.kernel_name
     st = qs.new_state()
     exact = kw["kind"] == "additive" and not kw.get("lrb_rank")
     _log(f"[parity] edge {case}")
