@@ -62,6 +62,7 @@ struct Plan {
   int keymap_rpl = 1;
   int dense_threads = 256;
   uint32_t lds = 0;
+  uint32_t rbuf = 0;            // mixed family: LDS for random bits by slot
   uint64_t prot_mask[4] = {0, 0, 0, 0};   // dense family: protected heads (H <= 256)
   uint64_t code_hblk = 0, hp_hblk = 0;
 };
@@ -203,10 +204,11 @@ qs_status make_plan(const qstate_config* c, Plan* p) {
     // one workgroup per head; the buffer and the head's vectors live in
     // static LDS
     p->family = qs::kFamLrb;
-  } else if (c->map_mode == QS_MAP_KEY && c->hp_dtype != QS_FP32 && dk == 128) {
-    // key-channel maps with 16-bit protected values: rows in storage order,
-    // 8 lanes per row, each with 16 code slots and keymap_eh protected
-    // slots, keymap_rpl rows per lane group (4 lanes per row measured slower)
+  } else if (c->map_mode == QS_MAP_KEY && dk == 128) {
+    // key-channel maps at dk 128 (16-bit or fp32 protected values): rows in
+    // storage order, 8 lanes per row, each with 16 code slots and keymap_eh
+    // protected slots, keymap_rpl rows per lane group (4 lanes per row
+    // measured slower)
     p->family = qs::kFamKeymap;
     p->dense_lpr = 8;
     p->dense_rpl = 1;
@@ -221,7 +223,7 @@ qs_status make_plan(const qstate_config* c, Plan* p) {
     const int rows = 256 / p->dense_lpr * krpl;
     p->row_chunks = (dv + rows - 1) / rows;
   } else if (c->map_mode == QS_MAP_KEY || (c->map_mode == QS_MAP_HEAD && H > 256)) {
-    // key-channel maps (other than the 16-bit dk 128 ones above) and head
+    // key-channel maps at dk 64 and 256 and head
     // maps over more than 256 heads run the LDS-staged kernel; the dense
     // kernel handles whole-head maps with 16-bit or fp32 protected heads
     // (addressed from a 256-bit head mask in the kernel arguments)
@@ -233,6 +235,15 @@ qs_status make_plan(const qstate_config* c, Plan* p) {
       mx = std::max(mx, cb + hb);
     }
     p->lds = (uint32_t)std::min<uint64_t>(mx, 0xFFFFFFFFu);
+    // stochastic rounding of mixed heads: each lane draws the random bits of
+    // a contiguous slot run (one Philox block per 8 or 16 slots) into LDS,
+    // 16 bits per slot for the 32 row groups, and gathers its own slots'
+    // bits from there; when that does not fit, one block per element
+    const uint64_t rb = c->rounding == QS_ROUND_STOCHASTIC ? 32ull * (uint64_t)dk * 2ull : 0ull;
+    if (rb > 0 && (uint64_t)p->lds + rb <= kMaxLds) {
+      p->rbuf = (uint32_t)rb;
+      p->lds += (uint32_t)rb;
+    }
     (void)any_mixed;
   } else {
     p->family = qs::kFamDense;
@@ -336,6 +347,7 @@ qs::Args base_args(const qstate_handle* h, const qstate_tensors* st) {
   a.seed_lo = (uint32_t)c.seed;
   a.seed_hi = (uint32_t)(c.seed >> 32);
   a.mixed_lds = h->plan.lds;
+  a.mixed_rbuf = h->plan.rbuf;
   a.bf16_layout = c.lrb_dtype == QS_BF16 ? 1 : 0;
   a.scale_axis = c.scale_axis;
   a.nslots = c.B;

@@ -67,6 +67,7 @@ struct Args {
   uint32_t seed_lo, seed_hi;
   uint32_t step_lo, step_hi;
   uint32_t mixed_lds;  // mixed kernel: dynamic LDS bytes
+  uint32_t mixed_rbuf; // mixed kernel: bytes of LDS for random bits by slot (0: one Philox block per element)
   int32_t bf16_layout; // scales and low-rank buffer factors stored as bf16 (LRB only)
   int32_t scale_axis;  // scale groups: 0 rows (value axis), 1 columns (key axis), 2 the head
   // batched entry point: batch element b reads its inputs and writes its

@@ -1,11 +1,11 @@
-// Step kernel for key-channel precision maps with 16-bit protected storage
-// (decay-based mixed precision per channel, abstract of "Quantizing
-// Recurrent Language Models Is Easier Than You Think").
+// Step kernel for key-channel precision maps at dk 128, protected storage
+// 16-bit or fp32 (decay-based mixed precision per channel, abstract of
+// "Quantizing Recurrent Language Models Is Easier Than You Think").
 //
 // A row of a mixed head is stored as two packed rows: the codes of its nq
 // quantized channels in ascending key order (slot j = the j-th quantized
-// channel) and the 16-bit values of its nhp protected channels, each row
-// padded to 4 bytes.  The kernel works in that storage order instead of key
+// channel) and the 16-bit or fp32 values of its nhp protected channels, each
+// row padded to 4 bytes.  The kernel works in that storage order instead of key
 // order: LPR lanes own a row, lane l holding code slots [l*EPL, l*EPL+EPL) and
 // protected slots [l*EH, l*EH+EH), so every lane reads and writes
 // consecutive dwords of both rows and runs the dense kernel's arithmetic on
@@ -115,14 +115,17 @@ __device__ __forceinline__ void store_dwords(uint8_t* p, uint32_t nbytes, const 
 // so each state access of the wave covers one contiguous stretch; the
 // workgroup's per-row outputs and scales are collected in LDS and stored as
 // whole cache lines.
-template <int QB, int RND, int DELTA, int EPL, int LPR, int EH, int BDR, int DKEY, int RPL, int INBF>
+// HP4: protected values stored as fp32 (one dword per slot), else 16-bit
+// (bf16 or fp16, two slots per dword).
+template <int QB, int RND, int DELTA, int EPL, int LPR, int EH, int BDR, int DKEY, int RPL, int INBF, int HP4>
 __global__ __launch_bounds__(256) void k_step_keymap(const Args a) {
   constexpr int DK = EPL * LPR;
   constexpr int GPW = 64 / LPR;            // row groups per wave
   constexpr int RW = 256 / LPR * RPL;      // rows per workgroup
   constexpr int SRB = sr_bits_of<RND>();
   constexpr int CW = EPL * QB / 32;        // code words per lane and row
-  constexpr int HW = EH / 2;               // 16-bit value words per lane and row
+  constexpr int HPB = HP4 ? 4 : 2;         // bytes per protected value
+  constexpr int HW = EH * HPB / 4;         // protected-value words per lane and row
   static_assert(EH % 2 == 0 && EH >= 2, "protected slots come in dword pairs");
   static_assert(DK <= 256, "one key per thread in the slot permutation");
   if (a.load_prio) __builtin_amdgcn_s_setprio(3);   // raised until the loads are issued
@@ -153,12 +156,12 @@ __global__ __launch_bounds__(256) void k_step_keymap(const Args a) {
   const uint64_t hoff_h = ((cu64_p)a.t.hp_off)[h];
   const int nhp = DK - nq;
   const uint32_t rq = code_row_bytes(nq, QB);
-  const uint32_t rh = hp_row_bytes(nhp, 2);
+  const uint32_t rh = hp_row_bytes(nhp, HPB);
   const uint8_t* cblk = a.codes + (uint64_t)bs * a.code_bstride + coff_h;
   const uint8_t* hblk = a.hp + (uint64_t)bs * a.hp_bstride + hoff_h;
 
   // this lane's byte ranges in the two rows, and how many of them exist
-  constexpr uint32_t CB = EPL * QB / 8, HB = EH * 2;
+  constexpr uint32_t CB = EPL * QB / 8, HB = EH * HPB;
   const uint32_t coff = (uint32_t)lane * CB, hoff = (uint32_t)lane * HB;
   const uint32_t cvalid = rq > coff ? (rq - coff < CB ? rq - coff : CB) : 0u;
   const uint32_t hvalid = rh > hoff ? (rh - hoff < HB ? rh - hoff : HB) : 0u;
@@ -227,7 +230,7 @@ __global__ __launch_bounds__(256) void k_step_keymap(const Args a) {
   uint32_t cmask[CW], hmask[HW];
   {
     const int cbits = min(max(nq - lane * EPL, 0), EPL) * QB;
-    const int hbits = min(max(nhp - lane * EH, 0), EH) * 16;
+    const int hbits = min(max(nhp - lane * EH, 0), EH) * 8 * HPB;
 #pragma unroll
     for (int i = 0; i < CW; ++i) {
       const int b = cbits - 32 * i;
@@ -270,6 +273,7 @@ __global__ __launch_bounds__(256) void k_step_keymap(const Args a) {
     else return (float)((int32_t)(cw[r][i >> 3] << (28 - 4 * (i & 7))) >> 28);
   };
   auto hp_at = [&](int i) -> float {
+    if constexpr (HP4) return __uint_as_float(hw[r][i]);
     const uint32_t bits = (hw[r][i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
     return is_bf16 ? bf16_bits_to_f32(bits) : f16_bits_to_f32(bits);
   };
@@ -293,7 +297,7 @@ __global__ __launch_bounds__(256) void k_step_keymap(const Args a) {
     u = beta * vin[r];
   }
 
-  // protected slots: update, readout share, 16-bit store
+  // protected slots: update, readout share, store (16-bit: rounded to nearest even)
   float o = 0.0f;
   {
     float sp[EH];
@@ -304,8 +308,10 @@ __global__ __launch_bounds__(256) void k_step_keymap(const Args a) {
     }
     uint32_t ow[HW > 0 ? HW : 1];
 #pragma unroll
-    for (int i = 0; i < HW; ++i)
-      ow[i] = is_bf16 ? pack_bf16x2(sp[2 * i], sp[2 * i + 1]) : pack_f16x2(sp[2 * i], sp[2 * i + 1]);
+    for (int i = 0; i < HW; ++i) {
+      if constexpr (HP4) ow[i] = __float_as_uint(sp[i]);
+      else ow[i] = is_bf16 ? pack_bf16x2(sp[2 * i], sp[2 * i + 1]) : pack_f16x2(sp[2 * i], sp[2 * i + 1]);
+    }
     store_dwords<HW>(const_cast<uint8_t*>(hblk) + (uint64_t)v * rh + hoff, hvalid, ow);
   }
 
@@ -398,18 +404,24 @@ __global__ __launch_bounds__(256) void k_step_keymap(const Args a) {
 // ---------------------------------------------------------------------------
 namespace {
 
-template <int QB, int RND, int DELTA, int LPR, int EH, int RPL, int INBF>
-hipError_t launch_keymap_eh(const Args& a, hipStream_t s) {
+template <int QB, int RND, int DELTA, int LPR, int EH, int RPL, int INBF, int HP4>
+hipError_t launch_keymap_hp(const Args& a, hipStream_t s) {
   constexpr int EPL = 128 / LPR;
   const dim3 grid((uint32_t)((uint64_t)a.B * (uint64_t)a.H * (uint64_t)a.row_chunks));
   if (a.bdr) {
-    if (a.decay_key) hipLaunchKernelGGL((k_step_keymap<QB, RND, DELTA, EPL, LPR, EH, 1, 1, RPL, INBF>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((k_step_keymap<QB, RND, DELTA, EPL, LPR, EH, 1, 0, RPL, INBF>), grid, dim3(256), 0, s, a);
+    if (a.decay_key) hipLaunchKernelGGL((k_step_keymap<QB, RND, DELTA, EPL, LPR, EH, 1, 1, RPL, INBF, HP4>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_step_keymap<QB, RND, DELTA, EPL, LPR, EH, 1, 0, RPL, INBF, HP4>), grid, dim3(256), 0, s, a);
   } else {
-    if (a.decay_key) hipLaunchKernelGGL((k_step_keymap<QB, RND, DELTA, EPL, LPR, EH, 0, 1, RPL, INBF>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((k_step_keymap<QB, RND, DELTA, EPL, LPR, EH, 0, 0, RPL, INBF>), grid, dim3(256), 0, s, a);
+    if (a.decay_key) hipLaunchKernelGGL((k_step_keymap<QB, RND, DELTA, EPL, LPR, EH, 0, 1, RPL, INBF, HP4>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_step_keymap<QB, RND, DELTA, EPL, LPR, EH, 0, 0, RPL, INBF, HP4>), grid, dim3(256), 0, s, a);
   }
   return hipGetLastError();
+}
+
+template <int QB, int RND, int DELTA, int LPR, int EH, int RPL, int INBF>
+hipError_t launch_keymap_eh(const Args& a, hipStream_t s) {
+  return a.hp_dtype == 0 ? launch_keymap_hp<QB, RND, DELTA, LPR, EH, RPL, INBF, 1>(a, s)
+                         : launch_keymap_hp<QB, RND, DELTA, LPR, EH, RPL, INBF, 0>(a, s);
 }
 
 template <int QB, int RND, int DELTA, int EH>

@@ -644,6 +644,9 @@ __global__ __launch_bounds__(256) void k_step_mixed(const Args a) {
   load_in<EPL>(a.q, a.in_bf16, (uint64_t)bh * DK + k0, qf);
   load_decay<EPL>(a, bh, k0, df);
   const float beta = a.beta ? a.beta[bh] : 1.0f;
+  // random bits by slot (stochastic rounding of a mixed head): this row
+  // group's DK 16-bit values, after the staged blocks
+  uint16_t* rbuf = reinterpret_cast<uint16_t*>(lds + code_bytes + hp_bytes) + rloc * DK;
   __syncthreads();
 
   for (int v = rloc; v < a.dv; v += 32) {
@@ -707,6 +710,16 @@ __global__ __launch_bounds__(256) void k_step_mixed(const Args a) {
     if constexpr (RND != 0) {
       if (nq == DK) {
         rand_bits<RND, EPL>(row * DK + (uint64_t)k0, a.seed_lo, a.seed_hi, ix.step_lo, ix.step_hi, rb);
+      } else if (a.mixed_rbuf) {
+        // the values of slots k0 .. k0 + EPL - 1 (element row * DK + slot, as
+        // for a fully quantized head), then each of this lane's elements by
+        // its own slot; the 8 lanes of the row are one wave's, so their LDS
+        // writes land before these reads
+        rand_bits<RND, EPL>(row * DK + (uint64_t)k0, a.seed_lo, a.seed_hi, ix.step_lo, ix.step_hi, rb);
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) rbuf[k0 + i] = (uint16_t)rb[i];
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) rb[i] = (sl[i] & kSlotProt) ? 0u : (uint32_t)rbuf[sl[i] & 0x7FFFu];
       } else {
 #pragma unroll
         for (int i = 0; i < EPL; ++i)

@@ -537,6 +537,16 @@ EDGE = {
                                          kernel="k_step_dense"),
     "headmap_h260_fp16_mixed": dict(kind="additive", decay_mode="head", dk=64, dv=8, H=260, B=1, qbits=8,
                                     map_mode="head", hp_dtype="fp16", kernel="k_step_mixed"),
+    # fp32 protected key channels at dk 128 in the key-map kernel (one dword
+    # per protected slot): few, half and most channels protected
+    "keymap_fp32_delta_dk128": dict(kind="delta", decay_mode="head", dk=128, dv=72, H=3, B=2, qbits=8,
+                                    map_mode="key", hp_dtype="fp32", map_density=0.1, kernel="k_step_keymap"),
+    "keymap_fp32_int4_keydecay_bdr": dict(kind="additive", decay_mode="key", dk=128, dv=40, H=3, B=2, qbits=4,
+                                          bdr=True, map_mode="key", hp_dtype="fp32", map_density=0.5,
+                                          kernel="k_step_keymap"),
+    "keymap_fp32_sr8_dense_map": dict(kind="additive", decay_mode="head", dk=128, dv=24, H=3, B=2, qbits=8,
+                                      sr_bits=8, map_mode="key", hp_dtype="fp32", map_density=0.9,
+                                      kernel="k_step_keymap"),
     # scale groups other than rows: one per key channel, one per head
     "axis_key_additive_sr": dict(kind="additive", decay_mode="key", dk=128, dv=64, H=2, B=2, qbits=8,
                                  scale_axis="key"),
