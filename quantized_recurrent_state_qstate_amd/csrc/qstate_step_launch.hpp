@@ -1,6 +1,6 @@
-// Launchers of the dense and mixed step kernels, templated on qbits and
-// rounding mode; qstate_step_dense.hip and qstate_step_mixed.hip are compiled
-// once per (qbits, rounding) pair so the instantiations build in parallel.
+// Launchers of the dense step kernel, templated on qbits and rounding mode;
+// qstate_step_dense.hip is compiled once per (qbits, rounding) pair so the
+// instantiations build in parallel.
 #pragma once
 #include "qstate_step_kernels.hpp"
 
@@ -46,13 +46,6 @@ hipError_t launch_dense_t(const Args& a, hipStream_t s) {
   }
 }
 
-template <int QB, int RND, int DELTA, int EPL>
-hipError_t launch_mixed_t(const Args& a, hipStream_t s) {
-  const uint64_t grid = (uint64_t)a.B * (uint64_t)a.H;
-  hipLaunchKernelGGL((k_step_mixed<QB, RND, DELTA, EPL>), dim3((uint32_t)grid), dim3(256), a.mixed_lds, s, a);
-  return hipGetLastError();
-}
-
 template <int QB, int RND, int DELTA>
 hipError_t launch_dense_dk(const Args& a, hipStream_t s) {
   switch (a.dk) {
@@ -65,26 +58,11 @@ hipError_t launch_dense_dk(const Args& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-template <int QB, int RND, int DELTA>
-hipError_t launch_mixed_dk(const Args& a, hipStream_t s) {
-  switch (a.dk) {
-    case 64: return launch_mixed_t<QB, RND, DELTA, 8>(a, s);
-    case 128: return launch_mixed_t<QB, RND, DELTA, 16>(a, s);
-    case 256: return launch_mixed_t<QB, RND, DELTA, 32>(a, s);
-  }
-  return hipErrorInvalidValue;
-}
-
 }  // namespace
 
 template <int QB, int RND>
 hipError_t launch_dense(int delta, const Args& a, hipStream_t s) {
   return delta ? launch_dense_dk<QB, RND, 1>(a, s) : launch_dense_dk<QB, RND, 0>(a, s);
-}
-
-template <int QB, int RND>
-hipError_t launch_mixed(int delta, const Args& a, hipStream_t s) {
-  return delta ? launch_mixed_dk<QB, RND, 1>(a, s) : launch_mixed_dk<QB, RND, 0>(a, s);
 }
 
 }  // namespace qs
