@@ -4,7 +4,8 @@ Translation units:
   qstate_step_<family>.hip   one per step-kernel family (dense, mixed, keymap,
                              lrb, grouped), compiled once per (qbits, rounding)
                              pair with -DQS_QB=<8|4> -DQS_RND=<0|1|2> (lrb once
-                             per kind too, -DQS_DELTA=<0|1>): 36 objects that
+                             per kind too, -DQS_DELTA=<0|1>; keymap once per
+                             dk, -DQS_DK=<64|128|256>): 48 objects that
                              compile in parallel
   qstate_misc.hip            quantize / dequantize / fill kernels, dispatch
   qstate_host.cpp            the C ABI: validation, planning, launches
@@ -59,6 +60,11 @@ def units():
                 for delta in (0, 1):
                     obj = os.path.join(OBJ, f"qstate_step_{fam}_q{qb}_{RND_NAME[rnd]}_d{delta}.o")
                     out.append((src, [f"-DQS_QB={qb}", f"-DQS_RND={rnd}", f"-DQS_DELTA={delta}"], obj))
+                continue
+            if fam == "keymap":   # one per dk as well
+                for dk in (64, 128, 256):
+                    obj = os.path.join(OBJ, f"qstate_step_{fam}_q{qb}_{RND_NAME[rnd]}_k{dk}.o")
+                    out.append((src, [f"-DQS_QB={qb}", f"-DQS_RND={rnd}", f"-DQS_DK={dk}"], obj))
                 continue
             obj = os.path.join(OBJ, f"qstate_step_{fam}_q{qb}_{RND_NAME[rnd]}.o")
             out.append((src, [f"-DQS_QB={qb}", f"-DQS_RND={rnd}"], obj))
@@ -121,7 +127,7 @@ def build(force: bool = True, verbose: bool = False, jobs: int = 0) -> str:
     todo = [u for u in units() if force or _stale(u[0], u[2])]
     jobs = jobs or min(16, os.cpu_count() or 1)
     # the longest units first: low-rank bypass, then the other step kernels
-    todo.sort(key=lambda u: 0 if "qstate_step_lrb" in u[0] else (1 if "qstate_step_" in u[0] else 2))
+    todo.sort(key=lambda u: 0 if ("qstate_step_lrb" in u[0] or "_k256" in u[2]) else (1 if "qstate_step_" in u[0] else 2))
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
         list(ex.map(lambda u: _compile(u, verbose), todo))
     tmp = LIB + ".tmp"

@@ -204,9 +204,9 @@ qs_status make_plan(const qstate_config* c, Plan* p) {
     // one workgroup per head; the buffer and the head's vectors live in
     // static LDS
     p->family = qs::kFamLrb;
-  } else if (c->map_mode == QS_MAP_KEY && dk == 128) {
-    // key-channel maps at dk 128 (16-bit or fp32 protected values): rows in
-    // storage order, 8 lanes per row, each with 16 code slots and keymap_eh
+  } else if (c->map_mode == QS_MAP_KEY) {
+    // key-channel maps (16-bit or fp32 protected values): rows in storage
+    // order, 8 lanes per row, each with dk/8 code slots and keymap_eh
     // protected slots, keymap_rpl rows per lane group (4 lanes per row
     // measured slower)
     p->family = qs::kFamKeymap;
@@ -222,9 +222,8 @@ qs_status make_plan(const qstate_config* c, Plan* p) {
     p->keymap_rpl = krpl;
     const int rows = 256 / p->dense_lpr * krpl;
     p->row_chunks = (dv + rows - 1) / rows;
-  } else if (c->map_mode == QS_MAP_KEY || (c->map_mode == QS_MAP_HEAD && H > 256)) {
-    // key-channel maps at dk 64 and 256 and head
-    // maps over more than 256 heads run the LDS-staged kernel; the dense
+  } else if (c->map_mode == QS_MAP_HEAD && H > 256) {
+    // head maps over more than 256 heads run the LDS-staged kernel; the dense
     // kernel handles whole-head maps with 16-bit or fp32 protected heads
     // (addressed from a 256-bit head mask in the kernel arguments)
     p->family = qs::kFamMixed;

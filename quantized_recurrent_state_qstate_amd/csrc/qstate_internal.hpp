@@ -91,13 +91,13 @@ enum StepFamily : int { kFamDense = 0, kFamMixed = 1, kFamLrb = 2, kFamKeymap = 
 
 // Launchers.  Step kernels, one launcher per family, instantiated per
 // (qbits, rounding) in qstate_step_<family>.hip (the low-rank-bypass one per
-// kind too); launch_step (qstate_misc.hip) dispatches to them.  Return hipSuccess or the launch error.  `rnd`: 0
+// kind too, the key-map one per dk); launch_step (qstate_misc.hip) dispatches to them.  Return hipSuccess or the launch error.  `rnd`: 0
 // nearest, 1 stochastic 16-bit, 2 stochastic 8-bit.
 template <int QB, int RND>
 hipError_t launch_dense(int delta, const Args& a, hipStream_t s);
 template <int QB, int RND>
 hipError_t launch_mixed(int delta, const Args& a, hipStream_t s);
-template <int QB, int RND>
+template <int QB, int RND, int DK>
 hipError_t launch_keymap(int delta, const Args& a, hipStream_t s);
 template <int QB, int RND, int DELTA>
 hipError_t launch_lrb(const Args& a, hipStream_t s);

@@ -1,5 +1,5 @@
-// Step kernel for key-channel precision maps at dk 128, protected storage
-// 16-bit or fp32 (decay-based mixed precision per channel, abstract of
+// Step kernel for key-channel precision maps (dk 64, 128 or 256), protected
+// storage 16-bit or fp32 (decay-based mixed precision per channel, abstract of
 // "Quantizing Recurrent Language Models Is Easier Than You Think").
 //
 // A row of a mixed head is stored as two packed rows: the codes of its nq
@@ -404,9 +404,10 @@ __global__ __launch_bounds__(256) void k_step_keymap(const Args a) {
 // ---------------------------------------------------------------------------
 namespace {
 
-template <int QB, int RND, int DELTA, int LPR, int EH, int RPL, int INBF, int HP4>
+template <int QB, int RND, int DELTA, int DK, int EH, int RPL, int INBF, int HP4>
 hipError_t launch_keymap_hp(const Args& a, hipStream_t s) {
-  constexpr int EPL = 128 / LPR;
+  constexpr int LPR = 8;
+  constexpr int EPL = DK / LPR;
   const dim3 grid((uint32_t)((uint64_t)a.B * (uint64_t)a.H * (uint64_t)a.row_chunks));
   if (a.bdr) {
     if (a.decay_key) hipLaunchKernelGGL((k_step_keymap<QB, RND, DELTA, EPL, LPR, EH, 1, 1, RPL, INBF, HP4>), grid, dim3(256), 0, s, a);
@@ -418,44 +419,49 @@ hipError_t launch_keymap_hp(const Args& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int QB, int RND, int DELTA, int LPR, int EH, int RPL, int INBF>
+template <int QB, int RND, int DELTA, int DK, int EH, int RPL, int INBF>
 hipError_t launch_keymap_eh(const Args& a, hipStream_t s) {
-  return a.hp_dtype == 0 ? launch_keymap_hp<QB, RND, DELTA, LPR, EH, RPL, INBF, 1>(a, s)
-                         : launch_keymap_hp<QB, RND, DELTA, LPR, EH, RPL, INBF, 0>(a, s);
+  return a.hp_dtype == 0 ? launch_keymap_hp<QB, RND, DELTA, DK, EH, RPL, INBF, 1>(a, s)
+                         : launch_keymap_hp<QB, RND, DELTA, DK, EH, RPL, INBF, 0>(a, s);
 }
 
-template <int QB, int RND, int DELTA, int EH>
+template <int QB, int RND, int DELTA, int DK, int EH>
 hipError_t launch_keymap_rpl(const Args& a, hipStream_t s) {
-  switch (a.keymap_rpl) {
-    case 1: return a.in_bf16 ? launch_keymap_eh<QB, RND, DELTA, 8, EH, 1, 1>(a, s)
-                             : launch_keymap_eh<QB, RND, DELTA, 8, EH, 1, 0>(a, s);
-    case 2: return a.in_bf16 ? launch_keymap_eh<QB, RND, DELTA, 8, EH, 2, 1>(a, s)
-                             : launch_keymap_eh<QB, RND, DELTA, 8, EH, 2, 0>(a, s);
+  if constexpr (EH * 8 > DK) {   // more protected slots than keys: never planned
+    return hipErrorInvalidValue;
+  } else {
+    switch (a.keymap_rpl) {
+      case 1: return a.in_bf16 ? launch_keymap_eh<QB, RND, DELTA, DK, EH, 1, 1>(a, s)
+                               : launch_keymap_eh<QB, RND, DELTA, DK, EH, 1, 0>(a, s);
+      case 2: return a.in_bf16 ? launch_keymap_eh<QB, RND, DELTA, DK, EH, 2, 1>(a, s)
+                               : launch_keymap_eh<QB, RND, DELTA, DK, EH, 2, 0>(a, s);
+    }
+    return hipErrorInvalidValue;
   }
-  return hipErrorInvalidValue;
 }
 
-// dk 128: 8 lanes per row (16 code slots each); keymap_eh protected slots
-// per lane, keymap_rpl (1 or 2) rows per lane group
-template <int QB, int RND, int DELTA>
+// 8 lanes per row (dk/8 code slots each); keymap_eh protected slots per lane,
+// keymap_rpl (1 or 2) rows per lane group
+template <int QB, int RND, int DELTA, int DK>
 hipError_t launch_keymap_t(const Args& a, hipStream_t s) {
   switch (a.keymap_eh) {
-    case 2: return launch_keymap_rpl<QB, RND, DELTA, 2>(a, s);
-    case 4: return launch_keymap_rpl<QB, RND, DELTA, 4>(a, s);
-    case 8: return launch_keymap_rpl<QB, RND, DELTA, 8>(a, s);
-    case 16: return launch_keymap_rpl<QB, RND, DELTA, 16>(a, s);
+    case 2: return launch_keymap_rpl<QB, RND, DELTA, DK, 2>(a, s);
+    case 4: return launch_keymap_rpl<QB, RND, DELTA, DK, 4>(a, s);
+    case 8: return launch_keymap_rpl<QB, RND, DELTA, DK, 8>(a, s);
+    case 16: return launch_keymap_rpl<QB, RND, DELTA, DK, 16>(a, s);
+    case 32: return launch_keymap_rpl<QB, RND, DELTA, DK, 32>(a, s);
   }
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-// dk 128: 8 lanes per row (16 code slots each); keymap_eh protected slots
-// per lane, keymap_rpl (1 or 2) rows per lane group
-template <int QB, int RND>
+// dk 64, 128 or 256: 8 lanes per row (dk/8 code slots each); keymap_eh
+// protected slots per lane, keymap_rpl (1 or 2) rows per lane group
+template <int QB, int RND, int DK>
 hipError_t launch_keymap(int delta, const Args& a, hipStream_t s) {
-  if (a.dk != 128) return hipErrorInvalidValue;
-  return delta ? launch_keymap_t<QB, RND, 1>(a, s) : launch_keymap_t<QB, RND, 0>(a, s);
+  if (a.dk != DK) return hipErrorInvalidValue;
+  return delta ? launch_keymap_t<QB, RND, 1, DK>(a, s) : launch_keymap_t<QB, RND, 0, DK>(a, s);
 }
 
 }  // namespace qs

@@ -279,7 +279,13 @@ hipError_t launch_step_qr(int family, int delta, const Args& a, hipStream_t s) {
   switch (family) {
     case kFamDense: return launch_dense<QB, RND>(delta, a, s);
     case kFamMixed: return launch_mixed<QB, RND>(delta, a, s);
-    case kFamKeymap: return launch_keymap<QB, RND>(delta, a, s);
+    case kFamKeymap:
+      switch (a.dk) {
+        case 64: return launch_keymap<QB, RND, 64>(delta, a, s);
+        case 128: return launch_keymap<QB, RND, 128>(delta, a, s);
+        case 256: return launch_keymap<QB, RND, 256>(delta, a, s);
+      }
+      return hipErrorInvalidValue;
     case kFamLrb: return delta ? launch_lrb<QB, RND, 1>(a, s) : launch_lrb<QB, RND, 0>(a, s);
     case kFamGrouped: return launch_grouped<QB, RND>(delta, a, s);
   }

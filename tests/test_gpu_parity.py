@@ -547,6 +547,16 @@ EDGE = {
     "keymap_fp32_sr8_dense_map": dict(kind="additive", decay_mode="head", dk=128, dv=24, H=3, B=2, qbits=8,
                                       sr_bits=8, map_mode="key", hp_dtype="fp32", map_density=0.9,
                                       kernel="k_step_keymap"),
+    # key maps at dk 64 and 256 in the key-map kernel (8 lanes per row, dk/8
+    # code slots each), up to 32 protected slots per lane (head 2 all protected)
+    "keymap_dk256_bf16_delta": dict(kind="delta", decay_mode="head", dk=256, dv=40, H=3, B=2, qbits=8,
+                                    map_mode="key", hp_dtype="bf16", map_density=0.2, kernel="k_step_keymap"),
+    "keymap_dk256_fp32_int4_sr8": dict(kind="additive", decay_mode="key", dk=256, dv=24, H=3, B=2, qbits=4,
+                                       sr_bits=8, map_mode="key", hp_dtype="fp32", map_density=0.7,
+                                       kernel="k_step_keymap"),
+    "keymap_dk64_int4_rtn_bdr": dict(kind="additive", decay_mode="head", dk=64, dv=48, H=3, B=2, qbits=4,
+                                     rounding="nearest", bdr=True, map_mode="key", hp_dtype="fp16",
+                                     map_density=0.3, kernel="k_step_keymap"),
     # scale groups other than rows: one per key channel, one per head
     "axis_key_additive_sr": dict(kind="additive", decay_mode="key", dk=128, dv=64, H=2, B=2, qbits=8,
                                  scale_axis="key"),
@@ -702,8 +712,10 @@ BATCH_CASES = {
     "dense_delta_4lanes": dict(kind="delta", decay_mode="head", dk=128, dv=128, H=2, qbits=8),
     "keymap_fp16_delta": dict(kind="delta", decay_mode="head", dk=128, dv=72, H=2, qbits=8, map_mode="key",
                               hp_dtype="fp16"),
-    "mixed_fp32_keymap": dict(kind="additive", decay_mode="key", dk=64, dv=48, H=3, qbits=8, map_mode="key",
-                              hp_dtype="fp32"),
+    "keymap_fp32_dk64": dict(kind="additive", decay_mode="key", dk=64, dv=48, H=3, qbits=8, map_mode="key",
+                             hp_dtype="fp32"),
+    "mixed_headmap_h260": dict(kind="additive", decay_mode="head", dk=64, dv=8, H=260, qbits=8,
+                               map_mode="head", hp_dtype="fp16"),
     "lrb_delta_int4": dict(kind="delta", decay_mode="head", dk=128, dv=128, H=2, qbits=4, rounding="nearest",
                            bdr=True, lrb_rank=8, lrb_period=4),
 }

@@ -50,15 +50,27 @@ def test_plan_random_key_maps(qbits, hp):
                                          map=m))
             blocks = np.diff(np.append(o["code_off"], o["code_bstride"])) + \
                 np.diff(np.append(o["hp_off"], o["hp_bstride"]))
-            staged = not (dk == 128 and hp != "fp32")   # other key maps stage a head through LDS
-            try:
-                z = plan(StateConfig(B=3, H=H, dk=dk, dv=dv, qbits=qbits, hp_dtype=hp, map_mode="key", map=m))
-            except _lib.QStateError as e:
-                # a head staged whole through LDS: more than 64 KiB is unsupported
-                assert e.status == _lib.QS_EUNSUPPORTED and staged and blocks.max() > 65536
-                continue
-            assert blocks.max() <= 65536 or not staged
+            # every key map streams rows (no head is staged whole), so any head size plans
+            z = plan(StateConfig(B=3, H=H, dk=dk, dv=dv, qbits=qbits, hp_dtype=hp, map_mode="key", map=m))
             assert (z["codes"], z["scales"], z["hp"]) == (o["codes"], o["scales"], o["hp"])
+            assert blocks.max() > 0
+
+
+@pytest.mark.parametrize("hp", ["bf16", "fp32"])
+def test_plan_head_maps_over_256_heads(hp):
+    """Head maps of up to 256 heads use the streaming kernel's head mask; more
+    heads stage each head whole through LDS, which must fit 64 KiB."""
+    m = (np.arange(300) % 3 == 0).astype(np.uint8)
+    for H, dk, dv, ok in ((256, 256, 256, True), (257, 64, 8, True), (300, 256, 256, False)):
+        cfg = StateConfig(B=2, H=H, dk=dk, dv=dv, qbits=8, hp_dtype=hp, map_mode="head", map=m[:H])
+        o = oracle.layout(oracle.Cfg(B=2, H=H, dk=dk, dv=dv, qbits=8, hp_dtype=hp, map_mode="head", map=m[:H]))
+        if ok:
+            z = plan(cfg)
+            assert (z["codes"], z["scales"], z["hp"]) == (o["codes"], o["scales"], o["hp"])
+        else:
+            with pytest.raises(_lib.QStateError) as e:
+                plan(cfg)
+            assert e.value.status == _lib.QS_EUNSUPPORTED
 
 
 BAD = [
