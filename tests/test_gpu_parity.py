@@ -718,6 +718,12 @@ BATCH_CASES = {
                                map_mode="head", hp_dtype="fp16"),
     "lrb_delta_int4": dict(kind="delta", decay_mode="head", dk=128, dv=128, H=2, qbits=4, rounding="nearest",
                            bdr=True, lrb_rank=8, lrb_period=4),
+    "lrb_bf16_layout_key_decay": dict(kind="additive", decay_mode="key", dk=128, dv=64, H=2, qbits=4,
+                                      rounding="nearest", bdr=True, lrb_rank=8, lrb_period=3, scale_dtype="bf16",
+                                      lrb_dtype="bf16"),
+    "grouped_key_axis_sr": dict(kind="additive", decay_mode="key", dk=64, dv=40, H=3, qbits=8, scale_axis="key"),
+    "grouped_head_delta_int4": dict(kind="delta", decay_mode="head", dk=128, dv=24, H=2, qbits=4,
+                                    rounding="nearest", bdr=True, scale_axis="head"),
 }
 POOL = 6
 BATCH_SLOTS = [5, 1, 3, -1, 0]                       # -1: outside the pool, skipped
