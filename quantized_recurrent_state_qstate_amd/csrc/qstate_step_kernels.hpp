@@ -387,6 +387,26 @@ __device__ __forceinline__ void dense_quant_rows(const Args& a, uint8_t* blk, co
         for (int j = 0; j < CNT / 4; ++j)
           out[(gblk * PER) / 4 + j] = pack4<BYTE>(y[4 * j], y[4 * j + 1], y[4 * j + 2], y[4 * j + 3]);
       }
+    } else if constexpr (QB == 4 && RND != 0 && !BDR) {
+      // int4 with stochastic rounding: y = floor(x 2^SRB + 1/2) + rb holds
+      // the code (two's complement) from bit SRB up, so byte SRB/8 of y is the
+      // code's low byte and its low nibble the stored digit.  Byte permutes
+      // gather that byte of the even and of the odd elements of each 8, and
+      // one masked merge interleaves their nibbles: about one instruction per
+      // element for what took a shift and a shift-add
+      uint32_t rb[EPL];
+      rand_bits<RND, EPL>(row * DK + (uint64_t)k0, a.seed_lo, a.seed_hi, ix.step_lo, ix.step_hi, rb);
+      constexpr int BYTE = SRB / 8;
+#pragma unroll
+      for (int j = 0; j < EPL / 8; ++j) {
+        uint32_t y[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          y[e] = (uint32_t)(cvt_rpi(sp[8 * j + e] * invb) + (int32_t)rb[8 * j + e]);
+        const uint32_t ev = pack4<BYTE>(y[0], y[2], y[4], y[6]);
+        const uint32_t od = pack4<BYTE>(y[1], y[3], y[5], y[7]);
+        out[j] = (ev & 0x0F0F0F0Fu) | ((od << 4) & 0xF0F0F0F0u);
+      }
     } else {
       uint32_t rb[EPL];
       if constexpr (RND != 0)

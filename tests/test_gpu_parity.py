@@ -435,6 +435,10 @@ EDGE = {
     "dv1": dict(kind="delta", decay_mode="head", dk=64, dv=1, H=2, B=3, qbits=8),
     "dk256_int4": dict(kind="additive", decay_mode="head", dk=256, dv=72, H=2, B=2, qbits=4),
     "dk64_int4_sr8": dict(kind="additive", decay_mode="key", dk=64, dv=64, H=2, B=2, qbits=4, sr_bits=8),
+    # int4 with stochastic rounding in the dense kernel at dk 128: 8 bits
+    # (two code words per lane) and the delta rule's 4 lanes per row (four)
+    "int4_sr8_dk128_ragged": dict(kind="additive", decay_mode="key", dk=128, dv=40, H=2, B=2, qbits=4, sr_bits=8),
+    "delta_int4_sr16_4lanes": dict(kind="delta", decay_mode="head", dk=128, dv=40, H=2, B=2, qbits=4),
     "delta_fp32_in": dict(kind="delta", decay_mode="head", dk=128, dv=128, H=2, B=2, in_dtype="fp32"),
     "int4_keymap_bf16": dict(kind="additive", decay_mode="key", dk=128, dv=64, H=3, B=2, qbits=4,
                              map_mode="key", hp_dtype="bf16"),
