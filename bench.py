@@ -334,6 +334,7 @@ def main():
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (default: min(16, cpus))")
     ap.add_argument("--graph", action="store_true", help="replay the launches as one captured HIP graph")
     ap.add_argument("--sr-bits", type=int, default=0, help="override the workload's random bits per element")
+    ap.add_argument("--batch", type=int, default=0, help="override the workload's batch size B")
     ap.add_argument("--rounding", choices=["nearest", "stochastic"], default=None,
                     help="override the workload's rounding mode")
     ap.add_argument("--map-frac", type=float, default=None,
@@ -370,6 +371,8 @@ def main():
         w = w.scaled(rounding=args.rounding)
     if args.map_frac is not None:
         w = w.scaled(map_frac=args.map_frac)
+    if args.batch:
+        w = w.scaled(B=args.batch)
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
     m = None
@@ -422,7 +425,8 @@ def main():
 
     traffic = None
     pmc_path = os.path.join(ROOT, "profiles", f"traffic_{w.name}.json")
-    if os.path.exists(pmc_path):
+    # the record holds the workload's own bytes: none for another batch or map
+    if os.path.exists(pmc_path) and not args.batch and args.map_frac is None:
         with open(pmc_path) as f:
             rec = json.load(f)
         if rec.get("kernel_hash") == kernel_hash():
