@@ -90,8 +90,8 @@ __device__ __forceinline__ void slice_fix(uint32_t (&w)[NW], const uint32_t (&sh
 }
 
 // Stores without the nontemporal hint: rows of a mixed head are not whole
-// cache lines (gdn_large: 116 and 28 bytes), so a line is written by pieces
-// of several lanes and rows.  With the streaming hint a line left the L2
+// cache lines (115 int8 and 13 fp16 key channels: rows of 116 and 28
+// bytes), so a line is written by pieces of several lanes and rows.  With the streaming hint a line left the L2
 // part-written and was written again: counter-measured writes were 1.27x the
 // bytes stored and the step 2.7-3.2% slower; plain stores let the L2 merge
 // the pieces (writes equal the bytes stored).
