@@ -369,9 +369,11 @@ __device__ __forceinline__ void store_hp(uint8_t* p, int dt, const float (&f)[EP
 // overflows, is stored as zero.
 // ---------------------------------------------------------------------------
 
-// q / m rounded toward zero from its nearest value rn (q, m > 0, rn finite):
-// the residual q - rn * m is exact in one fma, and a negative one means rn
-// lies above the quotient, so the next float down is taken.
+// q / m rounded toward zero from an estimate rn within one unit in the last
+// place of it (q, m > 0, rn finite and positive): one of the two floats
+// around the quotient.  The residual q - rn * m is exact in one fma, and a
+// negative one means rn lies above the quotient, so the next float down is
+// taken.
 __device__ __forceinline__ float inv_toward_zero(float q, float m, float rn) {
   const float e = fmaf(-rn, m, q);
   return e < 0.0f ? __uint_as_float(__float_as_uint(rn) - 1u) : rn;

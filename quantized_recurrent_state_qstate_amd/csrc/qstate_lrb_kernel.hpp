@@ -369,9 +369,17 @@ __attribute__((amdgpu_waves_per_eu(lrb_min_waves<QB, RND, RANK, DELTA, DKEY>(), 
     }
   }
 
+  // Waves that hold neither a buffer row of W nor one of U (every thread
+  // from max(dv, dk) on: two of the four waves at dv = dk = 128) skip the
+  // per-thread buffer arithmetic below; their rows are zero, so they only
+  // add zeros to the block reductions, in which they still take part.
+  const bool act = (int)__builtin_amdgcn_readfirstlane((uint32_t)tid >> 6) * 64 < (dv > DK ? dv : DK);
+
   // 1. the buffer decays with the state (decay acts on the key side)
+  if (act) {
 #pragma unroll
-  for (int j = 0; j < RANK; ++j) Ur[j] = dd * Ur[j];
+    for (int j = 0; j < RANK; ++j) Ur[j] = dd * Ur[j];
+  }
 
   if constexpr (DELTA) {
     // the decayed buffer's part: W (U^T k); U's columns from n on are zero,
@@ -415,24 +423,33 @@ __attribute__((amdgpu_waves_per_eu(lrb_min_waves<QB, RND, RANK, DELTA, DKEY>(), 
   // Columns from n on are not part of the basis: zero them once here, so
   // every sum below runs over all RANK columns (their terms add exact zeros)
   // and no column test is needed.  U's columns from n on are zero already.
+  if (act) {
 #pragma unroll
-  for (int j = 0; j < RANK; ++j) Wr[j] = (j < n) ? Wr[j] : 0.0f;
+    for (int j = 0; j < RANK; ++j) Wr[j] = (j < n) ? Wr[j] : 0.0f;
+  }
 
   // 3. coefficients c = W^T u and g = max_v |u_v| / s_v
   float c[RANK];
   float g;
   {
     float p[RANK];
+    float gv = 0.0f;
 #pragma unroll
-    for (int j = 0; j < RANK; ++j) p[j] = Wr[j] * uv;
-    const float au = fabsf(uv);
-    const float gv = (so > 0.0f) ? au / so : (au > 0.0f ? __builtin_inff() : 0.0f);
+    for (int j = 0; j < RANK; ++j) p[j] = 0.0f;
+    if (act) {
+#pragma unroll
+      for (int j = 0; j < RANK; ++j) p[j] = Wr[j] * uv;
+      const float au = fabsf(uv);
+      gv = (so > 0.0f) ? au / so : (au > 0.0f ? __builtin_inff() : 0.0f);
+    }
     g = block_sum_vec<RANK>(p, tid < dv ? gv : 0.0f, c, P, red);
   }
   // remainder u_perp = u - W c, in column order
   float up = uv;
+  if (act) {
 #pragma unroll
-  for (int j = 0; j < RANK; ++j) up = fmaf(-c[j], Wr[j], up);
+    for (int j = 0; j < RANK; ++j) up = fmaf(-c[j], Wr[j], up);
+  }
 
   // 4. small key channels send c k_k into U
   bool sm = false;
@@ -444,12 +461,16 @@ __attribute__((amdgpu_waves_per_eu(lrb_min_waves<QB, RND, RANK, DELTA, DKEY>(), 
     }
   }
   if constexpr (BF) {   // the updated buffer in its storage format, before the merge test
+    if (act) {
 #pragma unroll
-    for (int j = 0; j < RANK; ++j) Ur[j] = round_bf16(Ur[j]);
+      for (int j = 0; j < RANK; ++j) Ur[j] = round_bf16(Ur[j]);
+    }
   }
-  // W transposed into LDS for the merge test and the rows
+  // W transposed into LDS for the merge test and the rows (rows below dv only)
+  if (act) {
 #pragma unroll
-  for (int j = 0; j < RANK; ++j) Wt[j][tid] = Wr[j];
+    for (int j = 0; j < RANK; ++j) Wt[j][tid] = Wr[j];
+  }
   if (tid < dv) {
     ul[tid] = uv;
     upl[tid] = up;
@@ -490,7 +511,11 @@ __attribute__((amdgpu_waves_per_eu(lrb_min_waves<QB, RND, RANK, DELTA, DKEY>(), 
   {
     float p[RANK];
 #pragma unroll
-    for (int j = 0; j < RANK; ++j) p[j] = Ur[j] * qq;   // all zero after a reset
+    for (int j = 0; j < RANK; ++j) p[j] = 0.0f;
+    if (act) {
+#pragma unroll
+      for (int j = 0; j < RANK; ++j) p[j] = Ur[j] * qq;   // all zero after a reset
+    }
     (void)block_sum_vec<RANK>(p, 0.0f, z, P, red);
   }
   if (tid < dv) {
@@ -532,7 +557,10 @@ __attribute__((amdgpu_waves_per_eu(lrb_min_waves<QB, RND, RANK, DELTA, DKEY>(), 
   // the lane's keys k0 .. k0 + EPL - 1 lie in one 64-bit word (EPL <= 32 divides 64)
   constexpr uint64_t kLaneBits = EPL == 32 ? 0xFFFFFFFFull : ((1ull << EPL) - 1ull);
   const uint32_t smask = (uint32_t)((smallw[k0 >> 6] >> (k0 & 63)) & kLaneBits);
-  const uint32_t mmask = (uint32_t)((mflagw[k0 >> 6] >> (k0 & 63)) & kLaneBits);
+  uint64_t mw = 0;   // some channel of the head merged on this step
+#pragma unroll
+  for (int w = 0; w < (DK + 63) / 64; ++w) mw |= mflagw[w];
+  const bool any_merge = __builtin_amdgcn_readfirstlane((uint32_t)((mw | (mw >> 32)) != 0)) != 0;
   uint8_t* gcode = const_cast<uint8_t*>(gc);
   auto row_step = [&](const int v, const uint32_t (&cw)[CW]) {
     const uint64_t row = bhs * (uint64_t)dv + (uint64_t)v;   // state row (Philox counter)
@@ -547,7 +575,13 @@ __attribute__((amdgpu_waves_per_eu(lrb_min_waves<QB, RND, RANK, DELTA, DKEY>(), 
       sh[i] = s_old * cf;
       sp[i] = fmaf(((smask >> i) & 1u) ? upv : uu, kf[i], (df[i] * s_old) * cf);
     }
-    if (mmask) {
+    if (any_merge) {   // workgroup-uniform
+      // The lane's merge flags are read here, past a compiler barrier, so
+      // that their per-key tests stay in this rare branch: as loop-invariant
+      // values of the whole kernel they were hoisted out of the row loop and
+      // cost two vector instructions per key on every step.
+      asm volatile("" ::: "memory");
+      const uint32_t mmask = (uint32_t)((mflagw[k0 >> 6] >> (k0 & 63)) & kLaneBits);
 #pragma unroll
       for (int i = 0; i < EPL; ++i)
         if ((mmask >> i) & 1u) {

@@ -118,15 +118,42 @@ __device__ __forceinline__ float div_by_q(float m) {
   return fmaf(r, RQ, q0);
 }
 
-// Row scale and inverse for one row, branch-free: scale = max/Q correctly
-// rounded, inv = Q/max rounded toward zero, invb = inv * 2^SRB; zero when the
-// nearest Q/max times 2^SRB overflows (max 0 gives Q/0 = inf).
+// Row scale and inverse for one row: scale = max/Q correctly rounded, inv =
+// Q/max rounded toward zero, invb = inv * 2^SRB; zero when the nearest Q/max
+// times 2^SRB overflows (max 0 gives Q/0 = inf).
+//
+// The overflow test is one compare: the nearest Q/m times 2^SRB is finite
+// exactly when m > Q 2^(SRB-128).  (It overflows when the nearest Q/m
+// reaches 2^(128-SRB), i.e. when Q/m reaches the midpoint 2^(128-SRB)
+// (1 - 2^-25) below it, and Q 2^(SRB-128) is the largest float m with Q/m at
+// or above that midpoint: the next float up is larger by more than a factor
+// 1 + 2^-25.)  Q 2^(SRB-128) is Q's bit pattern with the exponent lowered by
+// 128 - SRB, a normal float for both Q and every SRB used.
+//
+// inv needs no correctly rounded quotient: inv_toward_zero takes any
+// estimate within one unit in the last place of Q/m to the quotient rounded
+// toward zero.  v_rcp_f32 (within 1 ulp of 1/m for normal m whose reciprocal
+// is normal) and one Newton correction give such an estimate in 4
+// instructions instead of the IEEE division's 10, for m in [lo, 2^126];
+// rows outside that range (a max above 2^126, or, with SRB = 0, a Q/m within
+// a factor 4 of the float range's top, where Q * rcp(m) may overflow) take
+// the IEEE division, under a wave-uniform branch that never runs for
+// ordinary states.  The test suite checks the estimate path exhaustively on
+// the CPU for every float m in range, with the reciprocal taken as each of
+// the three floats nearest 1/m.
 template <int QB, int SRB>
 __device__ __forceinline__ void row_scale_fast(float m, float& scale, float& inv, float& invb) {
   constexpr float Q = (QB == 8) ? 127.0f : 7.0f;
-  const float i = Q / m;
-  const bool ok = __builtin_isfinite(i * (float)(1u << SRB));
-  const float iz = inv_toward_zero(Q, m, i);
+  constexpr uint32_t kQBits = (QB == 8) ? 0x42FE0000u : 0x40E00000u;   // bit pattern of Q
+  const float lim = __uint_as_float(kQBits - ((128u - (uint32_t)SRB) << 23));   // Q 2^(SRB-128)
+  const bool ok = m > lim;   // false for NaN
+  const float r = __builtin_amdgcn_rcpf(m);
+  const float q0 = Q * r;
+  float qf = fmaf(fmaf(-q0, m, Q), r, q0);
+  bool slow = m > 0x1p126f;
+  if constexpr (SRB == 0) slow = slow || (ok && m < Q * 0x1p-126f);
+  if (__ballot(slow)) qf = slow ? Q / m : qf;   // wave-uniform; not taken for ordinary rows
+  const float iz = inv_toward_zero(Q, m, qf);
   scale = ok ? div_by_q<QB>(m) : 0.0f;
   inv = ok ? iz : 0.0f;
   invb = ok ? iz * (float)(1u << SRB) : 0.0f;
