@@ -400,6 +400,85 @@ def test_protected_rounding_special_values(hp, mode):
     assert np.array_equal(got["codes"], ref["codes"])
 
 
+# Row maxima at the edges of the step's row-scale arithmetic: above 2^126
+# (the reciprocal estimate's range ends there and the IEEE division takes
+# over), on both sides of the overflow limit Q 2^(SRB-128) of the rounding
+# inverse, in the band (Q 2^-128, Q 2^-126) that nearest rounding also sends
+# to the division, subnormal and zero rows.
+EXTREME = {
+    "dense_int8_sr16": dict(kind="additive", qbits=8, rounding="stochastic"),
+    "dense_int8_rtn": dict(kind="additive", qbits=8, rounding="nearest"),
+    "dense_int4_rtn_headmap": dict(kind="additive", qbits=4, rounding="nearest", map_mode="head"),
+    "keymap_int8_sr16": dict(kind="additive", qbits=8, rounding="stochastic", map_mode="key"),
+    "delta_int8_sr16": dict(kind="delta", qbits=8, rounding="stochastic"),
+    "lrb_int4_rtn_bdr": dict(kind="additive", qbits=4, rounding="nearest", bdr=True, lrb_rank=8,
+                             lrb_period=64, lrb_theta=0.5),
+}
+
+
+def _extreme_rows(qbits, dv, dk, r):
+    Q = 127.0 if qbits == 8 else 7.0
+    f = np.float32
+    lims = [Q * 2.0 ** (srb - 128) for srb in (0, 8, 16)]
+    tops = [3.0e38, 1.0e38, 2.0 ** 126, float(np.nextafter(f(2.0 ** 126), f(np.inf))), 2.0 ** 125, 1.0]
+    near = []
+    for lim in lims + [Q * 2.0 ** -126]:
+        x = f(lim)
+        for k in range(-2, 3):
+            near.append(float(x) * (1.0 + k * 2.0 ** -23))
+    maxima = tops + near + [1e-40, 0.0]
+    rows = np.zeros((dv, dk), np.float32)
+    for v in range(dv):
+        mx = maxima[v % len(maxima)]
+        row = (r.random(dk) * 2.0 - 1.0) * mx
+        row[r.integers(dk)] = mx if v % 2 else -mx
+        rows[v] = row.astype(np.float32)
+    return rows
+
+
+@pytest.mark.parametrize("case", list(EXTREME))
+def test_row_scale_extreme_maxima(case):
+    kw = dict(EXTREME[case])
+    B, H, dk, dv = 1, 2, 64, 48
+    rounding = kw.pop("rounding")
+    m = None
+    if kw.get("map_mode") == "head":
+        m = np.array([0, 1], np.uint8)
+    elif kw.get("map_mode") == "key":
+        m = np.zeros((H, dk), np.uint8)
+        m[1, ::5] = 1
+    lcfg = StateConfig(B=B, H=H, dk=dk, dv=dv, decay_mode="head", in_dtype="fp32", rounding=rounding,
+                       sr_bits=16, map=m, seed=77, **kw)
+    ocfg = oracle.Cfg(B=B, H=H, dk=dk, dv=dv, decay_mode="head", rounding="rtn" if rounding == "nearest" else "sr",
+                      sr_bits=16, map=m, seed=77, **kw)
+    r = np.random.default_rng(11)
+    S = np.stack([_extreme_rows(kw["qbits"], dv, dk, r) for _ in range(B * H)]).reshape(B, H, dv, dk)
+    qs = QState(lcfg)
+    st = qs.new_state()
+    _log(f"[parity] extreme row maxima {case}")
+    qs.quantize(torch.from_numpy(S).to(DEV), st, step=0)
+    torch.cuda.synchronize()
+    ost = oracle.new_state(ocfg)
+    oracle.quantize(ocfg, S, ost, step=0)
+    got = gpu_state_to_oracle(st, ocfg.hp_dtype)
+    for key in ("codes", "scales", "hp"):
+        assert np.array_equal(got[key], ost[key]), f"{case}: quantize {key}"
+    exact = kw["kind"] == "additive" and not kw.get("lrb_rank")
+    zk = np.zeros((B, H, dk), np.float32)
+    for t, d in ((1, 1.0), (2, 0.5)):
+        # no update (k = 0): the step requantizes d * (dequantized state),
+        # so the row maxima stay at the edges above
+        inp = {"q": zk, "k": zk, "v": np.zeros((B, H, dv), np.float32), "decay": np.full((B, H), d, np.float32),
+               "beta": np.full((B, H), 0.5, np.float32) if kw["kind"] == "delta" else None}
+        ref = gpu_state_to_oracle(st, ocfg.hp_dtype)
+        o_ref = oracle.step(ocfg, ref, **inp, step=t)
+        o = qs.step(st, **{k: (None if v is None else torch.from_numpy(v).to(DEV)) for k, v in inp.items()},
+                    step=t)
+        torch.cuda.synchronize()
+        compare(ocfg, exact, ref, gpu_state_to_oracle(st, ocfg.hp_dtype), o_ref, o.cpu().numpy(),
+                what=f"{case} t={t}")
+
+
 def test_dequantize_with_buffer():
     w = WORKLOADS["gla_int4"]
     B = 2
