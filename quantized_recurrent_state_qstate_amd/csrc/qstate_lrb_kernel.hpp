@@ -254,6 +254,7 @@ __attribute__((amdgpu_waves_per_eu(lrb_min_waves<QB, RND, RANK, DELTA, DKEY>(), 
   float* const sl_ = P + 256;
   __shared__ float red[RANK + 4];
   __shared__ uint64_t smallw[4], mflagw[4];   // per-key flags, bit k of the DK-bit words
+  __shared__ uint64_t dbadw[4];               // keys whose decay lies outside [2^-20, 1]
 
   // the buffer factors and the row scales, fp32 or bf16 (BF)
   const uint64_t woff = bhs * (uint64_t)dv * (uint64_t)r, uoff = bhs * (uint64_t)DK * (uint64_t)r;
@@ -539,8 +540,10 @@ __attribute__((amdgpu_waves_per_eu(lrb_min_waves<QB, RND, RANK, DELTA, DKEY>(), 
   }
   {
     const uint64_t bs_ = __ballot(sm), bm_ = __ballot(merged);   // wave w: keys 64w .. 64w + 63
+    const uint64_t bd_ = __ballot(tid < DK && !(dd >= 0x1p-20f && dd <= 1.0f));
     if ((tid & 63) == 0 && tid < DK) {
       smallw[tid >> 6] = bs_;
+      dbadw[tid >> 6] = bd_;
       mflagw[tid >> 6] = bm_;
     }
   }
@@ -557,6 +560,10 @@ __attribute__((amdgpu_waves_per_eu(lrb_min_waves<QB, RND, RANK, DELTA, DKEY>(), 
   // the lane's keys k0 .. k0 + EPL - 1 lie in one 64-bit word (EPL <= 32 divides 64)
   constexpr uint64_t kLaneBits = EPL == 32 ? 0xFFFFFFFFull : ((1ull << EPL) - 1ull);
   const uint32_t smask = (uint32_t)((smallw[k0 >> 6] >> (k0 & 63)) & kLaneBits);
+  uint64_t dw = 0;   // some key's decay outside [2^-20, 1] (workgroup-uniform)
+#pragma unroll
+  for (int w = 0; w < (DK + 63) / 64; ++w) dw |= dbadw[w];
+  const bool dbad = __builtin_amdgcn_readfirstlane((uint32_t)((dw | (dw >> 32)) != 0)) != 0;
   uint64_t mw = 0;   // some channel of the head merged on this step
 #pragma unroll
   for (int w = 0; w < (DK + 63) / 64; ++w) mw |= mflagw[w];
@@ -567,13 +574,49 @@ __attribute__((amdgpu_waves_per_eu(lrb_min_waves<QB, RND, RANK, DELTA, DKEY>(), 
     const float s_old = sol[v];
     const float uu = ul[v], upv = upl[v];
     float sp[EPL], sh[EPL];
+    if constexpr (QB == 8 || DELTA) {
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      float cf;
-      if constexpr (QB == 8) cf = (float)(int32_t)(int8_t)(cw[i >> 2] >> (8 * (i & 3)));
-      else cf = (float)((int32_t)(cw[i >> 3] << (28 - 4 * (i & 7))) >> 28);
-      sh[i] = s_old * cf;
-      sp[i] = fmaf(((smask >> i) & 1u) ? upv : uu, kf[i], (df[i] * s_old) * cf);
+      for (int i = 0; i < EPL; ++i) {
+        float cf;
+        if constexpr (QB == 8) cf = (float)(int32_t)(int8_t)(cw[i >> 2] >> (8 * (i & 3)));
+        else cf = (float)((int32_t)(cw[i >> 3] << (28 - 4 * (i & 7))) >> 28);
+        sh[i] = s_old * cf;
+        sp[i] = fmaf(((smask >> i) & 1u) ? upv : uu, kf[i], (df[i] * s_old) * cf);
+      }
+    } else {
+      // int4 codes (additive kinds) as c/16 from v_cvt_off_f32_i4 (the low
+      // nibble of a selected byte: 9 instructions per 8 codes instead of a
+      // sign-extending extract and a conversion each), with the 16 moved into
+      // the row scale.  (Under the delta rule the same change measured 3%
+      // slower, so that instantiation keeps the extract.)
+      // (16 s) (c/16) is s c exactly, and (d (16 s)) (c/16) is (d s) c exactly
+      // while d s stays a normal float and 16 d s finite, which holds for
+      // s in [2^-100, 2^100] (or s = 0) and every decay of the head in [2^-20, 1].
+      // Other rows (a uniform branch, never taken by ordinary states) scale
+      // their codes back to c and keep s.
+      const bool fast = !dbad && ((s_old >= 0x1p-100f && s_old <= 0x1p100f) || s_old == 0.0f);
+      const bool anyslow = __ballot(!fast) != 0;
+      const float sf = fast ? 16.0f * s_old : s_old;
+#pragma unroll
+      for (int j = 0; j < EPL / 8; ++j) {
+        float cv[8];
+        const uint32_t wd = cw[j], wo = wd >> 4;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          cv[2 * b] = __builtin_amdgcn_cvt_off_f32_i4((int)((wd >> (8 * b)) & 0xFFu));
+          cv[2 * b + 1] = __builtin_amdgcn_cvt_off_f32_i4((int)((wo >> (8 * b)) & 0xFFu));
+        }
+        if (anyslow) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) cv[e] = fast ? cv[e] : 16.0f * cv[e];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int i = 8 * j + e;
+          sh[i] = sf * cv[e];
+          sp[i] = fmaf(((smask >> i) & 1u) ? upv : uu, kf[i], (df[i] * sf) * cv[e]);
+        }
+      }
     }
     if (any_merge) {   // workgroup-uniform
       // The lane's merge flags are read here, past a compiler barrier, so

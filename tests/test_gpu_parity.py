@@ -465,9 +465,11 @@ def test_row_scale_extreme_maxima(case):
         assert np.array_equal(got[key], ost[key]), f"{case}: quantize {key}"
     exact = kw["kind"] == "additive" and not kw.get("lrb_rank")
     zk = np.zeros((B, H, dk), np.float32)
-    for t, d in ((1, 1.0), (2, 0.5)):
+    for t, d in ((1, 1.0), (2, 0.5), (3, 1e-7)):
         # no update (k = 0): the step requantizes d * (dequantized state),
-        # so the row maxima stay at the edges above
+        # so the row maxima stay at the edges above; the last decay lies
+        # below the range in which the int4 buffer kernel moves the factor 16
+        # of its code conversion into the row scale (its other branch)
         inp = {"q": zk, "k": zk, "v": np.zeros((B, H, dv), np.float32), "decay": np.full((B, H), d, np.float32),
                "beta": np.full((B, H), 0.5, np.float32) if kw["kind"] == "delta" else None}
         ref = gpu_state_to_oracle(st, ocfg.hp_dtype)
